@@ -1,0 +1,41 @@
+"""CPU oracle for the ring AllReduce — TEST INFRASTRUCTURE ONLY.
+
+Nothing in the product imports this package.  It is used by the tests,
+by the entry point's smoke check and by the benchmark's CPU-baseline leg,
+and it shares no code with the HIP library (no kernels, headers, helpers,
+tables or constants).
+
+What it holds, each piece written from the pages on ring AllReduce:
+
+* ``ring``      the literal ring schedule executed on N host arrays with
+                FIFO mailboxes and byte counters (reduce-scatter then
+                all-gather, as stated on tirogla.com "Ring all-reduce",
+                section "How it works"), the standalone reduce-scatter and
+                all-gather, the element operators, bf16 round-to-nearest-even,
+                and the closed definition of the result (the ring's
+                association order) used for sampled checks at full size;
+* ``threaded``  one thread per rank with queue channels, the same program
+                the Rust listing on that page runs, with a receive time-out
+                that turns a stuck ring into an error;
+* ``explore``   brute force for tiny rings: every interleaving of the ranks'
+                send/receive events, and every bracketing of an N-term sum.
+
+Pins (what each part is checked against) are in ``tests/test_oracle_*.py``.
+Every function has a pin; none is "parity unpinned".
+"""
+
+from .ring import (  # noqa: F401
+    DTYPES,
+    OPS,
+    RingStats,
+    all_gather,
+    bf16_bits_to_f32,
+    chunk,
+    chunk_owner,
+    f32_to_bf16_bits,
+    reduce_op,
+    reduce_scatter,
+    ring_allreduce,
+    ring_order_fold,
+    ring_order_fold_columns,
+)
