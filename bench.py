@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark: ring AllReduce of 8 virtual ranks x 2^26 float32 (sum) on one MI355X.
+
+One step is one AllReduce through the fused one-pass kernel (the library's
+default algorithm) on synthetic N(0,1) inputs already resident in HBM.
+Prints one JSON line with algbw (S/t, the value), busbw (algbw * 2(N-1)/N),
+the kernel's HBM roofline and the CPU oracle timed on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Only one GPU is used: the N ranks are buffers in that GPU's memory.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "AllReduce algbw/busbw GB/s + % HBM peak, N=8 ranks x 64M fp32, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fused_allreduce_headline_counters.md")
+KERNEL_SOURCE = os.path.join(ROOT, "ring_allreduce_reduction_virtual_amd", "csrc", "ar_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def busbw_factor(coll: str, n: int) -> float:
+    """Bus bandwidth factor: 2(N-1)/N for AllReduce, (N-1)/N for one phase alone."""
+    return (2.0 if coll == "allreduce" else 1.0) * (n - 1) / n
+
+
+def algorithmic_bytes(coll: str, n: int, s_bytes: int) -> int:
+    """Minimum HBM traffic of one call: AllReduce reads N*S and writes N*S;
+    reduce-scatter reads N*S and writes S; all-gather reads S and writes N*S."""
+    return 2 * n * s_bytes if coll == "allreduce" else (n + 1) * s_bytes
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(per_launch_algo_bytes: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    m = re.search(r"^traffic_json: (\{.*\})\s*$", text, flags=re.M)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def ensure_library():
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+
+
+def time_calls(fn, steps: int, warmup: int, stream):
+    """Average milliseconds per call over `steps` calls, timed with HIP events on `stream`."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--no-extra", action="store_true", help="skip the ring / phase / copy side measurements")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the ring's N ranks are virtual, held as N buffers in "
+              "one GPU's HBM; there is no multi-GPU run", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    ensure_library()
+    import ring_allreduce_reduction_virtual_amd as ar
+    from inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS["headline"]
+    n, count = w.nranks, w.count
+    s_bytes = count * 4
+    log(f"[bench] device {torch.cuda.get_device_name(dev)}; workload N={n} x {count} f32 sum; drawing inputs")
+    t0 = time.perf_counter()
+    xs = make_inputs(w)
+    sends = [torch.from_numpy(x).to(dev) for x in xs]
+    recvs = [torch.empty(count, dtype=torch.float32, device=dev) for _ in range(n)]
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ar.ar_allreduce(sends, recvs)
+
+    # timed region: K AllReduce calls, synchronized on both sides
+    ms = time_calls(step, args.steps, args.warmup, stream)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
+    t_s = ms / 1e3
+    algbw = s_bytes / t_s / 1e9
+    busbw = algbw * busbw_factor("allreduce", n)
+    algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
+    hbm_gbps = algo_bytes / t_s / 1e9
+    log(f"[bench] fused AllReduce: {ms * 1e3:.1f} us/call (wall {wall_ms * 1e3:.1f} us), algbw {algbw:.1f} GB/s, "
+        f"busbw {busbw:.1f} GB/s, HBM {hbm_gbps:.0f} GB/s = {hbm_gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s")
+
+    # parity of the timed output: sampled positions against the oracle's fold
+    import oracle
+    from oracle.ring import chunk, chunk_owner, same_bits
+
+    rng = np.random.default_rng(12345)
+    pos = np.unique(np.concatenate([rng.integers(0, count, 2048)] +
+                                   [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1]) for c in range(n)]))
+    want = oracle.ring_order_fold_columns(np.stack([x[pos] for x in xs]), chunk_owner(pos, n, count))
+    idx = torch.from_numpy(pos).to(dev)
+    parity = all(same_bits(recvs[r][idx].cpu().numpy(), want, "f32") for r in range(n))
+    log(f"[bench] parity against the oracle at {len(pos)} sampled positions: {'pass' if parity else 'FAIL'}")
+
+    extra = {"wall_ms_per_step": round(wall_ms, 4)}
+    if not args.no_extra:
+        # the step-faithful ring mode and the phases alone, on the same buffers
+        ring_ms = time_calls(lambda: ar.ar_allreduce_ex(sends, recvs, algo="ring"), max(3, args.steps // 10), 1, stream)
+        extra["ring_mode_ms"] = round(ring_ms, 4)
+        extra["ring_mode_hbm_gbps_of_minimum"] = round(algo_bytes / (ring_ms / 1e3) / 1e9, 1)
+        shards = [recvs[r][slice(*chunk(r, n, count))] for r in range(n)]
+        rs_ms = time_calls(lambda: ar.ar_reduce_scatter(sends, shards), 20, 2, stream)
+        ag_ms = time_calls(lambda: ar.ar_all_gather(shards, sends), 20, 2, stream)
+        rs_bytes = algorithmic_bytes("reduce_scatter", n, s_bytes)
+        extra["reduce_scatter_ms"] = round(rs_ms, 4)
+        extra["reduce_scatter_hbm_gbps"] = round(rs_bytes / (rs_ms / 1e3) / 1e9, 1)
+        extra["all_gather_ms"] = round(ag_ms, 4)
+        extra["all_gather_hbm_gbps"] = round(rs_bytes / (ag_ms / 1e3) / 1e9, 1)
+        # a plain device-to-device copy of the same byte volume: the streaming ceiling for reference
+        src = torch.empty(n * count, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        copy_ms = time_calls(lambda: dst.copy_(src), 20, 2, stream)
+        extra["torch_copy_2x2GiB_hbm_gbps"] = round(2 * src.numel() * 4 / (copy_ms / 1e3) / 1e9, 1)
+        del src, dst
+        log(f"[bench] ring mode {ring_ms:.3f} ms; reduce-scatter {rs_ms:.3f} ms; all-gather {ag_ms:.3f} ms; "
+            f"torch copy {extra['torch_copy_2x2GiB_hbm_gbps']} GB/s")
+        # restore the inputs overwritten by the all-gather above
+        for r in range(n):
+            sends[r].copy_(torch.from_numpy(xs[r]).to(dev))
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        reps, spent = 0, 0.0
+        while reps < 3 and spent < 10.0:
+            t = time.perf_counter()
+            oracle.ring_allreduce(xs, check=False)
+            spent += time.perf_counter() - t
+            reps += 1
+        per = spent / reps
+        cpu = {"value": round(s_bytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the whole workload (8 ranks x 2^26 f32) through the oracle's executed ring schedule, "
+                         f"{reps} run(s), {per:.2f} s each, single-threaded numpy; host {cpu_model()}, "
+                         f"{len(os.sched_getaffinity(0))} cores available"}
+        log(f"[bench] CPU oracle: {per:.2f} s per AllReduce -> algbw {cpu['value']} GB/s (1 core)")
+
+    traffic = measured_traffic(algo_bytes)
+    out = {
+        "metric": METRIC,
+        "value": round(algbw, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "ring AllReduce, 8 virtual ranks x 2^26 float32 (256 MiB each), sum, fused kernel",
+                   "nranks": n, "count": count, "op": "sum", "algo": "fused", "inputs": "N(0,1), seed 1"},
+        "algbw_gbps": round(algbw, 2),
+        "busbw_gbps": round(busbw, 2),
+        "hbm_gbps": round(hbm_gbps, 1),
+        "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "k_fused_allreduce<f32,sum,vec16>",
+                     "algorithmic_bytes_per_launch": algo_bytes},
+        "cpu_baseline": cpu,
+        "parity": "pass" if parity else "fail",
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+    if not parity:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * ar.h — ring AllReduce over N virtual ranks resident in one GPU's HBM.
+ *
+ * C ABI of libar.so.  Every call is stateless ("State: none between calls",
+ * tirogla.com "Ring all-reduce", section "How it works", In/Out/State line)
+ * and asynchronous: it validates its arguments on the host, enqueues kernels
+ * on `stream` and returns.  The arguments follow the collective's statement
+ * on arjunsriva.com "AllReduce, All the Way Down", section "The Contract"
+ * (send buffer, receive buffer, count, datatype, reduction, participants,
+ * stream), with the communicator replaced by the number of virtual ranks and
+ * one send and one receive pointer per rank.
+ *
+ * Virtual rank r owns the device buffers sendbufs[r] and recvbufs[r].
+ * `count` is always the FULL per-rank length `len` in elements.  The ring
+ * cuts it into N chunks, chunk(c) = [c*len/N, (c+1)*len/N) with floor
+ * division (tirogla.com "Ring all-reduce", section "Code"); chunks may be
+ * uneven and, when len < N, empty.  cl(c) below is the length of chunk c.
+ *
+ * Result ("ring association order").  Element i of chunk c is reduced as it
+ * travels the ring from rank c: ((x_c (op) x_{c+1}) (op) x_{c+2}) ... with
+ * ranks taken mod N and the result rounded to the buffer type after every
+ * operation (arjunsriva.com, figure "Ring AllReduce · follow chunk 0";
+ * tirogla.com "Ring all-reduce", "How it works").  Both algorithms below give
+ * these bits exactly, and every rank receives identical bits.
+ *
+ * Pointers.  `sendbufs` and `recvbufs` are HOST arrays of `nranks` DEVICE
+ * pointers; the arrays are read during the call only and may be freed when
+ * it returns.  The device buffers are owned by the caller and must stay
+ * valid until the work enqueued on `stream` completes.  Buffers need only be
+ * aligned to their element size; when all the buffers a kernel streams share
+ * the same address residue modulo 16 bytes the kernels move 16-byte vectors,
+ * otherwise one element at a time (same results, lower bandwidth).
+ *
+ * Aliasing.  In place is allowed: AllReduce with sendbufs[r] == recvbufs[r];
+ * reduce-scatter with recvbufs[r] == sendbufs[r] + start(r) elements;
+ * all-gather with sendbufs[r] == recvbufs[r] + start(r) elements.  Receive
+ * buffers that overlap each other, or that overlap a send buffer in any
+ * other way, are rejected with AR_ERR_INVALID_ARGUMENT.
+ *
+ * Errors.  All validation happens before anything is enqueued; a call that
+ * returns an error has launched nothing.  count == 0 is a successful no-op.
+ * A HIP launch failure returns AR_ERR_HIP.  ar_get_last_error_detail()
+ * describes the most recent failure of the calling thread.
+ */
+#ifndef AR_H
+#define AR_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest number of virtual ranks one call accepts (the pointer tables travel
+ * in the kernel arguments). */
+#define AR_MAX_RANKS 128
+
+typedef enum {
+    AR_SUCCESS = 0,
+    AR_ERR_INVALID_ARGUMENT = 1,
+    AR_ERR_UNSUPPORTED = 2,
+    AR_ERR_HIP = 3,
+    AR_ERR_INTERNAL = 4
+} ar_result_t;
+
+/* Element types.  bf16 results are rounded to bf16 (nearest, ties to even)
+ * after every ring step, as a ring that keeps bf16 buffers does. */
+typedef enum {
+    AR_FLOAT32 = 0,
+    AR_BFLOAT16 = 1,
+    AR_INT32 = 2
+} ar_dtype_t;
+
+/* Reduction operators (sum, product, minimum, maximum: bitfern.com
+ * "AllReduce Explained", section "What Is AllReduce?").  int32 sum and
+ * product wrap modulo 2^32.  Float min/max are IEEE 754-2019 minimum and
+ * maximum: a NaN operand gives NaN, and -0 < +0. */
+typedef enum {
+    AR_SUM = 0,
+    AR_PROD = 1,
+    AR_MIN = 2,
+    AR_MAX = 3
+} ar_op_t;
+
+/* AR_ALGO_FUSED: one kernel reads element i from all N ranks, reduces it in
+ *   ring order and writes every output (N*S bytes read, N*S written for
+ *   AllReduce: the minimum).
+ * AR_ALGO_RING: the ring's steps one by one, one kernel launch per step:
+ *   N-1 reduce-scatter steps then N-1 all-gather steps, each rank adding the
+ *   chunk received from rank r-1 (tirogla.com "Ring all-reduce", "How it
+ *   works").  Same bits as the fused kernel. */
+typedef enum {
+    AR_ALGO_FUSED = 0,
+    AR_ALGO_RING = 1
+} ar_algo_t;
+
+typedef enum {
+    AR_COLL_ALLREDUCE = 0,
+    AR_COLL_REDUCE_SCATTER = 1,
+    AR_COLL_ALL_GATHER = 2
+} ar_coll_t;
+
+/* AllReduce (tirogla.com "Ring all-reduce"; "2.1 Collective communication
+ * primitives in detail", section 3.4): every recvbufs[r] (count elements)
+ * receives the reduction of all sendbufs[*] (count elements each).  Fused
+ * algorithm. */
+ar_result_t ar_allreduce(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                         ar_dtype_t dtype, ar_op_t op, int nranks, hipStream_t stream);
+
+/* Reduce-scatter ("2.1 Collective communication primitives in detail",
+ * section 3.5: rank i keeps reduced shard i): sendbufs[r] holds count
+ * elements; recvbufs[r] receives the cl(r) elements of chunk r of the
+ * reduction, packed.  The association order is AllReduce's, so
+ * all-gather after reduce-scatter reproduces AllReduce bit for bit.  Fused
+ * algorithm. */
+ar_result_t ar_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                              ar_dtype_t dtype, ar_op_t op, int nranks, hipStream_t stream);
+
+/* All-gather (ramchalamkr.github.io "NCCL Primitives Deep Dive", section
+ * "Ring All-Gather"; "2.1 ...", section 3.6): sendbufs[r] holds shard r,
+ * cl(r) elements; every recvbufs[r] (count elements) receives all shards
+ * concatenated in rank order.  No arithmetic.  Fused algorithm. */
+ar_result_t ar_all_gather(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                          ar_dtype_t dtype, int nranks, hipStream_t stream);
+
+/* The same three collectives with the algorithm chosen by the caller.
+ * `workspace` is device memory of at least ar_workspace_bytes(...) bytes
+ * owned by the caller (NULL when that size is 0); it must not overlap any
+ * buffer and must stay valid until the stream work completes.  Only the ring
+ * reduce-scatter with nranks >= 3 needs one: it holds the partial sums in
+ * flight between steps, since its receive buffers are only one shard long.
+ * The ring AllReduce and ring all-gather work in recvbufs. */
+ar_result_t ar_allreduce_ex(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                            ar_dtype_t dtype, ar_op_t op, int nranks, ar_algo_t algo,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+ar_result_t ar_reduce_scatter_ex(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                                 ar_dtype_t dtype, ar_op_t op, int nranks, ar_algo_t algo,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+ar_result_t ar_all_gather_ex(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                             ar_dtype_t dtype, int nranks, ar_algo_t algo,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace in bytes that a call with these arguments needs (0: none).
+ * Returns (size_t)-1 for invalid arguments. */
+size_t ar_workspace_bytes(ar_coll_t coll, ar_algo_t algo, size_t count, ar_dtype_t dtype, int nranks);
+
+/* Bounds of chunk c: *begin = c*count/nranks, *end = (c+1)*count/nranks
+ * (floor division in 64-bit integers; tirogla.com "Ring all-reduce",
+ * section "Code").  Host only; touches no device. */
+ar_result_t ar_chunk_range(int c, size_t count, int nranks, size_t* begin, size_t* end);
+
+/* Static text for a result code. */
+const char* ar_get_error_string(ar_result_t r);
+
+/* Description of the calling thread's most recent failed call ("" if none).
+ * The text stays valid until that thread's next call into the library. */
+const char* ar_get_last_error_detail(void);
+
+/* Size in bytes of one element of `dtype`, 0 if unknown. */
+size_t ar_dtype_size(ar_dtype_t dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AR_H */

@@ -4,10 +4,11 @@ This module is shared by the CPU oracle's tests, the GPU parity tests and
 the benchmark.  It only draws random numbers: it holds none of the
 collective's arithmetic (no chunking, no reduction, no rounding of sums).
 
-Each virtual rank ``r`` of a workload with seed ``s`` draws from its own
-PCG64 stream ``numpy.random.default_rng([s, r])``, values first and then
-(for the outlier workload) the outlier mask, so a rank's data does not
-depend on how many ranks are generated or in which order.
+Each virtual rank ``r`` of a workload with seed ``s`` draws its values from
+its own PCG64 stream ``numpy.random.default_rng([s, r])`` and (outlier
+workload only) its outlier mask from a second stream ``default_rng([s, r, 1])``,
+so a rank's data does not depend on how many ranks are generated or in which
+order, and a shortened buffer is exactly the head of the full-length one.
 
 Value recipes (the collective's pages name no dataset; gradient-like
 synthetic values stand in for "a gradient buffer on each worker"):
@@ -81,9 +82,8 @@ def _bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
 def make_rank(w: Workload, r: int, count: int | None = None) -> np.ndarray:
     """Draw rank ``r``'s buffer of workload ``w`` (``count`` overrides its length).
 
-    The first ``count`` elements are a prefix of the full-length draw for the
-    recipes that use one draw per element (all of them), so a shortened
-    workload is the head of the full one.
+    Every recipe draws element by element from per-rank streams, so the
+    first ``count`` elements equal the head of the full-length draw.
     """
     n = w.count if count is None else int(count)
     rng = np.random.default_rng([w.seed, r])
@@ -102,7 +102,7 @@ def make_rank(w: Workload, r: int, count: int | None = None) -> np.ndarray:
         return rng.integers(-(1 << 31), 1 << 31, size=n, dtype=np.int32)
     if w.values == "normal_outlier":
         x = rng.standard_normal(n, dtype=np.float32)
-        mask = rng.random(n, dtype=np.float32) < np.float32(0.01)
+        mask = np.random.default_rng([w.seed, r, 1]).random(n, dtype=np.float32) < np.float32(0.01)
         x[mask] *= np.float32(1e4)
         return x
     raise ValueError(f"unknown value recipe {w.values!r}")

@@ -1,0 +1,467 @@
+// Host side of libar.so: the C ABI declared in include/ar.h.
+//
+// Each entry point validates everything first (so an error launches
+// nothing), plans the launch (vector or element path, tiles per chunk, grid)
+// and enqueues kernels from ar_kernels.hip on the caller's stream.  No state
+// is kept between calls apart from a per-device cache of the compute-unit
+// count and the calling thread's last error text.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+#include <vector>
+
+#include "ar.h"
+#include "ar_internal.h"
+
+using arimpl::Kind;
+using arimpl::KernelArgs;
+using arimpl::Launch;
+
+namespace {
+
+thread_local std::string g_detail;
+
+ar_result_t fail(ar_result_t code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return code;
+}
+
+bool debug_enabled() {
+    static const bool on = [] {
+        const char* v = std::getenv("AR_DEBUG");
+        return v != nullptr && v[0] != '\0' && v[0] != '0';
+    }();
+    return on;
+}
+
+// Blocks launched per compute unit for the grid-stride kernels; 0 launches
+// one block per tile.  AR_BLOCKS_PER_CU overrides the default.
+unsigned blocks_per_cu() {
+    static const unsigned v = [] {
+        const char* e = std::getenv("AR_BLOCKS_PER_CU");
+        if (e != nullptr && e[0] != '\0') return static_cast<unsigned>(std::strtoul(e, nullptr, 10));
+        return 8u;
+    }();
+    return v;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+ar_result_t cu_count(int* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(AR_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *out = cached;
+            return AR_SUCCESS;
+        }
+    }
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(AR_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    if (cus <= 0) cus = 1;
+    if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    *out = cus;
+    return AR_SUCCESS;
+}
+
+size_t esize(ar_dtype_t dt) {
+    switch (dt) {
+        case AR_FLOAT32: return 4;
+        case AR_BFLOAT16: return 2;
+        case AR_INT32: return 4;
+    }
+    return 0;
+}
+
+const char* dtype_name(ar_dtype_t dt) {
+    switch (dt) {
+        case AR_FLOAT32: return "f32";
+        case AR_BFLOAT16: return "bf16";
+        case AR_INT32: return "i32";
+    }
+    return "?";
+}
+
+// Chunk bounds in 64-bit integers; c*count cannot overflow because count is
+// validated to be below 2^64 / AR_MAX_RANKS.
+inline uint64_t chunk_start(int c, uint64_t count, int n) {
+    return static_cast<uint64_t>(c) * count / static_cast<uint64_t>(n);
+}
+
+struct Interval {
+    uintptr_t lo, hi;
+    bool writable;
+    int rank;
+    int role;   // 0 send, 1 recv, 2 workspace
+};
+
+// Reject overlaps other than read-only buffers overlapping each other and the
+// exact in-place layouts the collective allows (checked by the caller and
+// passed in as `allowed(send_rank, recv_rank)`).
+template <typename Allowed>
+ar_result_t check_overlaps(std::vector<Interval>& v, Allowed allowed) {
+    std::sort(v.begin(), v.end(), [](const Interval& a, const Interval& b) { return a.lo < b.lo; });
+    std::vector<const Interval*> active;
+    for (const Interval& cur : v) {
+        active.erase(std::remove_if(active.begin(), active.end(),
+                                    [&](const Interval* x) { return x->hi <= cur.lo; }),
+                     active.end());
+        for (const Interval* x : active) {
+            if (!x->writable && !cur.writable) continue;
+            const Interval* s = x->role == 0 ? x : (cur.role == 0 ? &cur : nullptr);
+            const Interval* r = x->role == 1 ? x : (cur.role == 1 ? &cur : nullptr);
+            if (s != nullptr && r != nullptr && s != r && allowed(*s, *r)) continue;
+            static const char* names[] = {"sendbufs", "recvbufs", "workspace"};
+            return fail(AR_ERR_INVALID_ARGUMENT, "%s[%d] overlaps %s[%d]", names[x->role], x->rank,
+                        names[cur.role], cur.rank);
+        }
+        active.push_back(&cur);
+    }
+    return AR_SUCCESS;
+}
+
+struct Common {
+    const void* const* send;
+    void* const* recv;
+    uint64_t count;
+    ar_dtype_t dtype;
+    ar_op_t op;
+    int n;
+    size_t esz;
+};
+
+ar_result_t check_common(const Common& k, bool has_op) {
+    g_detail.clear();
+    if (k.esz == 0) return fail(AR_ERR_INVALID_ARGUMENT, "unknown dtype %d", static_cast<int>(k.dtype));
+    if (has_op && (k.op < AR_SUM || k.op > AR_MAX)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown op %d", static_cast<int>(k.op));
+    if (k.n < 1 || k.n > AR_MAX_RANKS) return fail(AR_ERR_INVALID_ARGUMENT, "nranks %d outside [1, %d]", k.n, AR_MAX_RANKS);
+    if (k.send == nullptr || k.recv == nullptr) return fail(AR_ERR_INVALID_ARGUMENT, "null pointer array");
+    if (k.count > (UINT64_MAX / AR_MAX_RANKS) / 16) return fail(AR_ERR_INVALID_ARGUMENT, "count %llu too large",
+                                                               static_cast<unsigned long long>(k.count));
+    return AR_SUCCESS;
+}
+
+// Bytes a buffer of `elems` elements spans; null is allowed only when empty.
+ar_result_t check_ptr(const void* p, uint64_t elems, size_t esz, const char* what, int r) {
+    if (elems == 0) return AR_SUCCESS;
+    if (p == nullptr) return fail(AR_ERR_INVALID_ARGUMENT, "%s[%d] is null", what, r);
+    if (reinterpret_cast<uintptr_t>(p) % esz != 0)
+        return fail(AR_ERR_INVALID_ARGUMENT, "%s[%d] not aligned to its %zu-byte element", what, r, esz);
+    return AR_SUCCESS;
+}
+
+// Common residue modulo 16 bytes of a set of addresses, or -1.
+int common_residue(const std::vector<uintptr_t>& ptrs) {
+    if (ptrs.empty()) return 0;
+    const int r0 = static_cast<int>(ptrs[0] & 15u);
+    for (uintptr_t p : ptrs) {
+        if (static_cast<int>(p & 15u) != r0) return -1;
+    }
+    return r0;
+}
+
+void fill_tables(KernelArgs& a, const Common& k) {
+    for (int r = 0; r < k.n; ++r) {
+        a.send[r] = static_cast<const char*>(k.send[r]);
+        a.recv[r] = static_cast<char*>(k.recv[r]);
+    }
+    a.count = k.count;
+    a.nranks = k.n;
+    a.step = 0;
+    a.shift = 0;
+    a.ofs = 0;
+    a.ws = nullptr;
+}
+
+// Tiles per chunk and grid size for a launch on the current device.
+ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, int residue) {
+    l.vec = residue >= 0;
+    a.ofs = l.vec ? static_cast<int32_t>(residue / static_cast<int>(k.esz)) : 0;
+    const uint64_t n = static_cast<uint64_t>(k.n);
+    const uint64_t max_chunk = (k.count + n - 1) / n;
+    const uint64_t per_unit = l.vec ? 16 / k.esz : 1;
+    const uint64_t units = max_chunk / per_unit + 1;
+    const uint64_t tile_units = static_cast<uint64_t>(arimpl::kThreads) * arimpl::kUnroll;
+    const uint64_t tpc = std::max<uint64_t>(1, (units + tile_units - 1) / tile_units);
+    if (tpc > UINT32_MAX) return fail(AR_ERR_INVALID_ARGUMENT, "buffer too large");
+    a.tiles_per_chunk = static_cast<uint32_t>(tpc);
+    int cus = 0;
+    const ar_result_t rc = cu_count(&cus);
+    if (rc != AR_SUCCESS) return rc;
+    const uint64_t tiles = n * tpc;
+    const unsigned bpc = blocks_per_cu();
+    uint64_t blocks = bpc == 0 ? tiles : std::min<uint64_t>(tiles, static_cast<uint64_t>(cus) * bpc);
+    blocks = std::min<uint64_t>(blocks, 0x7fffffffu);
+    l.blocks = static_cast<unsigned>(blocks);
+    return AR_SUCCESS;
+}
+
+const char* kind_name(Kind kd) {
+    switch (kd) {
+        case Kind::kFusedAllReduce: return "fused_allreduce";
+        case Kind::kFusedReduceScatter: return "fused_reduce_scatter";
+        case Kind::kFusedAllGather: return "fused_all_gather";
+        case Kind::kPlaceShards: return "place_shards";
+        case Kind::kRingReduceStep: return "ring_reduce_step";
+        case Kind::kRingReduceStepWs: return "ring_reduce_step_ws";
+        case Kind::kRingCopyStep: return "ring_copy_step";
+    }
+    return "?";
+}
+
+ar_result_t enqueue(Launch& l, Kind kind, const KernelArgs& a, const Common& k, hipStream_t stream) {
+    l.kind = kind;
+    l.dtype = k.dtype;
+    l.op = k.op;
+    if (debug_enabled()) {
+        std::fprintf(stderr,
+                     "[ar] %s dtype=%s op=%d n=%d count=%llu step=%d shift=%d vec=%d ofs=%d tiles/chunk=%u blocks=%u\n",
+                     kind_name(kind), dtype_name(k.dtype), static_cast<int>(k.op), k.n,
+                     static_cast<unsigned long long>(k.count), a.step, a.shift, l.vec ? 1 : 0, a.ofs,
+                     a.tiles_per_chunk, l.blocks);
+    }
+    const hipError_t e = arimpl::launch(l, a, stream);
+    if (e != hipSuccess) return fail(AR_ERR_HIP, "%s launch: %s", kind_name(kind), hipGetErrorString(e));
+    return AR_SUCCESS;
+}
+
+// ---------------------------------------------------------------------------
+
+ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, hipStream_t stream) {
+    ar_result_t rc = check_common(k, true);
+    if (rc != AR_SUCCESS) return rc;
+    if (algo != AR_ALGO_FUSED && algo != AR_ALGO_RING) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+    std::vector<Interval> iv;
+    std::vector<uintptr_t> ptrs;
+    const uint64_t bytes = k.count * k.esz;
+    for (int r = 0; r < k.n; ++r) {
+        if ((rc = check_ptr(k.send[r], k.count, k.esz, "sendbufs", r)) != AR_SUCCESS) return rc;
+        if ((rc = check_ptr(k.recv[r], k.count, k.esz, "recvbufs", r)) != AR_SUCCESS) return rc;
+        const uintptr_t s = reinterpret_cast<uintptr_t>(k.send[r]);
+        const uintptr_t d = reinterpret_cast<uintptr_t>(k.recv[r]);
+        if (bytes) {
+            iv.push_back({s, s + bytes, false, r, 0});
+            iv.push_back({d, d + bytes, true, r, 1});
+        }
+        ptrs.push_back(s);
+        ptrs.push_back(d);
+    }
+    rc = check_overlaps(iv, [&](const Interval& s, const Interval& d) {
+        return s.rank == d.rank && s.lo == d.lo;   // in place: send[r] == recv[r]
+    });
+    if (rc != AR_SUCCESS) return rc;
+    if (k.count == 0) return AR_SUCCESS;
+
+    KernelArgs a{};
+    Launch l{};
+    fill_tables(a, k);
+    if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
+    if (algo == AR_ALGO_FUSED || k.n == 1) return enqueue(l, Kind::kFusedAllReduce, a, k, stream);
+    for (int s = 0; s < k.n - 1; ++s) {          // reduce-scatter steps
+        a.step = s;
+        if ((rc = enqueue(l, Kind::kRingReduceStep, a, k, stream)) != AR_SUCCESS) return rc;
+    }
+    for (int s = 0; s < k.n - 1; ++s) {          // all-gather steps
+        a.step = s;
+        a.shift = 0;
+        if ((rc = enqueue(l, Kind::kRingCopyStep, a, k, stream)) != AR_SUCCESS) return rc;
+    }
+    return AR_SUCCESS;
+}
+
+uint64_t rs_workspace_bytes(uint64_t count, size_t esz, int n, ar_algo_t algo) {
+    if (algo != AR_ALGO_RING || n < 3 || count == 0) return 0;
+    return count * esz + 32;   // one full-length buffer of partials, plus room to match residues
+}
+
+ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_bytes, hipStream_t stream) {
+    ar_result_t rc = check_common(k, true);
+    if (rc != AR_SUCCESS) return rc;
+    if (algo != AR_ALGO_FUSED && algo != AR_ALGO_RING) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+    std::vector<Interval> iv;
+    std::vector<uintptr_t> ptrs;
+    const uint64_t bytes = k.count * k.esz;
+    for (int r = 0; r < k.n; ++r) {
+        const uint64_t st = chunk_start(r, k.count, k.n);
+        const uint64_t cl = chunk_start(r + 1, k.count, k.n) - st;
+        if ((rc = check_ptr(k.send[r], k.count, k.esz, "sendbufs", r)) != AR_SUCCESS) return rc;
+        if ((rc = check_ptr(k.recv[r], cl, k.esz, "recvbufs", r)) != AR_SUCCESS) return rc;
+        const uintptr_t s = reinterpret_cast<uintptr_t>(k.send[r]);
+        const uintptr_t d = reinterpret_cast<uintptr_t>(k.recv[r]);
+        if (bytes) iv.push_back({s, s + bytes, false, r, 0});
+        if (cl) iv.push_back({d, d + cl * k.esz, true, r, 1});
+        ptrs.push_back(s);
+    }
+    const uint64_t need = rs_workspace_bytes(k.count, k.esz, k.n, algo);
+    if (need) {
+        if (ws == nullptr || ws_bytes < need)
+            return fail(AR_ERR_INVALID_ARGUMENT, "ring reduce-scatter needs a workspace of %llu bytes",
+                        static_cast<unsigned long long>(need));
+        const uintptr_t w = reinterpret_cast<uintptr_t>(ws);
+        iv.push_back({w, w + need, true, 0, 2});
+    }
+    rc = check_overlaps(iv, [&](const Interval& s, const Interval& d) {
+        // in place: recv[r] == send[r] + start(r) elements
+        return s.rank == d.rank && d.lo == s.lo + chunk_start(d.rank, k.count, k.n) * k.esz;
+    });
+    if (rc != AR_SUCCESS) return rc;
+    if (k.count == 0) return AR_SUCCESS;
+
+    KernelArgs a{};
+    Launch l{};
+    fill_tables(a, k);
+    const int residue = common_residue(ptrs);
+    if ((rc = plan(a, l, k, residue)) != AR_SUCCESS) return rc;
+    if (algo == AR_ALGO_FUSED || k.n == 1) return enqueue(l, Kind::kFusedReduceScatter, a, k, stream);
+    if (need) {
+        // place the partials at the senders' residue so they stream as 16-byte vectors too
+        const uintptr_t w = (reinterpret_cast<uintptr_t>(ws) + 15u) & ~static_cast<uintptr_t>(15u);
+        a.ws = reinterpret_cast<char*>(w + static_cast<uintptr_t>(residue >= 0 ? residue : 0));
+    }
+    for (int s = 0; s < k.n - 1; ++s) {
+        a.step = s;
+        if ((rc = enqueue(l, Kind::kRingReduceStepWs, a, k, stream)) != AR_SUCCESS) return rc;
+    }
+    return AR_SUCCESS;
+}
+
+ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, hipStream_t stream) {
+    ar_result_t rc = check_common(k, false);
+    if (rc != AR_SUCCESS) return rc;
+    if (algo != AR_ALGO_FUSED && algo != AR_ALGO_RING) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+    std::vector<Interval> iv;
+    std::vector<uintptr_t> ptrs;
+    const uint64_t bytes = k.count * k.esz;
+    for (int r = 0; r < k.n; ++r) {
+        const uint64_t st = chunk_start(r, k.count, k.n);
+        const uint64_t cl = chunk_start(r + 1, k.count, k.n) - st;
+        if ((rc = check_ptr(k.send[r], cl, k.esz, "sendbufs", r)) != AR_SUCCESS) return rc;
+        if ((rc = check_ptr(k.recv[r], k.count, k.esz, "recvbufs", r)) != AR_SUCCESS) return rc;
+        const uintptr_t s = reinterpret_cast<uintptr_t>(k.send[r]);
+        const uintptr_t d = reinterpret_cast<uintptr_t>(k.recv[r]);
+        if (cl) iv.push_back({s, s + cl * k.esz, false, r, 0});
+        if (bytes) iv.push_back({d, d + bytes, true, r, 1});
+        ptrs.push_back(d);
+    }
+    rc = check_overlaps(iv, [&](const Interval& s, const Interval& d) {
+        // in place: send[r] == recv[r] + start(r) elements
+        return s.rank == d.rank && s.lo == d.lo + chunk_start(s.rank, k.count, k.n) * k.esz;
+    });
+    if (rc != AR_SUCCESS) return rc;
+    if (k.count == 0) return AR_SUCCESS;
+
+    KernelArgs a{};
+    Launch l{};
+    fill_tables(a, k);
+    if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
+    if (algo == AR_ALGO_FUSED || k.n == 1) return enqueue(l, Kind::kFusedAllGather, a, k, stream);
+    if ((rc = enqueue(l, Kind::kPlaceShards, a, k, stream)) != AR_SUCCESS) return rc;
+    for (int s = 0; s < k.n - 1; ++s) {
+        a.step = s;
+        a.shift = 1;
+        if ((rc = enqueue(l, Kind::kRingCopyStep, a, k, stream)) != AR_SUCCESS) return rc;
+    }
+    return AR_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+ar_result_t ar_allreduce(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
+                         ar_op_t op, int nranks, hipStream_t stream) {
+    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, AR_ALGO_FUSED, stream);
+}
+
+ar_result_t ar_allreduce_ex(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
+                            ar_op_t op, int nranks, ar_algo_t algo, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, stream);
+}
+
+ar_result_t ar_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
+                              ar_op_t op, int nranks, hipStream_t stream) {
+    return reduce_scatter_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, AR_ALGO_FUSED,
+                               nullptr, 0, stream);
+}
+
+ar_result_t ar_reduce_scatter_ex(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                                 ar_dtype_t dtype, ar_op_t op, int nranks, ar_algo_t algo, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    return reduce_scatter_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, workspace,
+                               workspace_bytes, stream);
+}
+
+ar_result_t ar_all_gather(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
+                          int nranks, hipStream_t stream) {
+    return all_gather_impl({sendbufs, recvbufs, count, dtype, AR_SUM, nranks, esize(dtype)}, AR_ALGO_FUSED, stream);
+}
+
+ar_result_t ar_all_gather_ex(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
+                             int nranks, ar_algo_t algo, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return all_gather_impl({sendbufs, recvbufs, count, dtype, AR_SUM, nranks, esize(dtype)}, algo, stream);
+}
+
+size_t ar_workspace_bytes(ar_coll_t coll, ar_algo_t algo, size_t count, ar_dtype_t dtype, int nranks) {
+    const size_t e = esize(dtype);
+    if (e == 0 || nranks < 1 || nranks > AR_MAX_RANKS || (algo != AR_ALGO_FUSED && algo != AR_ALGO_RING) ||
+        count > (UINT64_MAX / AR_MAX_RANKS) / 16)
+        return static_cast<size_t>(-1);
+    switch (coll) {
+        case AR_COLL_ALLREDUCE:
+        case AR_COLL_ALL_GATHER:
+            return 0;
+        case AR_COLL_REDUCE_SCATTER:
+            return static_cast<size_t>(rs_workspace_bytes(count, e, nranks, algo));
+    }
+    return static_cast<size_t>(-1);
+}
+
+ar_result_t ar_chunk_range(int c, size_t count, int nranks, size_t* begin, size_t* end) {
+    g_detail.clear();
+    if (nranks < 1 || nranks > AR_MAX_RANKS) return fail(AR_ERR_INVALID_ARGUMENT, "nranks %d outside [1, %d]", nranks, AR_MAX_RANKS);
+    if (c < 0 || c >= nranks) return fail(AR_ERR_INVALID_ARGUMENT, "chunk %d outside [0, %d)", c, nranks);
+    if (begin == nullptr || end == nullptr) return fail(AR_ERR_INVALID_ARGUMENT, "null output pointer");
+    if (count > (UINT64_MAX / AR_MAX_RANKS) / 16) return fail(AR_ERR_INVALID_ARGUMENT, "count too large");
+    *begin = static_cast<size_t>(chunk_start(c, count, nranks));
+    *end = static_cast<size_t>(chunk_start(c + 1, count, nranks));
+    return AR_SUCCESS;
+}
+
+const char* ar_get_error_string(ar_result_t r) {
+    switch (r) {
+        case AR_SUCCESS: return "success";
+        case AR_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case AR_ERR_UNSUPPORTED: return "unsupported";
+        case AR_ERR_HIP: return "HIP runtime error";
+        case AR_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown result code";
+}
+
+const char* ar_get_last_error_detail(void) { return g_detail.c_str(); }
+
+size_t ar_dtype_size(ar_dtype_t dtype) { return esize(dtype); }
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal interface between the host entry points (ar_api.hip) and the
+// kernels (ar_kernels.hip).  Not installed; include/ar.h is the public ABI.
+#pragma once
+
+#include <cstdint>
+
+#include "ar.h"
+
+namespace arimpl {
+
+constexpr int kThreads = 256;   // threads per block: four 64-wide wavefronts
+
+// What one launch does.
+enum class Kind : int {
+    kFusedAllReduce = 0,   // reduce element i over all ranks, store to every rank
+    kFusedReduceScatter,   // reduce element i over all ranks, store to the owner's shard
+    kFusedAllGather,       // copy shard c to position start(c) of every rank
+    kPlaceShards,          // copy shard c to position start(c) of rank c only
+    kRingReduceStep,       // AllReduce ring, reduce-scatter step `step`
+    kRingReduceStepWs,     // reduce-scatter ring, step `step`, partials in the workspace
+    kRingCopyStep,         // all-gather ring step `step` (rank mapping shifted by `shift`)
+};
+
+// Kernel arguments, passed by value.  Pointers are the callers' device
+// addresses.  On the vector path every streamed full-length buffer p has the
+// same residue `ofs` elements modulo 16 bytes, so its 16-byte vector v starts
+// at (p - ofs elements) + 16*v and holds elements [v*V - ofs, (v+1)*V - ofs),
+// V = 16 / element size.
+struct KernelArgs {
+    const char* send[AR_MAX_RANKS];
+    char* recv[AR_MAX_RANKS];
+    char* ws;                  // workspace for kRingReduceStepWs (already residue-adjusted)
+    uint64_t count;            // elements per rank (full length)
+    uint32_t tiles_per_chunk;  // grid tiles that cover one chunk's body
+    int32_t nranks;
+    int32_t step;              // ring step s
+    int32_t shift;             // kRingCopyStep: acting rank = (c + step + shift) mod N
+    int32_t ofs;               // common element residue of the streamed buffers (vector path)
+};
+
+struct Launch {
+    Kind kind;
+    ar_dtype_t dtype;
+    ar_op_t op;
+    bool vec;                  // 16-byte vector path (all streamed buffers share a residue)
+    unsigned blocks;
+};
+
+// Vectors of 16 bytes each thread handles per tile.
+constexpr int kUnroll = 2;
+
+// Enqueue one kernel; returns the HIP error of the launch.
+hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream);
+
+}  // namespace arimpl

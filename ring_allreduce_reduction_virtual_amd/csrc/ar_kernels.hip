@@ -1,0 +1,679 @@
+// HIP kernels (gfx950) for the ring AllReduce over N virtual ranks held in
+// one GPU's HBM.
+//
+// Every kernel walks the buffer chunk by chunk, chunk(c) =
+// [c*len/N, (c+1)*len/N) (tirogla.com "Ring all-reduce", section "Code"), so
+// the chunk index c, and with it the ring rotation that decides which rank's
+// buffer is read first, is the same for a whole block: the per-rank pointers
+// are picked with scalar loads from the kernel arguments and the fold over
+// ranks is a fixed sequence, never a register-indexed rotation.
+//
+// The work is a pure stream through HBM (one add per element per rank), so
+// there is no LDS staging and no MFMA: each thread moves 16-byte vectors,
+// `kUnroll` of them per rank per tile, issues a batch of up to `kBatch` ranks'
+// loads before it folds them in ring order, and writes results with
+// nontemporal stores.  Chunk edges that are not 16-byte aligned (uneven
+// chunks start anywhere) are done one element at a time by the first tile of
+// the chunk.
+//
+// Arithmetic follows the ring's association order exactly: element i of
+// chunk c is ((x_c (op) x_{c+1}) (op) x_{c+2}) ... (arjunsriva.com
+// "AllReduce, All the Way Down", figure "Ring AllReduce · follow chunk 0"),
+// one rounding per operation, no contraction (built with -ffp-contract=off),
+// bf16 rounded to nearest-even after every operation.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "ar_internal.h"
+
+namespace arimpl {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBatch = 8;   // ranks whose loads are in flight together
+
+template <int DT>
+constexpr int elem_size() { return DT == AR_BFLOAT16 ? 2 : 4; }
+
+// ---------------------------------------------------------------------------
+// element arithmetic
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// IEEE binary32 operations, round to nearest even.  min/max are IEEE
+// 754-2019 minimum/maximum: NaN if either operand is NaN, and for equal
+// operands the sign bits decide (-0 below +0).
+template <int OP>
+__device__ __forceinline__ float f32_apply(float a, float b) {
+    if constexpr (OP == AR_SUM) {
+        return a + b;
+    } else if constexpr (OP == AR_PROD) {
+        return a * b;
+    } else if constexpr (OP == AR_MIN) {
+        const float lo = (a < b) ? a : b;
+        const float tie = as_f(as_u(a) | as_u(b));
+        const float r = (a == b) ? tie : lo;
+        return (a != a || b != b) ? as_f(0x7fc00000u) : r;
+    } else {
+        const float hi = (a > b) ? a : b;
+        const float tie = as_f(as_u(a) & as_u(b));
+        const float r = (a == b) ? tie : hi;
+        return (a != a || b != b) ? as_f(0x7fc00000u) : r;
+    }
+}
+
+// int32: sum and product wrap modulo 2^32 (unsigned arithmetic).
+template <int OP>
+__device__ __forceinline__ uint32_t i32_apply(uint32_t a, uint32_t b) {
+    if constexpr (OP == AR_SUM) {
+        return a + b;
+    } else if constexpr (OP == AR_PROD) {
+        return a * b;
+    } else if constexpr (OP == AR_MIN) {
+        return (static_cast<int32_t>(a) < static_cast<int32_t>(b)) ? a : b;
+    } else {
+        return (static_cast<int32_t>(a) > static_cast<int32_t>(b)) ? a : b;
+    }
+}
+
+// bf16 bits are the upper half of the float32 with the same value.
+__device__ __forceinline__ float bf16_widen(uint32_t h) { return as_f(h << 16); }
+
+// float32 -> bf16, nearest with ties to even: adding 0x7FFF plus the last
+// kept bit carries into the upper half exactly when the dropped half is above
+// one half ulp, or equal to it with an odd last bit.  NaN -> quiet NaN.
+__device__ __forceinline__ uint32_t bf16_round(float f) {
+    const uint32_t u = as_u(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x40u;
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded;
+}
+
+template <int DT, int OP>
+struct Red {
+    // one element held in the low bits of a 32-bit value
+    static __device__ __forceinline__ uint32_t elem(uint32_t a, uint32_t b) {
+        if constexpr (DT == AR_FLOAT32) {
+            return as_u(f32_apply<OP>(as_f(a), as_f(b)));
+        } else if constexpr (DT == AR_INT32) {
+            return i32_apply<OP>(a, b);
+        } else {
+            return bf16_round(f32_apply<OP>(bf16_widen(a & 0xffffu), bf16_widen(b & 0xffffu)));
+        }
+    }
+    // one 32-bit word: one f32/i32 element or two bf16 elements
+    static __device__ __forceinline__ uint32_t word(uint32_t a, uint32_t b) {
+        if constexpr (DT == AR_BFLOAT16) {
+            return elem(a, b) | (elem(a >> 16, b >> 16) << 16);
+        } else {
+            return elem(a, b);
+        }
+    }
+    static __device__ __forceinline__ u32x4 vec(u32x4 a, u32x4 b) {
+        u32x4 r;
+        r.x = word(a.x, b.x);
+        r.y = word(a.y, b.y);
+        r.z = word(a.z, b.z);
+        r.w = word(a.w, b.w);
+        return r;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// memory access
+// ---------------------------------------------------------------------------
+
+template <int ESZ>
+__device__ __forceinline__ uint32_t load_elem(const char* p) {
+    if constexpr (ESZ == 2) {
+        return *reinterpret_cast<const uint16_t*>(p);
+    } else {
+        return *reinterpret_cast<const uint32_t*>(p);
+    }
+}
+
+template <int ESZ>
+__device__ __forceinline__ void store_elem(char* p, uint32_t v) {
+    if constexpr (ESZ == 2) {
+        __builtin_nontemporal_store(static_cast<uint16_t>(v), reinterpret_cast<uint16_t*>(p));
+    } else {
+        __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+    }
+}
+
+__device__ __forceinline__ u32x4 load16(const char* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void store16(char* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// Element e (0 <= e < 16/ESZ) of a 16-byte vector.
+template <int ESZ>
+__device__ __forceinline__ uint32_t vec_elem(u32x4 v, int e) {
+    const uint32_t w = (ESZ == 2) ? v[e >> 1] : v[e];
+    if constexpr (ESZ == 2) {
+        return (e & 1) ? (w >> 16) : (w & 0xffffu);
+    } else {
+        return w;
+    }
+}
+
+// A unit is what one thread moves per rank per access: a 16-byte vector on
+// the vector path (VEC > 1 elements) or one element (VEC == 1).
+template <int DT, int VEC>
+struct Unit {
+    static constexpr int kEsz = elem_size<DT>();
+    static constexpr int kBytes = (VEC > 1) ? 16 : kEsz;
+    using T = std::conditional_t<(VEC > 1), u32x4, uint32_t>;
+
+    // `base` is the buffer address minus the common residue (vector path).
+    static __device__ __forceinline__ T load(const char* base, uint64_t v) {
+        if constexpr (VEC > 1) {
+            return load16(base + v * 16u);
+        } else {
+            return load_elem<kEsz>(base + v * kEsz);
+        }
+    }
+    static __device__ __forceinline__ void store(char* base, uint64_t v, T x) {
+        if constexpr (VEC > 1) {
+            store16(base + v * 16u, x);
+        } else {
+            store_elem<kEsz>(base + v * kEsz, x);
+        }
+    }
+    template <int OP>
+    static __device__ __forceinline__ T combine(T a, T b) {
+        if constexpr (VEC > 1) {
+            return Red<DT, OP>::vec(a, b);
+        } else {
+            return Red<DT, OP>::elem(a, b);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// chunk geometry
+// ---------------------------------------------------------------------------
+
+struct Span {
+    uint64_t s, e;    // element bounds of the chunk
+    uint64_t vb, ve;  // units of the chunk body: vectors (VEC > 1) or elements
+    uint64_t hb, he;  // head elements [hb, he) done one by one (VEC > 1 only)
+    uint64_t tb, te;  // tail elements [tb, te)
+};
+
+template <int VEC>
+__device__ __forceinline__ Span chunk_span(int c, const KernelArgs& a) {
+    Span sp;
+    const uint64_t n = static_cast<uint64_t>(a.nranks);
+    sp.s = static_cast<uint64_t>(c) * a.count / n;
+    sp.e = static_cast<uint64_t>(c + 1) * a.count / n;
+    if constexpr (VEC > 1) {
+        const uint64_t ofs = static_cast<uint64_t>(a.ofs);
+        sp.vb = (sp.s + ofs + VEC - 1) / VEC;
+        sp.ve = (sp.e + ofs) / VEC;
+        if (sp.ve < sp.vb) sp.ve = sp.vb;
+        const uint64_t body_first = sp.vb * VEC - ofs;   // first element of the body (>= s)
+        const uint64_t body_end = sp.ve * VEC - ofs;     // one past its last element
+        // head [s, min(body_first, e)); tail from the body's end (or the head's end
+        // when the body is empty) up to e; both stay inside [s, e) also for
+        // empty and short chunks
+        sp.hb = sp.s;
+        sp.he = body_first < sp.e ? body_first : sp.e;
+        sp.tb = body_end > sp.he ? body_end : sp.he;
+        if (sp.tb > sp.e) sp.tb = sp.e;
+        sp.te = sp.e;
+    } else {
+        sp.vb = sp.s;
+        sp.ve = sp.e;
+        sp.hb = sp.he = sp.tb = sp.te = sp.s;
+    }
+    return sp;
+}
+
+// Element handled by thread j among the chunk's edge elements, or false.
+__device__ __forceinline__ bool edge_element(const Span& sp, unsigned j, uint64_t* i) {
+    const uint64_t nh = sp.he - sp.hb;
+    const uint64_t nt = sp.te - sp.tb;
+    if (j < nh) {
+        *i = sp.hb + j;
+        return true;
+    }
+    if (j < nh + nt) {
+        *i = sp.tb + (j - nh);
+        return true;
+    }
+    return false;
+}
+
+__device__ __forceinline__ int ring_rank(int c, int k, int n) {
+    // (c + k) mod n for 0 <= c < n, 0 <= k < 2n
+    int r = c + k;
+    r = (r >= n) ? r - n : r;
+    return (r >= n) ? r - n : r;
+}
+
+// ---------------------------------------------------------------------------
+// the ring-order fold of one chunk position across all ranks
+// ---------------------------------------------------------------------------
+
+// acc[u] = ((x_c (op) x_{c+1}) (op) ...) at units v0 + u*kThreads, for live u.
+template <int DT, int OP, int VEC>
+__device__ __forceinline__ void fold_units(const KernelArgs& a, int c, int64_t adj, uint64_t v0,
+                                           const bool (&live)[kUnroll],
+                                           typename Unit<DT, VEC>::T (&acc)[kUnroll]) {
+    using U = Unit<DT, VEC>;
+    const int n = a.nranks;
+    {
+        const char* p = a.send[c] - adj;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) acc[u] = U::load(p, v0 + static_cast<uint64_t>(u) * kThreads);
+        }
+    }
+    for (int k = 1; k < n; k += kBatch) {
+        typename U::T x[kBatch][kUnroll];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (k + j < n) {
+                const char* p = a.send[ring_rank(c, k + j, n)] - adj;
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    if (live[u]) x[j][u] = U::load(p, v0 + static_cast<uint64_t>(u) * kThreads);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (k + j < n) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    if (live[u]) acc[u] = U::template combine<OP>(acc[u], x[j][u]);
+                }
+            }
+        }
+    }
+}
+
+// Same fold for one element i (chunk edges).
+template <int DT, int OP>
+__device__ __forceinline__ uint32_t fold_element(const KernelArgs& a, int c, uint64_t i) {
+    constexpr int ESZ = elem_size<DT>();
+    const int n = a.nranks;
+    uint32_t acc = load_elem<ESZ>(a.send[c] + i * ESZ);
+    for (int k = 1; k < n; ++k) {
+        acc = Red<DT, OP>::elem(acc, load_elem<ESZ>(a.send[ring_rank(c, k, n)] + i * ESZ));
+    }
+    return acc;
+}
+
+// Store unit v of a result into a shard that starts at element `s` of the
+// full buffer (reduce-scatter output).  `aligned` says whether the shard's
+// 16-byte vectors line up with the source's.
+template <int DT, int VEC>
+__device__ __forceinline__ void store_shard_unit(char* shard, uint64_t s, int32_t ofs, bool aligned,
+                                                 uint64_t v, typename Unit<DT, VEC>::T x) {
+    constexpr int ESZ = elem_size<DT>();
+    if constexpr (VEC > 1) {
+        const uint64_t first = v * VEC - static_cast<uint64_t>(ofs);   // element index in the full buffer
+        if (aligned) {
+            store16(shard + (first - s) * ESZ, x);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) store_elem<ESZ>(shard + (first + e - s) * ESZ, vec_elem<ESZ>(x, e));
+        }
+    } else {
+        store_elem<ESZ>(shard + (v - s) * ESZ, x);
+    }
+}
+
+// Load unit v of the full-buffer position space from a shard starting at `s`.
+template <int DT, int VEC>
+__device__ __forceinline__ typename Unit<DT, VEC>::T load_shard_unit(const char* shard, uint64_t s, int32_t ofs,
+                                                                     bool aligned, uint64_t v) {
+    constexpr int ESZ = elem_size<DT>();
+    if constexpr (VEC > 1) {
+        const uint64_t first = v * VEC - static_cast<uint64_t>(ofs);
+        if (aligned) return load16(shard + (first - s) * ESZ);
+        u32x4 r = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const uint32_t x = load_elem<ESZ>(shard + (first + e - s) * ESZ);
+            if constexpr (ESZ == 2) {
+                r[e >> 1] |= (e & 1) ? (x << 16) : x;
+            } else {
+                r[e] = x;
+            }
+        }
+        return r;
+    } else {
+        return load_elem<ESZ>(shard + (v - s) * ESZ);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ bool shard_aligned(const void* shard, uint64_t s, int32_t ofs) {
+    constexpr int ESZ = elem_size<DT>();
+    const uint64_t q = reinterpret_cast<uint64_t>(shard) - (s + static_cast<uint64_t>(ofs)) * ESZ;
+    return (q & 15u) == 0;
+}
+
+#define AR_TILE_LOOP_BEGIN                                                                   \
+    const int n = a.nranks;                                                                  \
+    const uint64_t tpc = a.tiles_per_chunk;                                                  \
+    const uint64_t ntiles = static_cast<uint64_t>(n) * tpc;                                  \
+    const int64_t adj = (VEC > 1) ? static_cast<int64_t>(a.ofs) * elem_size<DT>() : 0;       \
+    for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {                     \
+        const int c = static_cast<int>(tile / tpc);                                          \
+        const uint64_t t = tile - static_cast<uint64_t>(c) * tpc;                            \
+        const Span sp = chunk_span<VEC>(c, a);                                               \
+        const uint64_t v0 = sp.vb + t * (kThreads * kUnroll) + threadIdx.x;                  \
+        bool live[kUnroll];                                                                  \
+        _Pragma("unroll") for (int u = 0; u < kUnroll; ++u)                                  \
+            live[u] = v0 + static_cast<uint64_t>(u) * kThreads < sp.ve;
+
+#define AR_TILE_LOOP_END }
+
+// ---------------------------------------------------------------------------
+// fused kernels: one pass over HBM
+// ---------------------------------------------------------------------------
+
+// AllReduce: every rank's output gets the ring-order fold.  Reads N*S,
+// writes N*S bytes.  In place (send[r] == recv[r]) is safe: each position is
+// read by the thread that later writes it, and by no other.
+template <int DT, int OP, int VEC>
+__global__ __launch_bounds__(kThreads) void k_fused_allreduce(const KernelArgs a) {
+    using U = Unit<DT, VEC>;
+    AR_TILE_LOOP_BEGIN
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            const uint32_t r = fold_element<DT, OP>(a, c, i);
+            for (int q = 0; q < n; ++q) store_elem<elem_size<DT>()>(a.recv[q] + i * elem_size<DT>(), r);
+        }
+    }
+    typename U::T acc[kUnroll];
+    fold_units<DT, OP, VEC>(a, c, adj, v0, live, acc);
+    for (int q = 0; q < n; ++q) {
+        char* p = a.recv[q] - adj;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) U::store(p, v0 + static_cast<uint64_t>(u) * kThreads, acc[u]);
+        }
+    }
+    AR_TILE_LOOP_END
+}
+
+// Reduce-scatter: the fold of chunk c goes to rank c's shard only.  Reads N*S,
+// writes S bytes.
+template <int DT, int OP, int VEC>
+__global__ __launch_bounds__(kThreads) void k_fused_reduce_scatter(const KernelArgs a) {
+    using U = Unit<DT, VEC>;
+    AR_TILE_LOOP_BEGIN
+    char* shard = a.recv[c];
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            store_elem<elem_size<DT>()>(shard + (i - sp.s) * elem_size<DT>(), fold_element<DT, OP>(a, c, i));
+        }
+    }
+    const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
+    typename U::T acc[kUnroll];
+    fold_units<DT, OP, VEC>(a, c, adj, v0, live, acc);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, v0 + static_cast<uint64_t>(u) * kThreads, acc[u]);
+    }
+    AR_TILE_LOOP_END
+}
+
+// All-gather: shard c (on rank c) goes to position start(c) of every rank
+// (ALL = true) or of rank c only (ALL = false, the ring all-gather's first
+// placement).  A store to the address it was loaded from is skipped (in place).
+template <int DT, int VEC, bool ALL>
+__global__ __launch_bounds__(kThreads) void k_gather_shards(const KernelArgs a) {
+    using U = Unit<DT, VEC>;
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    const char* shard = a.send[c];
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            const uint32_t x = load_elem<ESZ>(shard + (i - sp.s) * ESZ);
+            for (int q = ALL ? 0 : c; q < (ALL ? n : c + 1); ++q) {
+                char* dst = a.recv[q] + i * ESZ;
+                if (dst != shard + (i - sp.s) * ESZ) store_elem<ESZ>(dst, x);
+            }
+        }
+    }
+    const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
+    typename U::T x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) x[u] = load_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, v0 + static_cast<uint64_t>(u) * kThreads);
+    }
+    for (int q = ALL ? 0 : c; q < (ALL ? n : c + 1); ++q) {
+        if (a.recv[q] + sp.s * ESZ == shard) continue;   // the shard already sits there
+        char* p = a.recv[q] - adj;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) U::store(p, v0 + static_cast<uint64_t>(u) * kThreads, x[u]);
+        }
+    }
+    AR_TILE_LOOP_END
+}
+
+// ---------------------------------------------------------------------------
+// ring steps: one launch per step of the schedule on tirogla.com "Ring
+// all-reduce" ("How it works").  In one launch every chunk c is handled by
+// the one rank that receives it in this step.
+// ---------------------------------------------------------------------------
+
+// AllReduce, reduce-scatter step s: rank r receives chunk (r-s-1) mod N from
+// rank r-1 and adds its own values, i.e. chunk c is reduced on rank
+// r = c+s+1 from rank p = c+s.  recv[r][chunk c] = send[r] (op) P, with
+// P = send[p] at s = 0 and the partial recv[p] afterwards.  Reads 2*S and
+// writes S bytes.  No rank writes what another rank reads in the same step
+// (rank r writes chunk r-s-1, rank r+1 reads chunk r-s of rank r).
+template <int DT, int OP, int VEC>
+__global__ __launch_bounds__(kThreads) void k_ring_reduce_step(const KernelArgs a) {
+    using U = Unit<DT, VEC>;
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    const int r = ring_rank(c, a.step + 1, n);
+    const int p = ring_rank(c, a.step, n);
+    const char* local = a.send[r];
+    const char* incoming = (a.step == 0) ? a.send[p] : a.recv[p];
+    char* out = a.recv[r];
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            store_elem<ESZ>(out + i * ESZ, Red<DT, OP>::elem(load_elem<ESZ>(local + i * ESZ),
+                                                             load_elem<ESZ>(incoming + i * ESZ)));
+        }
+    }
+    typename U::T x[kUnroll], y[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) {
+            x[u] = U::load(local - adj, v0 + static_cast<uint64_t>(u) * kThreads);
+            y[u] = U::load(incoming - adj, v0 + static_cast<uint64_t>(u) * kThreads);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) U::store(out - adj, v0 + static_cast<uint64_t>(u) * kThreads, U::template combine<OP>(x[u], y[u]));
+    }
+    AR_TILE_LOOP_END
+}
+
+// Reduce-scatter ring step s with the partial sums in a workspace (the
+// receive buffers hold one shard only).  Chunk c is reduced on rank
+// r = c+s+1; the incoming partial is send[c] at s = 0 and the workspace
+// afterwards; the last step (s = N-2, on rank c-1) writes shard c.
+template <int DT, int OP, int VEC>
+__global__ __launch_bounds__(kThreads) void k_ring_reduce_step_ws(const KernelArgs a) {
+    using U = Unit<DT, VEC>;
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    const int r = ring_rank(c, a.step + 1, n);
+    const char* local = a.send[r];
+    const char* incoming = (a.step == 0) ? a.send[c] : a.ws;
+    const bool last = (a.step == n - 2);
+    char* shard = a.recv[c];
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            const uint32_t v = Red<DT, OP>::elem(load_elem<ESZ>(local + i * ESZ), load_elem<ESZ>(incoming + i * ESZ));
+            store_elem<ESZ>(last ? shard + (i - sp.s) * ESZ : a.ws + i * ESZ, v);
+        }
+    }
+    const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
+    typename U::T x[kUnroll], y[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) {
+            x[u] = U::load(local - adj, v0 + static_cast<uint64_t>(u) * kThreads);
+            y[u] = U::load(incoming - adj, v0 + static_cast<uint64_t>(u) * kThreads);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (!live[u]) continue;
+        const typename U::T z = U::template combine<OP>(x[u], y[u]);
+        const uint64_t v = v0 + static_cast<uint64_t>(u) * kThreads;
+        if (last) {
+            store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, v, z);
+        } else {
+            U::store(a.ws - adj, v, z);
+        }
+    }
+    AR_TILE_LOOP_END
+}
+
+// All-gather ring step s: chunk c is copied from rank r-1 to rank
+// r = c+s+shift.  shift = 0 is the AllReduce's all-gather phase (rank r
+// receives chunk (r-s) mod N); shift = 1 is the standalone all-gather (rank r
+// receives chunk (r-s-1) mod N, ramchalamkr.github.io "Ring All-Gather").
+template <int DT, int VEC>
+__global__ __launch_bounds__(kThreads) void k_ring_copy_step(const KernelArgs a) {
+    using U = Unit<DT, VEC>;
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    const int r = ring_rank(c, a.step + a.shift, n);
+    const int p = ring_rank(r, n - 1, n);
+    const char* src = a.recv[p];
+    char* dst = a.recv[r];
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) store_elem<ESZ>(dst + i * ESZ, load_elem<ESZ>(src + i * ESZ));
+    }
+    typename U::T x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) x[u] = U::load(src - adj, v0 + static_cast<uint64_t>(u) * kThreads);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) U::store(dst - adj, v0 + static_cast<uint64_t>(u) * kThreads, x[u]);
+    }
+    AR_TILE_LOOP_END
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+
+template <int DT, int OP, int VEC>
+hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
+    const dim3 grid(l.blocks), block(kThreads);
+    switch (l.kind) {
+        case Kind::kFusedAllReduce:
+            hipLaunchKernelGGL((k_fused_allreduce<DT, OP, VEC>), grid, block, 0, s, a);
+            break;
+        case Kind::kFusedReduceScatter:
+            hipLaunchKernelGGL((k_fused_reduce_scatter<DT, OP, VEC>), grid, block, 0, s, a);
+            break;
+        case Kind::kRingReduceStep:
+            hipLaunchKernelGGL((k_ring_reduce_step<DT, OP, VEC>), grid, block, 0, s, a);
+            break;
+        case Kind::kRingReduceStepWs:
+            hipLaunchKernelGGL((k_ring_reduce_step_ws<DT, OP, VEC>), grid, block, 0, s, a);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// Copies depend on the element size only: bf16 moves as 2-byte elements,
+// f32 and i32 as 4-byte ones.
+template <int DT, int VEC>
+hipError_t launch_copy(const Launch& l, const KernelArgs& a, hipStream_t s) {
+    const dim3 grid(l.blocks), block(kThreads);
+    switch (l.kind) {
+        case Kind::kFusedAllGather:
+            hipLaunchKernelGGL((k_gather_shards<DT, VEC, true>), grid, block, 0, s, a);
+            break;
+        case Kind::kPlaceShards:
+            hipLaunchKernelGGL((k_gather_shards<DT, VEC, false>), grid, block, 0, s, a);
+            break;
+        case Kind::kRingCopyStep:
+            hipLaunchKernelGGL((k_ring_copy_step<DT, VEC>), grid, block, 0, s, a);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int DT, int OP>
+hipError_t by_vec(const Launch& l, const KernelArgs& a, hipStream_t s) {
+    constexpr int V = 16 / elem_size<DT>();
+    return l.vec ? launch_reduce<DT, OP, V>(l, a, s) : launch_reduce<DT, OP, 1>(l, a, s);
+}
+
+template <int DT>
+hipError_t by_op(const Launch& l, const KernelArgs& a, hipStream_t s) {
+    switch (l.op) {
+        case AR_SUM: return by_vec<DT, AR_SUM>(l, a, s);
+        case AR_PROD: return by_vec<DT, AR_PROD>(l, a, s);
+        case AR_MIN: return by_vec<DT, AR_MIN>(l, a, s);
+        case AR_MAX: return by_vec<DT, AR_MAX>(l, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t copy_by_vec(const Launch& l, const KernelArgs& a, hipStream_t s) {
+    constexpr int V = 16 / elem_size<DT>();
+    return l.vec ? launch_copy<DT, V>(l, a, s) : launch_copy<DT, 1>(l, a, s);
+}
+
+}  // namespace
+
+hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream) {
+    const bool copy = l.kind == Kind::kFusedAllGather || l.kind == Kind::kPlaceShards ||
+                      l.kind == Kind::kRingCopyStep;
+    if (copy) {
+        // bf16 and the 4-byte types differ only in element size here
+        return (l.dtype == AR_BFLOAT16) ? copy_by_vec<AR_BFLOAT16>(l, a, stream)
+                                        : copy_by_vec<AR_FLOAT32>(l, a, stream);
+    }
+    switch (l.dtype) {
+        case AR_FLOAT32: return by_op<AR_FLOAT32>(l, a, stream);
+        case AR_BFLOAT16: return by_op<AR_BFLOAT16>(l, a, stream);
+        case AR_INT32: return by_op<AR_INT32>(l, a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace arimpl

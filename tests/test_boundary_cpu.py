@@ -1,0 +1,171 @@
+"""The C ABI without a GPU: the library loads and exports every function
+include/ar.h declares, the host-only calls agree with the oracle's chunk
+plan, and every argument error is reported before anything touches a device.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle.ring import chunk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return _lib.lib()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "ar.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ar_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(lib):
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    declared = _declared_functions()
+    assert len(declared) >= 11
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(_lib.EXPORTS) == declared
+
+
+def test_chunk_range_matches_the_oracle(lib):
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    for n in (1, 2, 3, 5, 8, 16, 64, 128):
+        for count in (0, 1, n - 1, n, n + 1, 1003, (1 << 26) + 7, (1 << 40) + 3):
+            for c in sorted({0, 1 % n, n // 2, n - 1}):
+                assert ar.ar_chunk_range(c, count, n) == chunk(c, n, count)
+
+
+def test_error_strings(lib):
+    for code, text in ((0, b"success"), (1, b"invalid argument"), (3, b"HIP runtime error")):
+        assert lib.ar_get_error_string(code) == text
+    assert lib.ar_dtype_size(0) == 4 and lib.ar_dtype_size(1) == 2 and lib.ar_dtype_size(2) == 4
+    assert lib.ar_dtype_size(7) == 0
+
+
+def test_workspace_sizes(lib):
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    assert ar.ar_workspace_bytes("allreduce", "ring", 1000, "f32", 8) == 0
+    assert ar.ar_workspace_bytes("reduce_scatter", "fused", 1000, "f32", 8) == 0
+    assert ar.ar_workspace_bytes("reduce_scatter", "ring", 1000, "f32", 2) == 0
+    assert ar.ar_workspace_bytes("reduce_scatter", "ring", 1000, "bf16", 8) >= 2000
+    with pytest.raises(ValueError):
+        ar.ar_workspace_bytes("reduce_scatter", "ring", 1000, "f32", 0)
+
+
+def _ptrs(vals):
+    arr = (ctypes.c_void_p * len(vals))()
+    for i, v in enumerate(vals):
+        arr[i] = v
+    return arr
+
+
+# fake device addresses: validation only compares them, never dereferences
+BASE = 0x7F0000000000
+
+
+def _call_ar(lib, sends, recvs, count, dtype=0, op=0, n=None):
+    n = len(sends) if n is None else n
+    return lib.ar_allreduce(_ptrs(sends), _ptrs(recvs), count, dtype, op, n, None)
+
+
+def test_argument_errors_are_caught_on_the_host(lib):
+    S = 1 << 20
+    sends = [BASE + r * S for r in range(4)]
+    recvs = [BASE + (8 + r) * S for r in range(4)]
+    assert lib.ar_allreduce(None, _ptrs(recvs), 10, 0, 0, 4, None) == 1
+    assert _call_ar(lib, sends, recvs, 10, n=0) == 1
+    assert _call_ar(lib, sends * 33, recvs * 33, 10, n=129) == 1
+    assert _call_ar(lib, sends, recvs, 10, dtype=5) == 1
+    assert _call_ar(lib, sends, recvs, 10, op=4) == 1
+    assert b"op" in lib.ar_get_last_error_detail()
+    assert _call_ar(lib, [0] + sends[1:], recvs, 10) == 1               # null buffer
+    assert _call_ar(lib, [sends[0] + 2] + sends[1:], recvs, 10) == 1    # not 4-byte aligned
+    assert _call_ar(lib, sends, [recvs[0], recvs[0] + 8] + recvs[2:], 10) == 1   # receive buffers overlap
+    assert _call_ar(lib, sends, [sends[1]] + recvs[1:], 10) == 1         # recv[0] is rank 1's send
+    assert _call_ar(lib, sends, recvs, (1 << 64) // 100) == 1            # count too large
+    # empty work is a success without touching a device
+    assert _call_ar(lib, sends, recvs, 0) == 0
+    assert _call_ar(lib, [0] * 4, [0] * 4, 0) == 0
+    assert lib.ar_get_last_error_detail() == b""
+
+
+def test_in_place_layouts_are_accepted_others_rejected(lib):
+    """Validation of the aliasing rules, stopped before any launch by count checks."""
+    n, count = 4, 1000
+    S = 1 << 20
+    sends = [BASE + r * S for r in range(n)]
+    starts = [chunk(r, n, count)[0] for r in range(n)]
+    # reduce-scatter: recv[r] == send[r] + start(r) is in place; recv[r] == send[r] + start(r) + 1 is not
+    shards_ok = [sends[r] + 4 * starts[r] for r in range(n)]
+    shards_bad = [sends[r] + 4 * starts[r] + 4 for r in range(n)]
+    rs = lib.ar_reduce_scatter_ex
+    # with algo = 7 (unknown) the call stops after the aliasing checks would have passed
+    assert rs(_ptrs(sends), _ptrs(shards_ok), count, 0, 0, n, 7, None, 0, None) == 1
+    assert b"algo" in lib.ar_get_last_error_detail()
+    assert rs(_ptrs(sends), _ptrs(shards_bad), count, 0, 0, n, 0, None, 0, None) == 1
+    assert b"overlaps" in lib.ar_get_last_error_detail()
+    # all-gather: send[r] == recv[r] + start(r)
+    recvs = [BASE + (8 + r) * S for r in range(n)]
+    ag = lib.ar_all_gather_ex
+    assert ag(_ptrs([recvs[r] + 4 * starts[r] + 4 for r in range(n)]), _ptrs(recvs), count, 0, n, 0, None, 0, None) == 1
+    assert b"overlaps" in lib.ar_get_last_error_detail()
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libar.so")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.lib()
+
+
+def test_product_and_oracle_do_not_import_each_other():
+    pkg = os.path.join(ROOT, "ring_allreduce_reduction_virtual_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", src, flags=re.M), f
+                assert "oracle/" not in src, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            src = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "ring_allreduce_reduction_virtual_amd" not in src, f
+            assert not re.search(r"^\s*(from|import)\s+inputs\b", src, flags=re.M), f
+
+
+def test_input_generators_are_seeded_and_prefix_stable():
+    from inputs import WORKLOADS, make_inputs, make_rank
+
+    w = WORKLOADS["c5"]
+    a = make_rank(w, 3, count=5000)
+    b = make_rank(w, 3, count=5000)
+    assert np.array_equal(a, b)
+    assert np.array_equal(make_rank(w, 3, count=2000), a[:2000])
+    xs = make_inputs(WORKLOADS["c1"])
+    assert len(xs) == 4 and all(x.dtype == np.float32 and x.min() >= -8 and x.max() <= 8 for x in xs)
+    assert all(np.all(x == np.round(x)) for x in xs)
+    c3 = make_rank(WORKLOADS["c3"], 0, count=100000)
+    assert c3.dtype == np.uint16
+    c4 = make_rank(WORKLOADS["c4"], 0, count=100000)
+    assert c4.dtype == np.int32 and c4.min() < -(2**30) and c4.max() > 2**30
+    frac = np.mean(np.abs(make_rank(w, 0, count=200000)) > 100)
+    assert 0.005 < frac < 0.015          # about 1% outliers scaled by 1e4

@@ -1,0 +1,263 @@
+"""GPU edge cases: rank counts, ragged and empty chunks, every dtype and
+operator, both algorithms, the three collectives, in-place and misaligned
+buffers, special float values, streams and error returns.  Each result is
+compared bit for bit with the CPU oracle (NaNs as a class)."""
+
+import ctypes
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.ring import f32_to_bf16_bits, same_bits
+
+from gpu_util import from_dev, require_gpu, tdtype, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _ar():
+    require_gpu()
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    return ar
+
+
+def _draw(dtype, n, length, seed, special=False):
+    rng = np.random.default_rng(seed)
+    xs = []
+    for _ in range(n):
+        if dtype == "i32":
+            x = rng.integers(-(2**31), 2**31, size=length, dtype=np.int32)
+            if special and length:
+                x[rng.integers(0, length, size=max(1, length // 8))] = np.int32(2**31 - 1)
+            xs.append(x)
+            continue
+        f = (rng.standard_normal(length) * 2.0 ** rng.integers(-20, 20, size=length)).astype(np.float32)
+        if special and length:
+            specials = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1e-42, -1e-40, 3.4e38, -3.4e38,
+                                 1.17549435e-38, 2.0 ** -149], np.float32)
+            where = rng.integers(0, length, size=max(1, length // 5))
+            f[where] = specials[rng.integers(0, len(specials), size=len(where))]
+        xs.append(f32_to_bf16_bits(f) if dtype == "bf16" else f)
+    return xs
+
+
+def _alloc(n, length, dtype):
+    import torch
+
+    return [torch.empty(length, dtype=tdtype(dtype), device="cuda:0") for _ in range(n)]
+
+
+def _allreduce_case(n, length, dtype, op, algo, special=False, seed=0):
+    import torch
+
+    ar = _ar()
+    xs = _draw(dtype, n, length, seed, special)
+    want, _ = oracle.ring_allreduce(xs, op=op, dtype=dtype)
+    sends = [to_dev(x, dtype) for x in xs]
+    recvs = _alloc(n, length, dtype)
+    ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(from_dev(recvs[r], dtype), want[r], dtype), f"rank {r}"
+    # inputs are untouched
+    for r in range(n):
+        assert same_bits(from_dev(sends[r], dtype), xs[r], dtype)
+
+
+SHAPES = [(1, 0), (1, 7), (2, 1), (2, 9), (3, 2), (3, 1000), (4, 3), (5, 1003), (8, 7), (8, 9),
+          (8, 4097), (16, 15), (16, 65541), (64, 63), (64, 64 * 33 + 7), (128, 127), (128, 128 * 20 + 3)]
+
+
+@pytest.mark.parametrize("algo", ["fused", "ring"])
+@pytest.mark.parametrize("n,length", SHAPES)
+def test_allreduce_shapes_f32_sum(n, length, algo):
+    _allreduce_case(n, length, "f32", "sum", algo, seed=n * 7 + length)
+
+
+@pytest.mark.parametrize("algo", ["fused", "ring"])
+@pytest.mark.parametrize("dtype,op", [(d, o) for d in ("f32", "bf16", "i32") for o in ("sum", "prod", "min", "max")])
+@pytest.mark.parametrize("n,length", [(3, 1001), (8, 8 * 64 + 5), (17, 4099)])
+def test_allreduce_dtypes_and_ops(n, length, dtype, op, algo):
+    _allreduce_case(n, length, dtype, op, algo, seed=zlib.crc32(f"{dtype}{op}".encode()) % 1000)
+
+
+@pytest.mark.parametrize("algo", ["fused", "ring"])
+@pytest.mark.parametrize("dtype,op", [("f32", "sum"), ("f32", "min"), ("f32", "max"), ("f32", "prod"),
+                                      ("bf16", "sum"), ("bf16", "max"), ("i32", "sum"), ("i32", "prod")])
+def test_special_values(dtype, op, algo):
+    _allreduce_case(6, 3001, dtype, op, algo, special=True, seed=5)
+
+
+@pytest.mark.parametrize("algo", ["fused", "ring"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n,length", [(1, 5), (2, 3), (4, 4), (5, 1003), (8, 4101), (64, 64 * 9 + 5), (128, 300)])
+def test_reduce_scatter_and_all_gather(n, length, dtype, algo):
+    import torch
+
+    ar = _ar()
+    xs = _draw(dtype, n, length, seed=n + length)
+    shards_want, _ = oracle.reduce_scatter(xs, dtype=dtype)
+    sends = [to_dev(x, dtype) for x in xs]
+    shards = [torch.empty(len(s), dtype=tdtype(dtype), device="cuda:0") for s in shards_want]
+    ar.ar_reduce_scatter_ex(sends, shards, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(from_dev(shards[r], dtype), shards_want[r], dtype), f"shard {r}"
+    want, _ = oracle.all_gather(shards_want, length, dtype=dtype)
+    outs = _alloc(n, length, dtype)
+    ar.ar_all_gather_ex(shards, outs, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(from_dev(outs[r], dtype), want[r], dtype), f"rank {r}"
+
+
+@pytest.mark.parametrize("algo", ["fused", "ring"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_in_place(dtype, algo):
+    import torch
+
+    ar = _ar()
+    n, length = 8, 8 * 1000 + 13
+    xs = _draw(dtype, n, length, seed=3)
+    want, _ = oracle.ring_allreduce(xs, dtype=dtype)
+    bufs = [to_dev(x, dtype) for x in xs]
+    ar.ar_allreduce_ex(bufs, None, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(from_dev(bufs[r], dtype), want[r], dtype)
+    # reduce-scatter in place: shard r is the chunk-r view of send[r]
+    shards_want, _ = oracle.reduce_scatter(xs, dtype=dtype)
+    bufs = [to_dev(x, dtype) for x in xs]
+    views = [bufs[r][slice(*ar.ar_chunk_range(r, length, n))] for r in range(n)]
+    ar.ar_reduce_scatter_ex(bufs, views, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(from_dev(views[r], dtype), shards_want[r], dtype)
+    # all-gather in place: shard r already sits in chunk r of recv[r]
+    outs = _alloc(n, length, dtype)
+    for r in range(n):
+        s, e = ar.ar_chunk_range(r, length, n)
+        outs[r][s:e].copy_(to_dev(shards_want[r], dtype))
+    shards_in_place = [outs[r][slice(*ar.ar_chunk_range(r, length, n))] for r in range(n)]
+    ar.ar_all_gather_ex(shards_in_place, outs, algo=algo)
+    torch.cuda.synchronize()
+    gathered, _ = oracle.all_gather(shards_want, length, dtype=dtype)
+    for r in range(n):
+        assert same_bits(from_dev(outs[r], dtype), gathered[r], dtype)
+
+
+@pytest.mark.parametrize("algo", ["fused", "ring"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", ["common_offset", "mixed_offsets"])
+def test_misaligned_buffers(layout, dtype, algo):
+    """Views that start 1..3 elements into an allocation: a shared residue keeps the
+    vector path (shifted), mixed residues take the element path; same bits either way."""
+    import torch
+
+    ar = _ar()
+    n, length = 5, 4096 + 11
+    xs = _draw(dtype, n, length, seed=9)
+    want, _ = oracle.ring_allreduce(xs, dtype=dtype)
+    sends, recvs = [], []
+    for r in range(n):
+        off = 1 if layout == "common_offset" else (r % 4)
+        base = torch.empty(length + 8, dtype=tdtype(dtype), device="cuda:0")
+        v = base[off:off + length]
+        v.copy_(to_dev(xs[r], dtype))
+        sends.append(v)
+        off2 = 1 if layout == "common_offset" else ((r + 1) % 3)
+        rb = torch.empty(length + 8, dtype=tdtype(dtype), device="cuda:0")
+        recvs.append(rb[off2:off2 + length])
+    ar.ar_allreduce_ex(sends, recvs, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(from_dev(recvs[r], dtype), want[r], dtype)
+    shards_want, _ = oracle.reduce_scatter(xs, dtype=dtype)
+    shards = []
+    for r in range(n):
+        s, e = ar.ar_chunk_range(r, length, n)
+        sb = torch.empty(e - s + 4, dtype=tdtype(dtype), device="cuda:0")
+        shards.append(sb[r % 3:r % 3 + e - s])
+    ar.ar_reduce_scatter_ex(sends, shards, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(from_dev(shards[r], dtype), shards_want[r], dtype)
+    ar.ar_all_gather_ex(shards, recvs, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(from_dev(recvs[r], dtype), want[r], dtype)
+
+
+def test_side_stream_and_repeat_calls():
+    import torch
+
+    ar = _ar()
+    n, length = 8, 1 << 16
+    xs = _draw("f32", n, length, seed=11)
+    want, _ = oracle.ring_allreduce(xs)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        sends = [to_dev(x, "f32") for x in xs]
+        recvs = _alloc(n, length, "f32")
+        for _ in range(3):
+            ar.ar_allreduce(sends, recvs, stream=s)
+            ar.ar_allreduce_ex(sends, recvs, algo="ring", stream=s)
+    s.synchronize()
+    for r in range(n):
+        assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32")
+
+
+def test_same_input_buffer_on_every_rank():
+    import torch
+
+    ar = _ar()
+    x = _draw("f32", 1, 1003, seed=2)[0]
+    t = to_dev(x, "f32")
+    n = 4
+    recvs = _alloc(n, 1003, "f32")
+    ar.ar_allreduce([t] * n, recvs)
+    torch.cuda.synchronize()
+    want, _ = oracle.ring_allreduce([x] * n)
+    assert same_bits(from_dev(recvs[2], "f32"), want[2], "f32")
+
+
+def test_errors_launch_nothing():
+    import torch
+
+    ar = _ar()
+    n, length = 4, 1000
+    sends = [torch.ones(length, device="cuda:0") for _ in range(n)]
+    recvs = _alloc(n, length, "f32")
+    for t in recvs:
+        t.fill_(7.0)
+    # two ranks receiving into the same memory
+    with pytest.raises(ar.ArError, match="overlaps"):
+        ar.ar_allreduce(sends, [recvs[0], recvs[0], recvs[2], recvs[3]])
+    # a receive buffer that overlaps another rank's send buffer
+    with pytest.raises(ar.ArError, match="overlaps"):
+        ar.ar_allreduce(sends, [recvs[0], sends[0], recvs[2], recvs[3]])
+    # ring reduce-scatter without its workspace, straight through the C ABI
+    L = ar.lib()
+    from ring_allreduce_reduction_virtual_amd._lib import ptr_array
+
+    shards = [torch.empty(250, device="cuda:0") for _ in range(n)]
+    rc = L.ar_reduce_scatter_ex(ptr_array([t.data_ptr() for t in sends]), ptr_array([t.data_ptr() for t in shards]),
+                                length, 0, 0, n, 1, None, 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 1 and b"workspace" in L.ar_get_last_error_detail()
+    # an unknown op and a rank count past the limit
+    rc = L.ar_allreduce(ptr_array([t.data_ptr() for t in sends]), ptr_array([t.data_ptr() for t in recvs]),
+                        length, 0, 9, n, None)
+    assert rc == 1
+    rc = L.ar_allreduce(ptr_array([t.data_ptr() for t in sends]), ptr_array([t.data_ptr() for t in recvs]),
+                        length, 0, 0, 129, None)
+    assert rc == 1
+    # count == 0 is a successful no-op
+    rc = L.ar_allreduce(ptr_array([t.data_ptr() for t in sends]), ptr_array([t.data_ptr() for t in recvs]),
+                        0, 0, 0, n, None)
+    assert rc == 0
+    torch.cuda.synchronize()
+    for t in recvs:
+        assert torch.all(t == 7.0)       # nothing was written by the failed calls
