@@ -46,13 +46,15 @@ bool debug_enabled() {
     return on;
 }
 
-// Blocks launched per compute unit for the grid-stride kernels; 0 launches
-// one block per tile.  AR_BLOCKS_PER_CU overrides the default.
+// Blocks launched per compute unit; 0 (the default, fastest when measured on
+// MI355X) launches one block per tile, a positive value caps the grid at that
+// many blocks per CU and the kernels stride over the tiles.
+// AR_BLOCKS_PER_CU overrides the default.
 unsigned blocks_per_cu() {
     static const unsigned v = [] {
         const char* e = std::getenv("AR_BLOCKS_PER_CU");
         if (e != nullptr && e[0] != '\0') return static_cast<unsigned>(std::strtoul(e, nullptr, 10));
-        return 8u;
+        return 0u;
     }();
     return v;
 }
@@ -182,6 +184,8 @@ void fill_tables(KernelArgs& a, const Common& k) {
         a.recv[r] = static_cast<char*>(k.recv[r]);
     }
     a.count = k.count;
+    a.count_q = k.count / static_cast<uint64_t>(k.n);
+    a.count_r = static_cast<uint32_t>(k.count % static_cast<uint64_t>(k.n));
     a.nranks = k.n;
     a.step = 0;
     a.shift = 0;
@@ -194,20 +198,26 @@ ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, int residue) {
     l.vec = residue >= 0;
     a.ofs = l.vec ? static_cast<int32_t>(residue / static_cast<int>(k.esz)) : 0;
     const uint64_t n = static_cast<uint64_t>(k.n);
-    const uint64_t max_chunk = (k.count + n - 1) / n;
+    // the largest chunk body in units (16-byte vectors or elements), as the
+    // kernels count it: vectors wholly inside [start, end) at the common residue
     const uint64_t per_unit = l.vec ? 16 / k.esz : 1;
-    const uint64_t units = max_chunk / per_unit + 1;
+    const uint64_t ofs = static_cast<uint64_t>(a.ofs);
+    uint64_t units = 0;
+    for (int c = 0; c < k.n; ++c) {
+        const uint64_t s = chunk_start(c, k.count, k.n), e = chunk_start(c + 1, k.count, k.n);
+        const uint64_t vb = (s + ofs + per_unit - 1) / per_unit, ve = (e + ofs) / per_unit;
+        units = std::max(units, ve > vb ? ve - vb : 0);
+    }
     const uint64_t tile_units = static_cast<uint64_t>(arimpl::kThreads) * arimpl::kUnroll;
     const uint64_t tpc = std::max<uint64_t>(1, (units + tile_units - 1) / tile_units);
-    if (tpc > UINT32_MAX) return fail(AR_ERR_INVALID_ARGUMENT, "buffer too large");
+    const uint64_t tiles = n * tpc;
+    if (tiles > 0x7fffffffu) return fail(AR_ERR_INVALID_ARGUMENT, "buffer too large for one launch");
     a.tiles_per_chunk = static_cast<uint32_t>(tpc);
     int cus = 0;
     const ar_result_t rc = cu_count(&cus);
     if (rc != AR_SUCCESS) return rc;
-    const uint64_t tiles = n * tpc;
     const unsigned bpc = blocks_per_cu();
-    uint64_t blocks = bpc == 0 ? tiles : std::min<uint64_t>(tiles, static_cast<uint64_t>(cus) * bpc);
-    blocks = std::min<uint64_t>(blocks, 0x7fffffffu);
+    const uint64_t blocks = bpc == 0 ? tiles : std::min<uint64_t>(tiles, static_cast<uint64_t>(cus) * bpc);
     l.blocks = static_cast<unsigned>(blocks);
     return AR_SUCCESS;
 }

@@ -31,6 +31,8 @@ struct KernelArgs {
     char* recv[AR_MAX_RANKS];
     char* ws;                  // workspace for kRingReduceStepWs (already residue-adjusted)
     uint64_t count;            // elements per rank (full length)
+    uint64_t count_q;          // count / nranks
+    uint32_t count_r;          // count % nranks: start(c) = c*count_q + (c*count_r)/nranks
     uint32_t tiles_per_chunk;  // grid tiles that cover one chunk's body
     int32_t nranks;
     int32_t step;              // ring step s
@@ -46,8 +48,11 @@ struct Launch {
     unsigned blocks;
 };
 
-// Vectors of 16 bytes each thread handles per tile.
-constexpr int kUnroll = 2;
+// Vectors of 16 bytes each thread handles per rank per tile.
+#ifndef AR_TILE_UNROLL
+#define AR_TILE_UNROLL 2
+#endif
+constexpr int kUnroll = AR_TILE_UNROLL;
 
 // Enqueue one kernel; returns the HIP error of the launch.
 hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream);

@@ -34,7 +34,24 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBatch = 8;   // ranks whose loads are in flight together
+// Ranks whose loads are in flight together before they are folded.
+#ifndef AR_RANK_BATCH
+#define AR_RANK_BATCH 8
+#endif
+constexpr int kBatch = AR_RANK_BATCH;
+
+// Nontemporal hints: the reducing kernels stream their N input buffers once
+// (AR_NT_LOADS), the copies read a shard that several ranks' stores follow
+// (AR_NT_LOADS_COPY), and every output is written once (AR_NT_STORES).
+#ifndef AR_NT_LOADS
+#define AR_NT_LOADS 1
+#endif
+#ifndef AR_NT_LOADS_COPY
+#define AR_NT_LOADS_COPY 0
+#endif
+#ifndef AR_NT_STORES
+#define AR_NT_STORES 1
+#endif
 
 template <int DT>
 constexpr int elem_size() { return DT == AR_BFLOAT16 ? 2 : 4; }
@@ -141,18 +158,35 @@ __device__ __forceinline__ uint32_t load_elem(const char* p) {
 template <int ESZ>
 __device__ __forceinline__ void store_elem(char* p, uint32_t v) {
     if constexpr (ESZ == 2) {
-        __builtin_nontemporal_store(static_cast<uint16_t>(v), reinterpret_cast<uint16_t*>(p));
+        if constexpr (AR_NT_STORES) {
+            __builtin_nontemporal_store(static_cast<uint16_t>(v), reinterpret_cast<uint16_t*>(p));
+        } else {
+            *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(v);
+        }
     } else {
-        __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+        if constexpr (AR_NT_STORES) {
+            __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+        } else {
+            *reinterpret_cast<uint32_t*>(p) = v;
+        }
     }
 }
 
+template <bool NT = AR_NT_LOADS>
 __device__ __forceinline__ u32x4 load16(const char* p) {
-    return *reinterpret_cast<const u32x4*>(p);
+    if constexpr (NT) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    } else {
+        return *reinterpret_cast<const u32x4*>(p);
+    }
 }
 
 __device__ __forceinline__ void store16(char* p, u32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    if constexpr (AR_NT_STORES) {
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    } else {
+        *reinterpret_cast<u32x4*>(p) = v;
+    }
 }
 
 // Element e (0 <= e < 16/ESZ) of a 16-byte vector.
@@ -167,26 +201,37 @@ __device__ __forceinline__ uint32_t vec_elem(u32x4 v, int e) {
 }
 
 // A unit is what one thread moves per rank per access: a 16-byte vector on
-// the vector path (VEC > 1 elements) or one element (VEC == 1).
-template <int DT, int VEC>
+// the vector path (VEC > 1 elements) or one element (VEC == 1).  A block
+// addresses each buffer through the start of its tile (`tile`, uniform over
+// the block) plus the thread's byte offset inside the tile (`lane_off`).
+template <int DT, int VEC, bool NT_LOAD = AR_NT_LOADS>
 struct Unit {
     static constexpr int kEsz = elem_size<DT>();
     static constexpr int kBytes = (VEC > 1) ? 16 : kEsz;
     using T = std::conditional_t<(VEC > 1), u32x4, uint32_t>;
 
-    // `base` is the buffer address minus the common residue (vector path).
-    static __device__ __forceinline__ T load(const char* base, uint64_t v) {
+    // `p` is the buffer address minus the common residue (vector path); tv0
+    // the tile's first unit.
+    static __device__ __forceinline__ const char* tile(const char* p, uint64_t tv0) { return p + tv0 * kBytes; }
+    static __device__ __forceinline__ char* tile(char* p, uint64_t tv0) { return p + tv0 * kBytes; }
+    // The thread's u-th unit inside the tile: one 16-byte access per lane per
+    // instruction, so each wave instruction covers 1 KiB contiguous.
+    static __device__ __forceinline__ uint32_t lane_unit(int u) {
+        return threadIdx.x + static_cast<uint32_t>(u) * kThreads;
+    }
+    static __device__ __forceinline__ uint32_t lane_off(int u) { return lane_unit(u) * kBytes; }
+    static __device__ __forceinline__ T load(const char* tb, uint32_t off) {
         if constexpr (VEC > 1) {
-            return load16(base + v * 16u);
+            return load16<NT_LOAD>(tb + off);
         } else {
-            return load_elem<kEsz>(base + v * kEsz);
+            return load_elem<kEsz>(tb + off);
         }
     }
-    static __device__ __forceinline__ void store(char* base, uint64_t v, T x) {
+    static __device__ __forceinline__ void store(char* tb, uint32_t off, T x) {
         if constexpr (VEC > 1) {
-            store16(base + v * 16u, x);
+            store16(tb + off, x);
         } else {
-            store_elem<kEsz>(base + v * kEsz, x);
+            store_elem<kEsz>(tb + off, x);
         }
     }
     template <int OP>
@@ -213,9 +258,12 @@ struct Span {
 template <int VEC>
 __device__ __forceinline__ Span chunk_span(int c, const KernelArgs& a) {
     Span sp;
-    const uint64_t n = static_cast<uint64_t>(a.nranks);
-    sp.s = static_cast<uint64_t>(c) * a.count / n;
-    sp.e = static_cast<uint64_t>(c + 1) * a.count / n;
+    // c*count/n = c*(count/n) + c*(count%n)/n; the last product is below 128^2,
+    // so only a 32-bit division is left
+    const uint32_t n = static_cast<uint32_t>(a.nranks);
+    const uint32_t cu = static_cast<uint32_t>(c);
+    sp.s = static_cast<uint64_t>(cu) * a.count_q + (cu * a.count_r) / n;
+    sp.e = static_cast<uint64_t>(cu + 1) * a.count_q + ((cu + 1) * a.count_r) / n;
     if constexpr (VEC > 1) {
         const uint64_t ofs = static_cast<uint64_t>(a.ofs);
         sp.vb = (sp.s + ofs + VEC - 1) / VEC;
@@ -265,18 +313,19 @@ __device__ __forceinline__ int ring_rank(int c, int k, int n) {
 // the ring-order fold of one chunk position across all ranks
 // ---------------------------------------------------------------------------
 
-// acc[u] = ((x_c (op) x_{c+1}) (op) ...) at units v0 + u*kThreads, for live u.
+// acc[u] = ((x_c (op) x_{c+1}) (op) ...) at the thread's units of the tile
+// that starts at unit tv0, for live u.
 template <int DT, int OP, int VEC>
-__device__ __forceinline__ void fold_units(const KernelArgs& a, int c, int64_t adj, uint64_t v0,
+__device__ __forceinline__ void fold_units(const KernelArgs& a, int c, int64_t adj, uint64_t tv0,
                                            const bool (&live)[kUnroll],
                                            typename Unit<DT, VEC>::T (&acc)[kUnroll]) {
     using U = Unit<DT, VEC>;
     const int n = a.nranks;
     {
-        const char* p = a.send[c] - adj;
+        const char* tb = U::tile(a.send[c] - adj, tv0);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (live[u]) acc[u] = U::load(p, v0 + static_cast<uint64_t>(u) * kThreads);
+            if (live[u]) acc[u] = U::load(tb, U::lane_off(u));
         }
     }
     for (int k = 1; k < n; k += kBatch) {
@@ -284,10 +333,10 @@ __device__ __forceinline__ void fold_units(const KernelArgs& a, int c, int64_t a
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             if (k + j < n) {
-                const char* p = a.send[ring_rank(c, k + j, n)] - adj;
+                const char* tb = U::tile(a.send[ring_rank(c, k + j, n)] - adj, tv0);
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    if (live[u]) x[j][u] = U::load(p, v0 + static_cast<uint64_t>(u) * kThreads);
+                    if (live[u]) x[j][u] = U::load(tb, U::lane_off(u));
                 }
             }
         }
@@ -336,13 +385,13 @@ __device__ __forceinline__ void store_shard_unit(char* shard, uint64_t s, int32_
 }
 
 // Load unit v of the full-buffer position space from a shard starting at `s`.
-template <int DT, int VEC>
+template <int DT, int VEC, bool NT_LOAD>
 __device__ __forceinline__ typename Unit<DT, VEC>::T load_shard_unit(const char* shard, uint64_t s, int32_t ofs,
                                                                      bool aligned, uint64_t v) {
     constexpr int ESZ = elem_size<DT>();
     if constexpr (VEC > 1) {
         const uint64_t first = v * VEC - static_cast<uint64_t>(ofs);
-        if (aligned) return load16(shard + (first - s) * ESZ);
+        if (aligned) return load16<NT_LOAD>(shard + (first - s) * ESZ);
         u32x4 r = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -366,19 +415,23 @@ __device__ __forceinline__ bool shard_aligned(const void* shard, uint64_t s, int
     return (q & 15u) == 0;
 }
 
+// Tile loop: tile -> (chunk c, tile t within the chunk); consecutive tiles
+// walk one chunk after another (measured faster on MI355X than cycling over
+// the chunks, or than renumbering tiles per XCD).  The host keeps
+// N * tiles_per_chunk below 2^31.
 #define AR_TILE_LOOP_BEGIN                                                                   \
     const int n = a.nranks;                                                                  \
-    const uint64_t tpc = a.tiles_per_chunk;                                                  \
-    const uint64_t ntiles = static_cast<uint64_t>(n) * tpc;                                  \
+    const uint32_t tpc = a.tiles_per_chunk;                                                  \
+    const uint32_t ntiles = static_cast<uint32_t>(n) * tpc;                                  \
     const int64_t adj = (VEC > 1) ? static_cast<int64_t>(a.ofs) * elem_size<DT>() : 0;       \
-    for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {                     \
+    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {                     \
         const int c = static_cast<int>(tile / tpc);                                          \
-        const uint64_t t = tile - static_cast<uint64_t>(c) * tpc;                            \
+        const uint64_t t = tile - static_cast<uint32_t>(c) * tpc;                            \
         const Span sp = chunk_span<VEC>(c, a);                                               \
-        const uint64_t v0 = sp.vb + t * (kThreads * kUnroll) + threadIdx.x;                  \
+        const uint64_t tv0 = sp.vb + t * (kThreads * kUnroll);                               \
         bool live[kUnroll];                                                                  \
         _Pragma("unroll") for (int u = 0; u < kUnroll; ++u)                                  \
-            live[u] = v0 + static_cast<uint64_t>(u) * kThreads < sp.ve;
+            live[u] = tv0 + U::lane_unit(u) < sp.ve;
 
 #define AR_TILE_LOOP_END }
 
@@ -401,12 +454,12 @@ __global__ __launch_bounds__(kThreads) void k_fused_allreduce(const KernelArgs a
         }
     }
     typename U::T acc[kUnroll];
-    fold_units<DT, OP, VEC>(a, c, adj, v0, live, acc);
+    fold_units<DT, OP, VEC>(a, c, adj, tv0, live, acc);
     for (int q = 0; q < n; ++q) {
-        char* p = a.recv[q] - adj;
+        char* tb = U::tile(a.recv[q] - adj, tv0);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (live[u]) U::store(p, v0 + static_cast<uint64_t>(u) * kThreads, acc[u]);
+            if (live[u]) U::store(tb, U::lane_off(u), acc[u]);
         }
     }
     AR_TILE_LOOP_END
@@ -427,10 +480,10 @@ __global__ __launch_bounds__(kThreads) void k_fused_reduce_scatter(const KernelA
     }
     const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
     typename U::T acc[kUnroll];
-    fold_units<DT, OP, VEC>(a, c, adj, v0, live, acc);
+    fold_units<DT, OP, VEC>(a, c, adj, tv0, live, acc);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        if (live[u]) store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, v0 + static_cast<uint64_t>(u) * kThreads, acc[u]);
+        if (live[u]) store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u), acc[u]);
     }
     AR_TILE_LOOP_END
 }
@@ -440,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_reduce_scatter(const KernelA
 // placement).  A store to the address it was loaded from is skipped (in place).
 template <int DT, int VEC, bool ALL>
 __global__ __launch_bounds__(kThreads) void k_gather_shards(const KernelArgs a) {
-    using U = Unit<DT, VEC>;
+    using U = Unit<DT, VEC, AR_NT_LOADS_COPY>;
     constexpr int ESZ = elem_size<DT>();
     AR_TILE_LOOP_BEGIN
     const char* shard = a.send[c];
@@ -458,14 +511,14 @@ __global__ __launch_bounds__(kThreads) void k_gather_shards(const KernelArgs a) 
     typename U::T x[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        if (live[u]) x[u] = load_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, v0 + static_cast<uint64_t>(u) * kThreads);
+        if (live[u]) x[u] = load_shard_unit<DT, VEC, AR_NT_LOADS_COPY>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u));
     }
     for (int q = ALL ? 0 : c; q < (ALL ? n : c + 1); ++q) {
         if (a.recv[q] + sp.s * ESZ == shard) continue;   // the shard already sits there
-        char* p = a.recv[q] - adj;
+        char* tb = U::tile(a.recv[q] - adj, tv0);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (live[u]) U::store(p, v0 + static_cast<uint64_t>(u) * kThreads, x[u]);
+            if (live[u]) U::store(tb, U::lane_off(u), x[u]);
         }
     }
     AR_TILE_LOOP_END
@@ -501,16 +554,19 @@ __global__ __launch_bounds__(kThreads) void k_ring_reduce_step(const KernelArgs 
         }
     }
     typename U::T x[kUnroll], y[kUnroll];
+    const char* tl = U::tile(local - adj, tv0);
+    const char* ti = U::tile(incoming - adj, tv0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         if (live[u]) {
-            x[u] = U::load(local - adj, v0 + static_cast<uint64_t>(u) * kThreads);
-            y[u] = U::load(incoming - adj, v0 + static_cast<uint64_t>(u) * kThreads);
+            x[u] = U::load(tl, U::lane_off(u));
+            y[u] = U::load(ti, U::lane_off(u));
         }
     }
+    char* to = U::tile(out - adj, tv0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        if (live[u]) U::store(out - adj, v0 + static_cast<uint64_t>(u) * kThreads, U::template combine<OP>(x[u], y[u]));
+        if (live[u]) U::store(to, U::lane_off(u), U::template combine<OP>(x[u], y[u]));
     }
     AR_TILE_LOOP_END
 }
@@ -538,22 +594,24 @@ __global__ __launch_bounds__(kThreads) void k_ring_reduce_step_ws(const KernelAr
     }
     const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
     typename U::T x[kUnroll], y[kUnroll];
+    const char* tl = U::tile(local - adj, tv0);
+    const char* ti = U::tile(incoming - adj, tv0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         if (live[u]) {
-            x[u] = U::load(local - adj, v0 + static_cast<uint64_t>(u) * kThreads);
-            y[u] = U::load(incoming - adj, v0 + static_cast<uint64_t>(u) * kThreads);
+            x[u] = U::load(tl, U::lane_off(u));
+            y[u] = U::load(ti, U::lane_off(u));
         }
     }
+    char* tw = U::tile(a.ws - adj, tv0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         if (!live[u]) continue;
         const typename U::T z = U::template combine<OP>(x[u], y[u]);
-        const uint64_t v = v0 + static_cast<uint64_t>(u) * kThreads;
         if (last) {
-            store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, v, z);
+            store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u), z);
         } else {
-            U::store(a.ws - adj, v, z);
+            U::store(tw, U::lane_off(u), z);
         }
     }
     AR_TILE_LOOP_END
@@ -565,7 +623,7 @@ __global__ __launch_bounds__(kThreads) void k_ring_reduce_step_ws(const KernelAr
 // receives chunk (r-s-1) mod N, ramchalamkr.github.io "Ring All-Gather").
 template <int DT, int VEC>
 __global__ __launch_bounds__(kThreads) void k_ring_copy_step(const KernelArgs a) {
-    using U = Unit<DT, VEC>;
+    using U = Unit<DT, VEC, AR_NT_LOADS_COPY>;
     constexpr int ESZ = elem_size<DT>();
     AR_TILE_LOOP_BEGIN
     const int r = ring_rank(c, a.step + a.shift, n);
@@ -577,13 +635,15 @@ __global__ __launch_bounds__(kThreads) void k_ring_copy_step(const KernelArgs a)
         if (edge_element(sp, threadIdx.x, &i)) store_elem<ESZ>(dst + i * ESZ, load_elem<ESZ>(src + i * ESZ));
     }
     typename U::T x[kUnroll];
+    const char* ts = U::tile(src - adj, tv0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        if (live[u]) x[u] = U::load(src - adj, v0 + static_cast<uint64_t>(u) * kThreads);
+        if (live[u]) x[u] = U::load(ts, U::lane_off(u));
     }
+    char* td = U::tile(dst - adj, tv0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        if (live[u]) U::store(dst - adj, v0 + static_cast<uint64_t>(u) * kThreads, x[u]);
+        if (live[u]) U::store(td, U::lane_off(u), x[u]);
     }
     AR_TILE_LOOP_END
 }
