@@ -93,6 +93,166 @@ def time_calls(fn, steps: int, warmup: int, stream):
     return start.elapsed_time(end) / steps
 
 
+def median_call_ms(fn, steps: int, warmup: int, stream):
+    """Median and minimum milliseconds of single calls, each bracketed by HIP events."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    times = sorted(a.elapsed_time(b) for a, b in evs)
+    return times[len(times) // 2], times[0]
+
+
+def _to_device(x, dtype, dev):
+    import numpy as np
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(x).to(dev)
+
+
+def _sampled_parity(xs, outs, dtype, op, positions):
+    """Outputs at chosen positions against the oracle's fold there (all ranks)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle.ring import chunk_owner, same_bits
+
+    n, count = len(xs), len(xs[0])
+    want = oracle.ring_order_fold_columns(np.stack([x[positions] for x in xs]),
+                                          chunk_owner(positions, n, count), op=op, dtype=dtype)
+    idx = torch.from_numpy(positions).to(outs[0].device)
+    for t in outs:
+        got = t[idx].cpu()
+        got = got.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else got.numpy()
+        if not same_bits(got, want, dtype):
+            return False
+    return True
+
+
+def run_configs(args):
+    """Every workload, fused and ring, timed per call (median of K), with sampled parity."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import ring_allreduce_reduction_virtual_amd as ar
+    from inputs import WORKLOADS, make_inputs
+    from oracle.ring import chunk
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}
+    esz = {"f32": 4, "bf16": 2, "i32": 4}
+    for name in ("c1", "c2", "c3", "c4", "c5", "headline"):
+        w = WORKLOADS[name]
+        n, count, dt = w.nranks, w.count, w.dtype
+        s_bytes = count * esz[dt]
+        xs = make_inputs(w)
+        sends = [_to_device(x, dt, dev) for x in xs]
+        recvs = [torch.empty(count, dtype=tdt[dt], device=dev) for _ in range(n)]
+        rng = np.random.default_rng(7)
+        pos = np.unique(np.concatenate([rng.integers(0, count, 1024)] +
+                                       [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1])
+                                        for c in range(n) if chunk(c, n, count)[1] > chunk(c, n, count)[0]]))
+        # the oracle's executed schedule on a bounded prefix of the workload, single-threaded
+        sample = min(count, 1 << 20)
+        t0 = time.perf_counter()
+        oracle.ring_allreduce([x[:sample] for x in xs], op=w.ops[0], dtype=dt, check=False)
+        oracle_s = time.perf_counter() - t0
+        steps = 200 if s_bytes < (1 << 24) else 20
+        for op in w.ops:
+            for algo in ("fused", "ring"):
+                fn = (lambda: ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo))
+                med, mn = median_call_ms(fn, steps, 3, stream)
+                ok = _sampled_parity(xs, recvs, dt, op, pos)
+                algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
+                print(json.dumps({
+                    "config": name, "collective": "allreduce", "algo": algo, "op": op, "dtype": dt, "nranks": n,
+                    "count": count, "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                    "algbw_gbps": round(s_bytes / (med / 1e3) / 1e9, 2),
+                    "busbw_gbps": round(s_bytes / (med / 1e3) / 1e9 * busbw_factor("allreduce", n), 2),
+                    "hbm_gbps_of_minimum": round(algo_bytes / (med / 1e3) / 1e9, 1),
+                    "hbm_frac": round(algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "parity_sampled": "pass" if ok else "fail",
+                    "oracle_s_on_prefix": round(oracle_s, 3), "oracle_prefix_elems": sample, "oracle_cores": 1,
+                }), flush=True)
+        if "reduce_scatter" in w.phases:
+            shards = [torch.empty(chunk(r, n, count)[1] - chunk(r, n, count)[0], dtype=tdt[dt], device=dev)
+                      for r in range(n)]
+            rs_bytes = algorithmic_bytes("reduce_scatter", n, s_bytes)
+            for algo in ("fused", "ring"):
+                med, mn = median_call_ms(lambda: ar.ar_reduce_scatter_ex(sends, shards, algo=algo), steps, 3, stream)
+                print(json.dumps({"config": name, "collective": "reduce_scatter", "algo": algo, "op": "sum",
+                                  "dtype": dt, "nranks": n, "count": count, "median_us": round(med * 1e3, 2),
+                                  "min_us": round(mn * 1e3, 2),
+                                  "algbw_gbps": round(s_bytes / (med / 1e3) / 1e9, 2),
+                                  "busbw_gbps": round(s_bytes / (med / 1e3) / 1e9 * busbw_factor("reduce_scatter", n), 2),
+                                  "hbm_gbps_of_minimum": round(rs_bytes / (med / 1e3) / 1e9, 1),
+                                  "hbm_frac": round(rs_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}), flush=True)
+            for algo in ("fused", "ring"):
+                med, mn = median_call_ms(lambda: ar.ar_all_gather_ex(shards, recvs, algo=algo), steps, 3, stream)
+                print(json.dumps({"config": name, "collective": "all_gather", "algo": algo, "dtype": dt,
+                                  "nranks": n, "count": count, "median_us": round(med * 1e3, 2),
+                                  "min_us": round(mn * 1e3, 2),
+                                  "algbw_gbps": round(s_bytes / (med / 1e3) / 1e9, 2),
+                                  "busbw_gbps": round(s_bytes / (med / 1e3) / 1e9 * busbw_factor("all_gather", n), 2),
+                                  "hbm_gbps_of_minimum": round(rs_bytes / (med / 1e3) / 1e9, 1),
+                                  "hbm_frac": round(rs_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}), flush=True)
+            del shards
+        del sends, recvs, xs
+        torch.cuda.empty_cache()
+
+
+def run_size_sweep(args):
+    """AllReduce time against message size, 8 ranks of float32, both algorithms.
+
+    Fits the cost model of tirogla.com "Ring all-reduce" on one GPU: the fused
+    kernel t = a + 2*N*S/B (one launch), the ring mode t = 2(N-1)*a' + 5(N-1)*S/B'
+    (one launch per step; 5(N-1)*S bytes move through HBM).
+    """
+    import numpy as np
+    import torch
+
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    n = 8
+    rows = []
+    for k in range(0, 27, 2):
+        count = 1 << k
+        sends = [torch.randn(count, device=dev) for _ in range(n)]
+        recvs = [torch.empty(count, device=dev) for _ in range(n)]
+        for algo in ("fused", "ring"):
+            med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 50, 5, stream)
+            rows.append((algo, count, med))
+            s_bytes = count * 4
+            print(json.dumps({"sweep": "allreduce", "algo": algo, "nranks": n, "count": count, "bytes_per_rank": s_bytes,
+                              "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                              "algbw_gbps": round(s_bytes / (med / 1e3) / 1e9, 3),
+                              "busbw_gbps": round(s_bytes / (med / 1e3) / 1e9 * busbw_factor("allreduce", n), 3)}),
+                  flush=True)
+        del sends, recvs
+    fits = {}
+    for algo, bytes_factor, launches in (("fused", 2 * n, 1), ("ring", 5 * (n - 1), 2 * (n - 1))):
+        pts = [(c * 4 * bytes_factor, t / 1e3) for a, c, t in rows if a == algo]
+        A = np.array([[launches, b] for b, _ in pts], dtype=np.float64)
+        y = np.array([t for _, t in pts])
+        (alpha, inv_b), *_ = np.linalg.lstsq(A, y, rcond=None)
+        fits[algo] = {"alpha_us_per_launch": round(alpha * 1e6, 3), "hbm_gbps": round(1 / inv_b / 1e9, 1)}
+    print(json.dumps({"sweep_fit": fits, "model": "t = launches*alpha + hbm_bytes/B"}), flush=True)
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -112,6 +272,12 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the ring / phase / copy side measurements")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the headline line: time every workload (c1..c5) with both algorithms, "
+                         "one JSON line each")
+    ap.add_argument("--size-sweep", action="store_true",
+                    help="instead of the headline line: AllReduce time against message size (8 ranks, f32), "
+                         "fused and ring, with an alpha-beta fit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -131,6 +297,12 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.configs:
+        run_configs(args)
+        return
+    if args.size_sweep:
+        run_size_sweep(args)
+        return
     w = WORKLOADS["headline"]
     n, count = w.nranks, w.count
     s_bytes = count * 4

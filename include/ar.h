@@ -89,11 +89,27 @@ typedef enum {
  * AR_ALGO_RING: the ring's steps one by one, one kernel launch per step:
  *   N-1 reduce-scatter steps then N-1 all-gather steps, each rank adding the
  *   chunk received from rank r-1 (tirogla.com "Ring all-reduce", "How it
- *   works").  Same bits as the fused kernel. */
+ *   works").
+ * AR_ALGO_PHASES: AllReduce as reduce-scatter followed by all-gather ("2.1
+ *   Collective communication primitives in detail", section 3.8), each phase
+ *   one fused pass: the reduced chunk c lands in chunk c of recvbufs[c], then
+ *   is copied to every other rank.  (2N+1)*S bytes, S more than the fused
+ *   kernel, but the read-heavy and the write-heavy halves run apart, which is
+ *   faster on MI355X HBM once N is large.
+ * AR_ALGO_AUTO: AR_ALGO_FUSED below AR_PHASES_MIN_RANKS ranks, AR_ALGO_PHASES
+ *   from there on (AllReduce); the fused kernel for the single phases.
+ * All algorithms give the same bits. */
 typedef enum {
     AR_ALGO_FUSED = 0,
-    AR_ALGO_RING = 1
+    AR_ALGO_RING = 1,
+    AR_ALGO_PHASES = 2,
+    AR_ALGO_AUTO = 3
 } ar_algo_t;
+
+/* Rank count from which AR_ALGO_AUTO runs an AllReduce as two fused phases
+ * (measured crossover on MI355X; the AR_PHASES_MIN_RANKS environment variable
+ * overrides it). */
+#define AR_PHASES_MIN_RANKS 24
 
 typedef enum {
     AR_COLL_ALLREDUCE = 0,
@@ -103,8 +119,8 @@ typedef enum {
 
 /* AllReduce (tirogla.com "Ring all-reduce"; "2.1 Collective communication
  * primitives in detail", section 3.4): every recvbufs[r] (count elements)
- * receives the reduction of all sendbufs[*] (count elements each).  Fused
- * algorithm. */
+ * receives the reduction of all sendbufs[*] (count elements each).
+ * Algorithm AR_ALGO_AUTO. */
 ar_result_t ar_allreduce(const void* const* sendbufs, void* const* recvbufs, size_t count,
                          ar_dtype_t dtype, ar_op_t op, int nranks, hipStream_t stream);
 
@@ -113,14 +129,15 @@ ar_result_t ar_allreduce(const void* const* sendbufs, void* const* recvbufs, siz
  * elements; recvbufs[r] receives the cl(r) elements of chunk r of the
  * reduction, packed.  The association order is AllReduce's, so
  * all-gather after reduce-scatter reproduces AllReduce bit for bit.  Fused
- * algorithm. */
+ * algorithm (AR_ALGO_PHASES and AR_ALGO_AUTO mean the same here). */
 ar_result_t ar_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, size_t count,
                               ar_dtype_t dtype, ar_op_t op, int nranks, hipStream_t stream);
 
 /* All-gather (ramchalamkr.github.io "NCCL Primitives Deep Dive", section
  * "Ring All-Gather"; "2.1 ...", section 3.6): sendbufs[r] holds shard r,
  * cl(r) elements; every recvbufs[r] (count elements) receives all shards
- * concatenated in rank order.  No arithmetic.  Fused algorithm. */
+ * concatenated in rank order.  No arithmetic.  Fused algorithm
+ * (AR_ALGO_PHASES and AR_ALGO_AUTO mean the same here). */
 ar_result_t ar_all_gather(const void* const* sendbufs, void* const* recvbufs, size_t count,
                           ar_dtype_t dtype, int nranks, hipStream_t stream);
 

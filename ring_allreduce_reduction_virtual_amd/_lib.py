@@ -17,7 +17,7 @@ RESULT_NAMES = {0: "AR_SUCCESS", 1: "AR_ERR_INVALID_ARGUMENT", 2: "AR_ERR_UNSUPP
                 3: "AR_ERR_HIP", 4: "AR_ERR_INTERNAL"}
 DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3}
-ALGOS = {"fused": 0, "ring": 1}
+ALGOS = {"fused": 0, "ring": 1, "phases": 2, "auto": 3}
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
 MAX_RANKS = 128
 

@@ -168,14 +168,23 @@ ar_result_t check_ptr(const void* p, uint64_t elems, size_t esz, const char* wha
     return AR_SUCCESS;
 }
 
-// Common residue modulo 16 bytes of a set of addresses, or -1.
-int common_residue(const std::vector<uintptr_t>& ptrs) {
-    if (ptrs.empty()) return 0;
-    const int r0 = static_cast<int>(ptrs[0] & 15u);
-    for (uintptr_t p : ptrs) {
-        if (static_cast<int>(p & 15u) != r0) return -1;
+// Streamed buffers share their address residue modulo `align` bytes.  The
+// vector path needs 16; 256 lets every chunk body start and end on whole
+// cache lines in all buffers at once.
+struct Residue {
+    int bytes;    // common residue modulo `align`, or -1 when not even 16 works
+    int align;    // 256, 128, 64, 32 or 16
+};
+
+Residue common_residue(const std::vector<uintptr_t>& ptrs) {
+    for (int align = 256; align >= 16; align /= 2) {
+        const uintptr_t m = static_cast<uintptr_t>(align - 1);
+        const uintptr_t r0 = ptrs.empty() ? 0 : (ptrs[0] & m);
+        bool same = true;
+        for (uintptr_t p : ptrs) same = same && ((p & m) == r0);
+        if (same) return {static_cast<int>(r0), align};
     }
-    return r0;
+    return {-1, 16};
 }
 
 void fill_tables(KernelArgs& a, const Common& k) {
@@ -193,33 +202,59 @@ void fill_tables(KernelArgs& a, const Common& k) {
     a.ws = nullptr;
 }
 
+// Grid for the tiles [tile_first, tile_end) of a launch.
+ar_result_t grid_for(const KernelArgs& a, Launch& l) {
+    int cus = 0;
+    const ar_result_t rc = cu_count(&cus);
+    if (rc != AR_SUCCESS) return rc;
+    const uint64_t tiles = a.tile_end - a.tile_first;
+    const unsigned bpc = blocks_per_cu();
+    const uint64_t blocks = bpc == 0 ? tiles : std::min<uint64_t>(tiles, static_cast<uint64_t>(cus) * bpc);
+    l.blocks = static_cast<unsigned>(std::max<uint64_t>(blocks, 1));
+    return AR_SUCCESS;
+}
+
 // Tiles per chunk and grid size for a launch on the current device.
-ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, int residue) {
-    l.vec = residue >= 0;
-    a.ofs = l.vec ? static_cast<int32_t>(residue / static_cast<int>(k.esz)) : 0;
+ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, Residue res) {
+    l.vec = res.bytes >= 0;
+    const uint64_t block = l.vec ? static_cast<uint64_t>(res.align) / k.esz : 1;   // A elements
+    a.ofs = l.vec ? static_cast<int32_t>(res.bytes / static_cast<int>(k.esz)) : 0;
+    int shift = 0;
+    while ((1ull << shift) < block) ++shift;
+    a.align_shift = shift;
     const uint64_t n = static_cast<uint64_t>(k.n);
     // the largest chunk body in units (16-byte vectors or elements), as the
-    // kernels count it: vectors wholly inside [start, end) at the common residue
+    // kernels count it: whole aligned blocks of A elements inside [start, end)
     const uint64_t per_unit = l.vec ? 16 / k.esz : 1;
     const uint64_t ofs = static_cast<uint64_t>(a.ofs);
     uint64_t units = 0;
     for (int c = 0; c < k.n; ++c) {
         const uint64_t s = chunk_start(c, k.count, k.n), e = chunk_start(c + 1, k.count, k.n);
-        const uint64_t vb = (s + ofs + per_unit - 1) / per_unit, ve = (e + ofs) / per_unit;
-        units = std::max(units, ve > vb ? ve - vb : 0);
+        const uint64_t fb = (s + ofs + block - 1) / block, eb = (e + ofs) / block;
+        units = std::max(units, eb > fb ? (eb - fb) * block / per_unit : 0);
     }
     const uint64_t tile_units = static_cast<uint64_t>(arimpl::kThreads) * arimpl::kUnroll;
     const uint64_t tpc = std::max<uint64_t>(1, (units + tile_units - 1) / tile_units);
     const uint64_t tiles = n * tpc;
     if (tiles > 0x7fffffffu) return fail(AR_ERR_INVALID_ARGUMENT, "buffer too large for one launch");
     a.tiles_per_chunk = static_cast<uint32_t>(tpc);
-    int cus = 0;
-    const ar_result_t rc = cu_count(&cus);
-    if (rc != AR_SUCCESS) return rc;
-    const unsigned bpc = blocks_per_cu();
-    const uint64_t blocks = bpc == 0 ? tiles : std::min<uint64_t>(tiles, static_cast<uint64_t>(cus) * bpc);
-    l.blocks = static_cast<unsigned>(blocks);
-    return AR_SUCCESS;
+    a.tile_first = 0;
+    a.tile_end = static_cast<uint32_t>(tiles);
+    return grid_for(a, l);
+}
+
+bool algo_known(ar_algo_t algo) {
+    return algo == AR_ALGO_FUSED || algo == AR_ALGO_RING || algo == AR_ALGO_PHASES || algo == AR_ALGO_AUTO;
+}
+
+// Rank count from which AR_ALGO_AUTO runs AllReduce as two fused phases.
+int phases_min_ranks() {
+    static const int v = [] {
+        const char* e = std::getenv("AR_PHASES_MIN_RANKS");
+        if (e != nullptr && e[0] != '\0') return static_cast<int>(std::strtol(e, nullptr, 10));
+        return AR_PHASES_MIN_RANKS;
+    }();
+    return v;
 }
 
 const char* kind_name(Kind kd) {
@@ -256,7 +291,7 @@ ar_result_t enqueue(Launch& l, Kind kind, const KernelArgs& a, const Common& k, 
 ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, hipStream_t stream) {
     ar_result_t rc = check_common(k, true);
     if (rc != AR_SUCCESS) return rc;
-    if (algo != AR_ALGO_FUSED && algo != AR_ALGO_RING) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+    if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;
     const uint64_t bytes = k.count * k.esz;
@@ -278,11 +313,34 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, hipStream_t stream) 
     if (rc != AR_SUCCESS) return rc;
     if (k.count == 0) return AR_SUCCESS;
 
+    if (algo == AR_ALGO_AUTO) algo = (k.n >= phases_min_ranks()) ? AR_ALGO_PHASES : AR_ALGO_FUSED;
+    if (k.n == 1) algo = AR_ALGO_FUSED;           // a copy
     KernelArgs a{};
     Launch l{};
     fill_tables(a, k);
+    if (algo == AR_ALGO_PHASES) {
+        // reduce-scatter: chunk c of the reduction into chunk c of recv[c] ...
+        std::vector<uintptr_t> sends;
+        for (int r = 0; r < k.n; ++r) {
+            a.recv[r] = static_cast<char*>(k.recv[r]) + chunk_start(r, k.count, k.n) * k.esz;
+            sends.push_back(reinterpret_cast<uintptr_t>(k.send[r]));
+        }
+        if ((rc = plan(a, l, k, common_residue(sends))) != AR_SUCCESS) return rc;
+        if ((rc = enqueue(l, Kind::kFusedReduceScatter, a, k, stream)) != AR_SUCCESS) return rc;
+        // ... then all-gather in place: chunk c of recv[c] to every other rank
+        KernelArgs g{};
+        Launch lg{};
+        fill_tables(g, k);
+        std::vector<uintptr_t> recvs;
+        for (int r = 0; r < k.n; ++r) {
+            g.send[r] = static_cast<const char*>(k.recv[r]) + chunk_start(r, k.count, k.n) * k.esz;
+            recvs.push_back(reinterpret_cast<uintptr_t>(k.recv[r]));
+        }
+        if ((rc = plan(g, lg, k, common_residue(recvs))) != AR_SUCCESS) return rc;
+        return enqueue(lg, Kind::kFusedAllGather, g, k, stream);
+    }
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
-    if (algo == AR_ALGO_FUSED || k.n == 1) return enqueue(l, Kind::kFusedAllReduce, a, k, stream);
+    if (algo == AR_ALGO_FUSED) return enqueue(l, Kind::kFusedAllReduce, a, k, stream);
     for (int s = 0; s < k.n - 1; ++s) {          // reduce-scatter steps
         a.step = s;
         if ((rc = enqueue(l, Kind::kRingReduceStep, a, k, stream)) != AR_SUCCESS) return rc;
@@ -297,13 +355,14 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, hipStream_t stream) 
 
 uint64_t rs_workspace_bytes(uint64_t count, size_t esz, int n, ar_algo_t algo) {
     if (algo != AR_ALGO_RING || n < 3 || count == 0) return 0;
-    return count * esz + 32;   // one full-length buffer of partials, plus room to match residues
+    return count * esz + 512;  // one full-length buffer of partials, plus room to match residues
 }
 
 ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_bytes, hipStream_t stream) {
     ar_result_t rc = check_common(k, true);
     if (rc != AR_SUCCESS) return rc;
-    if (algo != AR_ALGO_FUSED && algo != AR_ALGO_RING) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+    if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+    if (algo != AR_ALGO_RING) algo = AR_ALGO_FUSED;
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;
     const uint64_t bytes = k.count * k.esz;
@@ -336,13 +395,13 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
     KernelArgs a{};
     Launch l{};
     fill_tables(a, k);
-    const int residue = common_residue(ptrs);
+    const Residue residue = common_residue(ptrs);
     if ((rc = plan(a, l, k, residue)) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_FUSED || k.n == 1) return enqueue(l, Kind::kFusedReduceScatter, a, k, stream);
     if (need) {
-        // place the partials at the senders' residue so they stream as 16-byte vectors too
-        const uintptr_t w = (reinterpret_cast<uintptr_t>(ws) + 15u) & ~static_cast<uintptr_t>(15u);
-        a.ws = reinterpret_cast<char*>(w + static_cast<uintptr_t>(residue >= 0 ? residue : 0));
+        // place the partials at the senders' residue so they stream as aligned vectors too
+        const uintptr_t w = (reinterpret_cast<uintptr_t>(ws) + 255u) & ~static_cast<uintptr_t>(255u);
+        a.ws = reinterpret_cast<char*>(w + static_cast<uintptr_t>(residue.bytes >= 0 ? residue.bytes : 0));
     }
     for (int s = 0; s < k.n - 1; ++s) {
         a.step = s;
@@ -354,7 +413,8 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
 ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, hipStream_t stream) {
     ar_result_t rc = check_common(k, false);
     if (rc != AR_SUCCESS) return rc;
-    if (algo != AR_ALGO_FUSED && algo != AR_ALGO_RING) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+    if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+    if (algo != AR_ALGO_RING) algo = AR_ALGO_FUSED;
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;
     const uint64_t bytes = k.count * k.esz;
@@ -396,7 +456,7 @@ extern "C" {
 
 ar_result_t ar_allreduce(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
                          ar_op_t op, int nranks, hipStream_t stream) {
-    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, AR_ALGO_FUSED, stream);
+    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, AR_ALGO_AUTO, stream);
 }
 
 ar_result_t ar_allreduce_ex(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
@@ -435,7 +495,7 @@ ar_result_t ar_all_gather_ex(const void* const* sendbufs, void* const* recvbufs,
 
 size_t ar_workspace_bytes(ar_coll_t coll, ar_algo_t algo, size_t count, ar_dtype_t dtype, int nranks) {
     const size_t e = esize(dtype);
-    if (e == 0 || nranks < 1 || nranks > AR_MAX_RANKS || (algo != AR_ALGO_FUSED && algo != AR_ALGO_RING) ||
+    if (e == 0 || nranks < 1 || nranks > AR_MAX_RANKS || !algo_known(algo) ||
         count > (UINT64_MAX / AR_MAX_RANKS) / 16)
         return static_cast<size_t>(-1);
     switch (coll) {

@@ -23,9 +23,13 @@ enum class Kind : int {
 
 // Kernel arguments, passed by value.  Pointers are the callers' device
 // addresses.  On the vector path every streamed full-length buffer p has the
-// same residue `ofs` elements modulo 16 bytes, so its 16-byte vector v starts
-// at (p - ofs elements) + 16*v and holds elements [v*V - ofs, (v+1)*V - ofs),
-// V = 16 / element size.
+// same residue `ofs` elements modulo A = 2^align_shift elements (A * element
+// size is 256 bytes when the buffers allow it, and at least 16), so its
+// 16-byte vector v starts at (p - ofs elements) + 16*v and holds elements
+// [v*V - ofs, (v+1)*V - ofs), V = 16 / element size.  Each chunk's body of
+// vectors starts and ends on an A-element boundary in every buffer, so whole
+// cache lines are written; the few elements before and after it are done one
+// at a time.
 struct KernelArgs {
     const char* send[AR_MAX_RANKS];
     char* recv[AR_MAX_RANKS];
@@ -34,10 +38,13 @@ struct KernelArgs {
     uint64_t count_q;          // count / nranks
     uint32_t count_r;          // count % nranks: start(c) = c*count_q + (c*count_r)/nranks
     uint32_t tiles_per_chunk;  // grid tiles that cover one chunk's body
+    uint32_t tile_first;       // this launch covers tiles [tile_first, tile_end) of N * tiles_per_chunk
+    uint32_t tile_end;
     int32_t nranks;
     int32_t step;              // ring step s
     int32_t shift;             // kRingCopyStep: acting rank = (c + step + shift) mod N
-    int32_t ofs;               // common element residue of the streamed buffers (vector path)
+    int32_t ofs;               // common element residue of the streamed buffers modulo the body alignment
+    int32_t align_shift;       // log2 of the body alignment in elements (vector path)
 };
 
 struct Launch {

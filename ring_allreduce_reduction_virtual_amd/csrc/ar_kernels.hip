@@ -265,9 +265,13 @@ __device__ __forceinline__ Span chunk_span(int c, const KernelArgs& a) {
     sp.s = static_cast<uint64_t>(cu) * a.count_q + (cu * a.count_r) / n;
     sp.e = static_cast<uint64_t>(cu + 1) * a.count_q + ((cu + 1) * a.count_r) / n;
     if constexpr (VEC > 1) {
+        // the body: whole aligned blocks of A = 2^align_shift elements, as vectors
         const uint64_t ofs = static_cast<uint64_t>(a.ofs);
-        sp.vb = (sp.s + ofs + VEC - 1) / VEC;
-        sp.ve = (sp.e + ofs) / VEC;
+        const uint32_t sh = static_cast<uint32_t>(a.align_shift);
+        const uint64_t first_block = (sp.s + ofs + (1ull << sh) - 1) >> sh;
+        const uint64_t end_block = (sp.e + ofs) >> sh;
+        sp.vb = (first_block << sh) / VEC;
+        sp.ve = (end_block << sh) / VEC;
         if (sp.ve < sp.vb) sp.ve = sp.vb;
         const uint64_t body_first = sp.vb * VEC - ofs;   // first element of the body (>= s)
         const uint64_t body_end = sp.ve * VEC - ofs;     // one past its last element
@@ -417,14 +421,14 @@ __device__ __forceinline__ bool shard_aligned(const void* shard, uint64_t s, int
 
 // Tile loop: tile -> (chunk c, tile t within the chunk); consecutive tiles
 // walk one chunk after another (measured faster on MI355X than cycling over
-// the chunks, or than renumbering tiles per XCD).  The host keeps
-// N * tiles_per_chunk below 2^31.
+// the chunks, or than renumbering tiles per XCD).  A launch covers tiles
+// [tile_first, tile_end); the host keeps N * tiles_per_chunk below 2^31.
 #define AR_TILE_LOOP_BEGIN                                                                   \
     const int n = a.nranks;                                                                  \
     const uint32_t tpc = a.tiles_per_chunk;                                                  \
-    const uint32_t ntiles = static_cast<uint32_t>(n) * tpc;                                  \
+    const uint32_t ntiles = a.tile_end;                                                      \
     const int64_t adj = (VEC > 1) ? static_cast<int64_t>(a.ofs) * elem_size<DT>() : 0;       \
-    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {                     \
+    for (uint32_t tile = a.tile_first + blockIdx.x; tile < ntiles; tile += gridDim.x) {      \
         const int c = static_cast<int>(tile / tpc);                                          \
         const uint64_t t = tile - static_cast<uint32_t>(c) * tpc;                            \
         const Span sp = chunk_span<VEC>(c, a);                                               \
@@ -668,6 +672,7 @@ hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
         case Kind::kRingReduceStepWs:
             hipLaunchKernelGGL((k_ring_reduce_step_ws<DT, OP, VEC>), grid, block, 0, s, a);
             break;
+
         default:
             return hipErrorInvalidValue;
     }
@@ -689,6 +694,7 @@ hipError_t launch_copy(const Launch& l, const KernelArgs& a, hipStream_t s) {
         case Kind::kRingCopyStep:
             hipLaunchKernelGGL((k_ring_copy_step<DT, VEC>), grid, block, 0, s, a);
             break;
+
         default:
             return hipErrorInvalidValue;
     }
