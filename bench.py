@@ -171,7 +171,7 @@ def run_configs(args):
         oracle_s = time.perf_counter() - t0
         steps = 200 if s_bytes < (1 << 24) else 20
         for op in w.ops:
-            for algo in ("fused", "ring"):
+            for algo in ("fused", "phases", "ring"):
                 fn = (lambda: ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo))
                 med, mn = median_call_ms(fn, steps, 3, stream)
                 ok = _sampled_parity(xs, recvs, dt, op, pos)
