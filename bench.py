@@ -110,6 +110,32 @@ def median_call_ms(fn, steps: int, warmup: int, stream):
     return times[len(times) // 2], times[0]
 
 
+def graph_ms_per_call(fn, calls: int, stream, replays: int = 5):
+    """Milliseconds per call when `calls` calls are captured in one HIP graph and replayed."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / (replays * calls)
+
+
 def _to_device(x, dtype, dev):
     import numpy as np
     import torch
@@ -176,7 +202,15 @@ def run_configs(args):
                 med, mn = median_call_ms(fn, steps, 3, stream)
                 ok = _sampled_parity(xs, recvs, dt, op, pos)
                 algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
-                print(json.dumps({
+                latency = {}
+                if s_bytes * n <= (64 << 20):
+                    # small messages: the same call as a persistent plan, and replayed from a HIP graph
+                    plan = ar.ar_allreduce_init(sends, recvs, op=op, algo=algo)
+                    pmed, _ = median_call_ms(plan.start, steps, 3, stream)
+                    latency["plan_median_us"] = round(pmed * 1e3, 2)
+                    latency["graph_us_per_call"] = round(graph_ms_per_call(plan.start, 50, stream) * 1e3, 2)
+                    plan.close()
+                print(json.dumps({**latency, 
                     "config": name, "collective": "allreduce", "algo": algo, "op": op, "dtype": dt, "nranks": n,
                     "count": count, "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
                     "algbw_gbps": round(s_bytes / (med / 1e3) / 1e9, 2),

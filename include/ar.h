@@ -158,6 +158,33 @@ ar_result_t ar_all_gather_ex(const void* const* sendbufs, void* const* recvbufs,
                              ar_dtype_t dtype, int nranks, ar_algo_t algo,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Persistent collectives, in the manner of MPI's persistent AllReduce request
+ * (bitfern.com "AllReduce Explained", section "MPI_Allreduce"): *_init
+ * validates the arguments and plans the launches once, with the same
+ * arguments, rules and errors as the matching *_ex call; ar_plan_start then
+ * only enqueues the planned kernels on `stream`, as often as wanted, so a hot
+ * loop or a HIP graph capture pays no validation.  The plan keeps the device
+ * pointers it was given: the buffers (and workspace) must stay valid, and
+ * hold the inputs, whenever the plan is started.  Starts whose work overlaps
+ * on the GPU write the same outputs and race.  *_init allocates the plan in
+ * host memory and sets *plan (NULL on error); ar_plan_free releases it
+ * (NULL is accepted).  A plan may be started from several threads. */
+typedef struct ar_plan_s* ar_plan_t;
+
+ar_result_t ar_allreduce_init(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                              ar_dtype_t dtype, ar_op_t op, int nranks, ar_algo_t algo,
+                              void* workspace, size_t workspace_bytes, ar_plan_t* plan);
+ar_result_t ar_reduce_scatter_init(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                                   ar_dtype_t dtype, ar_op_t op, int nranks, ar_algo_t algo,
+                                   void* workspace, size_t workspace_bytes, ar_plan_t* plan);
+ar_result_t ar_all_gather_init(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                               ar_dtype_t dtype, int nranks, ar_algo_t algo,
+                               void* workspace, size_t workspace_bytes, ar_plan_t* plan);
+ar_result_t ar_plan_start(ar_plan_t plan, hipStream_t stream);
+/* Kernel launches one start enqueues (0 for count == 0), or -1 for NULL. */
+int ar_plan_num_launches(ar_plan_t plan);
+ar_result_t ar_plan_free(ar_plan_t plan);
+
 /* Workspace in bytes that a call with these arguments needs (0: none).
  * Returns (size_t)-1 for invalid arguments. */
 size_t ar_workspace_bytes(ar_coll_t coll, ar_algo_t algo, size_t count, ar_dtype_t dtype, int nranks);

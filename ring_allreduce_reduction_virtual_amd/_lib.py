@@ -27,6 +27,8 @@ EXPORTS = (
     "ar_allreduce_ex", "ar_reduce_scatter_ex", "ar_all_gather_ex",
     "ar_workspace_bytes", "ar_chunk_range", "ar_get_error_string",
     "ar_get_last_error_detail", "ar_dtype_size",
+    "ar_allreduce_init", "ar_reduce_scatter_init", "ar_all_gather_init",
+    "ar_plan_start", "ar_plan_num_launches", "ar_plan_free",
 )
 
 _lib = None
@@ -50,6 +52,12 @@ def _declare(lib):
         "ar_get_error_string": (ctypes.c_char_p, [_int]),
         "ar_get_last_error_detail": (ctypes.c_char_p, []),
         "ar_dtype_size": (_sz, [_int]),
+        "ar_allreduce_init": (_int, [_vpp, _vpp, _sz, _int, _int, _int, _int, _vp, _sz, _vpp]),
+        "ar_reduce_scatter_init": (_int, [_vpp, _vpp, _sz, _int, _int, _int, _int, _vp, _sz, _vpp]),
+        "ar_all_gather_init": (_int, [_vpp, _vpp, _sz, _int, _int, _int, _vp, _sz, _vpp]),
+        "ar_plan_start": (_int, [_vp, _vp]),
+        "ar_plan_num_launches": (_int, [_vp]),
+        "ar_plan_free": (_int, [_vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -9,7 +9,12 @@ memory and the stream.
 ``sendbufs`` / ``recvbufs`` are sequences of one tensor per virtual rank.
 ``count`` is always the full per-rank length (see include/ar.h): for
 reduce-scatter the receive tensors hold one chunk each, for all-gather the
-send tensors do.
+send tensors do.  ``algo`` is one of "fused", "ring", "phases", "auto".
+
+The ``*_init`` functions return a :class:`Plan`, the persistent form of a
+call: validated once, then enqueued by :meth:`Plan.start` (or
+:func:`ar_plan_start`) as often as wanted, including inside a HIP graph
+capture.
 """
 
 from __future__ import annotations
@@ -31,30 +36,39 @@ def _stream_handle(stream):
     return int(stream)
 
 
-def _dtype_of(tensors):
-    dt = tensors[0].dtype
+def _marshal(sendbufs, recvbufs):
+    """Check the two tensor lists; return (device, dtype name, send array, recv array)."""
+    n = len(sendbufs)
+    if len(recvbufs) != n:
+        raise ValueError("need one send and one receive buffer per rank")
+    if not 1 <= n <= _lib.MAX_RANKS:
+        raise ValueError(f"nranks must be in [1, {_lib.MAX_RANKS}]")
+    t0 = sendbufs[0]
+    if not isinstance(t0, torch.Tensor) or not t0.is_cuda:
+        raise ValueError("buffers must be CUDA tensors")
+    dev, dt = t0.device, t0.dtype
     if dt not in _TORCH_DTYPES:
         raise TypeError(f"unsupported dtype {dt}; use float32, bfloat16 or int32")
-    for t in tensors:
-        if t.dtype != dt:
-            raise TypeError("all buffers must have the same dtype")
-    return _TORCH_DTYPES[dt]
+    sp = (ctypes.c_void_p * n)()
+    rp = (ctypes.c_void_p * n)()
+    for i in range(n):
+        s, r = sendbufs[i], recvbufs[i]
+        for t in (s, r):
+            if not isinstance(t, torch.Tensor) or t.device != dev:
+                raise ValueError("all buffers must be tensors on the same GPU")
+            if t.dtype != dt:
+                raise TypeError("all buffers must have the same dtype")
+            if not t.is_contiguous():
+                raise ValueError("buffers must be contiguous")
+        sp[i] = s.data_ptr()
+        rp[i] = r.data_ptr()
+    return dev, _TORCH_DTYPES[dt], sp, rp
 
 
-def _check_tensors(sendbufs, recvbufs):
-    if len(sendbufs) != len(recvbufs):
-        raise ValueError("need one send and one receive buffer per rank")
-    if not 1 <= len(sendbufs) <= _lib.MAX_RANKS:
-        raise ValueError(f"nranks must be in [1, {_lib.MAX_RANKS}]")
-    dev = sendbufs[0].device
-    for t in list(sendbufs) + list(recvbufs):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError("buffers must be torch tensors")
-        if t.device.type != "cuda" or t.device != dev:
-            raise ValueError("all buffers must be on the same GPU")
-        if not t.is_contiguous():
-            raise ValueError("buffers must be contiguous")
-    return dev
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
 def ar_chunk_range(c: int, count: int, nranks: int):
@@ -79,134 +93,208 @@ def ar_dtype_size(dtype: str) -> int:
     return _lib.lib().ar_dtype_size(_lib.DTYPES[dtype])
 
 
-def _device_guard(dev):
-    return torch.cuda.device(dev)
+def _check_counts(coll, sendbufs, recvbufs):
+    n = len(sendbufs)
+    if coll == "allreduce":
+        count = sendbufs[0].numel()
+        if any(t.numel() != count for t in list(sendbufs) + list(recvbufs)):
+            raise ValueError("every AllReduce buffer must hold count elements")
+        return count
+    full, shards, what = (sendbufs, recvbufs, "recvbufs") if coll == "reduce_scatter" else \
+        (recvbufs, sendbufs, "sendbufs")
+    count = full[0].numel()
+    if any(t.numel() != count for t in full):
+        raise ValueError("every full-length buffer must hold count elements")
+    for r, t in enumerate(shards):
+        b, e = ar_chunk_range(r, count, n)
+        if t.numel() != e - b:
+            raise ValueError(f"{what}[{r}] must hold chunk {r}: {e - b} elements")
+    return count
 
 
-def ar_allreduce_ex(sendbufs, recvbufs=None, op: str = "sum", algo: str = "fused", workspace=None, stream=None):
-    """AllReduce of the ranks' send tensors into every receive tensor (in place when recvbufs is None)."""
-    recvbufs = sendbufs if recvbufs is None else recvbufs
-    dev = _check_tensors(sendbufs, recvbufs)
-    dtype = _dtype_of(list(sendbufs) + list(recvbufs))
-    count = sendbufs[0].numel()
-    if any(t.numel() != count for t in list(sendbufs) + list(recvbufs)):
-        raise ValueError("every AllReduce buffer must hold count elements")
-    with _device_guard(dev):
-        L = _lib.lib()
-        rc = L.ar_allreduce_ex(_lib.ptr_array([t.data_ptr() for t in sendbufs]),
-                               _lib.ptr_array([t.data_ptr() for t in recvbufs]),
-                               count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs), _lib.ALGOS[algo],
-                               None if workspace is None else workspace.data_ptr(),
-                               0 if workspace is None else workspace.numel() * workspace.element_size(),
-                               _stream_handle(stream))
-    _lib.check("ar_allreduce_ex", rc)
-    return recvbufs
+def _rs_workspace(algo, count, dtype, n, workspace, dev, stream):
+    need = ar_workspace_bytes("reduce_scatter", algo, count, dtype, n)
+    if need and workspace is None:
+        if stream is not None and not isinstance(stream, torch.cuda.Stream):
+            raise ValueError("pass a workspace when the stream is a raw handle")
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if stream is not None:
+            workspace.record_stream(stream)   # freed only after the stream's work
+    return workspace
 
+
+# --------------------------------------------------------------------------
+# one-shot calls
+# --------------------------------------------------------------------------
 
 def ar_allreduce(sendbufs, recvbufs=None, op: str = "sum", stream=None):
-    """AllReduce with the fused one-pass kernel."""
+    """AllReduce (algorithm AR_ALGO_AUTO); in place when recvbufs is None."""
     recvbufs = sendbufs if recvbufs is None else recvbufs
-    dev = _check_tensors(sendbufs, recvbufs)
-    dtype = _dtype_of(list(sendbufs) + list(recvbufs))
-    count = sendbufs[0].numel()
-    if any(t.numel() != count for t in list(sendbufs) + list(recvbufs)):
-        raise ValueError("every AllReduce buffer must hold count elements")
-    with _device_guard(dev):
-        rc = _lib.lib().ar_allreduce(_lib.ptr_array([t.data_ptr() for t in sendbufs]),
-                                     _lib.ptr_array([t.data_ptr() for t in recvbufs]),
-                                     count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    count = _check_counts("allreduce", sendbufs, recvbufs)
+    with torch.cuda.device(dev):
+        rc = _lib.lib().ar_allreduce(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
                                      _stream_handle(stream))
     _lib.check("ar_allreduce", rc)
     return recvbufs
 
 
-def _check_shards(shards, count, n, what):
-    for r, t in enumerate(shards):
-        b, e = ar_chunk_range(r, count, n)
-        if t.numel() != e - b:
-            raise ValueError(f"{what}[{r}] must hold chunk {r}: {e - b} elements")
-
-
-def ar_reduce_scatter_ex(sendbufs, recvbufs, op: str = "sum", algo: str = "fused", workspace=None, stream=None):
-    """Reduce-scatter: recvbufs[r] receives chunk r of the reduction.
-
-    The ring algorithm needs a workspace (ar_workspace_bytes); when none is
-    given one is taken from torch's allocator on the stream of the call.
-    """
-    dev = _check_tensors(sendbufs, recvbufs)
-    dtype = _dtype_of(list(sendbufs) + list(recvbufs))
-    n = len(sendbufs)
-    count = sendbufs[0].numel()
-    if any(t.numel() != count for t in sendbufs):
-        raise ValueError("every send buffer must hold count elements")
-    _check_shards(recvbufs, count, n, "recvbufs")
-    need = ar_workspace_bytes("reduce_scatter", algo, count, dtype, n)
-    with _device_guard(dev):
-        if need and workspace is None:
-            if stream is not None and not isinstance(stream, torch.cuda.Stream):
-                raise ValueError("pass a workspace when the stream is a raw handle")
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-            if stream is not None:
-                workspace.record_stream(stream)   # freed only after the stream's work
-        rc = _lib.lib().ar_reduce_scatter_ex(_lib.ptr_array([t.data_ptr() for t in sendbufs]),
-                                             _lib.ptr_array([t.data_ptr() for t in recvbufs]),
-                                             count, _lib.DTYPES[dtype], _lib.OPS[op], n, _lib.ALGOS[algo],
-                                             None if workspace is None else workspace.data_ptr(),
-                                             0 if workspace is None else workspace.numel() * workspace.element_size(),
-                                             _stream_handle(stream))
-    _lib.check("ar_reduce_scatter_ex", rc)
+def ar_allreduce_ex(sendbufs, recvbufs=None, op: str = "sum", algo: str = "fused", workspace=None, stream=None):
+    """AllReduce with the algorithm chosen by the caller; in place when recvbufs is None."""
+    recvbufs = sendbufs if recvbufs is None else recvbufs
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    count = _check_counts("allreduce", sendbufs, recvbufs)
+    wp, wb = _ws(workspace)
+    with torch.cuda.device(dev):
+        rc = _lib.lib().ar_allreduce_ex(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
+                                        _lib.ALGOS[algo], wp, wb, _stream_handle(stream))
+    _lib.check("ar_allreduce_ex", rc)
     return recvbufs
 
 
 def ar_reduce_scatter(sendbufs, recvbufs, op: str = "sum", stream=None):
-    """Reduce-scatter with the fused one-pass kernel."""
-    dev = _check_tensors(sendbufs, recvbufs)
-    dtype = _dtype_of(list(sendbufs) + list(recvbufs))
-    n = len(sendbufs)
-    count = sendbufs[0].numel()
-    if any(t.numel() != count for t in sendbufs):
-        raise ValueError("every send buffer must hold count elements")
-    _check_shards(recvbufs, count, n, "recvbufs")
-    with _device_guard(dev):
-        rc = _lib.lib().ar_reduce_scatter(_lib.ptr_array([t.data_ptr() for t in sendbufs]),
-                                          _lib.ptr_array([t.data_ptr() for t in recvbufs]),
-                                          count, _lib.DTYPES[dtype], _lib.OPS[op], n, _stream_handle(stream))
+    """Reduce-scatter with the fused kernel: recvbufs[r] receives chunk r of the reduction."""
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    count = _check_counts("reduce_scatter", sendbufs, recvbufs)
+    with torch.cuda.device(dev):
+        rc = _lib.lib().ar_reduce_scatter(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
+                                          _stream_handle(stream))
     _lib.check("ar_reduce_scatter", rc)
     return recvbufs
 
 
-def ar_all_gather_ex(sendbufs, recvbufs, algo: str = "fused", workspace=None, stream=None):
-    """All-gather: every recvbufs[r] receives all shards sendbufs[*] in rank order."""
-    dev = _check_tensors(sendbufs, recvbufs)
-    dtype = _dtype_of(list(sendbufs) + list(recvbufs))
+def ar_reduce_scatter_ex(sendbufs, recvbufs, op: str = "sum", algo: str = "fused", workspace=None, stream=None):
+    """Reduce-scatter with the algorithm chosen by the caller.
+
+    The ring algorithm needs a workspace (ar_workspace_bytes); when none is
+    given one is taken from torch's allocator on the stream of the call.
+    """
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    count = _check_counts("reduce_scatter", sendbufs, recvbufs)
     n = len(sendbufs)
-    count = recvbufs[0].numel()
-    if any(t.numel() != count for t in recvbufs):
-        raise ValueError("every receive buffer must hold count elements")
-    _check_shards(sendbufs, count, n, "sendbufs")
-    with _device_guard(dev):
-        rc = _lib.lib().ar_all_gather_ex(_lib.ptr_array([t.data_ptr() for t in sendbufs]),
-                                         _lib.ptr_array([t.data_ptr() for t in recvbufs]),
-                                         count, _lib.DTYPES[dtype], n, _lib.ALGOS[algo],
-                                         None if workspace is None else workspace.data_ptr(),
-                                         0 if workspace is None else workspace.numel() * workspace.element_size(),
-                                         _stream_handle(stream))
-    _lib.check("ar_all_gather_ex", rc)
+    with torch.cuda.device(dev):
+        workspace = _rs_workspace(algo, count, dtype, n, workspace, dev, stream)
+        wp, wb = _ws(workspace)
+        rc = _lib.lib().ar_reduce_scatter_ex(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], n,
+                                             _lib.ALGOS[algo], wp, wb, _stream_handle(stream))
+    _lib.check("ar_reduce_scatter_ex", rc)
     return recvbufs
 
 
 def ar_all_gather(sendbufs, recvbufs, stream=None):
-    """All-gather with the fused one-pass kernel."""
-    dev = _check_tensors(sendbufs, recvbufs)
-    dtype = _dtype_of(list(sendbufs) + list(recvbufs))
-    n = len(sendbufs)
-    count = recvbufs[0].numel()
-    if any(t.numel() != count for t in recvbufs):
-        raise ValueError("every receive buffer must hold count elements")
-    _check_shards(sendbufs, count, n, "sendbufs")
-    with _device_guard(dev):
-        rc = _lib.lib().ar_all_gather(_lib.ptr_array([t.data_ptr() for t in sendbufs]),
-                                      _lib.ptr_array([t.data_ptr() for t in recvbufs]),
-                                      count, _lib.DTYPES[dtype], n, _stream_handle(stream))
+    """All-gather with the fused kernel: every recvbufs[r] receives all shards in rank order."""
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    count = _check_counts("all_gather", sendbufs, recvbufs)
+    with torch.cuda.device(dev):
+        rc = _lib.lib().ar_all_gather(sp, rp, count, _lib.DTYPES[dtype], len(sendbufs), _stream_handle(stream))
     _lib.check("ar_all_gather", rc)
     return recvbufs
+
+
+def ar_all_gather_ex(sendbufs, recvbufs, algo: str = "fused", workspace=None, stream=None):
+    """All-gather with the algorithm chosen by the caller."""
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    count = _check_counts("all_gather", sendbufs, recvbufs)
+    wp, wb = _ws(workspace)
+    with torch.cuda.device(dev):
+        rc = _lib.lib().ar_all_gather_ex(sp, rp, count, _lib.DTYPES[dtype], len(sendbufs), _lib.ALGOS[algo],
+                                         wp, wb, _stream_handle(stream))
+    _lib.check("ar_all_gather_ex", rc)
+    return recvbufs
+
+
+# --------------------------------------------------------------------------
+# persistent collectives
+# --------------------------------------------------------------------------
+
+class Plan:
+    """A persistent collective from one of the ``*_init`` calls.
+
+    Holds references to its tensors (and workspace) so they outlive it;
+    :meth:`start` enqueues the planned kernels; the plan is freed by
+    :meth:`close` or when collected.
+    """
+
+    def __init__(self, handle, device, keep):
+        self._handle = handle
+        self.device = device
+        self._keep = keep
+
+    @property
+    def num_launches(self) -> int:
+        return _lib.lib().ar_plan_num_launches(self._handle)
+
+    def start(self, stream=None):
+        if self._handle is None:
+            raise ValueError("plan is closed")
+        _lib.check("ar_plan_start", _lib.lib().ar_plan_start(self._handle, _stream_handle(stream)))
+
+    def close(self):
+        if self._handle is not None:
+            _lib.lib().ar_plan_free(self._handle)
+            self._handle = None
+            self._keep = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+
+def _make_plan(fn_name, call, device, keep):
+    handle = ctypes.c_void_p()
+    with torch.cuda.device(device):
+        rc = call(ctypes.byref(handle))
+    _lib.check(fn_name, rc)
+    return Plan(handle, device, keep)
+
+
+def ar_allreduce_init(sendbufs, recvbufs=None, op: str = "sum", algo: str = "auto", workspace=None) -> Plan:
+    """Persistent AllReduce; in place when recvbufs is None."""
+    recvbufs = sendbufs if recvbufs is None else recvbufs
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    count = _check_counts("allreduce", sendbufs, recvbufs)
+    wp, wb = _ws(workspace)
+    L = _lib.lib()
+    return _make_plan("ar_allreduce_init",
+                      lambda h: L.ar_allreduce_init(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
+                                                    _lib.ALGOS[algo], wp, wb, h),
+                      dev, (list(sendbufs), list(recvbufs), workspace))
+
+
+def ar_reduce_scatter_init(sendbufs, recvbufs, op: str = "sum", algo: str = "fused", workspace=None) -> Plan:
+    """Persistent reduce-scatter (the ring algorithm gets a workspace from torch if none is given)."""
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    count = _check_counts("reduce_scatter", sendbufs, recvbufs)
+    n = len(sendbufs)
+    with torch.cuda.device(dev):
+        workspace = _rs_workspace(algo, count, dtype, n, workspace, dev, None)
+    wp, wb = _ws(workspace)
+    L = _lib.lib()
+    return _make_plan("ar_reduce_scatter_init",
+                      lambda h: L.ar_reduce_scatter_init(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], n,
+                                                         _lib.ALGOS[algo], wp, wb, h),
+                      dev, (list(sendbufs), list(recvbufs), workspace))
+
+
+def ar_all_gather_init(sendbufs, recvbufs, algo: str = "fused", workspace=None) -> Plan:
+    """Persistent all-gather."""
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    count = _check_counts("all_gather", sendbufs, recvbufs)
+    wp, wb = _ws(workspace)
+    L = _lib.lib()
+    return _make_plan("ar_all_gather_init",
+                      lambda h: L.ar_all_gather_init(sp, rp, count, _lib.DTYPES[dtype], len(sendbufs),
+                                                     _lib.ALGOS[algo], wp, wb, h),
+                      dev, (list(sendbufs), list(recvbufs), workspace))
+
+
+def ar_plan_start(plan: Plan, stream=None):
+    """Enqueue a persistent collective's kernels (same as ``plan.start``)."""
+    plan.start(stream)
+
+
+def ar_plan_free(plan: Plan):
+    """Release a persistent collective (same as ``plan.close``)."""
+    plan.close()

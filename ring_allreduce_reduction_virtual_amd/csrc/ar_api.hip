@@ -14,6 +14,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -270,25 +271,51 @@ const char* kind_name(Kind kd) {
     return "?";
 }
 
-ar_result_t enqueue(Launch& l, Kind kind, const KernelArgs& a, const Common& k, hipStream_t stream) {
-    l.kind = kind;
-    l.dtype = k.dtype;
-    l.op = k.op;
-    if (debug_enabled()) {
-        std::fprintf(stderr,
-                     "[ar] %s dtype=%s op=%d n=%d count=%llu step=%d shift=%d vec=%d ofs=%d tiles/chunk=%u blocks=%u\n",
-                     kind_name(kind), dtype_name(k.dtype), static_cast<int>(k.op), k.n,
-                     static_cast<unsigned long long>(k.count), a.step, a.shift, l.vec ? 1 : 0, a.ofs,
-                     a.tiles_per_chunk, l.blocks);
-    }
+struct Step {
+    Launch l;
+    KernelArgs a;
+};
+
+ar_result_t launch_step(const Launch& l, const KernelArgs& a, hipStream_t stream) {
     const hipError_t e = arimpl::launch(l, a, stream);
-    if (e != hipSuccess) return fail(AR_ERR_HIP, "%s launch: %s", kind_name(kind), hipGetErrorString(e));
+    if (e != hipSuccess) return fail(AR_ERR_HIP, "%s launch: %s", kind_name(l.kind), hipGetErrorString(e));
     return AR_SUCCESS;
 }
 
+// Where planned launches go: straight onto a stream, or into a persistent plan.
+class Sink {
+public:
+    explicit Sink(hipStream_t stream) : stream_(stream) {}
+    explicit Sink(std::vector<Step>* steps) : steps_(steps) {}
+
+    ar_result_t emit(Launch& l, Kind kind, const KernelArgs& a, const Common& k) {
+        l.kind = kind;
+        l.dtype = k.dtype;
+        l.op = k.op;
+        if (debug_enabled()) {
+            std::fprintf(stderr,
+                         "[ar] %s dtype=%s op=%d n=%d count=%llu step=%d shift=%d vec=%d ofs=%d align=2^%d "
+                         "tiles=[%u,%u) tiles/chunk=%u blocks=%u%s\n",
+                         kind_name(kind), dtype_name(k.dtype), static_cast<int>(k.op), k.n,
+                         static_cast<unsigned long long>(k.count), a.step, a.shift, l.vec ? 1 : 0, a.ofs,
+                         a.align_shift, a.tile_first, a.tile_end, a.tiles_per_chunk, l.blocks,
+                         steps_ != nullptr ? " (planned)" : "");
+        }
+        if (steps_ != nullptr) {
+            steps_->push_back(Step{l, a});
+            return AR_SUCCESS;
+        }
+        return launch_step(l, a, stream_);
+    }
+
+private:
+    hipStream_t stream_ = nullptr;
+    std::vector<Step>* steps_ = nullptr;
+};
+
 // ---------------------------------------------------------------------------
 
-ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, hipStream_t stream) {
+ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, Sink& sink) {
     ar_result_t rc = check_common(k, true);
     if (rc != AR_SUCCESS) return rc;
     if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
@@ -326,7 +353,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, hipStream_t stream) 
             sends.push_back(reinterpret_cast<uintptr_t>(k.send[r]));
         }
         if ((rc = plan(a, l, k, common_residue(sends))) != AR_SUCCESS) return rc;
-        if ((rc = enqueue(l, Kind::kFusedReduceScatter, a, k, stream)) != AR_SUCCESS) return rc;
+        if ((rc = sink.emit(l, Kind::kFusedReduceScatter, a, k)) != AR_SUCCESS) return rc;
         // ... then all-gather in place: chunk c of recv[c] to every other rank
         KernelArgs g{};
         Launch lg{};
@@ -337,18 +364,18 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, hipStream_t stream) 
             recvs.push_back(reinterpret_cast<uintptr_t>(k.recv[r]));
         }
         if ((rc = plan(g, lg, k, common_residue(recvs))) != AR_SUCCESS) return rc;
-        return enqueue(lg, Kind::kFusedAllGather, g, k, stream);
+        return sink.emit(lg, Kind::kFusedAllGather, g, k);
     }
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
-    if (algo == AR_ALGO_FUSED) return enqueue(l, Kind::kFusedAllReduce, a, k, stream);
+    if (algo == AR_ALGO_FUSED) return sink.emit(l, Kind::kFusedAllReduce, a, k);
     for (int s = 0; s < k.n - 1; ++s) {          // reduce-scatter steps
         a.step = s;
-        if ((rc = enqueue(l, Kind::kRingReduceStep, a, k, stream)) != AR_SUCCESS) return rc;
+        if ((rc = sink.emit(l, Kind::kRingReduceStep, a, k)) != AR_SUCCESS) return rc;
     }
     for (int s = 0; s < k.n - 1; ++s) {          // all-gather steps
         a.step = s;
         a.shift = 0;
-        if ((rc = enqueue(l, Kind::kRingCopyStep, a, k, stream)) != AR_SUCCESS) return rc;
+        if ((rc = sink.emit(l, Kind::kRingCopyStep, a, k)) != AR_SUCCESS) return rc;
     }
     return AR_SUCCESS;
 }
@@ -358,7 +385,7 @@ uint64_t rs_workspace_bytes(uint64_t count, size_t esz, int n, ar_algo_t algo) {
     return count * esz + 512;  // one full-length buffer of partials, plus room to match residues
 }
 
-ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_bytes, hipStream_t stream) {
+ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_bytes, Sink& sink) {
     ar_result_t rc = check_common(k, true);
     if (rc != AR_SUCCESS) return rc;
     if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
@@ -397,7 +424,7 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
     fill_tables(a, k);
     const Residue residue = common_residue(ptrs);
     if ((rc = plan(a, l, k, residue)) != AR_SUCCESS) return rc;
-    if (algo == AR_ALGO_FUSED || k.n == 1) return enqueue(l, Kind::kFusedReduceScatter, a, k, stream);
+    if (algo == AR_ALGO_FUSED || k.n == 1) return sink.emit(l, Kind::kFusedReduceScatter, a, k);
     if (need) {
         // place the partials at the senders' residue so they stream as aligned vectors too
         const uintptr_t w = (reinterpret_cast<uintptr_t>(ws) + 255u) & ~static_cast<uintptr_t>(255u);
@@ -405,12 +432,12 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
     }
     for (int s = 0; s < k.n - 1; ++s) {
         a.step = s;
-        if ((rc = enqueue(l, Kind::kRingReduceStepWs, a, k, stream)) != AR_SUCCESS) return rc;
+        if ((rc = sink.emit(l, Kind::kRingReduceStepWs, a, k)) != AR_SUCCESS) return rc;
     }
     return AR_SUCCESS;
 }
 
-ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, hipStream_t stream) {
+ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, Sink& sink) {
     ar_result_t rc = check_common(k, false);
     if (rc != AR_SUCCESS) return rc;
     if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
@@ -440,13 +467,41 @@ ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, hipStream_t stream)
     Launch l{};
     fill_tables(a, k);
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
-    if (algo == AR_ALGO_FUSED || k.n == 1) return enqueue(l, Kind::kFusedAllGather, a, k, stream);
-    if ((rc = enqueue(l, Kind::kPlaceShards, a, k, stream)) != AR_SUCCESS) return rc;
+    if (algo == AR_ALGO_FUSED || k.n == 1) return sink.emit(l, Kind::kFusedAllGather, a, k);
+    if ((rc = sink.emit(l, Kind::kPlaceShards, a, k)) != AR_SUCCESS) return rc;
     for (int s = 0; s < k.n - 1; ++s) {
         a.step = s;
         a.shift = 1;
-        if ((rc = enqueue(l, Kind::kRingCopyStep, a, k, stream)) != AR_SUCCESS) return rc;
+        if ((rc = sink.emit(l, Kind::kRingCopyStep, a, k)) != AR_SUCCESS) return rc;
     }
+    return AR_SUCCESS;
+}
+
+}  // namespace
+
+// A persistent collective: the launches one call makes, validated and planned.
+struct ar_plan_s {
+    std::vector<Step> steps;
+};
+
+namespace {
+
+// Persistent collectives: validate and plan once, enqueue many times.
+
+template <typename Build>
+ar_result_t make_plan(ar_plan_t* out, Build build) {
+    g_detail.clear();
+    if (out == nullptr) return fail(AR_ERR_INVALID_ARGUMENT, "null plan pointer");
+    *out = nullptr;
+    ar_plan_s* p = new (std::nothrow) ar_plan_s;
+    if (p == nullptr) return fail(AR_ERR_INTERNAL, "out of host memory");
+    Sink sink(&p->steps);
+    const ar_result_t rc = build(sink);
+    if (rc != AR_SUCCESS) {
+        delete p;
+        return rc;
+    }
+    *out = p;
     return AR_SUCCESS;
 }
 
@@ -456,7 +511,8 @@ extern "C" {
 
 ar_result_t ar_allreduce(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
                          ar_op_t op, int nranks, hipStream_t stream) {
-    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, AR_ALGO_AUTO, stream);
+    Sink sink(stream);
+    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, AR_ALGO_AUTO, sink);
 }
 
 ar_result_t ar_allreduce_ex(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
@@ -464,25 +520,29 @@ ar_result_t ar_allreduce_ex(const void* const* sendbufs, void* const* recvbufs, 
                             hipStream_t stream) {
     (void)workspace;
     (void)workspace_bytes;
-    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, stream);
+    Sink sink(stream);
+    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, sink);
 }
 
 ar_result_t ar_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
                               ar_op_t op, int nranks, hipStream_t stream) {
+    Sink sink(stream);
     return reduce_scatter_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, AR_ALGO_FUSED,
-                               nullptr, 0, stream);
+                               nullptr, 0, sink);
 }
 
 ar_result_t ar_reduce_scatter_ex(const void* const* sendbufs, void* const* recvbufs, size_t count,
                                  ar_dtype_t dtype, ar_op_t op, int nranks, ar_algo_t algo, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
+    Sink sink(stream);
     return reduce_scatter_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, workspace,
-                               workspace_bytes, stream);
+                               workspace_bytes, sink);
 }
 
 ar_result_t ar_all_gather(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
                           int nranks, hipStream_t stream) {
-    return all_gather_impl({sendbufs, recvbufs, count, dtype, AR_SUM, nranks, esize(dtype)}, AR_ALGO_FUSED, stream);
+    Sink sink(stream);
+    return all_gather_impl({sendbufs, recvbufs, count, dtype, AR_SUM, nranks, esize(dtype)}, AR_ALGO_FUSED, sink);
 }
 
 ar_result_t ar_all_gather_ex(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
@@ -490,7 +550,55 @@ ar_result_t ar_all_gather_ex(const void* const* sendbufs, void* const* recvbufs,
                              hipStream_t stream) {
     (void)workspace;
     (void)workspace_bytes;
-    return all_gather_impl({sendbufs, recvbufs, count, dtype, AR_SUM, nranks, esize(dtype)}, algo, stream);
+    Sink sink(stream);
+    return all_gather_impl({sendbufs, recvbufs, count, dtype, AR_SUM, nranks, esize(dtype)}, algo, sink);
+}
+
+ar_result_t ar_allreduce_init(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
+                              ar_op_t op, int nranks, ar_algo_t algo, void* workspace, size_t workspace_bytes,
+                              ar_plan_t* plan) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return make_plan(plan, [&](Sink& sink) {
+        return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, sink);
+    });
+}
+
+ar_result_t ar_reduce_scatter_init(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                                   ar_dtype_t dtype, ar_op_t op, int nranks, ar_algo_t algo, void* workspace,
+                                   size_t workspace_bytes, ar_plan_t* plan) {
+    return make_plan(plan, [&](Sink& sink) {
+        return reduce_scatter_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, workspace,
+                                   workspace_bytes, sink);
+    });
+}
+
+ar_result_t ar_all_gather_init(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
+                               int nranks, ar_algo_t algo, void* workspace, size_t workspace_bytes,
+                               ar_plan_t* plan) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return make_plan(plan, [&](Sink& sink) {
+        return all_gather_impl({sendbufs, recvbufs, count, dtype, AR_SUM, nranks, esize(dtype)}, algo, sink);
+    });
+}
+
+ar_result_t ar_plan_start(ar_plan_t plan, hipStream_t stream) {
+    if (plan == nullptr) return fail(AR_ERR_INVALID_ARGUMENT, "null plan");
+    for (const Step& st : plan->steps) {
+        const ar_result_t rc = launch_step(st.l, st.a, stream);
+        if (rc != AR_SUCCESS) return rc;
+    }
+    return AR_SUCCESS;
+}
+
+int ar_plan_num_launches(ar_plan_t plan) {
+    return plan == nullptr ? -1 : static_cast<int>(plan->steps.size());
+}
+
+ar_result_t ar_plan_free(ar_plan_t plan) {
+    delete plan;
+    return AR_SUCCESS;
 }
 
 size_t ar_workspace_bytes(ar_coll_t coll, ar_algo_t algo, size_t count, ar_dtype_t dtype, int nranks) {

@@ -169,3 +169,30 @@ def test_input_generators_are_seeded_and_prefix_stable():
     assert c4.dtype == np.int32 and c4.min() < -(2**30) and c4.max() > 2**30
     frac = np.mean(np.abs(make_rank(w, 0, count=200000)) > 100)
     assert 0.005 < frac < 0.015          # about 1% outliers scaled by 1e4
+
+
+def test_persistent_plan_host_side(lib):
+    """Plan creation validates like the one-shot calls; empty work plans no launch."""
+    S = 1 << 20
+    sends = [BASE + r * S for r in range(4)]
+    recvs = [BASE + (8 + r) * S for r in range(4)]
+    plan = ctypes.c_void_p(12345)
+    # invalid op: error, and the plan handle is cleared
+    rc = lib.ar_allreduce_init(_ptrs(sends), _ptrs(recvs), 10, 0, 9, 4, 0, None, 0, ctypes.byref(plan))
+    assert rc == 1 and plan.value is None
+    # overlapping receive buffers
+    rc = lib.ar_allreduce_init(_ptrs(sends), _ptrs([recvs[0]] * 4), 10, 0, 0, 4, 0, None, 0, ctypes.byref(plan))
+    assert rc == 1 and b"overlaps" in lib.ar_get_last_error_detail()
+    # ring reduce-scatter without its workspace
+    rc = lib.ar_reduce_scatter_init(_ptrs(sends), _ptrs(recvs), 1000, 0, 0, 4, 1, None, 0, ctypes.byref(plan))
+    assert rc == 1 and b"workspace" in lib.ar_get_last_error_detail()
+    # count == 0: a valid plan that launches nothing and starts without a device
+    rc = lib.ar_allreduce_init(_ptrs(sends), _ptrs(recvs), 0, 0, 0, 4, 1, None, 0, ctypes.byref(plan))
+    assert rc == 0 and plan.value
+    assert lib.ar_plan_num_launches(plan) == 0
+    assert lib.ar_plan_start(plan, None) == 0
+    assert lib.ar_plan_free(plan) == 0
+    assert lib.ar_plan_num_launches(None) == -1
+    assert lib.ar_plan_start(None, None) == 1
+    assert lib.ar_plan_free(None) == 0
+    assert lib.ar_allreduce_init(_ptrs(sends), _ptrs(recvs), 0, 0, 0, 4, 0, None, 0, None) == 1

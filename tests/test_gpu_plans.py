@@ -1,0 +1,118 @@
+"""Persistent collectives (``*_init`` / ``ar_plan_start``) and HIP graph capture.
+
+A plan must give the same bits as the one-shot call, follow its buffers'
+current contents on every start, launch the expected number of kernels, and
+replay correctly from a captured graph, replay after replay, with eager work
+changing the inputs in between.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.ring import chunk, same_bits
+
+from gpu_util import from_dev, require_gpu, tdtype, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _ar():
+    require_gpu()
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    return ar
+
+
+def _draw(n, length, seed, dtype="f32"):
+    rng = np.random.default_rng(seed)
+    xs = [rng.standard_normal(length).astype(np.float32) for _ in range(n)]
+    if dtype == "bf16":
+        xs = [oracle.f32_to_bf16_bits(x) for x in xs]
+    return xs
+
+
+@pytest.mark.parametrize("algo,launches", [("fused", lambda n: 1), ("phases", lambda n: 2),
+                                           ("ring", lambda n: 2 * (n - 1)), ("auto", lambda n: 1 if n < 24 else 2)])
+@pytest.mark.parametrize("n,length", [(5, 1003), (8, 8 * 4096 + 5), (32, 32 * 257 + 3)])
+def test_allreduce_plan_matches_and_follows_inputs(n, length, algo, launches):
+    import torch
+
+    ar = _ar()
+    xs = _draw(n, length, seed=n)
+    sends = [to_dev(x, "f32") for x in xs]
+    recvs = [torch.empty(length, device="cuda:0") for _ in range(n)]
+    plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
+    assert plan.num_launches == launches(n)
+    for rep in range(3):
+        want, _ = oracle.ring_allreduce(xs)
+        plan.start()
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32"), (rep, r)
+        # new contents in the same buffers: the next start must see them
+        xs = [x * np.float32(1.5) + np.float32(rep) for x in xs]
+        for r in range(n):
+            sends[r].copy_(to_dev(xs[r], "f32"))
+    plan.close()
+    plan.close()
+
+
+@pytest.mark.parametrize("algo", ["fused", "ring"])
+def test_phase_plans(algo):
+    import torch
+
+    ar = _ar()
+    n, length = 7, 7 * 1000 + 6
+    xs = _draw(n, length, seed=3, dtype="bf16")
+    sends = [to_dev(x, "bf16") for x in xs]
+    shards = [torch.empty(chunk(r, n, length)[1] - chunk(r, n, length)[0], dtype=torch.bfloat16, device="cuda:0")
+              for r in range(n)]
+    outs = [torch.empty(length, dtype=torch.bfloat16, device="cuda:0") for _ in range(n)]
+    rs = ar.ar_reduce_scatter_init(sends, shards, algo=algo)
+    ag = ar.ar_all_gather_init(shards, outs, algo=algo)
+    assert rs.num_launches == (1 if algo == "fused" else n - 1)
+    assert ag.num_launches == (1 if algo == "fused" else n)
+    ar.ar_plan_start(rs)
+    ar.ar_plan_start(ag)
+    torch.cuda.synchronize()
+    want, _ = oracle.ring_allreduce(xs, dtype="bf16")
+    for r in range(n):
+        assert same_bits(from_dev(outs[r], "bf16"), want[r], "bf16")
+    ar.ar_plan_free(rs)
+    ar.ar_plan_free(ag)
+
+
+@pytest.mark.parametrize("algo", ["fused", "phases", "ring"])
+def test_graph_capture_replays(algo):
+    """Capture 3 starts of a plan in a HIP graph; replay it 4 times with eager input
+    changes in between, checking every replay against the oracle."""
+    import torch
+
+    ar = _ar()
+    n, length = 8, 8 * 2048 + 3
+    xs = _draw(n, length, seed=11)
+    sends = [to_dev(x, "f32") for x in xs]
+    recvs = [torch.empty(length, device="cuda:0") for _ in range(n)]
+    plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.start(side)                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            plan.start()
+    for rep in range(4):
+        xs = [x + np.float32(rep + 1) * np.float32(0.25) for x in xs]
+        for r in range(n):
+            sends[r].copy_(to_dev(xs[r], "f32"))       # eager work between replays
+        for r in range(n):
+            recvs[r].fill_(-7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        want, _ = oracle.ring_allreduce(xs)
+        for r in range(n):
+            assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32"), (rep, r)
