@@ -32,7 +32,10 @@ from .ring import (  # noqa: F401
     bf16_bits_to_f32,
     chunk,
     chunk_owner,
+    f16_bits_to_f32,
     f32_to_bf16_bits,
+    f32_to_f16_bits,
+    finish,
     reduce_op,
     reduce_scatter,
     ring_allreduce,

@@ -28,10 +28,19 @@ Readings where the pages leave a step open (each is listed in the design doc):
   bf16 values is formed in float32 and rounded to nearest-even once);
 * int32 sum and product wrap modulo 2^32;
 * float min/max follow IEEE 754-2019 minimum/maximum: a NaN operand gives
-  NaN, and -0 is below +0.
+  NaN, and -0 is below +0;
+* ``avg`` is the ring's sum followed by one division by N, done by the rank
+  that finishes the chunk ("2.1 Collective communication primitives in
+  detail", section 3.4, and bitfern.com "AllReduce Explained": sum, then
+  divide by the number of workers): float division rounded once to the
+  buffer type, integer division truncating toward zero;
+* ``bf16acc32`` keeps bf16 buffers but lets the partial sums travel in
+  float32, rounding to bf16 once when a chunk is finished (tirogla.com "Ring
+  all-reduce", implementation notes: reduce in fp32, or bf16 with fp32
+  accumulation).
 
-Buffers: ``f32`` -> numpy float32, ``i32`` -> numpy int32, ``bf16`` -> numpy
-uint16 holding the raw bfloat16 bit patterns.
+Buffers: ``f32`` -> numpy float32, ``i32`` -> numpy int32, ``bf16``,
+``bf16acc32`` and ``f16`` -> numpy uint16 holding the raw bit patterns.
 """
 
 from __future__ import annotations
@@ -41,11 +50,13 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-DTYPES = ("f32", "bf16", "i32")
-OPS = ("sum", "prod", "min", "max")
+DTYPES = ("f32", "bf16", "i32", "f16", "bf16acc32")
+OPS = ("sum", "prod", "min", "max", "avg")
 
-_STORAGE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32}
-_ITEMSIZE = {"f32": 4, "bf16": 2, "i32": 4}
+_STORAGE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32, "f16": np.uint16, "bf16acc32": np.uint16}
+_ITEMSIZE = {"f32": 4, "bf16": 2, "i32": 4, "f16": 2, "bf16acc32": 2}
+# precision the partial sums travel in: the buffer's own, except float32 partials for bf16acc32
+_WORK = {"f32": "f32", "bf16": "bf16", "i32": "i32", "f16": "f16", "bf16acc32": "f32"}
 
 
 # --------------------------------------------------------------------------
@@ -101,6 +112,21 @@ def f32_to_bf16_bits(f: np.ndarray) -> np.ndarray:
     return np.where(np.isnan(f), quiet_nan, rounded)
 
 
+def f16_bits_to_f32(u: np.ndarray) -> np.ndarray:
+    """Widen IEEE binary16 bit patterns to float32 (exact)."""
+    return np.asarray(u, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def f32_to_f16_bits(f: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16, to nearest with ties to even (numpy's conversion).
+
+    Overflow gives infinity, results below the normal range keep binary16's
+    subnormal spacing of 2^-24, and NaN stays NaN.
+    """
+    with np.errstate(over="ignore", invalid="ignore"):
+        return np.ascontiguousarray(f, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 # --------------------------------------------------------------------------
 # element operators
 # --------------------------------------------------------------------------
@@ -137,16 +163,21 @@ def reduce_op(op: str, dtype: str, a: np.ndarray, b: np.ndarray) -> np.ndarray:
     """``a (op) b`` elementwise, rounded to the buffer dtype.
 
     f32: one IEEE binary32 operation, round to nearest even.
-    bf16: the operation in float32 on the widened values, then one rounding
-    to bf16 (the per-step rounding a bf16 ring performs).
+    bf16 / f16: the operation in float32 on the widened values, then one
+    rounding to the 16-bit type (the per-step rounding such a ring performs).
     i32: sum and product wrap modulo 2^32; min and max are exact.
+    ``avg`` combines like ``sum``; its division happens once, in :func:`finish`.
     """
     if op not in OPS:
         raise ValueError(f"unknown op {op!r}")
+    if op == "avg":
+        op = "sum"
     if dtype == "f32":
         return _f32_op(op, np.asarray(a, np.float32), np.asarray(b, np.float32))
     if dtype == "bf16":
         return f32_to_bf16_bits(_f32_op(op, bf16_bits_to_f32(a), bf16_bits_to_f32(b)))
+    if dtype == "f16":
+        return f32_to_f16_bits(_f32_op(op, f16_bits_to_f32(a), f16_bits_to_f32(b)))
     if dtype == "i32":
         a = np.asarray(a, np.int32)
         b = np.asarray(b, np.int32)
@@ -158,6 +189,39 @@ def reduce_op(op: str, dtype: str, a: np.ndarray, b: np.ndarray) -> np.ndarray:
             return np.minimum(a, b)
         return np.maximum(a, b)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def to_work(x: np.ndarray, dtype: str) -> np.ndarray:
+    """A rank's buffer in the precision its partial sums travel in (a copy)."""
+    if dtype == "bf16acc32":
+        return bf16_bits_to_f32(x)
+    return np.array(x, dtype=_STORAGE[dtype], copy=True)
+
+
+def finish(op: str, dtype: str, v: np.ndarray, n: int) -> np.ndarray:
+    """Complete a finished chunk (in working precision) and return it in the buffer type.
+
+    ``avg`` divides the sum by N once: float division rounded to the buffer
+    type (16-bit types: the float32 quotient rounded once more, which is the
+    correctly rounded quotient since 24 >= 2*11+2), int32 division truncating
+    toward zero.  bf16acc32 rounds its float32 partial to bf16 here.
+    """
+    wd = _WORK[dtype]
+    if op == "avg":
+        if wd == "f32":
+            with np.errstate(over="ignore", invalid="ignore"):
+                v = np.divide(np.asarray(v, np.float32), np.float32(n), dtype=np.float32)
+        elif wd == "bf16":
+            v = f32_to_bf16_bits(np.divide(bf16_bits_to_f32(v), np.float32(n), dtype=np.float32))
+        elif wd == "f16":
+            v = f32_to_f16_bits(np.divide(f16_bits_to_f32(v), np.float32(n), dtype=np.float32))
+        else:
+            w = np.asarray(v, np.int32).astype(np.int64)
+            q = np.where(w >= 0, w // n, -((-w) // n))
+            v = q.astype(np.int32)
+    if dtype == "bf16acc32":
+        return f32_to_bf16_bits(np.asarray(v, np.float32))
+    return np.asarray(v, dtype=_STORAGE[dtype])
 
 
 # --------------------------------------------------------------------------
@@ -188,7 +252,11 @@ def _check_inputs(xs, dtype: str):
 
 
 def _reduce_scatter_phase(buf, mailbox, stats, op, dtype, on_step):
-    """Reduce-scatter: N-1 steps; each rank sends one chunk right and adds the one from the left."""
+    """Reduce-scatter: N-1 steps; each rank sends one chunk right and adds the one from the left.
+
+    ``buf`` holds the ranks' working copies and ``dtype`` is the working
+    precision (messages are counted at its element size).
+    """
     n = len(buf)
     length = len(buf[0])
     esz = _ITEMSIZE[dtype]
@@ -249,11 +317,9 @@ def ring_allreduce(xs, op: str = "sum", dtype: str = "f32", on_step=None, check=
     holds the same bits.
     """
     n, length = _check_inputs(xs, dtype)
-    buf = [np.array(x, dtype=_STORAGE[dtype], copy=True) for x in xs]
-    mailbox = [deque() for _ in range(n)]
     stats = RingStats(sent=[0] * n, received=[0] * n)
-
-    _reduce_scatter_phase(buf, mailbox, stats, op, dtype, on_step)
+    buf = _reduce_scatter_and_finish(xs, op, dtype, on_step, stats)
+    mailbox = [deque() for _ in range(n)]
     if check and n > 1:
         want = ring_order_fold(xs, op, dtype)
         for r in range(n):
@@ -273,6 +339,25 @@ def ring_allreduce(xs, op: str = "sum", dtype: str = "f32", on_step=None, check=
     return buf, stats
 
 
+def _reduce_scatter_and_finish(xs, op, dtype, on_step, stats):
+    """The reduce-scatter steps in working precision; then rank r completes the
+    chunk it finished, chunk (r+1) mod N, and every buffer returns to the
+    buffer type (its unfinished chunks are overwritten by the all-gather)."""
+    n, length = len(xs), len(xs[0])
+    buf = [to_work(x, dtype) for x in xs]
+    mailbox = [deque() for _ in range(n)]
+    _reduce_scatter_phase(buf, mailbox, stats, op, _WORK[dtype], on_step)
+    if any(mailbox):
+        raise AssertionError("messages left undelivered")
+    out = []
+    for r in range(n):
+        a, b = chunk((r + 1) % n, n, length)
+        o = f32_to_bf16_bits(buf[r]) if dtype == "bf16acc32" else buf[r]
+        o[a:b] = finish(op, dtype, buf[r][a:b], n)
+        out.append(o)
+    return out
+
+
 def reduce_scatter(xs, op: str = "sum", dtype: str = "f32", on_step=None):
     """Standalone reduce-scatter: returns (shards, stats) with shard c on rank c.
 
@@ -281,10 +366,8 @@ def reduce_scatter(xs, op: str = "sum", dtype: str = "f32", on_step=None):
     "2.1 Collective communication primitives in detail", section 3.5).
     """
     n, length = _check_inputs(xs, dtype)
-    buf = [np.array(x, dtype=_STORAGE[dtype], copy=True) for x in xs]
-    mailbox = [deque() for _ in range(n)]
     stats = RingStats(sent=[0] * n, received=[0] * n)
-    _reduce_scatter_phase(buf, mailbox, stats, op, dtype, on_step)
+    buf = _reduce_scatter_and_finish(xs, op, dtype, on_step, stats)
     shards = []
     for c in range(n):
         a, b = chunk(c, n, length)
@@ -298,16 +381,16 @@ def all_gather(shards, length: int, dtype: str = "f32", on_step=None, poison=Non
     Follows ramchalamkr.github.io "NCCL Primitives Deep Dive", section "Ring
     All-Gather": the shard sits in slot r, and at step s rank r sends slot
     (r-s) mod N and receives slot (r-s-1) mod N.  Slots not yet received hold
-    ``poison`` (NaN for floats, 0xDEADBEEF / 0xDEAD for integers and bf16
-    bits) so a missed slot cannot pass unnoticed.  ``on_step`` also sees the
+    ``poison`` (NaN for float32, 0xDEADBEEF for int32, 0xDEAD for the 16-bit
+    types) so a missed slot cannot pass unnoticed.  ``on_step`` also sees the
     starting state, as phase "start" with step -1.
     """
     n = len(shards)
     if dtype not in DTYPES:
         raise ValueError(f"unknown dtype {dtype!r}")
     if poison is None:
-        poison = {"f32": np.float32(np.nan), "bf16": np.uint16(0xDEAD),
-                  "i32": np.uint32(0xDEADBEEF).view(np.int32)}[dtype]
+        poison = {"f32": np.float32(np.nan), "bf16": np.uint16(0xDEAD), "bf16acc32": np.uint16(0xDEAD),
+                  "f16": np.uint16(0xDEAD), "i32": np.uint32(0xDEADBEEF).view(np.int32)}[dtype]
     buf = []
     for r in range(n):
         a, b = chunk(r, n, length)
@@ -342,13 +425,14 @@ def ring_order_fold(xs, op: str = "sum", dtype: str = "f32") -> np.ndarray:
     rounded to the buffer dtype after every operation.
     """
     n, length = _check_inputs(xs, dtype)
+    wd = _WORK[dtype]
     out = np.empty(length, dtype=_STORAGE[dtype])
     for c in range(n):
         a, b = chunk(c, n, length)
-        acc = np.array(xs[c][a:b], dtype=_STORAGE[dtype], copy=True)
+        acc = to_work(xs[c][a:b], dtype)
         for k in range(1, n):
-            acc = reduce_op(op, dtype, acc, xs[(c + k) % n][a:b])
-        out[a:b] = acc
+            acc = reduce_op(op, wd, acc, to_work(xs[(c + k) % n][a:b], dtype))
+        out[a:b] = finish(op, dtype, acc, n)
     return out
 
 
@@ -362,12 +446,13 @@ def ring_order_fold_columns(cols: np.ndarray, owners, op: str = "sum", dtype: st
     """
     cols = np.asarray(cols)
     n, m = cols.shape
+    wd = _WORK.get(dtype, dtype)
     owners = np.asarray(owners, dtype=np.int64)
     j = np.arange(m)
-    acc = cols[owners % n, j].copy()
+    acc = to_work(cols[owners % n, j], dtype)
     for k in range(1, n):
-        acc = reduce_op(op, dtype, acc, cols[(owners + k) % n, j])
-    return acc
+        acc = reduce_op(op, wd, acc, to_work(cols[(owners + k) % n, j], dtype))
+    return finish(op, dtype, acc, n)
 
 
 def _same_bits(a: np.ndarray, b: np.ndarray, dtype: str) -> bool:
@@ -380,8 +465,9 @@ def _same_bits(a: np.ndarray, b: np.ndarray, dtype: str) -> bool:
         nan_a, nan_b = np.isnan(a), np.isnan(b)
         return bool(np.array_equal(nan_a, nan_b)
                     and np.array_equal(a.view(np.uint32)[~nan_a], b.view(np.uint32)[~nan_b]))
-    if dtype == "bf16":
-        fa, fb = bf16_bits_to_f32(a), bf16_bits_to_f32(b)
+    if dtype in ("bf16", "bf16acc32", "f16"):
+        widen = f16_bits_to_f32 if dtype == "f16" else bf16_bits_to_f32
+        fa, fb = widen(a), widen(b)
         nan_a, nan_b = np.isnan(fa), np.isnan(fb)
         return bool(np.array_equal(nan_a, nan_b) and np.array_equal(a[~nan_a], b[~nan_b]))
     return bool(np.array_equal(a, b))
