@@ -64,23 +64,34 @@ typedef enum {
     AR_ERR_INTERNAL = 4
 } ar_result_t;
 
-/* Element types.  bf16 results are rounded to bf16 (nearest, ties to even)
- * after every ring step, as a ring that keeps bf16 buffers does. */
+/* Element types.  AR_BFLOAT16 and AR_FLOAT16 results are rounded to the
+ * 16-bit type (nearest, ties to even) after every ring step, as a ring that
+ * keeps 16-bit buffers does.  AR_BFLOAT16_ACC_F32 has bf16 buffers but keeps
+ * the partial sums in float32 and rounds to bf16 once, when a chunk is
+ * complete (tirogla.com "Ring all-reduce", implementation notes: reduce in
+ * fp32, or at least bf16 with fp32 accumulation). */
 typedef enum {
     AR_FLOAT32 = 0,
     AR_BFLOAT16 = 1,
-    AR_INT32 = 2
+    AR_INT32 = 2,
+    AR_FLOAT16 = 3,
+    AR_BFLOAT16_ACC_F32 = 4
 } ar_dtype_t;
 
-/* Reduction operators (sum, product, minimum, maximum: bitfern.com
+/* Reduction operators (sum, product, minimum, maximum, average: bitfern.com
  * "AllReduce Explained", section "What Is AllReduce?").  int32 sum and
  * product wrap modulo 2^32.  Float min/max are IEEE 754-2019 minimum and
- * maximum: a NaN operand gives NaN, and -0 < +0. */
+ * maximum: a NaN operand gives NaN, and -0 < +0.  AR_AVG is the ring's sum
+ * divided by nranks once, when a chunk is complete ("2.1 Collective
+ * communication primitives in detail", section 3.4: sum, then divide by N):
+ * a float quotient rounded once to the buffer type, or an int32 quotient
+ * truncated toward zero from the wrapped sum. */
 typedef enum {
     AR_SUM = 0,
     AR_PROD = 1,
     AR_MIN = 2,
-    AR_MAX = 3
+    AR_MAX = 3,
+    AR_AVG = 4
 } ar_op_t;
 
 /* AR_ALGO_FUSED: one kernel reads element i from all N ranks, reduces it in
@@ -145,9 +156,11 @@ ar_result_t ar_all_gather(const void* const* sendbufs, void* const* recvbufs, si
  * `workspace` is device memory of at least ar_workspace_bytes(...) bytes
  * owned by the caller (NULL when that size is 0); it must not overlap any
  * buffer and must stay valid until the stream work completes.  Only the ring
- * reduce-scatter with nranks >= 3 needs one: it holds the partial sums in
- * flight between steps, since its receive buffers are only one shard long.
- * The ring AllReduce and ring all-gather work in recvbufs. */
+ * algorithm needs one, for nranks >= 3: the reduce-scatter keeps the partial
+ * sums in flight between steps in it, since its receive buffers are only one
+ * shard long, and so does the AllReduce of AR_BFLOAT16_ACC_F32, whose float32
+ * partials do not fit the bf16 buffers.  Other ring AllReduces and the ring
+ * all-gather work in recvbufs. */
 ar_result_t ar_allreduce_ex(const void* const* sendbufs, void* const* recvbufs, size_t count,
                             ar_dtype_t dtype, ar_op_t op, int nranks, ar_algo_t algo,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -15,8 +15,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libar.so")
 AR_SUCCESS = 0
 RESULT_NAMES = {0: "AR_SUCCESS", 1: "AR_ERR_INVALID_ARGUMENT", 2: "AR_ERR_UNSUPPORTED",
                 3: "AR_ERR_HIP", 4: "AR_ERR_INTERNAL"}
-DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
-OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3}
+DTYPES = {"f32": 0, "bf16": 1, "i32": 2, "f16": 3, "bf16acc32": 4}
+OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
 ALGOS = {"fused": 0, "ring": 1, "phases": 2, "auto": 3}
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
 MAX_RANKS = 128

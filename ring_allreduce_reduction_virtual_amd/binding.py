@@ -9,7 +9,10 @@ memory and the stream.
 ``sendbufs`` / ``recvbufs`` are sequences of one tensor per virtual rank.
 ``count`` is always the full per-rank length (see include/ar.h): for
 reduce-scatter the receive tensors hold one chunk each, for all-gather the
-send tensors do.  ``algo`` is one of "fused", "ring", "phases", "auto".
+send tensors do.  ``algo`` is one of "fused", "ring", "phases", "auto";
+``op`` one of "sum", "prod", "min", "max", "avg".  The element type follows
+the tensors (float32, bfloat16, float16, int32); ``dtype="bf16acc32"`` with
+bfloat16 tensors keeps the partial sums in float32.
 
 The ``*_init`` functions return a :class:`Plan`, the persistent form of a
 call: validated once, then enqueued by :meth:`Plan.start` (or
@@ -25,7 +28,7 @@ import torch
 
 from . import _lib
 
-_TORCH_DTYPES = {torch.float32: "f32", torch.bfloat16: "bf16", torch.int32: "i32"}
+_TORCH_DTYPES = {torch.float32: "f32", torch.bfloat16: "bf16", torch.int32: "i32", torch.float16: "f16"}
 
 
 def _stream_handle(stream):
@@ -36,7 +39,7 @@ def _stream_handle(stream):
     return int(stream)
 
 
-def _marshal(sendbufs, recvbufs):
+def _marshal(sendbufs, recvbufs, dtype=None):
     """Check the two tensor lists; return (device, dtype name, send array, recv array)."""
     n = len(sendbufs)
     if len(recvbufs) != n:
@@ -48,7 +51,12 @@ def _marshal(sendbufs, recvbufs):
         raise ValueError("buffers must be CUDA tensors")
     dev, dt = t0.device, t0.dtype
     if dt not in _TORCH_DTYPES:
-        raise TypeError(f"unsupported dtype {dt}; use float32, bfloat16 or int32")
+        raise TypeError(f"unsupported dtype {dt}; use float32, bfloat16, float16 or int32")
+    name = _TORCH_DTYPES[dt]
+    if dtype is not None and dtype != name:
+        if not (dtype == "bf16acc32" and name == "bf16"):
+            raise TypeError(f"dtype {dtype!r} does not fit {dt} tensors")
+        name = dtype
     sp = (ctypes.c_void_p * n)()
     rp = (ctypes.c_void_p * n)()
     for i in range(n):
@@ -62,7 +70,7 @@ def _marshal(sendbufs, recvbufs):
                 raise ValueError("buffers must be contiguous")
         sp[i] = s.data_ptr()
         rp[i] = r.data_ptr()
-    return dev, _TORCH_DTYPES[dt], sp, rp
+    return dev, name, sp, rp
 
 
 def _ws(workspace):
@@ -112,8 +120,8 @@ def _check_counts(coll, sendbufs, recvbufs):
     return count
 
 
-def _rs_workspace(algo, count, dtype, n, workspace, dev, stream):
-    need = ar_workspace_bytes("reduce_scatter", algo, count, dtype, n)
+def _workspace(coll, algo, count, dtype, n, workspace, dev, stream):
+    need = ar_workspace_bytes(coll, algo, count, dtype, n)
     if need and workspace is None:
         if stream is not None and not isinstance(stream, torch.cuda.Stream):
             raise ValueError("pass a workspace when the stream is a raw handle")
@@ -127,10 +135,10 @@ def _rs_workspace(algo, count, dtype, n, workspace, dev, stream):
 # one-shot calls
 # --------------------------------------------------------------------------
 
-def ar_allreduce(sendbufs, recvbufs=None, op: str = "sum", stream=None):
+def ar_allreduce(sendbufs, recvbufs=None, op: str = "sum", stream=None, dtype=None):
     """AllReduce (algorithm AR_ALGO_AUTO); in place when recvbufs is None."""
     recvbufs = sendbufs if recvbufs is None else recvbufs
-    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("allreduce", sendbufs, recvbufs)
     with torch.cuda.device(dev):
         rc = _lib.lib().ar_allreduce(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
@@ -139,22 +147,28 @@ def ar_allreduce(sendbufs, recvbufs=None, op: str = "sum", stream=None):
     return recvbufs
 
 
-def ar_allreduce_ex(sendbufs, recvbufs=None, op: str = "sum", algo: str = "fused", workspace=None, stream=None):
-    """AllReduce with the algorithm chosen by the caller; in place when recvbufs is None."""
+def ar_allreduce_ex(sendbufs, recvbufs=None, op: str = "sum", algo: str = "fused", workspace=None, stream=None,
+                    dtype=None):
+    """AllReduce with the algorithm chosen by the caller; in place when recvbufs is None.
+
+    A ring AllReduce with float32 partials needs a workspace; when none is
+    given one is taken from torch's allocator on the stream of the call.
+    """
     recvbufs = sendbufs if recvbufs is None else recvbufs
-    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("allreduce", sendbufs, recvbufs)
-    wp, wb = _ws(workspace)
     with torch.cuda.device(dev):
+        workspace = _workspace("allreduce", algo, count, dtype, len(sendbufs), workspace, dev, stream)
+        wp, wb = _ws(workspace)
         rc = _lib.lib().ar_allreduce_ex(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
                                         _lib.ALGOS[algo], wp, wb, _stream_handle(stream))
     _lib.check("ar_allreduce_ex", rc)
     return recvbufs
 
 
-def ar_reduce_scatter(sendbufs, recvbufs, op: str = "sum", stream=None):
+def ar_reduce_scatter(sendbufs, recvbufs, op: str = "sum", stream=None, dtype=None):
     """Reduce-scatter with the fused kernel: recvbufs[r] receives chunk r of the reduction."""
-    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("reduce_scatter", sendbufs, recvbufs)
     with torch.cuda.device(dev):
         rc = _lib.lib().ar_reduce_scatter(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
@@ -163,17 +177,18 @@ def ar_reduce_scatter(sendbufs, recvbufs, op: str = "sum", stream=None):
     return recvbufs
 
 
-def ar_reduce_scatter_ex(sendbufs, recvbufs, op: str = "sum", algo: str = "fused", workspace=None, stream=None):
+def ar_reduce_scatter_ex(sendbufs, recvbufs, op: str = "sum", algo: str = "fused", workspace=None, stream=None,
+                         dtype=None):
     """Reduce-scatter with the algorithm chosen by the caller.
 
     The ring algorithm needs a workspace (ar_workspace_bytes); when none is
     given one is taken from torch's allocator on the stream of the call.
     """
-    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("reduce_scatter", sendbufs, recvbufs)
     n = len(sendbufs)
     with torch.cuda.device(dev):
-        workspace = _rs_workspace(algo, count, dtype, n, workspace, dev, stream)
+        workspace = _workspace("reduce_scatter", algo, count, dtype, n, workspace, dev, stream)
         wp, wb = _ws(workspace)
         rc = _lib.lib().ar_reduce_scatter_ex(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], n,
                                              _lib.ALGOS[algo], wp, wb, _stream_handle(stream))
@@ -250,11 +265,14 @@ def _make_plan(fn_name, call, device, keep):
     return Plan(handle, device, keep)
 
 
-def ar_allreduce_init(sendbufs, recvbufs=None, op: str = "sum", algo: str = "auto", workspace=None) -> Plan:
+def ar_allreduce_init(sendbufs, recvbufs=None, op: str = "sum", algo: str = "auto", workspace=None,
+                      dtype=None) -> Plan:
     """Persistent AllReduce; in place when recvbufs is None."""
     recvbufs = sendbufs if recvbufs is None else recvbufs
-    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("allreduce", sendbufs, recvbufs)
+    with torch.cuda.device(dev):
+        workspace = _workspace("allreduce", algo, count, dtype, len(sendbufs), workspace, dev, None)
     wp, wb = _ws(workspace)
     L = _lib.lib()
     return _make_plan("ar_allreduce_init",
@@ -263,13 +281,14 @@ def ar_allreduce_init(sendbufs, recvbufs=None, op: str = "sum", algo: str = "aut
                       dev, (list(sendbufs), list(recvbufs), workspace))
 
 
-def ar_reduce_scatter_init(sendbufs, recvbufs, op: str = "sum", algo: str = "fused", workspace=None) -> Plan:
+def ar_reduce_scatter_init(sendbufs, recvbufs, op: str = "sum", algo: str = "fused", workspace=None,
+                           dtype=None) -> Plan:
     """Persistent reduce-scatter (the ring algorithm gets a workspace from torch if none is given)."""
-    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("reduce_scatter", sendbufs, recvbufs)
     n = len(sendbufs)
     with torch.cuda.device(dev):
-        workspace = _rs_workspace(algo, count, dtype, n, workspace, dev, None)
+        workspace = _workspace("reduce_scatter", algo, count, dtype, n, workspace, dev, None)
     wp, wb = _ws(workspace)
     L = _lib.lib()
     return _make_plan("ar_reduce_scatter_init",

@@ -88,15 +88,22 @@ size_t esize(ar_dtype_t dt) {
         case AR_FLOAT32: return 4;
         case AR_BFLOAT16: return 2;
         case AR_INT32: return 4;
+        case AR_FLOAT16: return 2;
+        case AR_BFLOAT16_ACC_F32: return 2;
     }
     return 0;
 }
+
+// Bytes of one partial sum between ring steps: float32 for AR_BFLOAT16_ACC_F32.
+size_t partial_size(ar_dtype_t dt) { return dt == AR_BFLOAT16_ACC_F32 ? 4 : esize(dt); }
 
 const char* dtype_name(ar_dtype_t dt) {
     switch (dt) {
         case AR_FLOAT32: return "f32";
         case AR_BFLOAT16: return "bf16";
         case AR_INT32: return "i32";
+        case AR_FLOAT16: return "f16";
+        case AR_BFLOAT16_ACC_F32: return "bf16acc32";
     }
     return "?";
 }
@@ -152,7 +159,7 @@ struct Common {
 ar_result_t check_common(const Common& k, bool has_op) {
     g_detail.clear();
     if (k.esz == 0) return fail(AR_ERR_INVALID_ARGUMENT, "unknown dtype %d", static_cast<int>(k.dtype));
-    if (has_op && (k.op < AR_SUM || k.op > AR_MAX)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown op %d", static_cast<int>(k.op));
+    if (has_op && (k.op < AR_SUM || k.op > AR_AVG)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown op %d", static_cast<int>(k.op));
     if (k.n < 1 || k.n > AR_MAX_RANKS) return fail(AR_ERR_INVALID_ARGUMENT, "nranks %d outside [1, %d]", k.n, AR_MAX_RANKS);
     if (k.send == nullptr || k.recv == nullptr) return fail(AR_ERR_INVALID_ARGUMENT, "null pointer array");
     if (k.count > (UINT64_MAX / AR_MAX_RANKS) / 16) return fail(AR_ERR_INVALID_ARGUMENT, "count %llu too large",
@@ -315,7 +322,40 @@ private:
 
 // ---------------------------------------------------------------------------
 
-ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, Sink& sink) {
+// Workspace of the ring algorithm: one full-length buffer of partial sums
+// for the reduce-scatter, and for the AllReduce of AR_BFLOAT16_ACC_F32; none
+// with fewer than 3 ranks, where the only reduce step is also the last.  The
+// extra 1024 bytes cover placing the partials at the senders' residue: up to
+// 255 bytes to reach a 256-byte boundary, plus the residue itself in
+// partial-sized elements (below 256 / element size elements of 4 bytes).
+constexpr uint64_t kWorkspaceSlack = 1024;
+
+uint64_t ring_workspace_bytes(ar_coll_t coll, uint64_t count, ar_dtype_t dt, int n, ar_algo_t algo) {
+    if (algo != AR_ALGO_RING || n < 3 || count == 0) return 0;
+    if (coll == AR_COLL_REDUCE_SCATTER || (coll == AR_COLL_ALLREDUCE && dt == AR_BFLOAT16_ACC_F32))
+        return count * partial_size(dt) + kWorkspaceSlack;
+    return 0;
+}
+
+// Check the caller's workspace and place the partials at the senders'
+// residue (in partial-sized elements) so that they stream as aligned vectors.
+ar_result_t use_workspace(KernelArgs& a, const Common& k, ar_coll_t coll, ar_algo_t algo, void* ws,
+                          size_t ws_bytes, std::vector<Interval>* iv) {
+    const uint64_t need = ring_workspace_bytes(coll, k.count, k.dtype, k.n, algo);
+    if (need == 0) return AR_SUCCESS;
+    if (ws == nullptr || ws_bytes < need)
+        return fail(AR_ERR_INVALID_ARGUMENT, "the ring algorithm needs a workspace of %llu bytes here",
+                    static_cast<unsigned long long>(need));
+    const uintptr_t w = reinterpret_cast<uintptr_t>(ws);
+    if (iv != nullptr) iv->push_back({w, w + need, true, 0, 2});
+    const uintptr_t base = (w + 255u) & ~static_cast<uintptr_t>(255u);
+    const uintptr_t shift = base - w + static_cast<uintptr_t>(a.ofs) * partial_size(k.dtype);
+    if (shift + k.count * partial_size(k.dtype) > need) return fail(AR_ERR_INTERNAL, "workspace placement");
+    a.ws = reinterpret_cast<char*>(w + shift);
+    return AR_SUCCESS;
+}
+
+ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_bytes, Sink& sink) {
     ar_result_t rc = check_common(k, true);
     if (rc != AR_SUCCESS) return rc;
     if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
@@ -334,14 +374,18 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, Sink& sink) {
         ptrs.push_back(s);
         ptrs.push_back(d);
     }
+    if (algo == AR_ALGO_AUTO) algo = (k.n >= phases_min_ranks()) ? AR_ALGO_PHASES : AR_ALGO_FUSED;
+    if (k.n == 1) algo = AR_ALGO_FUSED;           // a copy
+    {
+        KernelArgs probe{};
+        if ((rc = use_workspace(probe, k, AR_COLL_ALLREDUCE, algo, ws, ws_bytes, &iv)) != AR_SUCCESS) return rc;
+    }
     rc = check_overlaps(iv, [&](const Interval& s, const Interval& d) {
         return s.rank == d.rank && s.lo == d.lo;   // in place: send[r] == recv[r]
     });
     if (rc != AR_SUCCESS) return rc;
     if (k.count == 0) return AR_SUCCESS;
 
-    if (algo == AR_ALGO_AUTO) algo = (k.n >= phases_min_ranks()) ? AR_ALGO_PHASES : AR_ALGO_FUSED;
-    if (k.n == 1) algo = AR_ALGO_FUSED;           // a copy
     KernelArgs a{};
     Launch l{};
     fill_tables(a, k);
@@ -368,9 +412,22 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, Sink& sink) {
     }
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_FUSED) return sink.emit(l, Kind::kFusedAllReduce, a, k);
-    for (int s = 0; s < k.n - 1; ++s) {          // reduce-scatter steps
-        a.step = s;
-        if ((rc = sink.emit(l, Kind::kRingReduceStep, a, k)) != AR_SUCCESS) return rc;
+    if (k.dtype == AR_BFLOAT16_ACC_F32) {
+        // float32 partials travel through the workspace; the last step leaves
+        // finished chunk c in chunk c of rank c-1's own buffer, as the ring does
+        KernelArgs w = a;
+        if ((rc = use_workspace(w, k, AR_COLL_ALLREDUCE, algo, ws, ws_bytes, nullptr)) != AR_SUCCESS) return rc;
+        for (int c = 0; c < k.n; ++c)
+            w.recv[c] = static_cast<char*>(k.recv[(c + k.n - 1) % k.n]) + chunk_start(c, k.count, k.n) * k.esz;
+        for (int s = 0; s < k.n - 1; ++s) {
+            w.step = s;
+            if ((rc = sink.emit(l, Kind::kRingReduceStepWs, w, k)) != AR_SUCCESS) return rc;
+        }
+    } else {
+        for (int s = 0; s < k.n - 1; ++s) {      // reduce-scatter steps
+            a.step = s;
+            if ((rc = sink.emit(l, Kind::kRingReduceStep, a, k)) != AR_SUCCESS) return rc;
+        }
     }
     for (int s = 0; s < k.n - 1; ++s) {          // all-gather steps
         a.step = s;
@@ -378,11 +435,6 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, Sink& sink) {
         if ((rc = sink.emit(l, Kind::kRingCopyStep, a, k)) != AR_SUCCESS) return rc;
     }
     return AR_SUCCESS;
-}
-
-uint64_t rs_workspace_bytes(uint64_t count, size_t esz, int n, ar_algo_t algo) {
-    if (algo != AR_ALGO_RING || n < 3 || count == 0) return 0;
-    return count * esz + 512;  // one full-length buffer of partials, plus room to match residues
 }
 
 ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_bytes, Sink& sink) {
@@ -404,13 +456,9 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
         if (cl) iv.push_back({d, d + cl * k.esz, true, r, 1});
         ptrs.push_back(s);
     }
-    const uint64_t need = rs_workspace_bytes(k.count, k.esz, k.n, algo);
-    if (need) {
-        if (ws == nullptr || ws_bytes < need)
-            return fail(AR_ERR_INVALID_ARGUMENT, "ring reduce-scatter needs a workspace of %llu bytes",
-                        static_cast<unsigned long long>(need));
-        const uintptr_t w = reinterpret_cast<uintptr_t>(ws);
-        iv.push_back({w, w + need, true, 0, 2});
+    {
+        KernelArgs probe{};
+        if ((rc = use_workspace(probe, k, AR_COLL_REDUCE_SCATTER, algo, ws, ws_bytes, &iv)) != AR_SUCCESS) return rc;
     }
     rc = check_overlaps(iv, [&](const Interval& s, const Interval& d) {
         // in place: recv[r] == send[r] + start(r) elements
@@ -425,11 +473,7 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
     const Residue residue = common_residue(ptrs);
     if ((rc = plan(a, l, k, residue)) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_FUSED || k.n == 1) return sink.emit(l, Kind::kFusedReduceScatter, a, k);
-    if (need) {
-        // place the partials at the senders' residue so they stream as aligned vectors too
-        const uintptr_t w = (reinterpret_cast<uintptr_t>(ws) + 255u) & ~static_cast<uintptr_t>(255u);
-        a.ws = reinterpret_cast<char*>(w + static_cast<uintptr_t>(residue.bytes >= 0 ? residue.bytes : 0));
-    }
+    if ((rc = use_workspace(a, k, AR_COLL_REDUCE_SCATTER, algo, ws, ws_bytes, nullptr)) != AR_SUCCESS) return rc;
     for (int s = 0; s < k.n - 1; ++s) {
         a.step = s;
         if ((rc = sink.emit(l, Kind::kRingReduceStepWs, a, k)) != AR_SUCCESS) return rc;
@@ -512,16 +556,16 @@ extern "C" {
 ar_result_t ar_allreduce(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
                          ar_op_t op, int nranks, hipStream_t stream) {
     Sink sink(stream);
-    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, AR_ALGO_AUTO, sink);
+    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, AR_ALGO_AUTO, nullptr, 0,
+                          sink);
 }
 
 ar_result_t ar_allreduce_ex(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
                             ar_op_t op, int nranks, ar_algo_t algo, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     Sink sink(stream);
-    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, sink);
+    return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, workspace,
+                          workspace_bytes, sink);
 }
 
 ar_result_t ar_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
@@ -557,10 +601,9 @@ ar_result_t ar_all_gather_ex(const void* const* sendbufs, void* const* recvbufs,
 ar_result_t ar_allreduce_init(const void* const* sendbufs, void* const* recvbufs, size_t count, ar_dtype_t dtype,
                               ar_op_t op, int nranks, ar_algo_t algo, void* workspace, size_t workspace_bytes,
                               ar_plan_t* plan) {
-    (void)workspace;
-    (void)workspace_bytes;
     return make_plan(plan, [&](Sink& sink) {
-        return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, sink);
+        return allreduce_impl({sendbufs, recvbufs, count, dtype, op, nranks, esize(dtype)}, algo, workspace,
+                              workspace_bytes, sink);
     });
 }
 
@@ -609,9 +652,8 @@ size_t ar_workspace_bytes(ar_coll_t coll, ar_algo_t algo, size_t count, ar_dtype
     switch (coll) {
         case AR_COLL_ALLREDUCE:
         case AR_COLL_ALL_GATHER:
-            return 0;
         case AR_COLL_REDUCE_SCATTER:
-            return static_cast<size_t>(rs_workspace_bytes(count, e, nranks, algo));
+            return static_cast<size_t>(ring_workspace_bytes(coll, count, dtype, nranks, algo));
     }
     return static_cast<size_t>(-1);
 }

@@ -53,12 +53,25 @@ constexpr int kBatch = AR_RANK_BATCH;
 #define AR_NT_STORES 1
 #endif
 
+// Element types: float32 and int32 (4 bytes); bf16, IEEE binary16 and bf16
+// with float32 partial sums (2 bytes).
 template <int DT>
-constexpr int elem_size() { return DT == AR_BFLOAT16 ? 2 : 4; }
+constexpr int elem_size() { return (DT == AR_FLOAT32 || DT == AR_INT32) ? 4 : 2; }
+
+// AR_BFLOAT16_ACC_F32 keeps its partial sums in float32 and rounds to bf16
+// once, when a chunk is complete; every other type keeps its partials in the
+// buffer type, rounded after each operation.
+template <int DT>
+constexpr bool acc_f32() { return DT == AR_BFLOAT16_ACC_F32; }
+
+// avg combines like sum; its one division by N happens when a chunk is complete.
+constexpr int combine_op(int op) { return op == AR_AVG ? AR_SUM : op; }
 
 // ---------------------------------------------------------------------------
 // element arithmetic
 // ---------------------------------------------------------------------------
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
@@ -112,21 +125,35 @@ __device__ __forceinline__ uint32_t bf16_round(float f) {
     return ((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded;
 }
 
+// IEEE binary16 <-> float32 with the hardware conversions (exact widening;
+// narrowing to nearest even, subnormals kept, overflow to infinity).
+__device__ __forceinline__ float f16_widen(uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+__device__ __forceinline__ uint32_t f16_round(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// One operation of the ring on values held in the buffer type.
 template <int DT, int OP>
 struct Red {
+    static constexpr int kOp = combine_op(OP);
+
     // one element held in the low bits of a 32-bit value
     static __device__ __forceinline__ uint32_t elem(uint32_t a, uint32_t b) {
         if constexpr (DT == AR_FLOAT32) {
-            return as_u(f32_apply<OP>(as_f(a), as_f(b)));
+            return as_u(f32_apply<kOp>(as_f(a), as_f(b)));
         } else if constexpr (DT == AR_INT32) {
-            return i32_apply<OP>(a, b);
+            return i32_apply<kOp>(a, b);
+        } else if constexpr (DT == AR_FLOAT16) {
+            return f16_round(f32_apply<kOp>(f16_widen(a & 0xffffu), f16_widen(b & 0xffffu)));
         } else {
-            return bf16_round(f32_apply<OP>(bf16_widen(a & 0xffffu), bf16_widen(b & 0xffffu)));
+            return bf16_round(f32_apply<kOp>(bf16_widen(a & 0xffffu), bf16_widen(b & 0xffffu)));
         }
     }
-    // one 32-bit word: one f32/i32 element or two bf16 elements
+    // one 32-bit word: one 4-byte element or two 2-byte elements
     static __device__ __forceinline__ uint32_t word(uint32_t a, uint32_t b) {
-        if constexpr (DT == AR_BFLOAT16) {
+        if constexpr (elem_size<DT>() == 2) {
             return elem(a, b) | (elem(a >> 16, b >> 16) << 16);
         } else {
             return elem(a, b);
@@ -138,6 +165,35 @@ struct Red {
         r.y = word(a.y, b.y);
         r.z = word(a.z, b.z);
         r.w = word(a.w, b.w);
+        return r;
+    }
+
+    // avg: the one division by N of a complete sum, rounded to the buffer
+    // type (int32: truncating toward zero)
+    static __device__ __forceinline__ uint32_t avg_elem(uint32_t v, int n) {
+        if constexpr (DT == AR_FLOAT32) {
+            return as_u(as_f(v) / static_cast<float>(n));
+        } else if constexpr (DT == AR_INT32) {
+            return static_cast<uint32_t>(static_cast<int32_t>(v) / n);
+        } else if constexpr (DT == AR_FLOAT16) {
+            return f16_round(f16_widen(v & 0xffffu) / static_cast<float>(n));
+        } else {
+            return bf16_round(bf16_widen(v & 0xffffu) / static_cast<float>(n));
+        }
+    }
+    static __device__ __forceinline__ uint32_t avg_word(uint32_t v, int n) {
+        if constexpr (elem_size<DT>() == 2) {
+            return avg_elem(v, n) | (avg_elem(v >> 16, n) << 16);
+        } else {
+            return avg_elem(v, n);
+        }
+    }
+    static __device__ __forceinline__ u32x4 avg_vec(u32x4 v, int n) {
+        u32x4 r;
+        r.x = avg_word(v.x, n);
+        r.y = avg_word(v.y, n);
+        r.z = avg_word(v.z, n);
+        r.w = avg_word(v.w, n);
         return r;
     }
 };
@@ -244,6 +300,91 @@ struct Unit {
     }
 };
 
+// The fold of one unit across ranks: the chunk owner's value starts it
+// (`first`), every later rank's value is combined in (`add`), and `done`
+// completes it (avg divides by N once; float32 partials of
+// AR_BFLOAT16_ACC_F32 are rounded to bf16).  A is the type partials are kept
+// in: the buffer type, or float32 for AR_BFLOAT16_ACC_F32.
+template <int DT, int OP, int VEC>
+struct Fold {
+    using U = Unit<DT, VEC>;
+    using T = typename U::T;
+    using A = std::conditional_t<acc_f32<DT>(), std::conditional_t<(VEC > 1), f32x8, float>, T>;
+    static constexpr int kOp = combine_op(OP);
+
+    static __device__ __forceinline__ A widen(T x) {
+        if constexpr (!acc_f32<DT>()) {
+            return x;
+        } else if constexpr (VEC > 1) {
+            f32x8 r;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r[2 * k] = bf16_widen(x[k] & 0xffffu);
+                r[2 * k + 1] = bf16_widen(x[k] >> 16);
+            }
+            return r;
+        } else {
+            return bf16_widen(x & 0xffffu);
+        }
+    }
+    static __device__ __forceinline__ A first(T x) { return widen(x); }
+    static __device__ __forceinline__ A add(A acc, T x) {
+        if constexpr (!acc_f32<DT>()) {
+            return U::template combine<OP>(acc, x);
+        } else if constexpr (VEC > 1) {
+            const f32x8 w = widen(x);
+            f32x8 r;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) r[k] = f32_apply<kOp>(acc[k], w[k]);
+            return r;
+        } else {
+            return f32_apply<kOp>(acc, widen(x));
+        }
+    }
+    // two partials (ring step: the local value and the incoming partial)
+    static __device__ __forceinline__ A add_acc(A acc, A y) {
+        if constexpr (!acc_f32<DT>()) {
+            return U::template combine<OP>(acc, y);
+        } else if constexpr (VEC > 1) {
+            f32x8 r;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) r[k] = f32_apply<kOp>(acc[k], y[k]);
+            return r;
+        } else {
+            return f32_apply<kOp>(acc, y);
+        }
+    }
+    static __device__ __forceinline__ T done(A acc, int n) {
+        if constexpr (!acc_f32<DT>()) {
+            if constexpr (OP == AR_AVG) {
+                if constexpr (VEC > 1) {
+                    return Red<DT, OP>::avg_vec(acc, n);
+                } else {
+                    return Red<DT, OP>::avg_elem(acc, n);
+                }
+            } else {
+                return acc;
+            }
+        } else if constexpr (VEC > 1) {
+            u32x4 r;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float lo = acc[2 * k], hi = acc[2 * k + 1];
+                if constexpr (OP == AR_AVG) {
+                    lo = lo / static_cast<float>(n);
+                    hi = hi / static_cast<float>(n);
+                }
+                r[k] = bf16_round(lo) | (bf16_round(hi) << 16);
+            }
+            return r;
+        } else {
+            float v = acc;
+            if constexpr (OP == AR_AVG) v = v / static_cast<float>(n);
+            return bf16_round(v);
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // chunk geometry
 // ---------------------------------------------------------------------------
@@ -322,14 +463,15 @@ __device__ __forceinline__ int ring_rank(int c, int k, int n) {
 template <int DT, int OP, int VEC>
 __device__ __forceinline__ void fold_units(const KernelArgs& a, int c, int64_t adj, uint64_t tv0,
                                            const bool (&live)[kUnroll],
-                                           typename Unit<DT, VEC>::T (&acc)[kUnroll]) {
+                                           typename Fold<DT, OP, VEC>::A (&acc)[kUnroll]) {
     using U = Unit<DT, VEC>;
+    using F = Fold<DT, OP, VEC>;
     const int n = a.nranks;
     {
         const char* tb = U::tile(a.send[c] - adj, tv0);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (live[u]) acc[u] = U::load(tb, U::lane_off(u));
+            if (live[u]) acc[u] = F::first(U::load(tb, U::lane_off(u)));
         }
     }
     for (int k = 1; k < n; k += kBatch) {
@@ -349,23 +491,24 @@ __device__ __forceinline__ void fold_units(const KernelArgs& a, int c, int64_t a
             if (k + j < n) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    if (live[u]) acc[u] = U::template combine<OP>(acc[u], x[j][u]);
+                    if (live[u]) acc[u] = F::add(acc[u], x[j][u]);
                 }
             }
         }
     }
 }
 
-// Same fold for one element i (chunk edges).
+// Same fold for one element i (chunk edges), completed.
 template <int DT, int OP>
 __device__ __forceinline__ uint32_t fold_element(const KernelArgs& a, int c, uint64_t i) {
     constexpr int ESZ = elem_size<DT>();
+    using F = Fold<DT, OP, 1>;
     const int n = a.nranks;
-    uint32_t acc = load_elem<ESZ>(a.send[c] + i * ESZ);
+    typename F::A acc = F::first(load_elem<ESZ>(a.send[c] + i * ESZ));
     for (int k = 1; k < n; ++k) {
-        acc = Red<DT, OP>::elem(acc, load_elem<ESZ>(a.send[ring_rank(c, k, n)] + i * ESZ));
+        acc = F::add(acc, load_elem<ESZ>(a.send[ring_rank(c, k, n)] + i * ESZ));
     }
-    return acc;
+    return F::done(acc, n);
 }
 
 // Store unit v of a result into a shard that starts at element `s` of the
@@ -457,13 +600,18 @@ __global__ __launch_bounds__(kThreads) void k_fused_allreduce(const KernelArgs a
             for (int q = 0; q < n; ++q) store_elem<elem_size<DT>()>(a.recv[q] + i * elem_size<DT>(), r);
         }
     }
-    typename U::T acc[kUnroll];
+    typename Fold<DT, OP, VEC>::A acc[kUnroll];
     fold_units<DT, OP, VEC>(a, c, adj, tv0, live, acc);
+    typename U::T res[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) res[u] = Fold<DT, OP, VEC>::done(acc[u], n);
+    }
     for (int q = 0; q < n; ++q) {
         char* tb = U::tile(a.recv[q] - adj, tv0);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (live[u]) U::store(tb, U::lane_off(u), acc[u]);
+            if (live[u]) U::store(tb, U::lane_off(u), res[u]);
         }
     }
     AR_TILE_LOOP_END
@@ -483,11 +631,14 @@ __global__ __launch_bounds__(kThreads) void k_fused_reduce_scatter(const KernelA
         }
     }
     const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
-    typename U::T acc[kUnroll];
+    typename Fold<DT, OP, VEC>::A acc[kUnroll];
     fold_units<DT, OP, VEC>(a, c, adj, tv0, live, acc);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        if (live[u]) store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u), acc[u]);
+        if (live[u]) {
+            store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u),
+                                      Fold<DT, OP, VEC>::done(acc[u], n));
+        }
     }
     AR_TILE_LOOP_END
 }
@@ -537,12 +688,17 @@ __global__ __launch_bounds__(kThreads) void k_gather_shards(const KernelArgs a) 
 // AllReduce, reduce-scatter step s: rank r receives chunk (r-s-1) mod N from
 // rank r-1 and adds its own values, i.e. chunk c is reduced on rank
 // r = c+s+1 from rank p = c+s.  recv[r][chunk c] = send[r] (op) P, with
-// P = send[p] at s = 0 and the partial recv[p] afterwards.  Reads 2*S and
-// writes S bytes.  No rank writes what another rank reads in the same step
-// (rank r writes chunk r-s-1, rank r+1 reads chunk r-s of rank r).
+// P = send[p] at s = 0 and the partial recv[p] afterwards; the last step
+// (s = N-2) completes the chunk (avg divides by N).  Reads 2*S and writes S
+// bytes.  No rank writes what another rank reads in the same step (rank r
+// writes chunk r-s-1, rank r+1 reads chunk r-s of rank r).  Types whose
+// partials are kept in the buffer type only.
 template <int DT, int OP, int VEC>
 __global__ __launch_bounds__(kThreads) void k_ring_reduce_step(const KernelArgs a) {
+    static_assert(!acc_f32<DT>(), "float32 partials need the workspace step");
     using U = Unit<DT, VEC>;
+    using F = Fold<DT, OP, VEC>;
+    using F1 = Fold<DT, OP, 1>;
     constexpr int ESZ = elem_size<DT>();
     AR_TILE_LOOP_BEGIN
     const int r = ring_rank(c, a.step + 1, n);
@@ -550,11 +706,13 @@ __global__ __launch_bounds__(kThreads) void k_ring_reduce_step(const KernelArgs 
     const char* local = a.send[r];
     const char* incoming = (a.step == 0) ? a.send[p] : a.recv[p];
     char* out = a.recv[r];
+    const bool last = (a.step == n - 2);
     if (VEC > 1 && t == 0) {
         uint64_t i;
         if (edge_element(sp, threadIdx.x, &i)) {
-            store_elem<ESZ>(out + i * ESZ, Red<DT, OP>::elem(load_elem<ESZ>(local + i * ESZ),
-                                                             load_elem<ESZ>(incoming + i * ESZ)));
+            uint32_t v = F1::add(load_elem<ESZ>(local + i * ESZ), load_elem<ESZ>(incoming + i * ESZ));
+            if (last) v = F1::done(v, n);
+            store_elem<ESZ>(out + i * ESZ, v);
         }
     }
     typename U::T x[kUnroll], y[kUnroll];
@@ -570,52 +728,132 @@ __global__ __launch_bounds__(kThreads) void k_ring_reduce_step(const KernelArgs 
     char* to = U::tile(out - adj, tv0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        if (live[u]) U::store(to, U::lane_off(u), U::template combine<OP>(x[u], y[u]));
+        if (!live[u]) continue;
+        typename U::T z = F::add(x[u], y[u]);
+        if (last) z = F::done(z, n);
+        U::store(to, U::lane_off(u), z);
     }
     AR_TILE_LOOP_END
 }
 
-// Reduce-scatter ring step s with the partial sums in a workspace (the
-// receive buffers hold one shard only).  Chunk c is reduced on rank
-// r = c+s+1; the incoming partial is send[c] at s = 0 and the workspace
-// afterwards; the last step (s = N-2, on rank c-1) writes shard c.
+// Partial sums kept in the workspace between ring steps: the buffer type, or
+// float32 (4 bytes per element, 32 bytes per unit of eight bf16) for
+// AR_BFLOAT16_ACC_F32.  `base` is the workspace minus the common residue in
+// partial-sized elements, so unit v sits at base + v * kBytes.
+template <int DT, int VEC>
+struct Partials {
+    static constexpr bool kF32 = acc_f32<DT>();
+    static constexpr int kElemBytes = kF32 ? 4 : elem_size<DT>();
+    static constexpr int kBytes = kF32 ? (VEC > 1 ? 32 : 4) : Unit<DT, VEC>::kBytes;
+    using A = typename Fold<DT, AR_SUM, VEC>::A;
+
+    static __device__ __forceinline__ A load(const char* base, uint64_t v) {
+        const char* p = base + v * kBytes;
+        if constexpr (!kF32) {
+            return Unit<DT, VEC, false>::load(p, 0);
+        } else if constexpr (VEC > 1) {
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+            f32x8 r;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r[k] = as_f(lo[k]);
+                r[k + 4] = as_f(hi[k]);
+            }
+            return r;
+        } else {
+            return *reinterpret_cast<const float*>(p);
+        }
+    }
+    static __device__ __forceinline__ void store(char* base, uint64_t v, A x) {
+        char* p = base + v * kBytes;
+        if constexpr (!kF32 && VEC > 1) {
+            *reinterpret_cast<u32x4*>(p) = x;
+        } else if constexpr (!kF32) {
+            // one element of the buffer type, held in the low bits of x
+            if constexpr (elem_size<DT>() == 2) {
+                *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(x);
+            } else {
+                *reinterpret_cast<uint32_t*>(p) = x;
+            }
+        } else if constexpr (VEC > 1) {
+            u32x4 lo, hi;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                lo[k] = as_u(x[k]);
+                hi[k] = as_u(x[k + 4]);
+            }
+            *reinterpret_cast<u32x4*>(p) = lo;
+            *reinterpret_cast<u32x4*>(p + 16) = hi;
+        } else {
+            *reinterpret_cast<float*>(p) = x;
+        }
+    }
+};
+
+// Reduce-scatter ring step s with the partial sums in a workspace.  Chunk c
+// is reduced on rank r = c+s+1: its own value (op) the incoming partial,
+// which is send[c] at s = 0 and the workspace afterwards.  The last step
+// (s = N-2, on rank c-1) completes the chunk and writes it through
+// recv[c], a pointer to where chunk c's element start(c) belongs: the shard
+// of rank c (reduce-scatter), or chunk c of rank c-1's own buffer (the
+// AllReduce ring of AR_BFLOAT16_ACC_F32, whose partials travel as float32).
 template <int DT, int OP, int VEC>
 __global__ __launch_bounds__(kThreads) void k_ring_reduce_step_ws(const KernelArgs a) {
     using U = Unit<DT, VEC>;
+    using F = Fold<DT, OP, VEC>;
+    using F1 = Fold<DT, OP, 1>;
+    using P = Partials<DT, VEC>;
+    using P1 = Partials<DT, 1>;
     constexpr int ESZ = elem_size<DT>();
     AR_TILE_LOOP_BEGIN
     const int r = ring_rank(c, a.step + 1, n);
     const char* local = a.send[r];
-    const char* incoming = (a.step == 0) ? a.send[c] : a.ws;
+    const bool first_step = (a.step == 0);
     const bool last = (a.step == n - 2);
     char* shard = a.recv[c];
+    const char* ws_base = a.ws - static_cast<int64_t>(a.ofs) * P::kElemBytes;
     if (VEC > 1 && t == 0) {
         uint64_t i;
         if (edge_element(sp, threadIdx.x, &i)) {
-            const uint32_t v = Red<DT, OP>::elem(load_elem<ESZ>(local + i * ESZ), load_elem<ESZ>(incoming + i * ESZ));
-            store_elem<ESZ>(last ? shard + (i - sp.s) * ESZ : a.ws + i * ESZ, v);
+            typename F1::A in;
+            if (first_step) {
+                in = F1::first(load_elem<ESZ>(a.send[c] + i * ESZ));
+            } else {
+                in = P1::load(a.ws, i);   // the workspace is touched only after the first step
+            }
+            const typename F1::A v = F1::add_acc(F1::first(load_elem<ESZ>(local + i * ESZ)), in);
+            if (last) {
+                store_elem<ESZ>(shard + (i - sp.s) * ESZ, F1::done(v, n));
+            } else {
+                P1::store(a.ws, i, v);
+            }
         }
     }
     const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
-    typename U::T x[kUnroll], y[kUnroll];
+    typename U::T x[kUnroll];
+    typename F::A y[kUnroll];
     const char* tl = U::tile(local - adj, tv0);
-    const char* ti = U::tile(incoming - adj, tv0);
+    const char* ts = U::tile(a.send[c] - adj, tv0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         if (live[u]) {
             x[u] = U::load(tl, U::lane_off(u));
-            y[u] = U::load(ti, U::lane_off(u));
+            if (first_step) {
+                y[u] = F::first(U::load(ts, U::lane_off(u)));
+            } else {
+                y[u] = P::load(ws_base, tv0 + U::lane_unit(u));
+            }
         }
     }
-    char* tw = U::tile(a.ws - adj, tv0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         if (!live[u]) continue;
-        const typename U::T z = U::template combine<OP>(x[u], y[u]);
+        const typename F::A z = F::add_acc(F::first(x[u]), y[u]);
         if (last) {
-            store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u), z);
+            store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u), F::done(z, n));
         } else {
-            U::store(tw, U::lane_off(u), z);
+            P::store(const_cast<char*>(ws_base), tv0 + U::lane_unit(u), z);
         }
     }
     AR_TILE_LOOP_END
@@ -667,20 +905,23 @@ hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
             hipLaunchKernelGGL((k_fused_reduce_scatter<DT, OP, VEC>), grid, block, 0, s, a);
             break;
         case Kind::kRingReduceStep:
-            hipLaunchKernelGGL((k_ring_reduce_step<DT, OP, VEC>), grid, block, 0, s, a);
+            if constexpr (acc_f32<DT>()) {
+                return hipErrorInvalidValue;   // float32 partials always take the workspace step
+            } else {
+                hipLaunchKernelGGL((k_ring_reduce_step<DT, OP, VEC>), grid, block, 0, s, a);
+            }
             break;
         case Kind::kRingReduceStepWs:
             hipLaunchKernelGGL((k_ring_reduce_step_ws<DT, OP, VEC>), grid, block, 0, s, a);
             break;
-
         default:
             return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-// Copies depend on the element size only: bf16 moves as 2-byte elements,
-// f32 and i32 as 4-byte ones.
+// Copies depend on the element size only: the 2-byte types move as bf16
+// elements, the 4-byte ones as float32 elements (bit patterns unchanged).
 template <int DT, int VEC>
 hipError_t launch_copy(const Launch& l, const KernelArgs& a, hipStream_t s) {
     const dim3 grid(l.blocks), block(kThreads);
@@ -694,7 +935,6 @@ hipError_t launch_copy(const Launch& l, const KernelArgs& a, hipStream_t s) {
         case Kind::kRingCopyStep:
             hipLaunchKernelGGL((k_ring_copy_step<DT, VEC>), grid, block, 0, s, a);
             break;
-
         default:
             return hipErrorInvalidValue;
     }
@@ -714,6 +954,7 @@ hipError_t by_op(const Launch& l, const KernelArgs& a, hipStream_t s) {
         case AR_PROD: return by_vec<DT, AR_PROD>(l, a, s);
         case AR_MIN: return by_vec<DT, AR_MIN>(l, a, s);
         case AR_MAX: return by_vec<DT, AR_MAX>(l, a, s);
+        case AR_AVG: return by_vec<DT, AR_AVG>(l, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -730,14 +971,15 @@ hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream) {
     const bool copy = l.kind == Kind::kFusedAllGather || l.kind == Kind::kPlaceShards ||
                       l.kind == Kind::kRingCopyStep;
     if (copy) {
-        // bf16 and the 4-byte types differ only in element size here
-        return (l.dtype == AR_BFLOAT16) ? copy_by_vec<AR_BFLOAT16>(l, a, stream)
-                                        : copy_by_vec<AR_FLOAT32>(l, a, stream);
+        const bool two_bytes = l.dtype == AR_BFLOAT16 || l.dtype == AR_FLOAT16 || l.dtype == AR_BFLOAT16_ACC_F32;
+        return two_bytes ? copy_by_vec<AR_BFLOAT16>(l, a, stream) : copy_by_vec<AR_FLOAT32>(l, a, stream);
     }
     switch (l.dtype) {
         case AR_FLOAT32: return by_op<AR_FLOAT32>(l, a, stream);
         case AR_BFLOAT16: return by_op<AR_BFLOAT16>(l, a, stream);
         case AR_INT32: return by_op<AR_INT32>(l, a, stream);
+        case AR_FLOAT16: return by_op<AR_FLOAT16>(l, a, stream);
+        case AR_BFLOAT16_ACC_F32: return by_op<AR_BFLOAT16_ACC_F32>(l, a, stream);
     }
     return hipErrorInvalidValue;
 }

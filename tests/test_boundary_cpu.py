@@ -54,7 +54,7 @@ def test_chunk_range_matches_the_oracle(lib):
 def test_error_strings(lib):
     for code, text in ((0, b"success"), (1, b"invalid argument"), (3, b"HIP runtime error")):
         assert lib.ar_get_error_string(code) == text
-    assert lib.ar_dtype_size(0) == 4 and lib.ar_dtype_size(1) == 2 and lib.ar_dtype_size(2) == 4
+    assert [lib.ar_dtype_size(d) for d in range(5)] == [4, 2, 4, 2, 2]
     assert lib.ar_dtype_size(7) == 0
 
 
@@ -93,7 +93,8 @@ def test_argument_errors_are_caught_on_the_host(lib):
     assert _call_ar(lib, sends, recvs, 10, n=0) == 1
     assert _call_ar(lib, sends * 33, recvs * 33, 10, n=129) == 1
     assert _call_ar(lib, sends, recvs, 10, dtype=5) == 1
-    assert _call_ar(lib, sends, recvs, 10, op=4) == 1
+    assert _call_ar(lib, sends, recvs, 10, dtype=-1) == 1
+    assert _call_ar(lib, sends, recvs, 10, op=5) == 1
     assert b"op" in lib.ar_get_last_error_detail()
     assert _call_ar(lib, [0] + sends[1:], recvs, 10) == 1               # null buffer
     assert _call_ar(lib, [sends[0] + 2] + sends[1:], recvs, 10) == 1    # not 4-byte aligned
@@ -196,3 +197,15 @@ def test_persistent_plan_host_side(lib):
     assert lib.ar_plan_start(None, None) == 1
     assert lib.ar_plan_free(None) == 0
     assert lib.ar_allreduce_init(_ptrs(sends), _ptrs(recvs), 0, 0, 0, 4, 0, None, 0, None) == 1
+
+
+def test_workspace_sizes_for_float32_partials(lib):
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    assert ar.ar_workspace_bytes("allreduce", "ring", 1000, "bf16acc32", 8) == 1000 * 4 + 1024
+    assert ar.ar_workspace_bytes("allreduce", "ring", 1000, "bf16acc32", 2) == 0
+    assert ar.ar_workspace_bytes("allreduce", "fused", 1000, "bf16acc32", 8) == 0
+    assert ar.ar_workspace_bytes("allreduce", "ring", 1000, "f16", 8) == 0
+    assert ar.ar_workspace_bytes("reduce_scatter", "ring", 1000, "bf16acc32", 8) == 1000 * 4 + 1024
+    assert ar.ar_workspace_bytes("reduce_scatter", "ring", 1000, "f16", 8) == 1000 * 2 + 1024
+    assert ar.ar_workspace_bytes("all_gather", "ring", 1000, "bf16acc32", 8) == 0
