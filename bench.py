@@ -159,7 +159,7 @@ def _sampled_parity(xs, outs, dtype, op, positions):
     idx = torch.from_numpy(positions).to(outs[0].device)
     for t in outs:
         got = t[idx].cpu()
-        got = got.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else got.numpy()
+        got = got.view(torch.int16).numpy().view(np.uint16) if dtype in ("bf16", "bf16acc32", "f16") else got.numpy()
         if not same_bits(got, want, dtype):
             return False
     return True
@@ -247,6 +247,53 @@ def run_configs(args):
         torch.cuda.empty_cache()
 
 
+def run_variants(args):
+    """The precision and operator variants at full size: the bf16 workload (8 x 2^26)
+    with float32 partials and with avg, the headline workload with avg, and
+    an 8 x 2^26 binary16 AllReduce of N(0,1) values; sampled parity each."""
+    import numpy as np
+    import torch
+
+    import ring_allreduce_reduction_virtual_amd as ar
+    from inputs import WORKLOADS, make_inputs
+    from oracle.ring import chunk, f32_to_f16_bits
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    c3 = make_inputs(WORKLOADS["c3"])
+    head = make_inputs(WORKLOADS["headline"])
+    f16 = [f32_to_f16_bits(x) for x in head]          # the headline draws, rounded to binary16
+    cases = [("c3 8 x 2^26 bf16", c3, "bf16acc32", "sum", torch.bfloat16),
+             ("c3 8 x 2^26 bf16", c3, "bf16acc32", "avg", torch.bfloat16),
+             ("c3 8 x 2^26 bf16", c3, "bf16", "avg", torch.bfloat16),
+             ("headline 8 x 2^26 f32", head, "f32", "avg", torch.float32),
+             ("8 x 2^26 f16, N(0,1)", f16, "f16", "sum", torch.float16)]
+    for label, xs, dt, op, tdt in cases:
+        n, count = len(xs), len(xs[0])
+        if tdt == torch.float32:
+            sends = [torch.from_numpy(x).to(dev) for x in xs]
+        else:
+            sends = [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(tdt) for x in xs]
+        recvs = [torch.empty(count, dtype=tdt, device=dev) for _ in range(n)]
+        s_bytes = count * sends[0].element_size()
+        rng = np.random.default_rng(3)
+        pos = np.unique(np.concatenate([rng.integers(0, count, 1024)] +
+                                       [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1]) for c in range(n)]))
+        for algo in ("fused", "phases", "ring"):
+            med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo, dtype=dt), 20, 3, stream)
+            ok = _sampled_parity(xs, recvs, dt, op, pos)
+            algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
+            print(json.dumps({"workload": label, "dtype": dt, "op": op, "algo": algo, "nranks": n, "count": count,
+                              "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                              "algbw_gbps": round(s_bytes / (med / 1e3) / 1e9, 2),
+                              "busbw_gbps": round(s_bytes / (med / 1e3) / 1e9 * busbw_factor("allreduce", n), 2),
+                              "hbm_gbps_of_minimum": round(algo_bytes / (med / 1e3) / 1e9, 1),
+                              "hbm_frac": round(algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                              "parity_sampled": "pass" if ok else "fail"}), flush=True)
+        del sends, recvs
+        torch.cuda.empty_cache()
+
+
 def run_size_sweep(args):
     """AllReduce time against message size, 8 ranks of float32, both algorithms.
 
@@ -309,6 +356,9 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the headline line: time every workload (c1..c5) with both algorithms, "
                          "one JSON line each")
+    ap.add_argument("--variants", action="store_true",
+                    help="instead of the headline line: time the precision and operator variants "
+                         "(float32 partials for bf16, avg, binary16) at full size, one JSON line each")
     ap.add_argument("--size-sweep", action="store_true",
                     help="instead of the headline line: AllReduce time against message size (8 ranks, f32), "
                          "fused and ring, with an alpha-beta fit")
@@ -336,6 +386,9 @@ def main():
         return
     if args.size_sweep:
         run_size_sweep(args)
+        return
+    if args.variants:
+        run_variants(args)
         return
     w = WORKLOADS["headline"]
     n, count = w.nranks, w.count

@@ -209,3 +209,25 @@ def test_workspace_sizes_for_float32_partials(lib):
     assert ar.ar_workspace_bytes("reduce_scatter", "ring", 1000, "bf16acc32", 8) == 1000 * 4 + 1024
     assert ar.ar_workspace_bytes("reduce_scatter", "ring", 1000, "f16", 8) == 1000 * 2 + 1024
     assert ar.ar_workspace_bytes("all_gather", "ring", 1000, "bf16acc32", 8) == 0
+
+
+def test_plain_c_consumer_of_the_header(tmp_path, lib):
+    """include/ar.h compiles as C and its host-side calls behave from a C program."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    exe = tmp_path / "abi_host_check"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    cmd = [gcc, "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           os.path.join(ROOT, "tests", "c_abi", "abi_host_check.c"),
+           "-L", libdir, "-l:libar.so", f"-Wl,-rpath,{libdir}", "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stderr
+    assert "passed" in res.stdout
