@@ -17,6 +17,10 @@ What it holds, each piece written from the pages on ring AllReduce:
 * ``threaded``  one thread per rank with queue channels, the same program
                 the Rust listing on that page runs, with a receive time-out
                 that turns a stuck ring into an error;
+* ``orders``    the tree-shaped schedules (binomial tree reduce and
+                distribution, recursive doubling, and Rabenseifner's recursive
+                halving and doubling), executed the same way, and the
+                bracketings they compute written from their definitions;
 * ``explore``   brute force for tiny rings: every interleaving of the ranks'
                 send/receive events, and every bracketing of an N-term sum.
 
@@ -41,4 +45,17 @@ from .ring import (  # noqa: F401
     ring_allreduce,
     ring_order_fold,
     ring_order_fold_columns,
+)
+from .orders import (  # noqa: F401,E402
+    ORDERS,
+    OrderStats,
+    binomial_tree,
+    halving_doubling_allreduce,
+    halving_tree,
+    order_allreduce,
+    order_bracketing,
+    recursive_doubling_allreduce,
+    tree_allreduce,
+    tree_order_fold,
+    tree_order_fold_columns,
 )
