@@ -109,12 +109,40 @@ typedef enum {
  *   faster on MI355X HBM once N is large.
  * AR_ALGO_AUTO: AR_ALGO_FUSED below AR_PHASES_MIN_RANKS ranks, AR_ALGO_PHASES
  *   from there on (AllReduce); the fused kernel for the single phases.
- * All algorithms give the same bits. */
+ * These four give the same bits: the ring's association order.
+ *
+ * The remaining algorithms are AllReduce only (AR_ERR_UNSUPPORTED for
+ * reduce-scatter and all-gather) and bracket the reduction differently from
+ * the ring, so their float results differ from the ring's in the last bits:
+ * AR_ALGO_TREE: the binomial tree of bitfern.com "AllReduce Explained"
+ *   (section "Tree AllReduce": reduce toward a root, then send the result
+ *   back down): rank r (r mod 2d = 0) adds the partial of rank r+d for
+ *   d = 1, 2, 4, ..., so element i is ((x0 x1)(x2 x3))((x4 x5)(x6 x7))...
+ *   for any N.  One fused pass (2*N*S bytes).
+ * AR_ALGO_TREE_STEPS: the same tree stage by stage: ceil(log2 N) reducing
+ *   launches toward rank 0, then as many distributing launches.
+ * AR_ALGO_RECURSIVE_DOUBLING: the same bracketing reached by exchanges
+ *   (same section, "Recursive Doubling"): log2 N launches, in launch k rank
+ *   r and rank r XOR 2^k both get r (op) r XOR 2^k.  N a power of two.
+ * AR_ALGO_HALVING_DOUBLING: Rabenseifner's order (tirogla.com "Ring
+ *   all-reduce", "How it works", cost model: recursive-halving
+ *   reduce-scatter, recursive-doubling all-gather): partners at distance
+ *   N/2 first, so element i is ((x0 x4)(x2 x6))((x1 x5)(x3 x7)) at N = 8.
+ *   One fused pass.  N a power of two.
+ * AR_ALGO_HALVING_DOUBLING_STEPS: the same schedule stage by stage: log2 N
+ *   recursive-halving launches (chunk c finishes on rank c), then log2 N
+ *   recursive-doubling launches.  N a power of two.
+ * A power-of-two algorithm with another N fails with AR_ERR_UNSUPPORTED. */
 typedef enum {
     AR_ALGO_FUSED = 0,
     AR_ALGO_RING = 1,
     AR_ALGO_PHASES = 2,
-    AR_ALGO_AUTO = 3
+    AR_ALGO_AUTO = 3,
+    AR_ALGO_TREE = 4,
+    AR_ALGO_TREE_STEPS = 5,
+    AR_ALGO_RECURSIVE_DOUBLING = 6,
+    AR_ALGO_HALVING_DOUBLING = 7,
+    AR_ALGO_HALVING_DOUBLING_STEPS = 8
 } ar_algo_t;
 
 /* Rank count from which AR_ALGO_AUTO runs an AllReduce as two fused phases
@@ -160,7 +188,11 @@ ar_result_t ar_all_gather(const void* const* sendbufs, void* const* recvbufs, si
  * sums in flight between steps in it, since its receive buffers are only one
  * shard long, and so does the AllReduce of AR_BFLOAT16_ACC_F32, whose float32
  * partials do not fit the bf16 buffers.  Other ring AllReduces and the ring
- * all-gather work in recvbufs. */
+ * all-gather work in recvbufs.  The staged tree algorithms
+ * (AR_ALGO_TREE_STEPS, AR_ALGO_RECURSIVE_DOUBLING,
+ * AR_ALGO_HALVING_DOUBLING_STEPS) keep their partials in recvbufs too,
+ * except for AR_BFLOAT16_ACC_F32, whose float32 partials take one
+ * count-element float32 slab per rank in the workspace (nranks >= 2). */
 ar_result_t ar_allreduce_ex(const void* const* sendbufs, void* const* recvbufs, size_t count,
                             ar_dtype_t dtype, ar_op_t op, int nranks, ar_algo_t algo,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);

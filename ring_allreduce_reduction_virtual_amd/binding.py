@@ -151,7 +151,8 @@ def ar_allreduce_ex(sendbufs, recvbufs=None, op: str = "sum", algo: str = "fused
                     dtype=None):
     """AllReduce with the algorithm chosen by the caller; in place when recvbufs is None.
 
-    A ring AllReduce with float32 partials needs a workspace; when none is
+    Algorithms that keep float32 partials between launches (the ring, and the
+    staged tree algorithms, for bf16acc32) need a workspace; when none is
     given one is taken from torch's allocator on the stream of the call.
     """
     recvbufs = sendbufs if recvbufs is None else recvbufs

@@ -1,7 +1,7 @@
 """Build libar.so (the HIP library behind include/ar.h) for gfx950 with hipcc.
 
 Usage: ``python -m ring_allreduce_reduction_virtual_amd.build`` or
-``build_library()``.  Writes ``libar.so`` next to this file.  The two
+``build_library()``.  Writes ``libar.so`` next to this file.  The
 translation units compile in parallel; the library is replaced atomically.
 """
 
@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libar.so")
 
-SOURCES = ("ar_api.hip", "ar_kernels.hip")
+SOURCES = ("ar_api.hip", "ar_kernels.hip", "ar_tree_kernels.hip")
 
 # -ffp-contract=off: no fused multiply-add, every add/mul rounds on its own.
 # -fno-fast-math: IEEE semantics (NaN, signed zero, no reassociation).

@@ -252,7 +252,34 @@ ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, Residue res) {
 }
 
 bool algo_known(ar_algo_t algo) {
-    return algo == AR_ALGO_FUSED || algo == AR_ALGO_RING || algo == AR_ALGO_PHASES || algo == AR_ALGO_AUTO;
+    return algo >= AR_ALGO_FUSED && algo <= AR_ALGO_HALVING_DOUBLING_STEPS;
+}
+
+// The AllReduce-only algorithms that bracket the reduction as a tree.
+bool tree_algo(ar_algo_t algo) { return algo >= AR_ALGO_TREE && algo <= AR_ALGO_HALVING_DOUBLING_STEPS; }
+
+// The tree algorithms that run stage by stage (and keep partials between stages).
+bool tree_steps_algo(ar_algo_t algo) {
+    return algo == AR_ALGO_TREE_STEPS || algo == AR_ALGO_RECURSIVE_DOUBLING || algo == AR_ALGO_HALVING_DOUBLING_STEPS;
+}
+
+// The ones defined for a power-of-two number of ranks only.
+bool power_of_two_algo(ar_algo_t algo) {
+    return algo == AR_ALGO_RECURSIVE_DOUBLING || algo == AR_ALGO_HALVING_DOUBLING ||
+           algo == AR_ALGO_HALVING_DOUBLING_STEPS;
+}
+
+int ceil_log2(int n) {
+    int l = 0;
+    while ((1 << l) < n) ++l;
+    return l;
+}
+
+// r with its low `bits` bits in reverse order.
+int bit_reverse(int r, int bits) {
+    int v = 0;
+    for (int b = 0; b < bits; ++b) v |= ((r >> b) & 1) << (bits - 1 - b);
+    return v;
 }
 
 // Rank count from which AR_ALGO_AUTO runs AllReduce as two fused phases.
@@ -274,6 +301,9 @@ const char* kind_name(Kind kd) {
         case Kind::kRingReduceStep: return "ring_reduce_step";
         case Kind::kRingReduceStepWs: return "ring_reduce_step_ws";
         case Kind::kRingCopyStep: return "ring_copy_step";
+        case Kind::kFusedTree: return "fused_tree";
+        case Kind::kTreeReduceStep: return "tree_reduce_step";
+        case Kind::kTreeCopyStep: return "tree_copy_step";
     }
     return "?";
 }
@@ -301,10 +331,10 @@ public:
         l.op = k.op;
         if (debug_enabled()) {
             std::fprintf(stderr,
-                         "[ar] %s dtype=%s op=%d n=%d count=%llu step=%d shift=%d vec=%d ofs=%d align=2^%d "
-                         "tiles=[%u,%u) tiles/chunk=%u blocks=%u%s\n",
+                         "[ar] %s dtype=%s op=%d n=%d count=%llu step=%d shift=%d mode=%d last=%d vec=%d ofs=%d "
+                         "align=2^%d tiles=[%u,%u) tiles/chunk=%u blocks=%u%s\n",
                          kind_name(kind), dtype_name(k.dtype), static_cast<int>(k.op), k.n,
-                         static_cast<unsigned long long>(k.count), a.step, a.shift, l.vec ? 1 : 0, a.ofs,
+                         static_cast<unsigned long long>(k.count), a.step, a.shift, a.mode, a.last, l.vec ? 1 : 0, a.ofs,
                          a.align_shift, a.tile_first, a.tile_end, a.tiles_per_chunk, l.blocks,
                          steps_ != nullptr ? " (planned)" : "");
         }
@@ -325,13 +355,20 @@ private:
 // Workspace of the ring algorithm: one full-length buffer of partial sums
 // for the reduce-scatter, and for the AllReduce of AR_BFLOAT16_ACC_F32; none
 // with fewer than 3 ranks, where the only reduce step is also the last.  The
-// extra 1024 bytes cover placing the partials at the senders' residue: up to
-// 255 bytes to reach a 256-byte boundary, plus the residue itself in
+// staged tree AllReduces of AR_BFLOAT16_ACC_F32 keep one float32 slab of
+// `count` elements per rank (each slab rounded up to 256 bytes).  The extra
+// 1024 bytes cover placing the partials at the senders' residue: up to 255
+// bytes to reach a 256-byte boundary, plus the residue itself in
 // partial-sized elements (below 256 / element size elements of 4 bytes).
 constexpr uint64_t kWorkspaceSlack = 1024;
 
+uint64_t slab_bytes(uint64_t count) { return (count * 4 + 255) & ~static_cast<uint64_t>(255); }
+
 uint64_t ring_workspace_bytes(ar_coll_t coll, uint64_t count, ar_dtype_t dt, int n, ar_algo_t algo) {
-    if (algo != AR_ALGO_RING || n < 3 || count == 0) return 0;
+    if (count == 0) return 0;
+    if (coll == AR_COLL_ALLREDUCE && tree_steps_algo(algo) && dt == AR_BFLOAT16_ACC_F32 && n >= 2)
+        return static_cast<uint64_t>(n) * slab_bytes(count) + kWorkspaceSlack;
+    if (algo != AR_ALGO_RING || n < 3) return 0;
     if (coll == AR_COLL_REDUCE_SCATTER || (coll == AR_COLL_ALLREDUCE && dt == AR_BFLOAT16_ACC_F32))
         return count * partial_size(dt) + kWorkspaceSlack;
     return 0;
@@ -344,15 +381,65 @@ ar_result_t use_workspace(KernelArgs& a, const Common& k, ar_coll_t coll, ar_alg
     const uint64_t need = ring_workspace_bytes(coll, k.count, k.dtype, k.n, algo);
     if (need == 0) return AR_SUCCESS;
     if (ws == nullptr || ws_bytes < need)
-        return fail(AR_ERR_INVALID_ARGUMENT, "the ring algorithm needs a workspace of %llu bytes here",
+        return fail(AR_ERR_INVALID_ARGUMENT, "this algorithm needs a workspace of %llu bytes here",
                     static_cast<unsigned long long>(need));
     const uintptr_t w = reinterpret_cast<uintptr_t>(ws);
     if (iv != nullptr) iv->push_back({w, w + need, true, 0, 2});
     const uintptr_t base = (w + 255u) & ~static_cast<uintptr_t>(255u);
     const uintptr_t shift = base - w + static_cast<uintptr_t>(a.ofs) * partial_size(k.dtype);
-    if (shift + k.count * partial_size(k.dtype) > need) return fail(AR_ERR_INTERNAL, "workspace placement");
+    const bool slabs = tree_steps_algo(algo);
+    a.ws_stride = slabs ? slab_bytes(k.count) : 0;
+    const uint64_t span = slabs ? static_cast<uint64_t>(k.n - 1) * a.ws_stride + k.count * 4
+                                : k.count * partial_size(k.dtype);
+    if (shift + span > need) return fail(AR_ERR_INTERNAL, "workspace placement");
     a.ws = reinterpret_cast<char*>(w + shift);
     return AR_SUCCESS;
+}
+
+// AllReduce in a tree-shaped order.  The fused kernel folds the send table as
+// a binomial tree; recursive halving's order is that tree over the ranks in
+// bit-reversed order.  The staged forms emit one launch per stage.
+ar_result_t tree_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_bytes,
+                           const std::vector<uintptr_t>& ptrs, Sink& sink) {
+    KernelArgs a{};
+    Launch l{};
+    fill_tables(a, k);
+    ar_result_t rc = plan(a, l, k, common_residue(ptrs));
+    if (rc != AR_SUCCESS) return rc;
+    const int L = ceil_log2(k.n);
+    if (algo == AR_ALGO_TREE || algo == AR_ALGO_HALVING_DOUBLING) {
+        if (algo == AR_ALGO_HALVING_DOUBLING)
+            for (int r = 0; r < k.n; ++r) a.send[r] = static_cast<const char*>(k.send[bit_reverse(r, L)]);
+        l.depth = k.n < 16 ? 4 : (k.n < 64 ? 6 : 8);
+        return sink.emit(l, Kind::kFusedTree, a, k);
+    }
+    if ((rc = use_workspace(a, k, AR_COLL_ALLREDUCE, algo, ws, ws_bytes, nullptr)) != AR_SUCCESS) return rc;
+    auto stage = [&](Kind kind, int mode, int step, bool last) {
+        a.mode = mode;
+        a.step = step;
+        a.last = last ? 1 : 0;
+        return sink.emit(l, kind, a, k);
+    };
+    switch (algo) {
+        case AR_ALGO_TREE_STEPS:
+            for (int s = 0; s < L; ++s)
+                if ((rc = stage(Kind::kTreeReduceStep, arimpl::kTreeReduce, s, s == L - 1)) != AR_SUCCESS) return rc;
+            for (int s = L - 1; s >= 0; --s)
+                if ((rc = stage(Kind::kTreeCopyStep, arimpl::kTreeBcast, s, false)) != AR_SUCCESS) return rc;
+            return AR_SUCCESS;
+        case AR_ALGO_RECURSIVE_DOUBLING:
+            for (int s = 0; s < L; ++s)
+                if ((rc = stage(Kind::kTreeReduceStep, arimpl::kRdExchange, s, s == L - 1)) != AR_SUCCESS) return rc;
+            return AR_SUCCESS;
+        case AR_ALGO_HALVING_DOUBLING_STEPS:
+            for (int s = 0; s < L; ++s)
+                if ((rc = stage(Kind::kTreeReduceStep, arimpl::kHalvingReduce, s, s == L - 1)) != AR_SUCCESS) return rc;
+            for (int s = 0; s < L; ++s)
+                if ((rc = stage(Kind::kTreeCopyStep, arimpl::kDoublingGather, s, false)) != AR_SUCCESS) return rc;
+            return AR_SUCCESS;
+        default:
+            return fail(AR_ERR_INTERNAL, "not a tree algorithm");
+    }
 }
 
 ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_bytes, Sink& sink) {
@@ -375,6 +462,9 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         ptrs.push_back(d);
     }
     if (algo == AR_ALGO_AUTO) algo = (k.n >= phases_min_ranks()) ? AR_ALGO_PHASES : AR_ALGO_FUSED;
+    if (power_of_two_algo(algo) && (k.n & (k.n - 1)) != 0)
+        return fail(AR_ERR_UNSUPPORTED, "algo %d needs a power-of-two number of ranks, not %d",
+                    static_cast<int>(algo), k.n);
     if (k.n == 1) algo = AR_ALGO_FUSED;           // a copy
     {
         KernelArgs probe{};
@@ -386,6 +476,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     if (rc != AR_SUCCESS) return rc;
     if (k.count == 0) return AR_SUCCESS;
 
+    if (tree_algo(algo)) return tree_allreduce(k, algo, ws, ws_bytes, ptrs, sink);
     KernelArgs a{};
     Launch l{};
     fill_tables(a, k);
@@ -441,6 +532,7 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
     ar_result_t rc = check_common(k, true);
     if (rc != AR_SUCCESS) return rc;
     if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+    if (tree_algo(algo)) return fail(AR_ERR_UNSUPPORTED, "algo %d is defined for AllReduce only", static_cast<int>(algo));
     if (algo != AR_ALGO_RING) algo = AR_ALGO_FUSED;
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;
@@ -485,6 +577,7 @@ ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, Sink& sink) {
     ar_result_t rc = check_common(k, false);
     if (rc != AR_SUCCESS) return rc;
     if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+    if (tree_algo(algo)) return fail(AR_ERR_UNSUPPORTED, "algo %d is defined for AllReduce only", static_cast<int>(algo));
     if (algo != AR_ALGO_RING) algo = AR_ALGO_FUSED;
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;

@@ -1,0 +1,624 @@
+// Device-side building blocks shared by the kernel sources (ar_kernels.hip:
+// the ring schedules; ar_tree_kernels.hip: the tree-shaped orders): element
+// arithmetic, 16-byte vector access, the fold over ranks, and the chunk
+// geometry with its tile loop.  Everything here is inline device code in an
+// unnamed namespace, so each kernel source gets its own copy.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "ar_internal.h"
+
+namespace arimpl {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Ranks whose loads are in flight together before they are folded.
+#ifndef AR_RANK_BATCH
+#define AR_RANK_BATCH 8
+#endif
+constexpr int kBatch = AR_RANK_BATCH;
+
+// Nontemporal hints: the reducing kernels stream their N input buffers once
+// (AR_NT_LOADS), the copies read a shard that several ranks' stores follow
+// (AR_NT_LOADS_COPY), and every output is written once (AR_NT_STORES).
+#ifndef AR_NT_LOADS
+#define AR_NT_LOADS 1
+#endif
+#ifndef AR_NT_LOADS_COPY
+#define AR_NT_LOADS_COPY 0
+#endif
+#ifndef AR_NT_STORES
+#define AR_NT_STORES 1
+#endif
+
+// Element types: float32 and int32 (4 bytes); bf16, IEEE binary16 and bf16
+// with float32 partial sums (2 bytes).
+template <int DT>
+constexpr int elem_size() { return (DT == AR_FLOAT32 || DT == AR_INT32) ? 4 : 2; }
+
+// AR_BFLOAT16_ACC_F32 keeps its partial sums in float32 and rounds to bf16
+// once, when a chunk is complete; every other type keeps its partials in the
+// buffer type, rounded after each operation.
+template <int DT>
+constexpr bool acc_f32() { return DT == AR_BFLOAT16_ACC_F32; }
+
+// avg combines like sum; its one division by N happens when a chunk is complete.
+constexpr int combine_op(int op) { return op == AR_AVG ? AR_SUM : op; }
+
+// ---------------------------------------------------------------------------
+// element arithmetic
+// ---------------------------------------------------------------------------
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// IEEE binary32 operations, round to nearest even.  min/max are IEEE
+// 754-2019 minimum/maximum: NaN if either operand is NaN, and for equal
+// operands the sign bits decide (-0 below +0).
+template <int OP>
+__device__ __forceinline__ float f32_apply(float a, float b) {
+    if constexpr (OP == AR_SUM) {
+        return a + b;
+    } else if constexpr (OP == AR_PROD) {
+        return a * b;
+    } else if constexpr (OP == AR_MIN) {
+        const float lo = (a < b) ? a : b;
+        const float tie = as_f(as_u(a) | as_u(b));
+        const float r = (a == b) ? tie : lo;
+        return (a != a || b != b) ? as_f(0x7fc00000u) : r;
+    } else {
+        const float hi = (a > b) ? a : b;
+        const float tie = as_f(as_u(a) & as_u(b));
+        const float r = (a == b) ? tie : hi;
+        return (a != a || b != b) ? as_f(0x7fc00000u) : r;
+    }
+}
+
+// int32: sum and product wrap modulo 2^32 (unsigned arithmetic).
+template <int OP>
+__device__ __forceinline__ uint32_t i32_apply(uint32_t a, uint32_t b) {
+    if constexpr (OP == AR_SUM) {
+        return a + b;
+    } else if constexpr (OP == AR_PROD) {
+        return a * b;
+    } else if constexpr (OP == AR_MIN) {
+        return (static_cast<int32_t>(a) < static_cast<int32_t>(b)) ? a : b;
+    } else {
+        return (static_cast<int32_t>(a) > static_cast<int32_t>(b)) ? a : b;
+    }
+}
+
+// bf16 bits are the upper half of the float32 with the same value.
+__device__ __forceinline__ float bf16_widen(uint32_t h) { return as_f(h << 16); }
+
+// float32 -> bf16, nearest with ties to even: adding 0x7FFF plus the last
+// kept bit carries into the upper half exactly when the dropped half is above
+// one half ulp, or equal to it with an odd last bit.  NaN -> quiet NaN.
+__device__ __forceinline__ uint32_t bf16_round(float f) {
+    const uint32_t u = as_u(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x40u;
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded;
+}
+
+// IEEE binary16 <-> float32 with the hardware conversions (exact widening;
+// narrowing to nearest even, subnormals kept, overflow to infinity).
+__device__ __forceinline__ float f16_widen(uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+__device__ __forceinline__ uint32_t f16_round(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// One operation of the ring on values held in the buffer type.
+template <int DT, int OP>
+struct Red {
+    static constexpr int kOp = combine_op(OP);
+
+    // one element held in the low bits of a 32-bit value
+    static __device__ __forceinline__ uint32_t elem(uint32_t a, uint32_t b) {
+        if constexpr (DT == AR_FLOAT32) {
+            return as_u(f32_apply<kOp>(as_f(a), as_f(b)));
+        } else if constexpr (DT == AR_INT32) {
+            return i32_apply<kOp>(a, b);
+        } else if constexpr (DT == AR_FLOAT16) {
+            return f16_round(f32_apply<kOp>(f16_widen(a & 0xffffu), f16_widen(b & 0xffffu)));
+        } else {
+            return bf16_round(f32_apply<kOp>(bf16_widen(a & 0xffffu), bf16_widen(b & 0xffffu)));
+        }
+    }
+    // one 32-bit word: one 4-byte element or two 2-byte elements
+    static __device__ __forceinline__ uint32_t word(uint32_t a, uint32_t b) {
+        if constexpr (elem_size<DT>() == 2) {
+            return elem(a, b) | (elem(a >> 16, b >> 16) << 16);
+        } else {
+            return elem(a, b);
+        }
+    }
+    static __device__ __forceinline__ u32x4 vec(u32x4 a, u32x4 b) {
+        u32x4 r;
+        r.x = word(a.x, b.x);
+        r.y = word(a.y, b.y);
+        r.z = word(a.z, b.z);
+        r.w = word(a.w, b.w);
+        return r;
+    }
+
+    // avg: the one division by N of a complete sum, rounded to the buffer
+    // type (int32: truncating toward zero)
+    static __device__ __forceinline__ uint32_t avg_elem(uint32_t v, int n) {
+        if constexpr (DT == AR_FLOAT32) {
+            return as_u(as_f(v) / static_cast<float>(n));
+        } else if constexpr (DT == AR_INT32) {
+            return static_cast<uint32_t>(static_cast<int32_t>(v) / n);
+        } else if constexpr (DT == AR_FLOAT16) {
+            return f16_round(f16_widen(v & 0xffffu) / static_cast<float>(n));
+        } else {
+            return bf16_round(bf16_widen(v & 0xffffu) / static_cast<float>(n));
+        }
+    }
+    static __device__ __forceinline__ uint32_t avg_word(uint32_t v, int n) {
+        if constexpr (elem_size<DT>() == 2) {
+            return avg_elem(v, n) | (avg_elem(v >> 16, n) << 16);
+        } else {
+            return avg_elem(v, n);
+        }
+    }
+    static __device__ __forceinline__ u32x4 avg_vec(u32x4 v, int n) {
+        u32x4 r;
+        r.x = avg_word(v.x, n);
+        r.y = avg_word(v.y, n);
+        r.z = avg_word(v.z, n);
+        r.w = avg_word(v.w, n);
+        return r;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// memory access
+// ---------------------------------------------------------------------------
+
+template <int ESZ>
+__device__ __forceinline__ uint32_t load_elem(const char* p) {
+    if constexpr (ESZ == 2) {
+        return *reinterpret_cast<const uint16_t*>(p);
+    } else {
+        return *reinterpret_cast<const uint32_t*>(p);
+    }
+}
+
+template <int ESZ>
+__device__ __forceinline__ void store_elem(char* p, uint32_t v) {
+    if constexpr (ESZ == 2) {
+        if constexpr (AR_NT_STORES) {
+            __builtin_nontemporal_store(static_cast<uint16_t>(v), reinterpret_cast<uint16_t*>(p));
+        } else {
+            *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(v);
+        }
+    } else {
+        if constexpr (AR_NT_STORES) {
+            __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+        } else {
+            *reinterpret_cast<uint32_t*>(p) = v;
+        }
+    }
+}
+
+template <bool NT = AR_NT_LOADS>
+__device__ __forceinline__ u32x4 load16(const char* p) {
+    if constexpr (NT) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    } else {
+        return *reinterpret_cast<const u32x4*>(p);
+    }
+}
+
+__device__ __forceinline__ void store16(char* p, u32x4 v) {
+    if constexpr (AR_NT_STORES) {
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    } else {
+        *reinterpret_cast<u32x4*>(p) = v;
+    }
+}
+
+// Element e (0 <= e < 16/ESZ) of a 16-byte vector.
+template <int ESZ>
+__device__ __forceinline__ uint32_t vec_elem(u32x4 v, int e) {
+    const uint32_t w = (ESZ == 2) ? v[e >> 1] : v[e];
+    if constexpr (ESZ == 2) {
+        return (e & 1) ? (w >> 16) : (w & 0xffffu);
+    } else {
+        return w;
+    }
+}
+
+// A unit is what one thread moves per rank per access: a 16-byte vector on
+// the vector path (VEC > 1 elements) or one element (VEC == 1).  A block
+// addresses each buffer through the start of its tile (`tile`, uniform over
+// the block) plus the thread's byte offset inside the tile (`lane_off`).
+template <int DT, int VEC, bool NT_LOAD = AR_NT_LOADS>
+struct Unit {
+    static constexpr int kEsz = elem_size<DT>();
+    static constexpr int kBytes = (VEC > 1) ? 16 : kEsz;
+    using T = std::conditional_t<(VEC > 1), u32x4, uint32_t>;
+
+    // `p` is the buffer address minus the common residue (vector path); tv0
+    // the tile's first unit.
+    static __device__ __forceinline__ const char* tile(const char* p, uint64_t tv0) { return p + tv0 * kBytes; }
+    static __device__ __forceinline__ char* tile(char* p, uint64_t tv0) { return p + tv0 * kBytes; }
+    // The thread's u-th unit inside the tile: one 16-byte access per lane per
+    // instruction, so each wave instruction covers 1 KiB contiguous.
+    static __device__ __forceinline__ uint32_t lane_unit(int u) {
+        return threadIdx.x + static_cast<uint32_t>(u) * kThreads;
+    }
+    static __device__ __forceinline__ uint32_t lane_off(int u) { return lane_unit(u) * kBytes; }
+    static __device__ __forceinline__ T load(const char* tb, uint32_t off) {
+        if constexpr (VEC > 1) {
+            return load16<NT_LOAD>(tb + off);
+        } else {
+            return load_elem<kEsz>(tb + off);
+        }
+    }
+    static __device__ __forceinline__ void store(char* tb, uint32_t off, T x) {
+        if constexpr (VEC > 1) {
+            store16(tb + off, x);
+        } else {
+            store_elem<kEsz>(tb + off, x);
+        }
+    }
+    template <int OP>
+    static __device__ __forceinline__ T combine(T a, T b) {
+        if constexpr (VEC > 1) {
+            return Red<DT, OP>::vec(a, b);
+        } else {
+            return Red<DT, OP>::elem(a, b);
+        }
+    }
+};
+
+// The fold of one unit across ranks: the chunk owner's value starts it
+// (`first`), every later rank's value is combined in (`add`), and `done`
+// completes it (avg divides by N once; float32 partials of
+// AR_BFLOAT16_ACC_F32 are rounded to bf16).  A is the type partials are kept
+// in: the buffer type, or float32 for AR_BFLOAT16_ACC_F32.
+template <int DT, int OP, int VEC>
+struct Fold {
+    using U = Unit<DT, VEC>;
+    using T = typename U::T;
+    using A = std::conditional_t<acc_f32<DT>(), std::conditional_t<(VEC > 1), f32x8, float>, T>;
+    static constexpr int kOp = combine_op(OP);
+
+    static __device__ __forceinline__ A widen(T x) {
+        if constexpr (!acc_f32<DT>()) {
+            return x;
+        } else if constexpr (VEC > 1) {
+            f32x8 r;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r[2 * k] = bf16_widen(x[k] & 0xffffu);
+                r[2 * k + 1] = bf16_widen(x[k] >> 16);
+            }
+            return r;
+        } else {
+            return bf16_widen(x & 0xffffu);
+        }
+    }
+    static __device__ __forceinline__ A first(T x) { return widen(x); }
+    static __device__ __forceinline__ A add(A acc, T x) {
+        if constexpr (!acc_f32<DT>()) {
+            return U::template combine<OP>(acc, x);
+        } else if constexpr (VEC > 1) {
+            const f32x8 w = widen(x);
+            f32x8 r;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) r[k] = f32_apply<kOp>(acc[k], w[k]);
+            return r;
+        } else {
+            return f32_apply<kOp>(acc, widen(x));
+        }
+    }
+    // two partials (ring step: the local value and the incoming partial)
+    static __device__ __forceinline__ A add_acc(A acc, A y) {
+        if constexpr (!acc_f32<DT>()) {
+            return U::template combine<OP>(acc, y);
+        } else if constexpr (VEC > 1) {
+            f32x8 r;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) r[k] = f32_apply<kOp>(acc[k], y[k]);
+            return r;
+        } else {
+            return f32_apply<kOp>(acc, y);
+        }
+    }
+    static __device__ __forceinline__ T done(A acc, int n) {
+        if constexpr (!acc_f32<DT>()) {
+            if constexpr (OP == AR_AVG) {
+                if constexpr (VEC > 1) {
+                    return Red<DT, OP>::avg_vec(acc, n);
+                } else {
+                    return Red<DT, OP>::avg_elem(acc, n);
+                }
+            } else {
+                return acc;
+            }
+        } else if constexpr (VEC > 1) {
+            u32x4 r;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float lo = acc[2 * k], hi = acc[2 * k + 1];
+                if constexpr (OP == AR_AVG) {
+                    lo = lo / static_cast<float>(n);
+                    hi = hi / static_cast<float>(n);
+                }
+                r[k] = bf16_round(lo) | (bf16_round(hi) << 16);
+            }
+            return r;
+        } else {
+            float v = acc;
+            if constexpr (OP == AR_AVG) v = v / static_cast<float>(n);
+            return bf16_round(v);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// chunk geometry
+// ---------------------------------------------------------------------------
+
+struct Span {
+    uint64_t s, e;    // element bounds of the chunk
+    uint64_t vb, ve;  // units of the chunk body: vectors (VEC > 1) or elements
+    uint64_t hb, he;  // head elements [hb, he) done one by one (VEC > 1 only)
+    uint64_t tb, te;  // tail elements [tb, te)
+};
+
+template <int VEC>
+__device__ __forceinline__ Span chunk_span(int c, const KernelArgs& a) {
+    Span sp;
+    // c*count/n = c*(count/n) + c*(count%n)/n; the last product is below 128^2,
+    // so only a 32-bit division is left
+    const uint32_t n = static_cast<uint32_t>(a.nranks);
+    const uint32_t cu = static_cast<uint32_t>(c);
+    sp.s = static_cast<uint64_t>(cu) * a.count_q + (cu * a.count_r) / n;
+    sp.e = static_cast<uint64_t>(cu + 1) * a.count_q + ((cu + 1) * a.count_r) / n;
+    if constexpr (VEC > 1) {
+        // the body: whole aligned blocks of A = 2^align_shift elements, as vectors
+        const uint64_t ofs = static_cast<uint64_t>(a.ofs);
+        const uint32_t sh = static_cast<uint32_t>(a.align_shift);
+        const uint64_t first_block = (sp.s + ofs + (1ull << sh) - 1) >> sh;
+        const uint64_t end_block = (sp.e + ofs) >> sh;
+        sp.vb = (first_block << sh) / VEC;
+        sp.ve = (end_block << sh) / VEC;
+        if (sp.ve < sp.vb) sp.ve = sp.vb;
+        const uint64_t body_first = sp.vb * VEC - ofs;   // first element of the body (>= s)
+        const uint64_t body_end = sp.ve * VEC - ofs;     // one past its last element
+        // head [s, min(body_first, e)); tail from the body's end (or the head's end
+        // when the body is empty) up to e; both stay inside [s, e) also for
+        // empty and short chunks
+        sp.hb = sp.s;
+        sp.he = body_first < sp.e ? body_first : sp.e;
+        sp.tb = body_end > sp.he ? body_end : sp.he;
+        if (sp.tb > sp.e) sp.tb = sp.e;
+        sp.te = sp.e;
+    } else {
+        sp.vb = sp.s;
+        sp.ve = sp.e;
+        sp.hb = sp.he = sp.tb = sp.te = sp.s;
+    }
+    return sp;
+}
+
+// Element handled by thread j among the chunk's edge elements, or false.
+__device__ __forceinline__ bool edge_element(const Span& sp, unsigned j, uint64_t* i) {
+    const uint64_t nh = sp.he - sp.hb;
+    const uint64_t nt = sp.te - sp.tb;
+    if (j < nh) {
+        *i = sp.hb + j;
+        return true;
+    }
+    if (j < nh + nt) {
+        *i = sp.tb + (j - nh);
+        return true;
+    }
+    return false;
+}
+
+__device__ __forceinline__ int ring_rank(int c, int k, int n) {
+    // (c + k) mod n for 0 <= c < n, 0 <= k < 2n
+    int r = c + k;
+    r = (r >= n) ? r - n : r;
+    return (r >= n) ? r - n : r;
+}
+
+// ---------------------------------------------------------------------------
+// the ring-order fold of one chunk position across all ranks
+// ---------------------------------------------------------------------------
+
+// acc[u] = ((x_c (op) x_{c+1}) (op) ...) at the thread's units of the tile
+// that starts at unit tv0, for live u.
+template <int DT, int OP, int VEC>
+__device__ __forceinline__ void fold_units(const KernelArgs& a, int c, int64_t adj, uint64_t tv0,
+                                           const bool (&live)[kUnroll],
+                                           typename Fold<DT, OP, VEC>::A (&acc)[kUnroll]) {
+    using U = Unit<DT, VEC>;
+    using F = Fold<DT, OP, VEC>;
+    const int n = a.nranks;
+    {
+        const char* tb = U::tile(a.send[c] - adj, tv0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) acc[u] = F::first(U::load(tb, U::lane_off(u)));
+        }
+    }
+    for (int k = 1; k < n; k += kBatch) {
+        typename U::T x[kBatch][kUnroll];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (k + j < n) {
+                const char* tb = U::tile(a.send[ring_rank(c, k + j, n)] - adj, tv0);
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    if (live[u]) x[j][u] = U::load(tb, U::lane_off(u));
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (k + j < n) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    if (live[u]) acc[u] = F::add(acc[u], x[j][u]);
+                }
+            }
+        }
+    }
+}
+
+// Same fold for one element i (chunk edges), completed.
+template <int DT, int OP>
+__device__ __forceinline__ uint32_t fold_element(const KernelArgs& a, int c, uint64_t i) {
+    constexpr int ESZ = elem_size<DT>();
+    using F = Fold<DT, OP, 1>;
+    const int n = a.nranks;
+    typename F::A acc = F::first(load_elem<ESZ>(a.send[c] + i * ESZ));
+    for (int k = 1; k < n; ++k) {
+        acc = F::add(acc, load_elem<ESZ>(a.send[ring_rank(c, k, n)] + i * ESZ));
+    }
+    return F::done(acc, n);
+}
+
+// Store unit v of a result into a shard that starts at element `s` of the
+// full buffer (reduce-scatter output).  `aligned` says whether the shard's
+// 16-byte vectors line up with the source's.
+template <int DT, int VEC>
+__device__ __forceinline__ void store_shard_unit(char* shard, uint64_t s, int32_t ofs, bool aligned,
+                                                 uint64_t v, typename Unit<DT, VEC>::T x) {
+    constexpr int ESZ = elem_size<DT>();
+    if constexpr (VEC > 1) {
+        const uint64_t first = v * VEC - static_cast<uint64_t>(ofs);   // element index in the full buffer
+        if (aligned) {
+            store16(shard + (first - s) * ESZ, x);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) store_elem<ESZ>(shard + (first + e - s) * ESZ, vec_elem<ESZ>(x, e));
+        }
+    } else {
+        store_elem<ESZ>(shard + (v - s) * ESZ, x);
+    }
+}
+
+// Load unit v of the full-buffer position space from a shard starting at `s`.
+template <int DT, int VEC, bool NT_LOAD>
+__device__ __forceinline__ typename Unit<DT, VEC>::T load_shard_unit(const char* shard, uint64_t s, int32_t ofs,
+                                                                     bool aligned, uint64_t v) {
+    constexpr int ESZ = elem_size<DT>();
+    if constexpr (VEC > 1) {
+        const uint64_t first = v * VEC - static_cast<uint64_t>(ofs);
+        if (aligned) return load16<NT_LOAD>(shard + (first - s) * ESZ);
+        u32x4 r = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const uint32_t x = load_elem<ESZ>(shard + (first + e - s) * ESZ);
+            if constexpr (ESZ == 2) {
+                r[e >> 1] |= (e & 1) ? (x << 16) : x;
+            } else {
+                r[e] = x;
+            }
+        }
+        return r;
+    } else {
+        return load_elem<ESZ>(shard + (v - s) * ESZ);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ bool shard_aligned(const void* shard, uint64_t s, int32_t ofs) {
+    constexpr int ESZ = elem_size<DT>();
+    const uint64_t q = reinterpret_cast<uint64_t>(shard) - (s + static_cast<uint64_t>(ofs)) * ESZ;
+    return (q & 15u) == 0;
+}
+
+// Tile loop: tile -> (chunk c, tile t within the chunk); consecutive tiles
+// walk one chunk after another (measured faster on MI355X than cycling over
+// the chunks, or than renumbering tiles per XCD).  A launch covers tiles
+// [tile_first, tile_end); the host keeps N * tiles_per_chunk below 2^31.
+#define AR_TILE_LOOP_BEGIN                                                                   \
+    const int n = a.nranks;                                                                  \
+    const uint32_t tpc = a.tiles_per_chunk;                                                  \
+    const uint32_t ntiles = a.tile_end;                                                      \
+    const int64_t adj = (VEC > 1) ? static_cast<int64_t>(a.ofs) * elem_size<DT>() : 0;       \
+    for (uint32_t tile = a.tile_first + blockIdx.x; tile < ntiles; tile += gridDim.x) {      \
+        const int c = static_cast<int>(tile / tpc);                                          \
+        const uint64_t t = tile - static_cast<uint32_t>(c) * tpc;                            \
+        const Span sp = chunk_span<VEC>(c, a);                                               \
+        const uint64_t tv0 = sp.vb + t * (kThreads * kUnroll);                               \
+        bool live[kUnroll];                                                                  \
+        _Pragma("unroll") for (int u = 0; u < kUnroll; ++u)                                  \
+            live[u] = tv0 + U::lane_unit(u) < sp.ve;
+
+#define AR_TILE_LOOP_END }
+
+// Partial sums kept between the steps of a schedule: the buffer type, or
+// float32 (4 bytes per element, 32 bytes per unit of eight bf16) for
+// AR_BFLOAT16_ACC_F32.  `base` is the workspace minus the common residue in
+// partial-sized elements, so unit v sits at base + v * kBytes.
+template <int DT, int VEC>
+struct Partials {
+    static constexpr bool kF32 = acc_f32<DT>();
+    static constexpr int kElemBytes = kF32 ? 4 : elem_size<DT>();
+    static constexpr int kBytes = kF32 ? (VEC > 1 ? 32 : 4) : Unit<DT, VEC>::kBytes;
+    using A = typename Fold<DT, AR_SUM, VEC>::A;
+
+    static __device__ __forceinline__ A load(const char* base, uint64_t v) {
+        const char* p = base + v * kBytes;
+        if constexpr (!kF32) {
+            return Unit<DT, VEC, false>::load(p, 0);
+        } else if constexpr (VEC > 1) {
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+            f32x8 r;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r[k] = as_f(lo[k]);
+                r[k + 4] = as_f(hi[k]);
+            }
+            return r;
+        } else {
+            return *reinterpret_cast<const float*>(p);
+        }
+    }
+    static __device__ __forceinline__ void store(char* base, uint64_t v, A x) {
+        char* p = base + v * kBytes;
+        if constexpr (!kF32 && VEC > 1) {
+            *reinterpret_cast<u32x4*>(p) = x;
+        } else if constexpr (!kF32) {
+            // one element of the buffer type, held in the low bits of x
+            if constexpr (elem_size<DT>() == 2) {
+                *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(x);
+            } else {
+                *reinterpret_cast<uint32_t*>(p) = x;
+            }
+        } else if constexpr (VEC > 1) {
+            u32x4 lo, hi;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                lo[k] = as_u(x[k]);
+                hi[k] = as_u(x[k + 4]);
+            }
+            *reinterpret_cast<u32x4*>(p) = lo;
+            *reinterpret_cast<u32x4*>(p + 16) = hi;
+        } else {
+            *reinterpret_cast<float*>(p) = x;
+        }
+    }
+};
+
+}  // namespace
+}  // namespace arimpl

@@ -19,6 +19,21 @@ enum class Kind : int {
     kRingReduceStep,       // AllReduce ring, reduce-scatter step `step`
     kRingReduceStepWs,     // reduce-scatter ring, step `step`, partials in the workspace
     kRingCopyStep,         // all-gather ring step `step` (rank mapping shifted by `shift`)
+    kFusedTree,            // reduce element i over all ranks in the binomial-tree bracketing of the
+                           // send table's order, store to every rank
+    kTreeReduceStep,       // one reducing stage of a tree-shaped schedule (`mode`, `step`)
+    kTreeCopyStep,         // one distributing stage of a tree-shaped schedule (`mode`, `step`)
+};
+
+// Stages of the tree-shaped schedules; at stage `step` the partner distance is d.
+enum TreeMode : int {
+    kTreeReduce = 0,       // binomial reduction, d = 2^step: rank r (r mod 2d == 0) adds rank r+d
+    kTreeBcast = 1,        // binomial distribution, d = 2^step: rank r (r mod 2d == 0) sends to r+d
+    kRdExchange = 2,       // recursive doubling, d = 2^step: ranks r and r^d both get r (op) r^d
+    kHalvingReduce = 3,    // recursive halving, d = N / 2^(step+1): of each pair sharing chunk c,
+                           // the rank whose bit d matches c's adds its partner's partial
+    kDoublingGather = 4,   // recursive doubling all-gather, d = 2^step: chunk c goes to the ranks
+                           // that lack it from their partner r^d
 };
 
 // Kernel arguments, passed by value.  Pointers are the callers' device
@@ -45,6 +60,9 @@ struct KernelArgs {
     int32_t shift;             // kRingCopyStep: acting rank = (c + step + shift) mod N
     int32_t ofs;               // common element residue of the streamed buffers modulo the body alignment
     int32_t align_shift;       // log2 of the body alignment in elements (vector path)
+    int32_t mode;              // kTree*Step: a TreeMode
+    int32_t last;              // kTreeReduceStep: nonzero on the stage that completes the values
+    uint64_t ws_stride;        // kTreeReduceStep with float32 partials: bytes between ranks' partials
 };
 
 struct Launch {
@@ -53,6 +71,7 @@ struct Launch {
     ar_op_t op;
     bool vec;                  // 16-byte vector path (all streamed buffers share a residue)
     unsigned blocks;
+    int depth;                 // kFusedTree: partial slots, 2^depth > N (4, 6 or 8)
 };
 
 // Vectors of 16 bytes each thread handles per rank per tile.
@@ -63,5 +82,9 @@ constexpr int kUnroll = AR_TILE_UNROLL;
 
 // Enqueue one kernel; returns the HIP error of the launch.
 hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream);
+
+// The kernels of the tree-shaped schedules (ar_tree_kernels.hip); `launch`
+// forwards the kFusedTree, kTreeReduceStep and kTreeCopyStep kinds here.
+hipError_t launch_tree(const Launch& l, const KernelArgs& a, hipStream_t stream);
 
 }  // namespace arimpl

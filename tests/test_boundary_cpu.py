@@ -117,8 +117,8 @@ def test_in_place_layouts_are_accepted_others_rejected(lib):
     shards_ok = [sends[r] + 4 * starts[r] for r in range(n)]
     shards_bad = [sends[r] + 4 * starts[r] + 4 for r in range(n)]
     rs = lib.ar_reduce_scatter_ex
-    # with algo = 7 (unknown) the call stops after the aliasing checks would have passed
-    assert rs(_ptrs(sends), _ptrs(shards_ok), count, 0, 0, n, 7, None, 0, None) == 1
+    # with algo = 99 (unknown) the call stops after the aliasing checks would have passed
+    assert rs(_ptrs(sends), _ptrs(shards_ok), count, 0, 0, n, 99, None, 0, None) == 1
     assert b"algo" in lib.ar_get_last_error_detail()
     assert rs(_ptrs(sends), _ptrs(shards_bad), count, 0, 0, n, 0, None, 0, None) == 1
     assert b"overlaps" in lib.ar_get_last_error_detail()
@@ -231,3 +231,42 @@ def test_plain_c_consumer_of_the_header(tmp_path, lib):
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert res.returncode == 0, res.stderr
     assert "passed" in res.stdout
+
+
+def test_tree_algorithm_host_rules(lib):
+    """Tree-order algorithms: AllReduce only, power-of-two N where the schedule needs it,
+    and float32 partial slabs for the staged forms of bf16acc32."""
+    import ring_allreduce_reduction_virtual_amd as ar
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    slab = ((1000 * 4 + 255) // 256) * 256
+    for algo in ("tree_steps", "recursive_doubling", "halving_doubling_steps"):
+        assert ar.ar_workspace_bytes("allreduce", algo, 1000, "bf16acc32", 8) == 8 * slab + 1024
+        assert ar.ar_workspace_bytes("allreduce", algo, 1000, "bf16acc32", 1) == 0
+        assert ar.ar_workspace_bytes("allreduce", algo, 1000, "bf16", 8) == 0
+        assert ar.ar_workspace_bytes("allreduce", algo, 0, "bf16acc32", 8) == 0
+    for algo in ("tree", "halving_doubling"):
+        assert ar.ar_workspace_bytes("allreduce", algo, 1000, "bf16acc32", 8) == 0
+    S = 1 << 20
+    sends = [BASE + r * S for r in range(8)]
+    recvs = [BASE + (16 + r) * S for r in range(8)]
+    for name in _lib.TREE_ALGOS:
+        algo = _lib.ALGOS[name]
+        # reduce-scatter and all-gather have no tree form
+        assert lib.ar_reduce_scatter_ex(_ptrs(sends), _ptrs(recvs), 100, 0, 0, 8, algo, None, 0, None) == 2
+        assert b"AllReduce only" in lib.ar_get_last_error_detail()
+        assert lib.ar_all_gather_ex(_ptrs(sends), _ptrs(recvs), 100, 0, 8, algo, None, 0, None) == 2
+        # six ranks: only the binomial tree is defined
+        rc = lib.ar_allreduce_ex(_ptrs(sends[:6]), _ptrs(recvs[:6]), 100, 0, 0, 6, algo, None, 0, None)
+        if name in ("tree", "tree_steps"):
+            assert rc in (0, 3)   # valid: reaches the device (none here) or succeeds
+        else:
+            assert rc == 2 and b"power-of-two" in lib.ar_get_last_error_detail()
+        # empty work plans no launch
+        plan = ctypes.c_void_p()
+        assert lib.ar_allreduce_init(_ptrs(sends), _ptrs(recvs), 0, 0, 0, 8, algo, None, 0, ctypes.byref(plan)) == 0
+        assert lib.ar_plan_num_launches(plan) == 0
+        assert lib.ar_plan_free(plan) == 0
+    # the staged forms of bf16acc32 need their workspace
+    rc = lib.ar_allreduce_ex(_ptrs(sends), _ptrs(recvs), 100, 4, 0, 8, _lib.ALGOS["tree_steps"], None, 0, None)
+    assert rc == 1 and b"workspace" in lib.ar_get_last_error_detail()
