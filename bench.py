@@ -29,7 +29,10 @@ if ROOT not in sys.path:
 METRIC = "AllReduce algbw/busbw GB/s + % HBM peak, N=8 ranks x 64M fp32, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fused_allreduce_headline_counters.md")
-KERNEL_SOURCE = os.path.join(ROOT, "ring_allreduce_reduction_virtual_amd", "csrc", "ar_kernels.hip")
+# the sources the fused AllReduce kernel is built from (its counters are only
+# used while these are unchanged)
+KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_reduction_virtual_amd", "csrc", f)
+                  for f in ("ar_kernels.hip", "ar_device.h", "ar_internal.h")]
 
 
 def log(*a):
@@ -48,8 +51,11 @@ def algorithmic_bytes(coll: str, n: int, s_bytes: int) -> int:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(per_launch_algo_bytes: int):
@@ -294,12 +300,89 @@ def run_variants(args):
         torch.cuda.empty_cache()
 
 
-def run_size_sweep(args):
-    """AllReduce time against message size, 8 ranks of float32, both algorithms.
+def run_orders(args):
+    """The tree-shaped orders beside the ring: full workloads timed with sampled
+    parity against the bracketing's evaluation, and small messages timed as
+    one-shot calls, persistent plans and HIP graph replays (the latency
+    regime, where the pages expect 2 log2 N stages to beat the ring's 2(N-1))."""
+    import numpy as np
+    import torch
 
-    Fits the cost model of tirogla.com "Ring all-reduce" on one GPU: the fused
-    kernel t = a + 2*N*S/B (one launch), the ring mode t = 2(N-1)*a' + 5(N-1)*S/B'
-    (one launch per step; 5(N-1)*S bytes move through HBM).
+    import ring_allreduce_reduction_virtual_amd as ar
+    from inputs import WORKLOADS, make_inputs
+    from oracle.orders import order_bracketing, tree_order_fold_columns
+    from oracle.ring import chunk, same_bits
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}
+    order_of = {"tree": "tree", "tree_steps": "tree", "recursive_doubling": "recursive_doubling",
+                "halving_doubling": "halving_doubling", "halving_doubling_steps": "halving_doubling"}
+
+    def parity(xs, outs, dt, algo, pos):
+        want = tree_order_fold_columns(np.stack([x[pos] for x in xs]), order_bracketing(order_of[algo], len(xs)),
+                                       "sum", dt)
+        idx = torch.from_numpy(pos).to(dev)
+        for t in outs:
+            got = t[idx].cpu()
+            got = got.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else got.numpy()
+            if not same_bits(got, want, dt):
+                return False
+        return True
+
+    for name in ("headline", "c3", "c4", "c5"):
+        w = WORKLOADS[name]
+        n, count, dt = w.nranks, w.count, w.dtype
+        xs = make_inputs(w)
+        sends = [_to_device(x, dt, dev) for x in xs]
+        recvs = [torch.empty(count, dtype=tdt[dt], device=dev) for _ in range(n)]
+        s_bytes = count * sends[0].element_size()
+        rng = np.random.default_rng(9)
+        pos = np.unique(np.concatenate([rng.integers(0, count, 1024)] +
+                                       [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1]) for c in range(n)]))
+        for algo in ("fused", "tree", "halving_doubling", "tree_steps", "recursive_doubling", "halving_doubling_steps"):
+            med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 10, 2, stream)
+            ok = (_sampled_parity(xs, recvs, dt, "sum", pos) if algo == "fused"
+                  else parity(xs, recvs, dt, algo, pos))
+            algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
+            print(json.dumps({"orders": name, "algo": algo, "dtype": dt, "nranks": n, "count": count,
+                              "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                              "algbw_gbps": round(s_bytes / (med / 1e3) / 1e9, 2),
+                              "hbm_gbps_of_minimum": round(algo_bytes / (med / 1e3) / 1e9, 1),
+                              "hbm_frac": round(algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                              "parity_sampled": "pass" if ok else "fail"}), flush=True)
+        del sends, recvs, xs
+        torch.cuda.empty_cache()
+
+    # latency regime: 4 KiB per rank at 4, 8 and 64 ranks
+    for n in (4, 8, 64):
+        count = 1024
+        sends = [torch.randn(count, device=dev) for _ in range(n)]
+        recvs = [torch.empty(count, device=dev) for _ in range(n)]
+        for algo in ("fused", "ring", "tree", "tree_steps", "recursive_doubling", "halving_doubling_steps"):
+            med, _ = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 200, 5, stream)
+            plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
+            pmed, _ = median_call_ms(plan.start, 200, 5, stream)
+            gus = graph_ms_per_call(plan.start, 50, stream) * 1e3
+            print(json.dumps({"latency": f"{n} x 1024 f32", "algo": algo, "launches": plan.num_launches,
+                              "one_shot_median_us": round(med * 1e3, 2), "plan_median_us": round(pmed * 1e3, 2),
+                              "graph_us_per_call": round(gus, 2)}), flush=True)
+            plan.close()
+        del sends, recvs
+
+
+SWEEP_ALGOS = ("fused", "ring", "tree", "tree_steps", "recursive_doubling", "halving_doubling_steps")
+
+
+def run_size_sweep(args):
+    """AllReduce time against message size, 8 ranks of float32, every schedule.
+
+    Fits the cost model of tirogla.com "Ring all-reduce" on one GPU,
+    t = launches * a + HBM bytes / B: one launch and 2*N*S bytes for the fused
+    kernels, 2(N-1) launches and 5(N-1)*S bytes for the ring's steps,
+    2 log2 N launches and 5(N-1)*S bytes for the staged tree and
+    halving/doubling, log2 N launches and 2*N*S*log2 N bytes for recursive
+    doubling.
     """
     import numpy as np
     import torch
@@ -314,7 +397,7 @@ def run_size_sweep(args):
         count = 1 << k
         sends = [torch.randn(count, device=dev) for _ in range(n)]
         recvs = [torch.empty(count, device=dev) for _ in range(n)]
-        for algo in ("fused", "ring"):
+        for algo in SWEEP_ALGOS:
             med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 50, 5, stream)
             rows.append((algo, count, med))
             s_bytes = count * 4
@@ -325,7 +408,11 @@ def run_size_sweep(args):
                   flush=True)
         del sends, recvs
     fits = {}
-    for algo, bytes_factor, launches in (("fused", 2 * n, 1), ("ring", 5 * (n - 1), 2 * (n - 1))):
+    L = (n - 1).bit_length()
+    for algo, bytes_factor, launches in (("fused", 2 * n, 1), ("ring", 5 * (n - 1), 2 * (n - 1)),
+                                         ("tree", 2 * n, 1), ("tree_steps", 5 * (n - 1), 2 * L),
+                                         ("recursive_doubling", 2 * n * L, L),
+                                         ("halving_doubling_steps", 5 * (n - 1), 2 * L)):
         pts = [(c * 4 * bytes_factor, t / 1e3) for a, c, t in rows if a == algo]
         A = np.array([[launches, b] for b, _ in pts], dtype=np.float64)
         y = np.array([t for _, t in pts])
@@ -359,6 +446,9 @@ def main():
     ap.add_argument("--variants", action="store_true",
                     help="instead of the headline line: time the precision and operator variants "
                          "(float32 partials for bf16, avg, binary16) at full size, one JSON line each")
+    ap.add_argument("--orders", action="store_true",
+                    help="instead of the headline line: the tree-shaped orders beside the ring at full size "
+                         "(sampled parity) and in the latency regime (one-shot, plan, graph)")
     ap.add_argument("--size-sweep", action="store_true",
                     help="instead of the headline line: AllReduce time against message size (8 ranks, f32), "
                          "fused and ring, with an alpha-beta fit")
@@ -389,6 +479,9 @@ def main():
         return
     if args.variants:
         run_variants(args)
+        return
+    if args.orders:
+        run_orders(args)
         return
     w = WORKLOADS["headline"]
     n, count = w.nranks, w.count

@@ -332,10 +332,10 @@ public:
         if (debug_enabled()) {
             std::fprintf(stderr,
                          "[ar] %s dtype=%s op=%d n=%d count=%llu step=%d shift=%d mode=%d last=%d vec=%d ofs=%d "
-                         "align=2^%d tiles=[%u,%u) tiles/chunk=%u blocks=%u%s\n",
+                         "align=2^%d tiles=[%u,%u) tiles/chunk=%u blocks=%u actors=%u%s\n",
                          kind_name(kind), dtype_name(k.dtype), static_cast<int>(k.op), k.n,
                          static_cast<unsigned long long>(k.count), a.step, a.shift, a.mode, a.last, l.vec ? 1 : 0, a.ofs,
-                         a.align_shift, a.tile_first, a.tile_end, a.tiles_per_chunk, l.blocks,
+                         a.align_shift, a.tile_first, a.tile_end, a.tiles_per_chunk, l.blocks, l.actors,
                          steps_ != nullptr ? " (planned)" : "");
         }
         if (steps_ != nullptr) {
@@ -396,6 +396,22 @@ ar_result_t use_workspace(KernelArgs& a, const Common& k, ar_coll_t coll, ar_alg
     return AR_SUCCESS;
 }
 
+// Ranks acting on one chunk in a stage of a tree-shaped schedule (the same
+// count the kernels derive; each gets its own row of blocks).
+unsigned stage_actors(int mode, int step, int n) {
+    switch (mode) {
+        case arimpl::kTreeReduce:
+        case arimpl::kTreeBcast: {
+            const int d = 1 << step;
+            return n > d ? static_cast<unsigned>((n - d + 2 * d - 1) / (2 * d)) : 0u;
+        }
+        case arimpl::kRdExchange: return static_cast<unsigned>(n / 2);
+        case arimpl::kHalvingReduce: return static_cast<unsigned>(n >> (step + 1));
+        case arimpl::kDoublingGather: return 1u << step;
+    }
+    return 0u;
+}
+
 // AllReduce in a tree-shaped order.  The fused kernel folds the send table as
 // a binomial tree; recursive halving's order is that tree over the ranks in
 // bit-reversed order.  The staged forms emit one launch per stage.
@@ -418,6 +434,7 @@ ar_result_t tree_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         a.mode = mode;
         a.step = step;
         a.last = last ? 1 : 0;
+        l.actors = stage_actors(mode, step, k.n);
         return sink.emit(l, kind, a, k);
     };
     switch (algo) {

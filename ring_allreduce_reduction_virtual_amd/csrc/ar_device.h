@@ -23,6 +23,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr int kBatch = AR_RANK_BATCH;
 
+// Ranks whose loads are in flight together when one element is folded on
+// its own (chunk edges).  Each batch costs a memory round trip, and when
+// chunks are only a few elements long (small messages over many ranks) the
+// edges are all there is.
+constexpr int kEdgeBatch = 8;
+
 // Nontemporal hints: the reducing kernels stream their N input buffers once
 // (AR_NT_LOADS), the copies read a shard that several ranks' stores follow
 // (AR_NT_LOADS_COPY), and every output is written once (AR_NT_STORES).
@@ -488,10 +494,38 @@ __device__ __forceinline__ uint32_t fold_element(const KernelArgs& a, int c, uin
     using F = Fold<DT, OP, 1>;
     const int n = a.nranks;
     typename F::A acc = F::first(load_elem<ESZ>(a.send[c] + i * ESZ));
-    for (int k = 1; k < n; ++k) {
-        acc = F::add(acc, load_elem<ESZ>(a.send[ring_rank(c, k, n)] + i * ESZ));
+    for (int k = 1; k < n; k += kEdgeBatch) {
+        uint32_t x[kEdgeBatch];
+#pragma unroll
+        for (int j = 0; j < kEdgeBatch; ++j) {
+            if (k + j < n) x[j] = load_elem<ESZ>(a.send[ring_rank(c, k + j, n)] + i * ESZ);
+        }
+#pragma unroll
+        for (int j = 0; j < kEdgeBatch; ++j) {
+            if (k + j < n) acc = F::add(acc, x[j]);
+        }
     }
     return F::done(acc, n);
+}
+
+// Store one element i to every rank's receive buffer (chunk edges).  The
+// receive pointers come from the kernel arguments kEdgeBatch at a time, so
+// their loads overlap instead of each store waiting for its own pointer
+// (which dominates when chunks are tiny).  The tiles' stores keep a plain
+// loop: batching their pointers costs registers, and occupancy, there.
+template <int ESZ>
+__device__ __forceinline__ void store_elem_all(const KernelArgs& a, int n, uint64_t i, uint32_t v) {
+    for (int q0 = 0; q0 < n; q0 += kEdgeBatch) {
+        char* p[kEdgeBatch];
+#pragma unroll
+        for (int j = 0; j < kEdgeBatch; ++j) {
+            if (q0 + j < n) p[j] = a.recv[q0 + j];
+        }
+#pragma unroll
+        for (int j = 0; j < kEdgeBatch; ++j) {
+            if (q0 + j < n) store_elem<ESZ>(p[j] + i * ESZ, v);
+        }
+    }
 }
 
 // Store unit v of a result into a shard that starts at element `s` of the

@@ -72,6 +72,7 @@ struct Launch {
     bool vec;                  // 16-byte vector path (all streamed buffers share a residue)
     unsigned blocks;
     int depth;                 // kFusedTree: partial slots, 2^depth > N (4, 6 or 8)
+    unsigned actors;           // kTree*Step: actors per chunk in the stage (the grid's y extent)
 };
 
 // Vectors of 16 bytes each thread handles per rank per tile.

@@ -41,8 +41,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_allreduce(const KernelArgs a
     if (VEC > 1 && t == 0) {
         uint64_t i;
         if (edge_element(sp, threadIdx.x, &i)) {
-            const uint32_t r = fold_element<DT, OP>(a, c, i);
-            for (int q = 0; q < n; ++q) store_elem<elem_size<DT>()>(a.recv[q] + i * elem_size<DT>(), r);
+            store_elem_all<elem_size<DT>()>(a, n, i, fold_element<DT, OP>(a, c, i));
         }
     }
     typename Fold<DT, OP, VEC>::A acc[kUnroll];

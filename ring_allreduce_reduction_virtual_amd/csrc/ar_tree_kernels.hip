@@ -96,10 +96,20 @@ __device__ __forceinline__ uint32_t tree_element(const KernelArgs& a, uint64_t i
     using F = Fold<DT, OP, 1>;
     typename F::A slot[D][kUnroll];
     const bool live[kUnroll] = {true};
-    for (int k = 0; k < a.nranks; ++k) {
-        typename F::A x[kUnroll];
-        x[0] = F::first(load_elem<ESZ>(a.send[k] + i * ESZ));
-        tree_push<DT, OP, 1, D>(slot, static_cast<uint32_t>(k), x, live);
+    for (int k = 0; k < a.nranks; k += kEdgeBatch) {
+        uint32_t v[kEdgeBatch];
+#pragma unroll
+        for (int j = 0; j < kEdgeBatch; ++j) {
+            if (k + j < a.nranks) v[j] = load_elem<ESZ>(a.send[k + j] + i * ESZ);
+        }
+#pragma unroll
+        for (int j = 0; j < kEdgeBatch; ++j) {
+            if (k + j < a.nranks) {
+                typename F::A x[kUnroll];
+                x[0] = F::first(v[j]);
+                tree_push<DT, OP, 1, D>(slot, static_cast<uint32_t>(k + j), x, live);
+            }
+        }
     }
     return F::done(tree_result<DT, OP, 1, D>(slot, static_cast<uint32_t>(a.nranks), 0), a.nranks);
 }
@@ -118,8 +128,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_tree(const KernelArgs a) {
     if (VEC > 1 && t == 0) {
         uint64_t i;
         if (edge_element(sp, threadIdx.x, &i)) {
-            const uint32_t r = tree_element<DT, OP, D>(a, i);
-            for (int q = 0; q < n; ++q) store_elem<elem_size<DT>()>(a.recv[q] + i * elem_size<DT>(), r);
+            store_elem_all<elem_size<DT>()>(a, n, i, tree_element<DT, OP, D>(a, i));
         }
     }
     typename F::A slot[D][kUnroll];
@@ -234,7 +243,7 @@ __device__ __forceinline__ const char* partial_of(const KernelArgs& a, int x) {
     }
 }
 
-// A reducing stage: for every actor of chunk c, out = left (op) right; the
+// A reducing stage: actor blockIdx.y of chunk c computes out = left (op) right; the
 // stage that completes the values (`last`) finishes them (avg divides by N,
 // float32 partials round to bf16) into the receive buffer.  Hazard-free:
 // in every mode no rank's partial is written in a stage where another rank
@@ -248,10 +257,11 @@ __global__ __launch_bounds__(kThreads) void k_tree_reduce_step(const KernelArgs 
     using P1 = Partials<DT, 1>;
     constexpr int ESZ = elem_size<DT>();
     const int64_t pofs = acc_f32<DT>() ? static_cast<int64_t>(a.ofs) * 4 : static_cast<int64_t>(a.ofs) * ESZ;
+    const int j = static_cast<int>(blockIdx.y);
+    if (j >= stage_actors(a.mode, a.step, a.nranks)) return;
     AR_TILE_LOOP_BEGIN
-    const int nact = stage_actors(a.mode, a.step, n);
     const bool last = a.last != 0;
-    for (int j = 0; j < nact; ++j) {
+    {
         const Actor ac = stage_actor(a.mode, a.step, n, c, j);
         const bool ls = operand_is_send(a, ac.left), rs = operand_is_send(a, ac.right);
         if (VEC > 1 && t == 0) {
@@ -316,15 +326,16 @@ __global__ __launch_bounds__(kThreads) void k_tree_reduce_step(const KernelArgs 
     AR_TILE_LOOP_END
 }
 
-// A distributing stage: for every actor of chunk c, recv[out] = recv[left].
+// A distributing stage: actor blockIdx.y of chunk c copies recv[left] to recv[out].
 // No rank is both a source and a destination of chunk c in one stage.
 template <int DT, int VEC>
 __global__ __launch_bounds__(kThreads) void k_tree_copy_step(const KernelArgs a) {
     using U = Unit<DT, VEC, AR_NT_LOADS_COPY>;
     constexpr int ESZ = elem_size<DT>();
+    const int j = static_cast<int>(blockIdx.y);
+    if (j >= stage_actors(a.mode, a.step, a.nranks)) return;
     AR_TILE_LOOP_BEGIN
-    const int nact = stage_actors(a.mode, a.step, n);
-    for (int j = 0; j < nact; ++j) {
+    {
         const Actor ac = stage_actor(a.mode, a.step, n, c, j);
         const char* src = a.recv[ac.left];
         char* dst = a.recv[ac.out];
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_copy_step(const KernelArgs a)
 
 template <int DT, int OP, int VEC>
 hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
-    const dim3 grid(l.blocks), block(kThreads);
+    const dim3 grid(l.blocks, l.actors > 0 ? l.actors : 1), block(kThreads);
     switch (l.kind) {
         case Kind::kFusedTree:
             switch (l.depth) {
@@ -394,7 +405,7 @@ hipError_t by_op(const Launch& l, const KernelArgs& a, hipStream_t s) {
 template <int DT>
 hipError_t copy_by_vec(const Launch& l, const KernelArgs& a, hipStream_t s) {
     constexpr int V = 16 / elem_size<DT>();
-    const dim3 grid(l.blocks), block(kThreads);
+    const dim3 grid(l.blocks, l.actors > 0 ? l.actors : 1), block(kThreads);
     if (l.vec) {
         hipLaunchKernelGGL((k_tree_copy_step<DT, V>), grid, block, 0, s, a);
     } else {
