@@ -371,6 +371,118 @@ def run_orders(args):
         del sends, recvs
 
 
+def run_interference(args):
+    """The fused AllReduce overlapping a bf16 GEMM on another stream.
+
+    arjunsriva.com "AllReduce, All the Way Down" (section on communication
+    sharing the machine with the model): an overlapped collective still takes
+    compute units and HBM bandwidth from the computation beside it, so the
+    fastest collective alone is not necessarily the fastest step.  Here the
+    AllReduce's footprint is bounded by capping its workgroups
+    (ar_plan_limit_blocks); for each cap: the AllReduce alone, the GEMM alone,
+    both launched together (each one's own duration and the makespan), against
+    running them one after the other.
+    """
+    import numpy as np
+    import torch
+
+    import ring_allreduce_reduction_virtual_amd as ar
+    from inputs import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["headline"]
+    n, count = w.nranks, w.count
+    s_bytes = count * 4
+    xs = make_inputs(w)
+    sends = [torch.from_numpy(x).to(dev) for x in xs]
+    recvs = [torch.empty(count, device=dev) for _ in range(n)]
+    plan = ar.ar_allreduce_init(sends, recvs, algo="fused")
+    dim = 8192
+    g = torch.Generator(device=dev).manual_seed(5)
+    a = torch.randn(dim, dim, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(dim, dim, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(dim, dim, device=dev, dtype=torch.bfloat16)
+    flops = 2.0 * dim ** 3
+    s_ar, s_mm = torch.cuda.Stream(), torch.cuda.Stream()
+    gemm_calls = 1
+
+    def gemm():
+        for _ in range(gemm_calls):
+            torch.matmul(a, b, out=c)
+
+    def alone(fn, stream, reps=15):
+        ts = []
+        with torch.cuda.stream(stream):
+            for i in range(reps + 3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                if i >= 3:
+                    ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    def together(ar_first, reps=15):
+        rows = []
+        for i in range(reps + 3):
+            go = torch.cuda.Event()
+            go.record(torch.cuda.current_stream())
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            s_ar.wait_event(go)
+            s_mm.wait_event(go)
+
+            def launch_gemm():
+                ev[0].record(s_mm)
+                with torch.cuda.stream(s_mm):
+                    gemm()
+                ev[1].record(s_mm)
+
+            def launch_ar():
+                ev[2].record(s_ar)
+                plan.start(s_ar)
+                ev[3].record(s_ar)
+
+            if ar_first:
+                launch_ar()
+                launch_gemm()
+            else:
+                launch_gemm()
+                launch_ar()
+            torch.cuda.synchronize()
+            if i >= 3:
+                t_mm = ev[0].elapsed_time(ev[1]) * 1e3
+                t_ar = ev[2].elapsed_time(ev[3]) * 1e3
+                first = ev[0] if ev[0].elapsed_time(ev[2]) >= 0 else ev[2]
+                last_mm = first.elapsed_time(ev[1]) * 1e3
+                last_ar = first.elapsed_time(ev[3]) * 1e3
+                rows.append((t_ar, t_mm, max(last_mm, last_ar)))
+        return [float(np.median([r[k] for r in rows])) for k in range(3)]
+
+    # size the GEMM side to about the AllReduce's length
+    t_one = alone(gemm, s_mm)
+    t_ar0 = alone(lambda: plan.start(s_ar), s_ar)
+    gemm_calls = max(1, int(round(t_ar0 / t_one)))
+    t_mm = alone(gemm, s_mm)
+    log(f"[interference] GEMM {dim}^3 bf16 x{gemm_calls}: {t_mm:.1f} us alone; AllReduce {t_ar0:.1f} us alone")
+    for cap in (0, 2048, 1024, 512, 256, 128, 64):
+        plan.limit_blocks(cap)
+        t_ar = alone(lambda: plan.start(s_ar), s_ar)
+        for ar_first in (False, True):
+            o_ar, o_mm, span = together(ar_first)
+            print(json.dumps({
+                "interference": "fused AllReduce 8 x 2^26 f32 beside bf16 GEMM",
+                "gemm": f"{dim}x{dim}x{dim} x{gemm_calls}", "launched_first": "allreduce" if ar_first else "gemm",
+                "ar_blocks": cap if cap else "one per tile",
+                "ar_alone_us": round(t_ar, 1), "ar_alone_hbm_gbps": round(2 * n * s_bytes / t_ar / 1e3, 1),
+                "gemm_alone_us": round(t_mm, 1), "gemm_alone_tflops": round(gemm_calls * flops / t_mm / 1e6, 1),
+                "ar_overlap_us": round(o_ar, 1), "gemm_overlap_us": round(o_mm, 1), "makespan_us": round(span, 1),
+                "sequential_us": round(t_ar + t_mm, 1),
+                "gemm_slowdown_us": round(o_mm - t_mm, 1), "ar_slowdown_us": round(o_ar - t_ar, 1)}), flush=True)
+    plan.limit_blocks(0)
+    plan.close()
+
+
 SWEEP_ALGOS = ("fused", "ring", "tree", "tree_steps", "recursive_doubling", "halving_doubling_steps")
 
 
@@ -449,6 +561,9 @@ def main():
     ap.add_argument("--orders", action="store_true",
                     help="instead of the headline line: the tree-shaped orders beside the ring at full size "
                          "(sampled parity) and in the latency regime (one-shot, plan, graph)")
+    ap.add_argument("--interference", action="store_true",
+                    help="instead of the headline line: the fused AllReduce overlapping a bf16 GEMM, "
+                         "with the AllReduce's workgroups capped at several sizes")
     ap.add_argument("--size-sweep", action="store_true",
                     help="instead of the headline line: AllReduce time against message size (8 ranks, f32), "
                          "fused and ring, with an alpha-beta fit")
@@ -482,6 +597,9 @@ def main():
         return
     if args.orders:
         run_orders(args)
+        return
+    if args.interference:
+        run_interference(args)
         return
     w = WORKLOADS["headline"]
     n, count = w.nranks, w.count

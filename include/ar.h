@@ -228,6 +228,16 @@ ar_result_t ar_all_gather_init(const void* const* sendbufs, void* const* recvbuf
 ar_result_t ar_plan_start(ar_plan_t plan, hipStream_t stream);
 /* Kernel launches one start enqueues (0 for count == 0), or -1 for NULL. */
 int ar_plan_num_launches(ar_plan_t plan);
+/* Cap the workgroups of every launch of the plan at `max_blocks` (each
+ * launch keeps at least one block per acting rank of its stage); the
+ * kernels then stride over their tiles, with the same results.  0 restores
+ * the planned grids (one block per tile).  This bounds the compute units a
+ * collective occupies while it overlaps other work: arjunsriva.com "AllReduce,
+ * All the Way Down" (section on communication sharing the machine with the
+ * model) notes that an overlapped collective still takes SMs and HBM
+ * bandwidth from the computation beside it.  Not safe to call while another
+ * thread starts the same plan. */
+ar_result_t ar_plan_limit_blocks(ar_plan_t plan, unsigned max_blocks);
 ar_result_t ar_plan_free(ar_plan_t plan);
 
 /* Workspace in bytes that a call with these arguments needs (0: none).

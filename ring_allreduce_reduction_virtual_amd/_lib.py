@@ -31,7 +31,7 @@ EXPORTS = (
     "ar_workspace_bytes", "ar_chunk_range", "ar_get_error_string",
     "ar_get_last_error_detail", "ar_dtype_size",
     "ar_allreduce_init", "ar_reduce_scatter_init", "ar_all_gather_init",
-    "ar_plan_start", "ar_plan_num_launches", "ar_plan_free",
+    "ar_plan_start", "ar_plan_num_launches", "ar_plan_free", "ar_plan_limit_blocks",
 )
 
 _lib = None
@@ -61,6 +61,7 @@ def _declare(lib):
         "ar_plan_start": (_int, [_vp, _vp]),
         "ar_plan_num_launches": (_int, [_vp]),
         "ar_plan_free": (_int, [_vp]),
+        "ar_plan_limit_blocks": (_int, [_vp, ctypes.c_uint]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -245,6 +245,12 @@ class Plan:
             raise ValueError("plan is closed")
         _lib.check("ar_plan_start", _lib.lib().ar_plan_start(self._handle, _stream_handle(stream)))
 
+    def limit_blocks(self, max_blocks: int):
+        """Cap the workgroups of every launch (0: back to the planned grids)."""
+        if self._handle is None:
+            raise ValueError("plan is closed")
+        _lib.check("ar_plan_limit_blocks", _lib.lib().ar_plan_limit_blocks(self._handle, int(max_blocks)))
+
     def close(self):
         if self._handle is not None:
             _lib.lib().ar_plan_free(self._handle)
@@ -318,3 +324,8 @@ def ar_plan_start(plan: Plan, stream=None):
 def ar_plan_free(plan: Plan):
     """Release a persistent collective (same as ``plan.close``)."""
     plan.close()
+
+
+def ar_plan_limit_blocks(plan: Plan, max_blocks: int):
+    """Cap the workgroups of a plan's launches (same as ``plan.limit_blocks``)."""
+    plan.limit_blocks(max_blocks)

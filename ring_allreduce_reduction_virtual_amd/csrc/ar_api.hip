@@ -311,6 +311,7 @@ const char* kind_name(Kind kd) {
 struct Step {
     Launch l;
     KernelArgs a;
+    unsigned planned_blocks = 0;   // the grid as planned (persistent plans)
 };
 
 ar_result_t launch_step(const Launch& l, const KernelArgs& a, hipStream_t stream) {
@@ -339,7 +340,7 @@ public:
                          steps_ != nullptr ? " (planned)" : "");
         }
         if (steps_ != nullptr) {
-            steps_->push_back(Step{l, a});
+            steps_->push_back(Step{l, a, l.blocks});
             return AR_SUCCESS;
         }
         return launch_step(l, a, stream_);
@@ -747,6 +748,20 @@ ar_result_t ar_plan_start(ar_plan_t plan, hipStream_t stream) {
 
 int ar_plan_num_launches(ar_plan_t plan) {
     return plan == nullptr ? -1 : static_cast<int>(plan->steps.size());
+}
+
+ar_result_t ar_plan_limit_blocks(ar_plan_t plan, unsigned max_blocks) {
+    g_detail.clear();
+    if (plan == nullptr) return fail(AR_ERR_INVALID_ARGUMENT, "null plan");
+    for (Step& st : plan->steps) {
+        if (max_blocks == 0) {
+            st.l.blocks = st.planned_blocks;
+            continue;
+        }
+        const unsigned rows = st.l.actors > 0 ? st.l.actors : 1;   // the grid's y extent
+        st.l.blocks = std::max(1u, std::min(st.planned_blocks, max_blocks / rows));
+    }
+    return AR_SUCCESS;
 }
 
 ar_result_t ar_plan_free(ar_plan_t plan) {

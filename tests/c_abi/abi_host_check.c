@@ -54,6 +54,8 @@ int main(void) {
     CHECK(ar_allreduce_init(sends, recvs, 0, AR_BFLOAT16, AR_AVG, 4, AR_ALGO_RING, NULL, 0, &plan) == AR_SUCCESS);
     CHECK(plan != NULL && ar_plan_num_launches(plan) == 0);
     CHECK(ar_plan_start(plan, NULL) == AR_SUCCESS);
+    CHECK(ar_plan_limit_blocks(plan, 16) == AR_SUCCESS);
+    CHECK(ar_plan_limit_blocks(NULL, 16) == AR_ERR_INVALID_ARGUMENT);
     CHECK(ar_plan_free(plan) == AR_SUCCESS);
 
     if (failures == 0) printf("ar.h host checks passed\n");

@@ -195,6 +195,7 @@ def test_persistent_plan_host_side(lib):
     assert lib.ar_plan_free(plan) == 0
     assert lib.ar_plan_num_launches(None) == -1
     assert lib.ar_plan_start(None, None) == 1
+    assert lib.ar_plan_limit_blocks(None, 4) == 1
     assert lib.ar_plan_free(None) == 0
     assert lib.ar_allreduce_init(_ptrs(sends), _ptrs(recvs), 0, 0, 0, 4, 0, None, 0, None) == 1
 

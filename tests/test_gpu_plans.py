@@ -116,3 +116,33 @@ def test_graph_capture_replays(algo):
         want, _ = oracle.ring_allreduce(xs)
         for r in range(n):
             assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32"), (rep, r)
+
+
+@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "tree", "tree_steps", "halving_doubling_steps"])
+def test_block_limits_keep_the_bits(algo):
+    """A plan capped at 1, 3, 64 blocks (the kernels stride over their tiles), then
+    uncapped again, gives the oracle's bits every time."""
+    import torch
+
+    from oracle.orders import order_allreduce
+
+    ar = _ar()
+    n, length = 8, 8 * 4096 + 5
+    xs = _draw(n, length, seed=21)
+    sends = [to_dev(x, "f32") for x in xs]
+    recvs = [torch.empty(length, device="cuda:0") for _ in range(n)]
+    if algo in ("fused", "phases", "ring"):
+        want, _ = oracle.ring_allreduce(xs)
+    else:
+        want, _ = order_allreduce({"tree": "tree", "tree_steps": "tree",
+                                   "halving_doubling_steps": "halving_doubling"}[algo], xs)
+    plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
+    for cap in (1, 3, 64, 0):
+        plan.limit_blocks(cap)
+        for r in range(n):
+            recvs[r].fill_(-3.0)
+        plan.start()
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32"), (cap, r)
+    plan.close()
