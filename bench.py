@@ -340,9 +340,10 @@ def run_orders(args):
         rng = np.random.default_rng(9)
         pos = np.unique(np.concatenate([rng.integers(0, count, 1024)] +
                                        [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1]) for c in range(n)]))
-        for algo in ("fused", "tree", "halving_doubling", "tree_steps", "recursive_doubling", "halving_doubling_steps"):
+        for algo in ("fused", "ring", "ring_persistent", "tree", "halving_doubling", "tree_steps",
+                     "recursive_doubling", "halving_doubling_steps"):
             med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 10, 2, stream)
-            ok = (_sampled_parity(xs, recvs, dt, "sum", pos) if algo == "fused"
+            ok = (_sampled_parity(xs, recvs, dt, "sum", pos) if algo in ("fused", "ring", "ring_persistent")
                   else parity(xs, recvs, dt, algo, pos))
             algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
             print(json.dumps({"orders": name, "algo": algo, "dtype": dt, "nranks": n, "count": count,
@@ -359,14 +360,16 @@ def run_orders(args):
         count = 1024
         sends = [torch.randn(count, device=dev) for _ in range(n)]
         recvs = [torch.empty(count, device=dev) for _ in range(n)]
-        for algo in ("fused", "ring", "tree", "tree_steps", "recursive_doubling", "halving_doubling_steps"):
+        for algo in ("fused", "ring", "ring_persistent", "tree", "tree_steps", "recursive_doubling",
+                     "halving_doubling_steps"):
             med, _ = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 200, 5, stream)
             plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
             pmed, _ = median_call_ms(plan.start, 200, 5, stream)
-            gus = graph_ms_per_call(plan.start, 50, stream) * 1e3
+            # the persistent ring refuses graph capture (its barrier needs a cooperative launch)
+            gus = None if algo == "ring_persistent" else round(graph_ms_per_call(plan.start, 50, stream) * 1e3, 2)
             print(json.dumps({"latency": f"{n} x 1024 f32", "algo": algo, "launches": plan.num_launches,
                               "one_shot_median_us": round(med * 1e3, 2), "plan_median_us": round(pmed * 1e3, 2),
-                              "graph_us_per_call": round(gus, 2)}), flush=True)
+                              "graph_us_per_call": gus}), flush=True)
             plan.close()
         del sends, recvs
 
@@ -483,7 +486,8 @@ def run_interference(args):
     plan.close()
 
 
-SWEEP_ALGOS = ("fused", "ring", "tree", "tree_steps", "recursive_doubling", "halving_doubling_steps")
+SWEEP_ALGOS = ("fused", "ring", "ring_persistent", "tree", "tree_steps", "recursive_doubling",
+               "halving_doubling_steps")
 
 
 def run_size_sweep(args):
@@ -494,7 +498,8 @@ def run_size_sweep(args):
     kernels, 2(N-1) launches and 5(N-1)*S bytes for the ring's steps,
     2 log2 N launches and 5(N-1)*S bytes for the staged tree and
     halving/doubling, log2 N launches and 2*N*S*log2 N bytes for recursive
-    doubling.
+    doubling.  The persistent ring is fitted like the ring's steps, its
+    2(N-1) steps separated by grid barriers instead of launches.
     """
     import numpy as np
     import torch
@@ -522,6 +527,7 @@ def run_size_sweep(args):
     fits = {}
     L = (n - 1).bit_length()
     for algo, bytes_factor, launches in (("fused", 2 * n, 1), ("ring", 5 * (n - 1), 2 * (n - 1)),
+                                         ("ring_persistent", 5 * (n - 1), 2 * (n - 1)),
                                          ("tree", 2 * n, 1), ("tree_steps", 5 * (n - 1), 2 * L),
                                          ("recursive_doubling", 2 * n * L, L),
                                          ("halving_doubling_steps", 5 * (n - 1), 2 * L)):

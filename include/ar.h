@@ -132,7 +132,15 @@ typedef enum {
  * AR_ALGO_HALVING_DOUBLING_STEPS: the same schedule stage by stage: log2 N
  *   recursive-halving launches (chunk c finishes on rank c), then log2 N
  *   recursive-doubling launches.  N a power of two.
- * A power-of-two algorithm with another N fails with AR_ERR_UNSUPPORTED. */
+ * A power-of-two algorithm with another N fails with AR_ERR_UNSUPPORTED.
+ *
+ * AR_ALGO_RING_PERSISTENT: the ring's 2(N-1) steps (the same work and the
+ *   same bits as AR_ALGO_RING) in one cooperative launch, with a grid-wide
+ *   barrier where AR_ALGO_RING has a kernel boundary.  AllReduce only; not
+ *   for AR_BFLOAT16_ACC_F32 (AR_ERR_UNSUPPORTED).  It cannot be enqueued
+ *   while the stream is being captured into a graph (AR_ERR_UNSUPPORTED),
+ *   and, since its blocks must all be resident at once, it should not
+ *   overlap other kernels on the device. */
 typedef enum {
     AR_ALGO_FUSED = 0,
     AR_ALGO_RING = 1,
@@ -142,7 +150,8 @@ typedef enum {
     AR_ALGO_TREE_STEPS = 5,
     AR_ALGO_RECURSIVE_DOUBLING = 6,
     AR_ALGO_HALVING_DOUBLING = 7,
-    AR_ALGO_HALVING_DOUBLING_STEPS = 8
+    AR_ALGO_HALVING_DOUBLING_STEPS = 8,
+    AR_ALGO_RING_PERSISTENT = 9
 } ar_algo_t;
 
 /* Rank count from which AR_ALGO_AUTO runs an AllReduce as two fused phases

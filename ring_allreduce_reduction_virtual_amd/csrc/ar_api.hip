@@ -252,7 +252,12 @@ ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, Residue res) {
 }
 
 bool algo_known(ar_algo_t algo) {
-    return algo >= AR_ALGO_FUSED && algo <= AR_ALGO_HALVING_DOUBLING_STEPS;
+    return algo >= AR_ALGO_FUSED && algo <= AR_ALGO_RING_PERSISTENT;
+}
+
+// AllReduce-only algorithms: the tree orders and the persistent ring.
+bool allreduce_only_algo(ar_algo_t algo) {
+    return (algo >= AR_ALGO_TREE && algo <= AR_ALGO_HALVING_DOUBLING_STEPS) || algo == AR_ALGO_RING_PERSISTENT;
 }
 
 // The AllReduce-only algorithms that bracket the reduction as a tree.
@@ -304,6 +309,7 @@ const char* kind_name(Kind kd) {
         case Kind::kFusedTree: return "fused_tree";
         case Kind::kTreeReduceStep: return "tree_reduce_step";
         case Kind::kTreeCopyStep: return "tree_copy_step";
+        case Kind::kRingPersistent: return "ring_persistent";
     }
     return "?";
 }
@@ -316,6 +322,8 @@ struct Step {
 
 ar_result_t launch_step(const Launch& l, const KernelArgs& a, hipStream_t stream) {
     const hipError_t e = arimpl::launch(l, a, stream);
+    if (e == hipErrorStreamCaptureUnsupported && l.kind == Kind::kRingPersistent)
+        return fail(AR_ERR_UNSUPPORTED, "the persistent ring cannot be captured into a graph");
     if (e != hipSuccess) return fail(AR_ERR_HIP, "%s launch: %s", kind_name(l.kind), hipGetErrorString(e));
     return AR_SUCCESS;
 }
@@ -480,6 +488,8 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         ptrs.push_back(d);
     }
     if (algo == AR_ALGO_AUTO) algo = (k.n >= phases_min_ranks()) ? AR_ALGO_PHASES : AR_ALGO_FUSED;
+    if (algo == AR_ALGO_RING_PERSISTENT && k.dtype == AR_BFLOAT16_ACC_F32)
+        return fail(AR_ERR_UNSUPPORTED, "the persistent ring has no form with float32 partials");
     if (power_of_two_algo(algo) && (k.n & (k.n - 1)) != 0)
         return fail(AR_ERR_UNSUPPORTED, "algo %d needs a power-of-two number of ranks, not %d",
                     static_cast<int>(algo), k.n);
@@ -521,6 +531,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     }
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_FUSED) return sink.emit(l, Kind::kFusedAllReduce, a, k);
+    if (algo == AR_ALGO_RING_PERSISTENT) return sink.emit(l, Kind::kRingPersistent, a, k);
     if (k.dtype == AR_BFLOAT16_ACC_F32) {
         // float32 partials travel through the workspace; the last step leaves
         // finished chunk c in chunk c of rank c-1's own buffer, as the ring does
@@ -550,7 +561,8 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
     ar_result_t rc = check_common(k, true);
     if (rc != AR_SUCCESS) return rc;
     if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
-    if (tree_algo(algo)) return fail(AR_ERR_UNSUPPORTED, "algo %d is defined for AllReduce only", static_cast<int>(algo));
+    if (allreduce_only_algo(algo))
+        return fail(AR_ERR_UNSUPPORTED, "algo %d is defined for AllReduce only", static_cast<int>(algo));
     if (algo != AR_ALGO_RING) algo = AR_ALGO_FUSED;
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;
@@ -595,7 +607,8 @@ ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, Sink& sink) {
     ar_result_t rc = check_common(k, false);
     if (rc != AR_SUCCESS) return rc;
     if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
-    if (tree_algo(algo)) return fail(AR_ERR_UNSUPPORTED, "algo %d is defined for AllReduce only", static_cast<int>(algo));
+    if (allreduce_only_algo(algo))
+        return fail(AR_ERR_UNSUPPORTED, "algo %d is defined for AllReduce only", static_cast<int>(algo));
     if (algo != AR_ALGO_RING) algo = AR_ALGO_FUSED;
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;

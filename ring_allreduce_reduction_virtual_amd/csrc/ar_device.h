@@ -654,5 +654,86 @@ struct Partials {
     }
 };
 
+
+// ---------------------------------------------------------------------------
+// the ring's steps over every chunk (tirogla.com "Ring all-reduce", "How it
+// works"): the bodies of the one-launch-per-step kernels, and of the
+// persistent ring that runs all steps in one launch
+// ---------------------------------------------------------------------------
+
+// Reduce-scatter step `step` of the AllReduce ring: chunk c is reduced on
+// rank r = c+step+1 from rank p = c+step (see k_ring_reduce_step).
+template <int DT, int OP, int VEC>
+__device__ __forceinline__ void ring_reduce_tiles(const KernelArgs& a, int step) {
+    static_assert(!acc_f32<DT>(), "float32 partials need the workspace step");
+    using U = Unit<DT, VEC>;
+    using F = Fold<DT, OP, VEC>;
+    using F1 = Fold<DT, OP, 1>;
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    const int r = ring_rank(c, step + 1, n);
+    const int p = ring_rank(c, step, n);
+    const char* local = a.send[r];
+    const char* incoming = (step == 0) ? a.send[p] : a.recv[p];
+    char* out = a.recv[r];
+    const bool last = (step == n - 2);
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            uint32_t v = F1::add(load_elem<ESZ>(local + i * ESZ), load_elem<ESZ>(incoming + i * ESZ));
+            if (last) v = F1::done(v, n);
+            store_elem<ESZ>(out + i * ESZ, v);
+        }
+    }
+    typename U::T x[kUnroll], y[kUnroll];
+    const char* tl = U::tile(local - adj, tv0);
+    const char* ti = U::tile(incoming - adj, tv0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) {
+            x[u] = U::load(tl, U::lane_off(u));
+            y[u] = U::load(ti, U::lane_off(u));
+        }
+    }
+    char* to = U::tile(out - adj, tv0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (!live[u]) continue;
+        typename U::T z = F::add(x[u], y[u]);
+        if (last) z = F::done(z, n);
+        U::store(to, U::lane_off(u), z);
+    }
+    AR_TILE_LOOP_END
+}
+
+// All-gather step `step`: chunk c is copied from rank r-1 to rank
+// r = c+step+shift (see k_ring_copy_step).
+template <int DT, int VEC>
+__device__ __forceinline__ void ring_copy_tiles(const KernelArgs& a, int step, int shift) {
+    using U = Unit<DT, VEC, AR_NT_LOADS_COPY>;
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    const int r = ring_rank(c, step + shift, n);
+    const int p = ring_rank(r, n - 1, n);
+    const char* src = a.recv[p];
+    char* dst = a.recv[r];
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) store_elem<ESZ>(dst + i * ESZ, load_elem<ESZ>(src + i * ESZ));
+    }
+    typename U::T x[kUnroll];
+    const char* ts = U::tile(src - adj, tv0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) x[u] = U::load(ts, U::lane_off(u));
+    }
+    char* td = U::tile(dst - adj, tv0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) U::store(td, U::lane_off(u), x[u]);
+    }
+    AR_TILE_LOOP_END
+}
+
 }  // namespace
 }  // namespace arimpl

@@ -23,6 +23,7 @@ enum class Kind : int {
                            // send table's order, store to every rank
     kTreeReduceStep,       // one reducing stage of a tree-shaped schedule (`mode`, `step`)
     kTreeCopyStep,         // one distributing stage of a tree-shaped schedule (`mode`, `step`)
+    kRingPersistent,       // all 2(N-1) ring steps in one cooperative launch
 };
 
 // Stages of the tree-shaped schedules; at stage `step` the partner distance is d.
@@ -87,5 +88,10 @@ hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream);
 // The kernels of the tree-shaped schedules (ar_tree_kernels.hip); `launch`
 // forwards the kFusedTree, kTreeReduceStep and kTreeCopyStep kinds here.
 hipError_t launch_tree(const Launch& l, const KernelArgs& a, hipStream_t stream);
+
+// The persistent ring (ar_persistent_kernels.hip): a cooperative launch on
+// at most as many blocks as the device holds at once.  Refuses
+// (hipErrorStreamCaptureUnsupported) while `stream` is capturing.
+hipError_t launch_persistent(const Launch& l, const KernelArgs& a, hipStream_t stream);
 
 }  // namespace arimpl

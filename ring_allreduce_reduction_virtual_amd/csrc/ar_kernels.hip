@@ -139,45 +139,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_shards(const KernelArgs a) 
 // partials are kept in the buffer type only.
 template <int DT, int OP, int VEC>
 __global__ __launch_bounds__(kThreads) void k_ring_reduce_step(const KernelArgs a) {
-    static_assert(!acc_f32<DT>(), "float32 partials need the workspace step");
-    using U = Unit<DT, VEC>;
-    using F = Fold<DT, OP, VEC>;
-    using F1 = Fold<DT, OP, 1>;
-    constexpr int ESZ = elem_size<DT>();
-    AR_TILE_LOOP_BEGIN
-    const int r = ring_rank(c, a.step + 1, n);
-    const int p = ring_rank(c, a.step, n);
-    const char* local = a.send[r];
-    const char* incoming = (a.step == 0) ? a.send[p] : a.recv[p];
-    char* out = a.recv[r];
-    const bool last = (a.step == n - 2);
-    if (VEC > 1 && t == 0) {
-        uint64_t i;
-        if (edge_element(sp, threadIdx.x, &i)) {
-            uint32_t v = F1::add(load_elem<ESZ>(local + i * ESZ), load_elem<ESZ>(incoming + i * ESZ));
-            if (last) v = F1::done(v, n);
-            store_elem<ESZ>(out + i * ESZ, v);
-        }
-    }
-    typename U::T x[kUnroll], y[kUnroll];
-    const char* tl = U::tile(local - adj, tv0);
-    const char* ti = U::tile(incoming - adj, tv0);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        if (live[u]) {
-            x[u] = U::load(tl, U::lane_off(u));
-            y[u] = U::load(ti, U::lane_off(u));
-        }
-    }
-    char* to = U::tile(out - adj, tv0);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        if (!live[u]) continue;
-        typename U::T z = F::add(x[u], y[u]);
-        if (last) z = F::done(z, n);
-        U::store(to, U::lane_off(u), z);
-    }
-    AR_TILE_LOOP_END
+    ring_reduce_tiles<DT, OP, VEC>(a, a.step);
 }
 
 // Reduce-scatter ring step s with the partial sums in a workspace.  Chunk c
@@ -254,29 +216,7 @@ __global__ __launch_bounds__(kThreads) void k_ring_reduce_step_ws(const KernelAr
 // receives chunk (r-s-1) mod N, ramchalamkr.github.io "Ring All-Gather").
 template <int DT, int VEC>
 __global__ __launch_bounds__(kThreads) void k_ring_copy_step(const KernelArgs a) {
-    using U = Unit<DT, VEC, AR_NT_LOADS_COPY>;
-    constexpr int ESZ = elem_size<DT>();
-    AR_TILE_LOOP_BEGIN
-    const int r = ring_rank(c, a.step + a.shift, n);
-    const int p = ring_rank(r, n - 1, n);
-    const char* src = a.recv[p];
-    char* dst = a.recv[r];
-    if (VEC > 1 && t == 0) {
-        uint64_t i;
-        if (edge_element(sp, threadIdx.x, &i)) store_elem<ESZ>(dst + i * ESZ, load_elem<ESZ>(src + i * ESZ));
-    }
-    typename U::T x[kUnroll];
-    const char* ts = U::tile(src - adj, tv0);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        if (live[u]) x[u] = U::load(ts, U::lane_off(u));
-    }
-    char* td = U::tile(dst - adj, tv0);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        if (live[u]) U::store(td, U::lane_off(u), x[u]);
-    }
-    AR_TILE_LOOP_END
+    ring_copy_tiles<DT, VEC>(a, a.step, a.shift);
 }
 
 // ---------------------------------------------------------------------------
@@ -359,6 +299,7 @@ hipError_t copy_by_vec(const Launch& l, const KernelArgs& a, hipStream_t s) {
 hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream) {
     if (l.kind == Kind::kFusedTree || l.kind == Kind::kTreeReduceStep || l.kind == Kind::kTreeCopyStep)
         return launch_tree(l, a, stream);
+    if (l.kind == Kind::kRingPersistent) return launch_persistent(l, a, stream);
     const bool copy = l.kind == Kind::kFusedAllGather || l.kind == Kind::kPlaceShards ||
                       l.kind == Kind::kRingCopyStep;
     if (copy) {

@@ -271,3 +271,23 @@ def test_tree_algorithm_host_rules(lib):
     # the staged forms of bf16acc32 need their workspace
     rc = lib.ar_allreduce_ex(_ptrs(sends), _ptrs(recvs), 100, 4, 0, 8, _lib.ALGOS["tree_steps"], None, 0, None)
     assert rc == 1 and b"workspace" in lib.ar_get_last_error_detail()
+
+
+def test_persistent_ring_host_rules(lib):
+    """The persistent ring: AllReduce only, no float32-partials form, no workspace."""
+    import ring_allreduce_reduction_virtual_amd as ar
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    algo = _lib.ALGOS["ring_persistent"]
+    assert ar.ar_workspace_bytes("allreduce", "ring_persistent", 1000, "bf16", 8) == 0
+    S = 1 << 20
+    sends = [BASE + r * S for r in range(8)]
+    recvs = [BASE + (16 + r) * S for r in range(8)]
+    assert lib.ar_reduce_scatter_ex(_ptrs(sends), _ptrs(recvs), 100, 0, 0, 8, algo, None, 0, None) == 2
+    assert lib.ar_all_gather_ex(_ptrs(sends), _ptrs(recvs), 100, 0, 8, algo, None, 0, None) == 2
+    rc = lib.ar_allreduce_ex(_ptrs(sends), _ptrs(recvs), 100, 4, 0, 8, algo, None, 0, None)
+    assert rc == 2 and b"float32 partials" in lib.ar_get_last_error_detail()
+    plan = ctypes.c_void_p()
+    assert lib.ar_allreduce_init(_ptrs(sends), _ptrs(recvs), 0, 0, 0, 8, algo, None, 0, ctypes.byref(plan)) == 0
+    assert lib.ar_plan_num_launches(plan) == 0
+    assert lib.ar_plan_free(plan) == 0

@@ -1,0 +1,170 @@
+"""GPU parity for the persistent ring (all 2(N-1) steps in one cooperative
+launch with grid barriers): the ring's bits for every dtype and operator,
+rank counts up to 128, layouts, persistent plans with workgroup caps, the
+full headline workload (sampled), and the refusal to be captured into a graph.
+
+Every launch here runs alone on the device, as the grid barrier requires."""
+
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.ring import f32_to_bf16_bits, f32_to_f16_bits, same_bits
+
+from gpu_util import from_dev, require_gpu, sample_positions, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TORCH_OF = {"f16": "float16", "bf16": "bfloat16", "f32": "float32", "i32": "int32"}
+
+
+def _ar():
+    require_gpu()
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    return ar
+
+
+def _draw(dtype, n, length, seed):
+    rng = np.random.default_rng(seed)
+    xs = []
+    for _ in range(n):
+        if dtype == "i32":
+            xs.append(rng.integers(-(2**31), 2**31, size=length, dtype=np.int32))
+            continue
+        f = (rng.standard_normal(length) * 2.0 ** rng.integers(-12, 12, size=length)).astype(np.float32)
+        xs.append(f32_to_f16_bits(f) if dtype == "f16" else f32_to_bf16_bits(f) if dtype == "bf16" else f)
+    return xs
+
+
+def _dev(x, dtype):
+    import torch
+
+    if dtype in ("f16", "bf16"):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda:0").view(getattr(torch, TORCH_OF[dtype]))
+    return to_dev(x, dtype)
+
+
+def _host(t, dtype):
+    import torch
+
+    if dtype in ("f16", "bf16"):
+        return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    return from_dev(t, dtype)
+
+
+def _empty(n, length, dtype):
+    import torch
+
+    return [torch.full((length,), 0x5A, dtype=getattr(torch, TORCH_OF[dtype]), device="cuda:0") for _ in range(n)]
+
+
+@pytest.mark.parametrize("dtype,op", [("f32", "sum"), ("f32", "prod"), ("f32", "min"), ("f32", "avg"),
+                                      ("bf16", "sum"), ("bf16", "max"), ("f16", "sum"), ("f16", "avg"),
+                                      ("i32", "sum"), ("i32", "max"), ("i32", "avg")])
+@pytest.mark.parametrize("n,length", [(1, 9), (2, 1001), (3, 7), (5, 1003), (8, 8 * 4096 + 13), (17, 4099),
+                                      (64, 64 * 300 + 5), (128, 128 * 40 + 3)])
+def test_persistent_ring_matches_the_oracle(n, length, dtype, op):
+    import torch
+
+    ar = _ar()
+    xs = _draw(dtype, n, length, seed=zlib.crc32(f"{dtype}{op}{n}".encode()))
+    want, _ = oracle.ring_allreduce(xs, op=op, dtype=dtype)
+    sends = [_dev(x, dtype) for x in xs]
+    recvs = _empty(n, length, dtype)
+    ar.ar_allreduce_ex(sends, recvs, op=op, algo="ring_persistent", dtype=dtype)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(_host(recvs[r], dtype), want[r], dtype), f"rank {r}"
+
+
+@pytest.mark.parametrize("layout", ["in_place", "common_offset", "mixed_offsets"])
+def test_persistent_ring_layouts(layout):
+    import torch
+
+    ar = _ar()
+    n, length = 6, 6 * 2048 + 11
+    xs = _draw("f32", n, length, seed=31)
+    want, _ = oracle.ring_allreduce(xs)
+    if layout == "in_place":
+        sends = [_dev(x, "f32") for x in xs]
+        recvs = sends
+    else:
+        sends, recvs = [], []
+        for r in range(n):
+            off = 1 if layout == "common_offset" else r % 4
+            base = torch.empty(length + 8, device="cuda:0")
+            v = base[off:off + length]
+            v.copy_(_dev(xs[r], "f32"))
+            sends.append(v)
+            off2 = 1 if layout == "common_offset" else (r + 1) % 3
+            recvs.append(torch.empty(length + 8, device="cuda:0")[off2:off2 + length])
+    ar.ar_allreduce_ex(sends, recvs, algo="ring_persistent")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(_host(recvs[r], "f32"), want[r], "f32"), f"rank {r}"
+
+
+def test_persistent_ring_plan_one_launch_and_caps():
+    import torch
+
+    ar = _ar()
+    n, length = 8, 8 * 4096 + 5
+    xs = _draw("bf16", n, length, seed=41)
+    want, _ = oracle.ring_allreduce(xs, dtype="bf16")
+    sends = [_dev(x, "bf16") for x in xs]
+    recvs = _empty(n, length, "bf16")
+    plan = ar.ar_allreduce_init(sends, recvs, algo="ring_persistent")
+    assert plan.num_launches == 1
+    for cap in (0, 1, 5, 64, 0):
+        plan.limit_blocks(cap)
+        for t in recvs:
+            t.zero_()
+        plan.start()
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert same_bits(_host(recvs[r], "bf16"), want[r], "bf16"), (cap, r)
+    plan.close()
+
+
+def test_persistent_ring_refuses_graph_capture():
+    import torch
+
+    ar = _ar()
+    n, length = 4, 4096
+    sends = [torch.randn(length, device="cuda:0") for _ in range(n)]
+    recvs = [torch.empty(length, device="cuda:0") for _ in range(n)]
+    plan = ar.ar_allreduce_init(sends, recvs, algo="ring_persistent")
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(ar.ArError) as err:
+        with torch.cuda.graph(g):
+            plan.start()
+    assert "captured" in str(err.value)
+    torch.cuda.synchronize()
+    plan.start()           # still usable outside a capture
+    torch.cuda.synchronize()
+    want, _ = oracle.ring_allreduce([s.cpu().numpy() for s in sends])
+    assert same_bits(recvs[0].cpu().numpy(), want[0], "f32")
+    plan.close()
+
+
+def test_persistent_ring_headline_full_size_sampled():
+    import torch
+
+    from inputs import WORKLOADS, make_inputs
+    from oracle.ring import chunk_owner
+
+    ar = _ar()
+    w = WORKLOADS["headline"]
+    xs = make_inputs(w)
+    sends = [_dev(x, "f32") for x in xs]
+    recvs = _empty(w.nranks, w.count, "f32")
+    ar.ar_allreduce_ex(sends, recvs, algo="ring_persistent")
+    torch.cuda.synchronize()
+    pos = sample_positions(w.count, w.nranks, seed=12)
+    want = oracle.ring_order_fold_columns(np.stack([x[pos] for x in xs]), chunk_owner(pos, w.nranks, w.count))
+    idx = torch.from_numpy(pos).to("cuda:0")
+    for r in range(w.nranks):
+        assert same_bits(recvs[r][idx].cpu().numpy(), want, "f32"), r
