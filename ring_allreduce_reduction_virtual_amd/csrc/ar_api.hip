@@ -287,6 +287,39 @@ int bit_reverse(int r, int bits) {
     return v;
 }
 
+// When a one-pass AllReduce uses the small-message kernels (all ranks'
+// values of a few positions staged in LDS) instead of the tiled ones: chunks
+// shorter than AR_SMALL_CHUNK_MAX_DEFAULT elements, and chunk * N^2 at most
+// AR_SMALL_WORK_MAX.  A block folds kThreads / N positions, each over N
+// values, so their cost grows as chunk * N^3 where the tiled kernels' grows
+// as chunk * N; measured on MI355X the small kernels win below both bounds
+// (64 ranks x 16 elements: 5.5 against 22 us) and lose above them (128 ranks
+// x 64 elements: 38 against 30 us).  The AR_SMALL_CHUNK_MAX environment
+// variable overrides the chunk bound; 0 turns the small kernels off.
+uint64_t small_chunk_max() {
+    static const uint64_t v = [] {
+        const char* e = std::getenv("AR_SMALL_CHUNK_MAX");
+        if (e != nullptr && e[0] != '\0') return static_cast<uint64_t>(std::strtoull(e, nullptr, 10));
+        return static_cast<uint64_t>(AR_SMALL_CHUNK_MAX_DEFAULT);
+    }();
+    return v;
+}
+
+bool small_message(const Common& k) {
+    const uint64_t n = static_cast<uint64_t>(k.n);
+    const uint64_t chunk = k.count / n;
+    return k.n > 1 && chunk < small_chunk_max() && chunk * n * n <= AR_SMALL_WORK_MAX;
+}
+
+// One block per P = threads / N positions; the kernels stride over the rest.
+void plan_small(KernelArgs& a, Launch& l, const Common& k) {
+    const uint64_t per_block = static_cast<uint64_t>(arimpl::kThreads / k.n);
+    l.vec = false;
+    l.blocks = static_cast<unsigned>(std::max<uint64_t>(1, std::min<uint64_t>((k.count + per_block - 1) / per_block,
+                                                                                0x7fffffffu)));
+    a.tile_first = a.tile_end = a.tiles_per_chunk = 0;
+}
+
 // Rank count from which AR_ALGO_AUTO runs AllReduce as two fused phases.
 int phases_min_ranks() {
     static const int v = [] {
@@ -310,6 +343,8 @@ const char* kind_name(Kind kd) {
         case Kind::kTreeReduceStep: return "tree_reduce_step";
         case Kind::kTreeCopyStep: return "tree_copy_step";
         case Kind::kRingPersistent: return "ring_persistent";
+        case Kind::kSmallAllReduce: return "small_allreduce";
+        case Kind::kSmallTree: return "small_tree";
     }
     return "?";
 }
@@ -436,6 +471,10 @@ ar_result_t tree_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         if (algo == AR_ALGO_HALVING_DOUBLING)
             for (int r = 0; r < k.n; ++r) a.send[r] = static_cast<const char*>(k.send[bit_reverse(r, L)]);
         l.depth = k.n < 16 ? 4 : (k.n < 64 ? 6 : 8);
+        if (small_message(k)) {
+            plan_small(a, l, k);
+            return sink.emit(l, Kind::kSmallTree, a, k);
+        }
         return sink.emit(l, Kind::kFusedTree, a, k);
     }
     if ((rc = use_workspace(a, k, AR_COLL_ALLREDUCE, algo, ws, ws_bytes, nullptr)) != AR_SUCCESS) return rc;
@@ -528,6 +567,10 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         }
         if ((rc = plan(g, lg, k, common_residue(recvs))) != AR_SUCCESS) return rc;
         return sink.emit(lg, Kind::kFusedAllGather, g, k);
+    }
+    if (algo == AR_ALGO_FUSED && small_message(k)) {
+        plan_small(a, l, k);
+        return sink.emit(l, Kind::kSmallAllReduce, a, k);
     }
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_FUSED) return sink.emit(l, Kind::kFusedAllReduce, a, k);

@@ -735,5 +735,42 @@ __device__ __forceinline__ void ring_copy_tiles(const KernelArgs& a, int step, i
     AR_TILE_LOOP_END
 }
 
+// ---------------------------------------------------------------------------
+// small messages: all ranks' values of a few positions staged in LDS
+// ---------------------------------------------------------------------------
+
+// When chunks are only a few elements long, the tiled kernels leave most
+// threads idle and fold each edge element rank by rank, a memory round trip
+// per batch of ranks.  The small-message kernels instead give a block
+// P = kThreads / N consecutive positions [i0, i0 + P): thread t = r*P + j
+// loads rank r's element i0 + j (one load per thread, all in flight at once)
+// into LDS, P threads fold their position from LDS, and every thread stores
+// one result to one rank.  Per-lane rank pointers are read from the kernel
+// argument segment through its address, so the table is never copied.
+__device__ __forceinline__ const KernelArgs* kernarg_table() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return reinterpret_cast<const KernelArgs*>(__builtin_amdgcn_kernarg_segment_ptr());
+#else
+    return nullptr;   // the host pass never runs device code
+#endif
+}
+
+template <int ESZ>
+__device__ __forceinline__ void small_stage(const KernelArgs& a, uint32_t* vals, int P, uint64_t i0) {
+    const int t = static_cast<int>(threadIdx.x);
+    const int r = t / P;
+    const uint64_t i = i0 + static_cast<uint64_t>(t - r * P);
+    if (r < a.nranks && i < a.count) vals[t] = load_elem<ESZ>(kernarg_table()->send[r] + i * ESZ);
+}
+
+template <int ESZ>
+__device__ __forceinline__ void small_store(const KernelArgs& a, const uint32_t* res, int P, uint64_t i0) {
+    const int t = static_cast<int>(threadIdx.x);
+    const int r = t / P;
+    const int j = t - r * P;
+    const uint64_t i = i0 + static_cast<uint64_t>(j);
+    if (r < a.nranks && i < a.count) store_elem<ESZ>(kernarg_table()->recv[r] + i * ESZ, res[j]);
+}
+
 }  // namespace
 }  // namespace arimpl

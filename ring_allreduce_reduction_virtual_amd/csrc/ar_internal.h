@@ -24,6 +24,8 @@ enum class Kind : int {
     kTreeReduceStep,       // one reducing stage of a tree-shaped schedule (`mode`, `step`)
     kTreeCopyStep,         // one distributing stage of a tree-shaped schedule (`mode`, `step`)
     kRingPersistent,       // all 2(N-1) ring steps in one cooperative launch
+    kSmallAllReduce,       // the fused AllReduce of a small message, staged through LDS
+    kSmallTree,            // kFusedTree for a small message, staged through LDS
 };
 
 // Stages of the tree-shaped schedules; at stage `step` the partner distance is d.
@@ -81,6 +83,15 @@ struct Launch {
 #define AR_TILE_UNROLL 2
 #endif
 constexpr int kUnroll = AR_TILE_UNROLL;
+
+// Bounds below which one-pass AllReduces take the small-message kernels:
+// chunk length in elements, and chunk * N^2 (measured crossovers on MI355X).
+#ifndef AR_SMALL_CHUNK_MAX_DEFAULT
+#define AR_SMALL_CHUNK_MAX_DEFAULT 8192
+#endif
+#ifndef AR_SMALL_WORK_MAX
+#define AR_SMALL_WORK_MAX (1ull << 19)
+#endif
 
 // Enqueue one kernel; returns the HIP error of the launch.
 hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream);

@@ -123,6 +123,37 @@ __global__ __launch_bounds__(kThreads) void k_gather_shards(const KernelArgs a) 
     AR_TILE_LOOP_END
 }
 
+// AllReduce of a small message: the ring-order fold of P = kThreads / N
+// positions per block, staged through LDS (see small_stage).  Position i
+// belongs to chunk c = floor(((i+1)*N - 1) / len), whose fold starts at rank
+// c.  In place is safe: a block loads all its positions from every rank
+// before it stores any.
+template <int DT, int OP>
+__global__ __launch_bounds__(kThreads) void k_small_allreduce(const KernelArgs a) {
+    constexpr int ESZ = elem_size<DT>();
+    using F = Fold<DT, OP, 1>;
+    __shared__ uint32_t vals[kThreads];
+    __shared__ uint32_t res[kThreads];
+    const int n = a.nranks;
+    const int P = kThreads / n;
+    const int t = static_cast<int>(threadIdx.x);
+    for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * P; i0 < a.count;
+         i0 += static_cast<uint64_t>(gridDim.x) * P) {
+        small_stage<ESZ>(a, vals, P, i0);
+        __syncthreads();
+        if (t < P && i0 + t < a.count) {
+            const uint64_t i = i0 + t;
+            const int c = static_cast<int>(((i + 1) * static_cast<uint64_t>(n) - 1) / a.count);
+            typename F::A acc = F::first(vals[c * P + t]);
+            for (int k = 1; k < n; ++k) acc = F::add(acc, vals[ring_rank(c, k, n) * P + t]);
+            res[t] = F::done(acc, n);
+        }
+        __syncthreads();
+        small_store<ESZ>(a, res, P, i0);
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // ring steps: one launch per step of the schedule on tirogla.com "Ring
 // all-reduce" ("How it works").  In one launch every chunk c is handled by
@@ -243,6 +274,9 @@ hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
         case Kind::kRingReduceStepWs:
             hipLaunchKernelGGL((k_ring_reduce_step_ws<DT, OP, VEC>), grid, block, 0, s, a);
             break;
+        case Kind::kSmallAllReduce:
+            hipLaunchKernelGGL((k_small_allreduce<DT, OP>), grid, block, 0, s, a);
+            break;
         default:
             return hipErrorInvalidValue;
     }
@@ -297,7 +331,8 @@ hipError_t copy_by_vec(const Launch& l, const KernelArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream) {
-    if (l.kind == Kind::kFusedTree || l.kind == Kind::kTreeReduceStep || l.kind == Kind::kTreeCopyStep)
+    if (l.kind == Kind::kFusedTree || l.kind == Kind::kTreeReduceStep || l.kind == Kind::kTreeCopyStep ||
+        l.kind == Kind::kSmallTree)
         return launch_tree(l, a, stream);
     if (l.kind == Kind::kRingPersistent) return launch_persistent(l, a, stream);
     const bool copy = l.kind == Kind::kFusedAllGather || l.kind == Kind::kPlaceShards ||

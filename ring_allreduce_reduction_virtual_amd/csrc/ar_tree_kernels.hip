@@ -171,6 +171,38 @@ __global__ __launch_bounds__(kThreads) void k_fused_tree(const KernelArgs a) {
     AR_TILE_LOOP_END
 }
 
+// The binomial-tree bracketing for a small message: P = kThreads / N
+// positions per block staged through LDS (see small_stage), each folded by
+// one thread over the leaves in the send table's order.
+template <int DT, int OP, int D>
+__global__ __launch_bounds__(kThreads) void k_small_tree(const KernelArgs a) {
+    constexpr int ESZ = elem_size<DT>();
+    using F = Fold<DT, OP, 1>;
+    __shared__ uint32_t vals[kThreads];
+    __shared__ uint32_t res[kThreads];
+    const int n = a.nranks;
+    const int P = kThreads / n;
+    const int t = static_cast<int>(threadIdx.x);
+    for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * P; i0 < a.count;
+         i0 += static_cast<uint64_t>(gridDim.x) * P) {
+        small_stage<ESZ>(a, vals, P, i0);
+        __syncthreads();
+        if (t < P && i0 + t < a.count) {
+            typename F::A slot[D][kUnroll];
+            const bool live[kUnroll] = {true};
+            for (int k = 0; k < n; ++k) {
+                typename F::A x[kUnroll];
+                x[0] = F::first(vals[k * P + t]);
+                tree_push<DT, OP, 1, D>(slot, static_cast<uint32_t>(k), x, live);
+            }
+            res[t] = F::done(tree_result<DT, OP, 1, D>(slot, static_cast<uint32_t>(n), 0), n);
+        }
+        __syncthreads();
+        small_store<ESZ>(a, res, P, i0);
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // stages: one launch per stage of a schedule
 // ---------------------------------------------------------------------------
@@ -376,6 +408,18 @@ hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
             break;
         case Kind::kTreeReduceStep:
             hipLaunchKernelGGL((k_tree_reduce_step<DT, OP, VEC>), grid, block, 0, s, a);
+            break;
+        case Kind::kSmallTree:
+            if constexpr (VEC == 1) {
+                switch (l.depth) {
+                    case 4: hipLaunchKernelGGL((k_small_tree<DT, OP, 4>), grid, block, 0, s, a); break;
+                    case 6: hipLaunchKernelGGL((k_small_tree<DT, OP, 6>), grid, block, 0, s, a); break;
+                    case 8: hipLaunchKernelGGL((k_small_tree<DT, OP, 8>), grid, block, 0, s, a); break;
+                    default: return hipErrorInvalidValue;
+                }
+            } else {
+                return hipErrorInvalidValue;
+            }
             break;
         default:
             return hipErrorInvalidValue;
