@@ -38,9 +38,12 @@ namespace {
 
 // Ranks whose loads are in flight together; fewer for the widest partial
 // slots, whose registers they share.
+#ifndef AR_TREE_BATCH
+#define AR_TREE_BATCH 8
+#endif
 template <int DT, int D>
 constexpr int tree_batch() {
-    return (D >= 8 && acc_f32<DT>()) ? 4 : kBatch;
+    return (D >= 8 && acc_f32<DT>()) ? 4 : AR_TREE_BATCH;
 }
 
 // Add leaf k (x) to the counter of partials: slot j holds the complete
