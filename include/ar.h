@@ -108,7 +108,9 @@ typedef enum {
  *   kernel, but the read-heavy and the write-heavy halves run apart, which is
  *   faster on MI355X HBM once N is large.
  * AR_ALGO_AUTO: AR_ALGO_FUSED below AR_PHASES_MIN_RANKS ranks, AR_ALGO_PHASES
- *   from there on (AllReduce); the fused kernel for the single phases.
+ *   from there on (AllReduce), except for small messages (chunks of a few
+ *   elements), which always take the fused path; the fused kernel for the
+ *   single phases.
  * These four give the same bits: the ring's association order.
  *
  * The remaining algorithms are AllReduce only (AR_ERR_UNSUPPORTED for

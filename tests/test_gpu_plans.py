@@ -32,9 +32,16 @@ def _draw(n, length, seed, dtype="f32"):
     return xs
 
 
-@pytest.mark.parametrize("algo,launches", [("fused", lambda n: 1), ("phases", lambda n: 2),
-                                           ("ring", lambda n: 2 * (n - 1)), ("auto", lambda n: 1 if n < 24 else 2)])
-@pytest.mark.parametrize("n,length", [(5, 1003), (8, 8 * 4096 + 5), (32, 32 * 257 + 3)])
+def _small(n, length):
+    # the library's rule for the small-message kernels: chunk < 8192 and chunk * N^2 <= 2^19
+    chunk = length // n
+    return chunk < 8192 and chunk * n * n <= (1 << 19)
+
+
+@pytest.mark.parametrize("algo,launches", [("fused", lambda n, m: 1), ("phases", lambda n, m: 2),
+                                           ("ring", lambda n, m: 2 * (n - 1)),
+                                           ("auto", lambda n, m: 1 if n < 24 or _small(n, m) else 2)])
+@pytest.mark.parametrize("n,length", [(5, 1003), (8, 8 * 4096 + 5), (32, 32 * 257 + 3), (32, 32 * 4100 + 3)])
 def test_allreduce_plan_matches_and_follows_inputs(n, length, algo, launches):
     import torch
 
@@ -43,7 +50,7 @@ def test_allreduce_plan_matches_and_follows_inputs(n, length, algo, launches):
     sends = [to_dev(x, "f32") for x in xs]
     recvs = [torch.empty(length, device="cuda:0") for _ in range(n)]
     plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
-    assert plan.num_launches == launches(n)
+    assert plan.num_launches == launches(n, length)
     for rep in range(3):
         want, _ = oracle.ring_allreduce(xs)
         plan.start()
