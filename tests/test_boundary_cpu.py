@@ -291,3 +291,23 @@ def test_persistent_ring_host_rules(lib):
     assert lib.ar_allreduce_init(_ptrs(sends), _ptrs(recvs), 0, 0, 0, 8, algo, None, 0, ctypes.byref(plan)) == 0
     assert lib.ar_plan_num_launches(plan) == 0
     assert lib.ar_plan_free(plan) == 0
+
+
+def test_binding_tables_match_the_header_enums():
+    """Every name the Python binding maps to an enum value carries the value ar.h gives it."""
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    text = open(os.path.join(ROOT, "include", "ar.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    values = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(AR_[A-Z0-9_]+)\s*=\s*(\d+)", text)}
+    dtypes = {"f32": "AR_FLOAT32", "bf16": "AR_BFLOAT16", "i32": "AR_INT32", "f16": "AR_FLOAT16",
+              "bf16acc32": "AR_BFLOAT16_ACC_F32"}
+    assert {k: values[v] for k, v in dtypes.items()} == _lib.DTYPES
+    assert {k: values["AR_" + k.upper()] for k in _lib.OPS} == _lib.OPS
+    assert {k: values["AR_ALGO_" + k.upper()] for k in _lib.ALGOS} == _lib.ALGOS
+    assert {k: values["AR_COLL_" + k.upper()] for k in _lib.COLLS} == _lib.COLLS
+    assert {values[v]: v for v in _lib.RESULT_NAMES.values()} == _lib.RESULT_NAMES
+    # every algorithm the header declares is reachable from Python
+    assert sorted(v for k, v in values.items() if k.startswith("AR_ALGO_")) == sorted(_lib.ALGOS.values())
+    defines = dict(re.findall(r"#define\s+(AR_[A-Z_]+)\s+(\d+)", text))
+    assert int(defines["AR_MAX_RANKS"]) == _lib.MAX_RANKS
