@@ -697,6 +697,17 @@ def main():
                          f"{reps} run(s), {per:.2f} s each, single-threaded numpy; host {cpu_model()}, "
                          f"{len(os.sched_getaffinity(0))} cores available"}
         log(f"[bench] CPU oracle: {per:.2f} s per AllReduce -> algbw {cpu['value']} GB/s (1 core)")
+        # beside it, the oracle's one-thread-per-rank ring (numpy releases the GIL in its array work)
+        from oracle.threaded import ring_allreduce_threaded
+
+        threads = min(n, len(os.sched_getaffinity(0)))
+        if threads == n:
+            t = time.perf_counter()
+            ring_allreduce_threaded(xs, timeout=600.0)
+            tt = time.perf_counter() - t
+            cpu["threaded"] = {"value": round(s_bytes / tt / 1e9, 4), "unit": "GB/s", "threads": n,
+                               "sample": f"the same workload, one thread per rank, 1 run of {tt:.2f} s"}
+            log(f"[bench] CPU oracle, one thread per rank: {tt:.2f} s -> algbw {cpu['threaded']['value']} GB/s")
 
     traffic = measured_traffic(algo_bytes)
     out = {
