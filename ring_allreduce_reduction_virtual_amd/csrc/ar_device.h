@@ -1,8 +1,10 @@
 // Device-side building blocks shared by the kernel sources (ar_kernels.hip:
-// the ring schedules; ar_tree_kernels.hip: the tree-shaped orders): element
-// arithmetic, 16-byte vector access, the fold over ranks, and the chunk
-// geometry with its tile loop.  Everything here is inline device code in an
-// unnamed namespace, so each kernel source gets its own copy.
+// the ring schedules; ar_tree_kernels.hip: the tree-shaped orders;
+// ar_persistent_kernels.hip: the ring in one launch): element arithmetic,
+// 16-byte vector access, the fold over ranks, the chunk geometry with its
+// tile loop, the ring's step bodies, and the LDS staging of small messages.
+// Everything here is inline device code in an unnamed namespace, so each
+// kernel source gets its own copy.
 #pragma once
 
 #include <hip/hip_runtime.h>

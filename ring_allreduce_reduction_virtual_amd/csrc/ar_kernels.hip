@@ -1,7 +1,7 @@
 // HIP kernels (gfx950) for the ring AllReduce over N virtual ranks held in
 // one GPU's HBM.
 //
-// Every kernel walks the buffer chunk by chunk, chunk(c) =
+// The tiled kernels walk the buffer chunk by chunk, chunk(c) =
 // [c*len/N, (c+1)*len/N) (tirogla.com "Ring all-reduce", section "Code"), so
 // the chunk index c, and with it the ring rotation that decides which rank's
 // buffer is read first, is the same for a whole block: the per-rank pointers
@@ -9,12 +9,14 @@
 // ranks is a fixed sequence, never a register-indexed rotation.
 //
 // The work is a pure stream through HBM (one add per element per rank), so
-// there is no LDS staging and no MFMA: each thread moves 16-byte vectors,
-// `kUnroll` of them per rank per tile, issues a batch of up to `kBatch` ranks'
-// loads before it folds them in ring order, and writes results with
-// nontemporal stores.  Chunk edges that are not 16-byte aligned (uneven
-// chunks start anywhere) are done one element at a time by the first tile of
-// the chunk.
+// the tiled kernels use no LDS and no MFMA: each thread moves 16-byte
+// vectors, `kUnroll` of them per rank per tile, issues a batch of up to
+// `kBatch` ranks' loads before it folds them in ring order, and writes
+// results with nontemporal stores.  Chunk edges that are not 16-byte aligned
+// (uneven chunks start anywhere) are done one element at a time by the first
+// tile of the chunk.  Messages whose chunks are only a few elements long take
+// k_small_allreduce instead, which stages every rank's values of a few
+// positions in LDS.
 //
 // Arithmetic follows the ring's association order exactly: element i of
 // chunk c is ((x_c (op) x_{c+1}) (op) x_{c+2}) ... (arjunsriva.com
