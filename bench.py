@@ -486,6 +486,69 @@ def run_interference(args):
     plan.close()
 
 
+def run_ceiling(args):
+    """What HBM allows for the AllReduce's traffic, measured beside it.
+
+    The probes of libarprobe.so stream the same buffers with the fused
+    kernel's access pattern (one block per 8 KiB tile of every buffer,
+    nontemporal hints): reads alone, writes alone, a copy, and an
+    AllReduce-shaped mix (read n buffers, store the integer sum to n buffers)
+    with none of the chunk logic or float work.  Reading N*S and writing N*S
+    over one memory bus cannot take less than the two streams take alone,
+    t_read + t_write; the fused AllReduce is reported against that bound and
+    against the mix probe.
+    """
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import ring_allreduce_reduction_virtual_amd as ar
+    from ring_allreduce_reduction_virtual_amd import build as arbuild
+
+    if not os.path.exists(arbuild.PROBE_PATH):
+        raise SystemExit(f"{arbuild.PROBE_PATH} is not built (python -m ring_allreduce_reduction_virtual_amd.build)")
+    lib = ctypes.CDLL(arbuild.PROBE_PATH)
+    lib.arprobe_stream.restype = ctypes.c_int
+    lib.arprobe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for n, count in ((8, 1 << 26), (16, 1 << 24)):
+        s_bytes = count * 4
+        src = [torch.randn(count, device=dev) for _ in range(n)]
+        dst = [torch.empty(count, device=dev) for _ in range(n)]
+        sp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in src])
+        dp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dst])
+        nvec = s_bytes // 16
+
+        def probe(kind):
+            rc = lib.arprobe_stream(kind, sp, dp, n, nvec, sink.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"arprobe_stream kind {kind}: error {rc}")
+
+        t = {}
+        for name, kind in (("read", 0), ("write", 1), ("copy", 2), ("mix", 3)):
+            t[name] = median_call_ms(lambda: probe(kind), 20, 3, stream)[0] * 1e3
+        t["fused"] = median_call_ms(lambda: ar.ar_allreduce_ex(src, dst, algo="fused"), 20, 3, stream)[0] * 1e3
+        nbytes = n * s_bytes
+        bound = t["read"] + t["write"]
+        print(json.dumps({
+            "ceiling": f"{n} buffers x {s_bytes >> 20} MiB",
+            "read_us": round(t["read"], 1), "read_gbps": round(nbytes / t["read"] / 1e3, 1),
+            "write_us": round(t["write"], 1), "write_gbps": round(nbytes / t["write"] / 1e3, 1),
+            "copy_us": round(t["copy"], 1), "copy_gbps": round(2 * nbytes / t["copy"] / 1e3, 1),
+            "mix_us": round(t["mix"], 1), "mix_gbps": round(2 * nbytes / t["mix"] / 1e3, 1),
+            "fused_allreduce_us": round(t["fused"], 1), "fused_allreduce_gbps": round(2 * nbytes / t["fused"] / 1e3, 1),
+            "bound_read_plus_write_us": round(bound, 1),
+            "bound_frac_of_8tbps": round(2 * nbytes / bound / 1e3 / HBM_PEAK_GBPS, 4),
+            "fused_frac_of_bound": round(bound / t["fused"], 4),
+            "fused_frac_of_mix_probe": round(t["mix"] / t["fused"], 4)}), flush=True)
+        del src, dst
+        torch.cuda.empty_cache()
+
+
 SWEEP_ALGOS = ("fused", "ring", "ring_persistent", "tree", "tree_steps", "recursive_doubling",
                "halving_doubling_steps")
 
@@ -570,6 +633,9 @@ def main():
     ap.add_argument("--interference", action="store_true",
                     help="instead of the headline line: the fused AllReduce overlapping a bf16 GEMM, "
                          "with the AllReduce's workgroups capped at several sizes")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="instead of the headline line: HBM read-only, write-only, copy and AllReduce-shaped "
+                         "probes beside the fused AllReduce (the bound its traffic allows)")
     ap.add_argument("--size-sweep", action="store_true",
                     help="instead of the headline line: AllReduce time against message size (8 ranks, f32), "
                          "fused and ring, with an alpha-beta fit")
@@ -606,6 +672,9 @@ def main():
         return
     if args.interference:
         run_interference(args)
+        return
+    if args.ceiling:
+        run_ceiling(args)
         return
     w = WORKLOADS["headline"]
     n, count = w.nranks, w.count

@@ -54,8 +54,35 @@ def _run(cmd):
     return out
 
 
+PROBE_SOURCE = "ar_probe.hip"
+PROBE_PATH = os.path.join(PKG_DIR, "libarprobe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile libarprobe.so, the HBM ceiling probes bench.py measures (not part of libar.so)."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="ar_probe_") as tmp:
+        tmp_lib = os.path.join(tmp, "libarprobe.so")
+        out = _run([cc, *HIPCC_FLAGS, "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", tmp_lib])
+        if verbose and out.strip():
+            print(out)
+        staged = PROBE_PATH + ".tmp"
+        shutil.copyfile(tmp_lib, staged)
+        os.chmod(staged, 0o755)
+        os.replace(staged, PROBE_PATH)
+    return PROBE_PATH
+
+
 def build_library(verbose: bool = False) -> str:
-    """Compile and link libar.so; return its path."""
+    """Compile and link libar.so (and the probe library beside it); return libar.so's path."""
+    with ThreadPoolExecutor(1) as ex:
+        probe = ex.submit(build_probe, verbose)
+        path = _build_main(verbose)
+        probe.result()
+    return path
+
+
+def _build_main(verbose: bool = False) -> str:
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="ar_build_") as tmp:
         objs = [os.path.join(tmp, s.replace(".hip", ".o")) for s in SOURCES]
