@@ -486,6 +486,41 @@ def run_interference(args):
     plan.close()
 
 
+def load_probe_library():
+    """libarprobe.so (the HBM ceiling probes), or None when it is not built."""
+    import ctypes
+
+    from ring_allreduce_reduction_virtual_amd import build as arbuild
+
+    if not os.path.exists(arbuild.PROBE_PATH):
+        return None
+    lib = ctypes.CDLL(arbuild.PROBE_PATH)
+    lib.arprobe_stream.restype = ctypes.c_int
+    lib.arprobe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def probe_times_us(lib, src, dst, stream, kinds=(("read", 0), ("write", 1), ("copy", 2), ("mix", 3)), steps=20):
+    """Median µs of each probe over the tensors src -> dst (n buffers of equal size)."""
+    import ctypes
+
+    import torch
+
+    n = len(src)
+    sink = torch.zeros(4, dtype=torch.int32, device=src[0].device)
+    sp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in src])
+    dp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dst])
+    nvec = src[0].numel() * src[0].element_size() // 16
+
+    def probe(kind):
+        rc = lib.arprobe_stream(kind, sp, dp, n, nvec, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"arprobe_stream kind {kind}: error {rc}")
+
+    return {name: median_call_ms(lambda: probe(kind), steps, 3, stream)[0] * 1e3 for name, kind in kinds}
+
+
 def run_ceiling(args):
     """What HBM allows for the AllReduce's traffic, measured beside it.
 
@@ -498,39 +533,20 @@ def run_ceiling(args):
     t_read + t_write; the fused AllReduce is reported against that bound and
     against the mix probe.
     """
-    import ctypes
-
-    import numpy as np
     import torch
 
     import ring_allreduce_reduction_virtual_amd as ar
-    from ring_allreduce_reduction_virtual_amd import build as arbuild
 
-    if not os.path.exists(arbuild.PROBE_PATH):
-        raise SystemExit(f"{arbuild.PROBE_PATH} is not built (python -m ring_allreduce_reduction_virtual_amd.build)")
-    lib = ctypes.CDLL(arbuild.PROBE_PATH)
-    lib.arprobe_stream.restype = ctypes.c_int
-    lib.arprobe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
-                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib = load_probe_library()
+    if lib is None:
+        raise SystemExit("libarprobe.so is not built (python -m ring_allreduce_reduction_virtual_amd.build)")
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    sink = torch.zeros(4, dtype=torch.int32, device=dev)
     for n, count in ((8, 1 << 26), (16, 1 << 24)):
         s_bytes = count * 4
         src = [torch.randn(count, device=dev) for _ in range(n)]
         dst = [torch.empty(count, device=dev) for _ in range(n)]
-        sp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in src])
-        dp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dst])
-        nvec = s_bytes // 16
-
-        def probe(kind):
-            rc = lib.arprobe_stream(kind, sp, dp, n, nvec, sink.data_ptr(), stream.cuda_stream)
-            if rc != 0:
-                raise RuntimeError(f"arprobe_stream kind {kind}: error {rc}")
-
-        t = {}
-        for name, kind in (("read", 0), ("write", 1), ("copy", 2), ("mix", 3)):
-            t[name] = median_call_ms(lambda: probe(kind), 20, 3, stream)[0] * 1e3
+        t = probe_times_us(lib, src, dst, stream)
         t["fused"] = median_call_ms(lambda: ar.ar_allreduce_ex(src, dst, algo="fused"), 20, 3, stream)[0] * 1e3
         nbytes = n * s_bytes
         bound = t["read"] + t["write"]
@@ -739,6 +755,17 @@ def main():
         copy_ms = time_calls(lambda: dst.copy_(src), 20, 2, stream)
         extra["torch_copy_2x2GiB_hbm_gbps"] = round(2 * src.numel() * 4 / (copy_ms / 1e3) / 1e9, 1)
         del src, dst
+        # what HBM gives this traffic: the probes of libarprobe.so on the same buffers (bench.py --ceiling)
+        plib = load_probe_library()
+        if plib is not None:
+            pt = probe_times_us(plib, sends, recvs, stream, kinds=(("read", 0), ("write", 1), ("mix", 3)))
+            extra["hbm_ceiling"] = {
+                "read_alone_us": round(pt["read"], 1), "write_alone_us": round(pt["write"], 1),
+                "read_plus_write_us": round(pt["read"] + pt["write"], 1),
+                "read_plus_write_frac_of_8tbps": round(algo_bytes / (pt["read"] + pt["write"]) / 1e3 / HBM_PEAK_GBPS, 4),
+                "mix_probe_us": round(pt["mix"], 1),
+                "fused_frac_of_read_plus_write": round((pt["read"] + pt["write"]) / (ms * 1e3), 4),
+                "fused_speed_vs_mix_probe": round(pt["mix"] / (ms * 1e3), 4)}
         log(f"[bench] ring mode {ring_ms:.3f} ms; reduce-scatter {rs_ms:.3f} ms; all-gather {ag_ms:.3f} ms; "
             f"torch copy {extra['torch_copy_2x2GiB_hbm_gbps']} GB/s")
         # restore the inputs overwritten by the all-gather above
