@@ -126,6 +126,33 @@ def _ring_pins(R):
         return (out[0].tolist() == [-(2**31), -7, 5]) and avg[0].tolist() == [-(2**31) // 3 + 1, -2, 1]
     pin("int32 wrap and avg", int_closed_forms)
 
+    # bf16 with float32 partials keeps what per-step rounding loses: 256 + 1 + 1 is 258 exactly,
+    # while per-step bf16 rounds 257 to 256 (ties to even) twice
+    def acc32():
+        xs = [R.f32_to_bf16_bits(np.array([v], np.float32)) for v in (256.0, 1.0, 1.0)]
+        per_step, _ = R.ring_allreduce(xs, "sum", "bf16")
+        acc, _ = R.ring_allreduce(xs, "sum", "bf16acc32")
+        return int(per_step[0][0]) == 0x4380 and int(acc[0][0]) == 0x4381
+    pin("bf16 with float32 partials", acc32)
+
+    # binary16: 1 + 2^-11 is a tie between 1 and 1 + 2^-10 and rounds to even (1), twice
+    def f16():
+        import torch
+        xs = [np.array([v], np.float16).view(np.uint16) for v in (1.0, 2.0 ** -11, 2.0 ** -11)]
+        out, _ = R.ring_allreduce(xs, "sum", "f16")
+        rng = np.random.default_rng(4)
+        vals = (rng.standard_normal(5000) * 2.0 ** rng.integers(-20, 16, 5000)).astype(np.float32)
+        want = torch.from_numpy(vals).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+        return int(out[0][0]) == 0x3C00 and np.array_equal(R.f32_to_f16_bits(vals), want)
+    pin("binary16", f16)
+
+    # float avg: the sum divided by N once, correctly rounded (7/3 in float32)
+    def avg_f32():
+        xs = [np.array([v], np.float32) for v in (1.0, 2.0, 4.0)]
+        out, _ = R.ring_allreduce(xs, "avg", "f32")
+        return float(out[0][0]) == float(np.float32(7.0) / np.float32(3.0))
+    pin("float avg", avg_f32)
+
     return out
 
 
@@ -144,6 +171,13 @@ RING_MUTANTS = [
     ("int sum saturates", ("return np.add(a.view(np.uint32), b.view(np.uint32), dtype=np.uint32).view(np.int32)",
                            "return np.clip(a.astype(np.int64) + b, -2**31, 2**31 - 1).astype(np.int32)")),
     ("shard taken from rank c", ("shards.append(buf[(c - 1) % n][a:b].copy())", "shards.append(buf[c][a:b].copy())")),
+    ("bf16acc32 rounds every step", ('"i32": "i32", "f16": "f16", "bf16acc32": "f32"}', '"i32": "i32", "f16": "f16", "bf16acc32": "bf16"}')),
+    ("f16 widened as bf16", ("return f32_to_f16_bits(_f32_op(op, f16_bits_to_f32(a), f16_bits_to_f32(b)))",
+                             "return f32_to_f16_bits(_f32_op(op, bf16_bits_to_f32(a), bf16_bits_to_f32(b)))")),
+    ("float avg multiplies", ("v = np.divide(np.asarray(v, np.float32), np.float32(n), dtype=np.float32)",
+                              "v = np.multiply(np.asarray(v, np.float32), np.float32(n), dtype=np.float32)")),
+    ("avg divides by N - 1", ("def finish(op: str, dtype: str, v: np.ndarray, n: int) -> np.ndarray:",
+                              "def finish(op: str, dtype: str, v: np.ndarray, n: int) -> np.ndarray:\n    n = max(1, n - 1)")),
     ("fold starts one rank late", ("        acc = to_work(xs[c][a:b], dtype)\n        for k in range(1, n):\n            acc = reduce_op(op, wd, acc, to_work(xs[(c + k) % n][a:b], dtype))",
                                    "        acc = to_work(xs[(c + 1) % n][a:b], dtype)\n        for k in range(2, n + 1):\n            acc = reduce_op(op, wd, acc, to_work(xs[(c + k) % n][a:b], dtype))")),
 ]
