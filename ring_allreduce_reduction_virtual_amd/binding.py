@@ -50,6 +50,7 @@ def _marshal(sendbufs, recvbufs, dtype=None):
     if not isinstance(t0, torch.Tensor) or not t0.is_cuda:
         raise ValueError("buffers must be CUDA tensors")
     dev, dt = t0.device, t0.dtype
+    index = t0.get_device()
     if dt not in _TORCH_DTYPES:
         raise TypeError(f"unsupported dtype {dt}; use float32, bfloat16, float16 or int32")
     name = _TORCH_DTYPES[dt]
@@ -59,18 +60,45 @@ def _marshal(sendbufs, recvbufs, dtype=None):
         name = dtype
     sp = (ctypes.c_void_p * n)()
     rp = (ctypes.c_void_p * n)()
+    tensor = torch.Tensor
     for i in range(n):
         s, r = sendbufs[i], recvbufs[i]
-        for t in (s, r):
-            if not isinstance(t, torch.Tensor) or t.device != dev:
-                raise ValueError("all buffers must be tensors on the same GPU")
-            if t.dtype != dt:
-                raise TypeError("all buffers must have the same dtype")
-            if not t.is_contiguous():
-                raise ValueError("buffers must be contiguous")
+        # one cheap test per tensor; the slow path below says what is wrong
+        if not (type(s) is tensor and type(r) is tensor and s.dtype is dt and r.dtype is dt
+                and s.get_device() == index and r.get_device() == index
+                and s.is_contiguous() and r.is_contiguous()):
+            for t in (s, r):
+                if not isinstance(t, torch.Tensor) or t.device != dev:
+                    raise ValueError("all buffers must be tensors on the same GPU")
+                if t.dtype != dt:
+                    raise TypeError("all buffers must have the same dtype")
+                if not t.is_contiguous():
+                    raise ValueError("buffers must be contiguous")
         sp[i] = s.data_ptr()
         rp[i] = r.data_ptr()
     return dev, name, sp, rp
+
+
+class _on_device:
+    """Make ``dev`` the current device for a call, switching only when it is not already."""
+
+    __slots__ = ("index", "prev")
+
+    def __init__(self, dev):
+        self.index = dev.index if dev.index is not None else torch.cuda.current_device()
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if cur != self.index:
+            self.prev = cur
+            torch.cuda.set_device(self.index)
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+        return False
 
 
 def _ws(workspace):
@@ -105,8 +133,12 @@ def _check_counts(coll, sendbufs, recvbufs):
     n = len(sendbufs)
     if coll == "allreduce":
         count = sendbufs[0].numel()
-        if any(t.numel() != count for t in list(sendbufs) + list(recvbufs)):
-            raise ValueError("every AllReduce buffer must hold count elements")
+        for t in sendbufs:
+            if t.numel() != count:
+                raise ValueError("every AllReduce buffer must hold count elements")
+        for t in recvbufs:
+            if t.numel() != count:
+                raise ValueError("every AllReduce buffer must hold count elements")
         return count
     full, shards, what = (sendbufs, recvbufs, "recvbufs") if coll == "reduce_scatter" else \
         (recvbufs, sendbufs, "sendbufs")
@@ -140,7 +172,7 @@ def ar_allreduce(sendbufs, recvbufs=None, op: str = "sum", stream=None, dtype=No
     recvbufs = sendbufs if recvbufs is None else recvbufs
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("allreduce", sendbufs, recvbufs)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         rc = _lib.lib().ar_allreduce(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
                                      _stream_handle(stream))
     _lib.check("ar_allreduce", rc)
@@ -158,7 +190,7 @@ def ar_allreduce_ex(sendbufs, recvbufs=None, op: str = "sum", algo: str = "fused
     recvbufs = sendbufs if recvbufs is None else recvbufs
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("allreduce", sendbufs, recvbufs)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         workspace = _workspace("allreduce", algo, count, dtype, len(sendbufs), workspace, dev, stream)
         wp, wb = _ws(workspace)
         rc = _lib.lib().ar_allreduce_ex(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
@@ -171,7 +203,7 @@ def ar_reduce_scatter(sendbufs, recvbufs, op: str = "sum", stream=None, dtype=No
     """Reduce-scatter with the fused kernel: recvbufs[r] receives chunk r of the reduction."""
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("reduce_scatter", sendbufs, recvbufs)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         rc = _lib.lib().ar_reduce_scatter(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
                                           _stream_handle(stream))
     _lib.check("ar_reduce_scatter", rc)
@@ -188,7 +220,7 @@ def ar_reduce_scatter_ex(sendbufs, recvbufs, op: str = "sum", algo: str = "fused
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("reduce_scatter", sendbufs, recvbufs)
     n = len(sendbufs)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         workspace = _workspace("reduce_scatter", algo, count, dtype, n, workspace, dev, stream)
         wp, wb = _ws(workspace)
         rc = _lib.lib().ar_reduce_scatter_ex(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], n,
@@ -201,7 +233,7 @@ def ar_all_gather(sendbufs, recvbufs, stream=None):
     """All-gather with the fused kernel: every recvbufs[r] receives all shards in rank order."""
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
     count = _check_counts("all_gather", sendbufs, recvbufs)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         rc = _lib.lib().ar_all_gather(sp, rp, count, _lib.DTYPES[dtype], len(sendbufs), _stream_handle(stream))
     _lib.check("ar_all_gather", rc)
     return recvbufs
@@ -212,7 +244,7 @@ def ar_all_gather_ex(sendbufs, recvbufs, algo: str = "fused", workspace=None, st
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
     count = _check_counts("all_gather", sendbufs, recvbufs)
     wp, wb = _ws(workspace)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         rc = _lib.lib().ar_all_gather_ex(sp, rp, count, _lib.DTYPES[dtype], len(sendbufs), _lib.ALGOS[algo],
                                          wp, wb, _stream_handle(stream))
     _lib.check("ar_all_gather_ex", rc)
@@ -278,7 +310,7 @@ def ar_allreduce_init(sendbufs, recvbufs=None, op: str = "sum", algo: str = "aut
     recvbufs = sendbufs if recvbufs is None else recvbufs
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("allreduce", sendbufs, recvbufs)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         workspace = _workspace("allreduce", algo, count, dtype, len(sendbufs), workspace, dev, None)
     wp, wb = _ws(workspace)
     L = _lib.lib()
@@ -294,7 +326,7 @@ def ar_reduce_scatter_init(sendbufs, recvbufs, op: str = "sum", algo: str = "fus
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("reduce_scatter", sendbufs, recvbufs)
     n = len(sendbufs)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         workspace = _workspace("reduce_scatter", algo, count, dtype, n, workspace, dev, None)
     wp, wb = _ws(workspace)
     L = _lib.lib()
