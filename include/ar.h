@@ -107,10 +107,9 @@ typedef enum {
  *   is copied to every other rank.  (2N+1)*S bytes, S more than the fused
  *   kernel, but the read-heavy and the write-heavy halves run apart, which is
  *   faster on MI355X HBM once N is large.
- * AR_ALGO_AUTO: AR_ALGO_FUSED below AR_PHASES_MIN_RANKS ranks, AR_ALGO_PHASES
- *   from there on (AllReduce), except for small messages (chunks of a few
- *   elements), which always take the fused path; the fused kernel for the
- *   single phases.
+ * AR_ALGO_AUTO: AR_ALGO_PHASES from AR_PHASES_MIN_RANKS ranks when every
+ *   rank holds at least AR_PHASES_MIN_BYTES bytes, AR_ALGO_FUSED otherwise
+ *   (AllReduce); the fused kernel for the single phases.
  * These four give the same bits: the ring's association order.
  *
  * The remaining algorithms are AllReduce only (AR_ERR_UNSUPPORTED for
@@ -160,6 +159,9 @@ typedef enum {
  * (measured crossover on MI355X; the AR_PHASES_MIN_RANKS environment variable
  * overrides it). */
 #define AR_PHASES_MIN_RANKS 24
+/* Bytes per rank from which AR_ALGO_AUTO may take the two phases (measured
+ * on MI355X: below it the single fused kernel is faster at every rank count). */
+#define AR_PHASES_MIN_BYTES (4u << 20)
 
 typedef enum {
     AR_COLL_ALLREDUCE = 0,

@@ -526,10 +526,13 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         ptrs.push_back(s);
         ptrs.push_back(d);
     }
-    // AUTO: two fused phases from phases_min_ranks() ranks, except for small
-    // messages, where the single small-message kernel beats both
+    // AUTO: two fused phases from phases_min_ranks() ranks when every rank
+    // holds at least AR_PHASES_MIN_BYTES; below that the one fused kernel wins
+    // (and the small-message kernel for the smallest messages)
     if (algo == AR_ALGO_AUTO)
-        algo = (k.n >= phases_min_ranks() && !small_message(k)) ? AR_ALGO_PHASES : AR_ALGO_FUSED;
+        algo = (k.n >= phases_min_ranks() && k.count * k.esz >= AR_PHASES_MIN_BYTES && !small_message(k))
+                   ? AR_ALGO_PHASES
+                   : AR_ALGO_FUSED;
     if (algo == AR_ALGO_RING_PERSISTENT && k.dtype == AR_BFLOAT16_ACC_F32)
         return fail(AR_ERR_UNSUPPORTED, "the persistent ring has no form with float32 partials");
     if (power_of_two_algo(algo) && (k.n & (k.n - 1)) != 0)

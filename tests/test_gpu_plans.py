@@ -40,8 +40,9 @@ def _small(n, length):
 
 @pytest.mark.parametrize("algo,launches", [("fused", lambda n, m: 1), ("phases", lambda n, m: 2),
                                            ("ring", lambda n, m: 2 * (n - 1)),
-                                           ("auto", lambda n, m: 1 if n < 24 or _small(n, m) else 2)])
-@pytest.mark.parametrize("n,length", [(5, 1003), (8, 8 * 4096 + 5), (32, 32 * 257 + 3), (32, 32 * 4100 + 3)])
+                                           ("auto", lambda n, m: 1 if n < 24 or _small(n, m) or m * 4 < (4 << 20) else 2)])
+@pytest.mark.parametrize("n,length", [(5, 1003), (8, 8 * 4096 + 5), (32, 32 * 257 + 3), (32, 32 * 4100 + 3),
+                                      (24, (1 << 20) + 3)])
 def test_allreduce_plan_matches_and_follows_inputs(n, length, algo, launches):
     import torch
 
