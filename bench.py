@@ -620,6 +620,40 @@ def run_size_sweep(args):
     print(json.dumps({"sweep_fit": fits, "model": "t = launches*alpha + hbm_bytes/B"}), flush=True)
 
 
+def run_cache_sweep(args):
+    """The fused AllReduce around the bound of its cache-allocating loads.
+
+    Inputs of N*S = 32 to 512 MiB of float32 at 8, 16 and 64 ranks, per call
+    in a replayed HIP graph of 20 plan starts (the same buffers every call, as
+    a benchmark loop or a training step's repeated bucket sees them).  The
+    library reads inputs of at most 256 MiB with cache-allocating loads and
+    larger ones with nontemporal loads; run under AR_CACHED_LOADS_MAX=0 (never
+    cached) or a huge value (always cached) for the other forms.
+    """
+    import torch
+
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    form = os.environ.get("AR_CACHED_LOADS_MAX", "default (256 MiB)")
+    for n in (8, 16, 64):
+        for mib in (32, 128, 192, 256, 320, 384, 512):
+            count = (mib << 20) // (4 * n)
+            sends = [torch.randn(count, device=dev) for _ in range(n)]
+            recvs = [torch.empty(count, device=dev) for _ in range(n)]
+            plan = ar.ar_allreduce_init(sends, recvs, algo="fused")
+            per_call = [graph_ms_per_call(plan.start, 20, stream, replays=3) * 1e3 for _ in range(3)]
+            us = sorted(per_call)[1]
+            print(json.dumps({"cache_sweep": "allreduce fused f32 sum", "AR_CACHED_LOADS_MAX": form, "nranks": n,
+                              "inputs_mib": mib, "count": count, "graph_us_per_call": round(us, 2),
+                              "hbm_frac": round(2 * n * count * 4 / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}),
+                  flush=True)
+            plan.close()
+            del sends, recvs
+            torch.cuda.empty_cache()
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -657,6 +691,9 @@ def main():
     ap.add_argument("--size-sweep", action="store_true",
                     help="instead of the headline line: AllReduce time against message size (8 ranks, f32), "
                          "fused and ring, with an alpha-beta fit")
+    ap.add_argument("--cache-sweep", action="store_true",
+                    help="instead of the headline line: the fused AllReduce at 32-512 MiB of inputs and 8, 16, "
+                         "64 ranks, per call in a replayed graph (around the bound of its cache-allocating loads)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -693,6 +730,9 @@ def main():
         return
     if args.ceiling:
         run_ceiling(args)
+        return
+    if args.cache_sweep:
+        run_cache_sweep(args)
         return
     w = WORKLOADS["headline"]
     n, count = w.nranks, w.count

@@ -96,7 +96,10 @@ typedef enum {
 
 /* AR_ALGO_FUSED: one kernel reads element i from all N ranks, reduces it in
  *   ring order and writes every output (N*S bytes read, N*S written for
- *   AllReduce: the minimum).
+ *   AllReduce: the minimum).  Inputs of at most 256 MiB in total (N*S) are
+ *   read with cache-allocating loads, so that a repeated call finds them in
+ *   the device's 256 MB last-level cache; larger ones stream past it.  The
+ *   choice affects speed only, never the result.
  * AR_ALGO_RING: the ring's steps one by one, one kernel launch per step:
  *   N-1 reduce-scatter steps then N-1 all-gather steps, each rank adding the
  *   chunk received from rank r-1 (tirogla.com "Ring all-reduce", "How it

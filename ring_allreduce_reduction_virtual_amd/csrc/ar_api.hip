@@ -320,6 +320,17 @@ void plan_small(KernelArgs& a, Launch& l, const Common& k) {
     a.tile_first = a.tile_end = a.tiles_per_chunk = 0;
 }
 
+// Total input bytes (N * S) up to which the fused AllReduce reads with
+// cache-allocating loads; AR_CACHED_LOADS_MAX overrides it, 0 turns it off.
+uint64_t cached_loads_max() {
+    static const uint64_t v = [] {
+        const char* e = std::getenv("AR_CACHED_LOADS_MAX");
+        if (e != nullptr && e[0] != '\0') return static_cast<uint64_t>(std::strtoull(e, nullptr, 10));
+        return static_cast<uint64_t>(AR_CACHED_LOADS_MAX_BYTES);
+    }();
+    return v;
+}
+
 // Rank count from which AR_ALGO_AUTO runs AllReduce as two fused phases.
 int phases_min_ranks() {
     static const int v = [] {
@@ -376,11 +387,11 @@ public:
         if (debug_enabled()) {
             std::fprintf(stderr,
                          "[ar] %s dtype=%s op=%d n=%d count=%llu step=%d shift=%d mode=%d last=%d vec=%d ofs=%d "
-                         "align=2^%d tiles=[%u,%u) tiles/chunk=%u blocks=%u actors=%u%s\n",
+                         "align=2^%d tiles=[%u,%u) tiles/chunk=%u blocks=%u actors=%u cached=%d%s\n",
                          kind_name(kind), dtype_name(k.dtype), static_cast<int>(k.op), k.n,
                          static_cast<unsigned long long>(k.count), a.step, a.shift, a.mode, a.last, l.vec ? 1 : 0, a.ofs,
                          a.align_shift, a.tile_first, a.tile_end, a.tiles_per_chunk, l.blocks, l.actors,
-                         steps_ != nullptr ? " (planned)" : "");
+                         l.cached ? 1 : 0, steps_ != nullptr ? " (planned)" : "");
         }
         if (steps_ != nullptr) {
             steps_->push_back(Step{l, a, l.blocks});
@@ -579,7 +590,10 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         return sink.emit(l, Kind::kSmallAllReduce, a, k);
     }
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
-    if (algo == AR_ALGO_FUSED) return sink.emit(l, Kind::kFusedAllReduce, a, k);
+    if (algo == AR_ALGO_FUSED) {
+        l.cached = l.vec && static_cast<uint64_t>(k.n) * k.count * k.esz <= cached_loads_max();
+        return sink.emit(l, Kind::kFusedAllReduce, a, k);
+    }
     if (algo == AR_ALGO_RING_PERSISTENT) return sink.emit(l, Kind::kRingPersistent, a, k);
     if (k.dtype == AR_BFLOAT16_ACC_F32) {
         // float32 partials travel through the workspace; the last step leaves

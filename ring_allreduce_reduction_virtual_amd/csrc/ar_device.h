@@ -450,12 +450,13 @@ __device__ __forceinline__ int ring_rank(int c, int k, int n) {
 // ---------------------------------------------------------------------------
 
 // acc[u] = ((x_c (op) x_{c+1}) (op) ...) at the thread's units of the tile
-// that starts at unit tv0, for live u.
-template <int DT, int OP, int VEC>
+// that starts at unit tv0, for live u.  NT_LOAD picks nontemporal or
+// cache-allocating loads.
+template <int DT, int OP, int VEC, bool NT_LOAD = AR_NT_LOADS>
 __device__ __forceinline__ void fold_units(const KernelArgs& a, int c, int64_t adj, uint64_t tv0,
                                            const bool (&live)[kUnroll],
                                            typename Fold<DT, OP, VEC>::A (&acc)[kUnroll]) {
-    using U = Unit<DT, VEC>;
+    using U = Unit<DT, VEC, NT_LOAD>;
     using F = Fold<DT, OP, VEC>;
     const int n = a.nranks;
     {

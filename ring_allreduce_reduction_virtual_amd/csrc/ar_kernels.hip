@@ -35,8 +35,10 @@ namespace {
 
 // AllReduce: every rank's output gets the ring-order fold.  Reads N*S,
 // writes N*S bytes.  In place (send[r] == recv[r]) is safe: each position is
-// read by the thread that later writes it, and by no other.
-template <int DT, int OP, int VEC>
+// read by the thread that later writes it, and by no other.  NT_LOAD: the
+// body's loads are nontemporal (inputs larger than the Infinity Cache) or
+// cache-allocating (inputs that fit in it).
+template <int DT, int OP, int VEC, bool NT_LOAD>
 __global__ __launch_bounds__(kThreads) void k_fused_allreduce(const KernelArgs a) {
     using U = Unit<DT, VEC>;
     AR_TILE_LOOP_BEGIN
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_allreduce(const KernelArgs a
         }
     }
     typename Fold<DT, OP, VEC>::A acc[kUnroll];
-    fold_units<DT, OP, VEC>(a, c, adj, tv0, live, acc);
+    fold_units<DT, OP, VEC, NT_LOAD>(a, c, adj, tv0, live, acc);
     typename U::T res[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -261,7 +263,13 @@ hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
     const dim3 grid(l.blocks), block(kThreads);
     switch (l.kind) {
         case Kind::kFusedAllReduce:
-            hipLaunchKernelGGL((k_fused_allreduce<DT, OP, VEC>), grid, block, 0, s, a);
+            if constexpr (VEC > 1) {
+                if (l.cached) {
+                    hipLaunchKernelGGL((k_fused_allreduce<DT, OP, VEC, false>), grid, block, 0, s, a);
+                    break;
+                }
+            }
+            hipLaunchKernelGGL((k_fused_allreduce<DT, OP, VEC, static_cast<bool>(AR_NT_LOADS)>), grid, block, 0, s, a);
             break;
         case Kind::kFusedReduceScatter:
             hipLaunchKernelGGL((k_fused_reduce_scatter<DT, OP, VEC>), grid, block, 0, s, a);

@@ -160,6 +160,31 @@ def test_headline_8_ranks_2p26_float32_full_size():
         assert torch.equal(bits(t), bits(fused[0]))
 
 
+# The fused AllReduce reads inputs of up to 256 MiB in total (N * S) with
+# cache-allocating loads and larger ones with nontemporal loads.
+CACHED_LOADS_MAX_BYTES = 256 << 20
+
+
+@pytest.mark.parametrize("count", [CACHED_LOADS_MAX_BYTES // 32, CACHED_LOADS_MAX_BYTES // 32 + 4])
+def test_fused_loads_either_side_of_the_cache_bound(count):
+    """8 ranks of float32 at exactly 256 MiB of inputs and just above: both load
+    forms give the oracle's bits at the sampled positions, call after call."""
+    import torch
+
+    ar = _ar()
+    xs = make_inputs(WORKLOADS["c2"], count=count)
+    sends, recvs = _run_allreduce(xs, "f32", "sum", "fused")
+    _sampled_check(xs, recvs, "f32", "sum", seed=105)
+    first = bits(recvs[0]).clone()
+    for t in recvs:
+        t.fill_(-1.0)
+    for _ in range(2):                     # again, with the inputs now possibly cached
+        ar.ar_allreduce_ex(sends, recvs, algo="fused")
+    torch.cuda.synchronize()
+    for r in range(len(recvs)):
+        assert torch.equal(bits(recvs[r]), first), f"rank {r}"
+
+
 def test_c3_bf16_full_size():
     w = WORKLOADS["c3"]
     xs = make_inputs(w)
