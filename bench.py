@@ -302,6 +302,10 @@ def run_variants(args):
         torch.cuda.empty_cache()
 
 
+# the algorithms that fold in the ring's association order (the ring's bits)
+RING_ORDER_ALGOS = ("fused", "phases", "ring", "ring_persistent", "ring_pipelined")
+
+
 def run_orders(args):
     """The tree-shaped orders beside the ring: full workloads timed with sampled
     parity against the bracketing's evaluation, and small messages timed as
@@ -342,10 +346,10 @@ def run_orders(args):
         rng = np.random.default_rng(9)
         pos = np.unique(np.concatenate([rng.integers(0, count, 1024)] +
                                        [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1]) for c in range(n)]))
-        for algo in ("fused", "ring", "ring_persistent", "tree", "halving_doubling", "tree_steps",
+        for algo in ("fused", "ring", "ring_persistent", "ring_pipelined", "tree", "halving_doubling", "tree_steps",
                      "recursive_doubling", "halving_doubling_steps"):
             med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 10, 2, stream)
-            ok = (_sampled_parity(xs, recvs, dt, "sum", pos) if algo in ("fused", "ring", "ring_persistent")
+            ok = (_sampled_parity(xs, recvs, dt, "sum", pos) if algo in RING_ORDER_ALGOS
                   else parity(xs, recvs, dt, algo, pos))
             algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
             print(json.dumps({"orders": name, "algo": algo, "dtype": dt, "nranks": n, "count": count,
@@ -362,7 +366,7 @@ def run_orders(args):
         count = 1024
         sends = [torch.randn(count, device=dev) for _ in range(n)]
         recvs = [torch.empty(count, device=dev) for _ in range(n)]
-        for algo in ("fused", "ring", "ring_persistent", "tree", "tree_steps", "recursive_doubling",
+        for algo in ("fused", "ring", "ring_persistent", "ring_pipelined", "tree", "tree_steps", "recursive_doubling",
                      "halving_doubling_steps"):
             med, _ = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 200, 5, stream)
             plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
@@ -567,7 +571,7 @@ def run_ceiling(args):
         torch.cuda.empty_cache()
 
 
-SWEEP_ALGOS = ("fused", "ring", "ring_persistent", "tree", "tree_steps", "recursive_doubling",
+SWEEP_ALGOS = ("fused", "ring", "ring_persistent", "ring_pipelined", "tree", "tree_steps", "recursive_doubling",
                "halving_doubling_steps")
 
 
@@ -580,7 +584,10 @@ def run_size_sweep(args):
     2 log2 N launches and 5(N-1)*S bytes for the staged tree and
     halving/doubling, log2 N launches and 2*N*S*log2 N bytes for recursive
     doubling.  The persistent ring is fitted like the ring's steps, its
-    2(N-1) steps separated by grid barriers instead of launches.
+    2(N-1) steps separated by grid barriers instead of launches; the
+    pipelined ring with one launch and the ring's 5(N-1)*S bytes, of which
+    the re-read partials mostly come from the caches (its fitted B is then
+    above what HBM alone would give those bytes).
     """
     import numpy as np
     import torch
@@ -609,6 +616,7 @@ def run_size_sweep(args):
     L = (n - 1).bit_length()
     for algo, bytes_factor, launches in (("fused", 2 * n, 1), ("ring", 5 * (n - 1), 2 * (n - 1)),
                                          ("ring_persistent", 5 * (n - 1), 2 * (n - 1)),
+                                         ("ring_pipelined", 5 * (n - 1), 1),
                                          ("tree", 2 * n, 1), ("tree_steps", 5 * (n - 1), 2 * L),
                                          ("recursive_doubling", 2 * n * L, L),
                                          ("halving_doubling_steps", 5 * (n - 1), 2 * L)):

@@ -144,7 +144,15 @@ typedef enum {
  *   for AR_BFLOAT16_ACC_F32 (AR_ERR_UNSUPPORTED).  It cannot be enqueued
  *   while the stream is being captured into a graph (AR_ERR_UNSUPPORTED),
  *   and, since its blocks must all be resident at once, it should not
- *   overlap other kernels on the device. */
+ *   overlap other kernels on the device.
+ * AR_ALGO_RING_PIPELINED: the ring's 2(N-1) steps in one ordinary launch,
+ *   slices of the chunks pipelined through the ring ("AllReduce, All the Way
+ *   Down": the tensor divided into chunks that are pipelined).  One
+ *   workgroup carries one slice of one chunk through every step in order,
+ *   loading the sender's partial from its buffer and storing its own, so
+ *   the steps need no barrier.  The same bits as AR_ALGO_RING.  AllReduce
+ *   only; not for AR_BFLOAT16_ACC_F32 (AR_ERR_UNSUPPORTED); can be captured
+ *   into a graph. */
 typedef enum {
     AR_ALGO_FUSED = 0,
     AR_ALGO_RING = 1,
@@ -155,7 +163,8 @@ typedef enum {
     AR_ALGO_RECURSIVE_DOUBLING = 6,
     AR_ALGO_HALVING_DOUBLING = 7,
     AR_ALGO_HALVING_DOUBLING_STEPS = 8,
-    AR_ALGO_RING_PERSISTENT = 9
+    AR_ALGO_RING_PERSISTENT = 9,
+    AR_ALGO_RING_PIPELINED = 10
 } ar_algo_t;
 
 /* Rank count from which AR_ALGO_AUTO runs an AllReduce as two fused phases

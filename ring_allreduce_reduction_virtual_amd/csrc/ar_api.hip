@@ -252,12 +252,13 @@ ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, Residue res) {
 }
 
 bool algo_known(ar_algo_t algo) {
-    return algo >= AR_ALGO_FUSED && algo <= AR_ALGO_RING_PERSISTENT;
+    return algo >= AR_ALGO_FUSED && algo <= AR_ALGO_RING_PIPELINED;
 }
 
-// AllReduce-only algorithms: the tree orders and the persistent ring.
+// AllReduce-only algorithms: the tree orders and the ring in one launch.
 bool allreduce_only_algo(ar_algo_t algo) {
-    return (algo >= AR_ALGO_TREE && algo <= AR_ALGO_HALVING_DOUBLING_STEPS) || algo == AR_ALGO_RING_PERSISTENT;
+    return (algo >= AR_ALGO_TREE && algo <= AR_ALGO_HALVING_DOUBLING_STEPS) || algo == AR_ALGO_RING_PERSISTENT ||
+           algo == AR_ALGO_RING_PIPELINED;
 }
 
 // The AllReduce-only algorithms that bracket the reduction as a tree.
@@ -354,6 +355,7 @@ const char* kind_name(Kind kd) {
         case Kind::kTreeReduceStep: return "tree_reduce_step";
         case Kind::kTreeCopyStep: return "tree_copy_step";
         case Kind::kRingPersistent: return "ring_persistent";
+        case Kind::kRingPipelined: return "ring_pipelined";
         case Kind::kSmallAllReduce: return "small_allreduce";
         case Kind::kSmallTree: return "small_tree";
     }
@@ -544,8 +546,8 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         algo = (k.n >= phases_min_ranks() && k.count * k.esz >= AR_PHASES_MIN_BYTES && !small_message(k))
                    ? AR_ALGO_PHASES
                    : AR_ALGO_FUSED;
-    if (algo == AR_ALGO_RING_PERSISTENT && k.dtype == AR_BFLOAT16_ACC_F32)
-        return fail(AR_ERR_UNSUPPORTED, "the persistent ring has no form with float32 partials");
+    if ((algo == AR_ALGO_RING_PERSISTENT || algo == AR_ALGO_RING_PIPELINED) && k.dtype == AR_BFLOAT16_ACC_F32)
+        return fail(AR_ERR_UNSUPPORTED, "the ring in one launch has no form with float32 partials");
     if (power_of_two_algo(algo) && (k.n & (k.n - 1)) != 0)
         return fail(AR_ERR_UNSUPPORTED, "algo %d needs a power-of-two number of ranks, not %d",
                     static_cast<int>(algo), k.n);
@@ -595,6 +597,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         return sink.emit(l, Kind::kFusedAllReduce, a, k);
     }
     if (algo == AR_ALGO_RING_PERSISTENT) return sink.emit(l, Kind::kRingPersistent, a, k);
+    if (algo == AR_ALGO_RING_PIPELINED) return sink.emit(l, Kind::kRingPipelined, a, k);
     if (k.dtype == AR_BFLOAT16_ACC_F32) {
         // float32 partials travel through the workspace; the last step leaves
         // finished chunk c in chunk c of rank c-1's own buffer, as the ring does

@@ -24,6 +24,7 @@ enum class Kind : int {
     kTreeReduceStep,       // one reducing stage of a tree-shaped schedule (`mode`, `step`)
     kTreeCopyStep,         // one distributing stage of a tree-shaped schedule (`mode`, `step`)
     kRingPersistent,       // all 2(N-1) ring steps in one cooperative launch
+    kRingPipelined,        // all 2(N-1) ring steps in one launch, slice by slice
     kSmallAllReduce,       // the fused AllReduce of a small message, staged through LDS
     kSmallTree,            // kFusedTree for a small message, staged through LDS
 };
@@ -112,9 +113,10 @@ hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream);
 // forwards the kFusedTree, kTreeReduceStep and kTreeCopyStep kinds here.
 hipError_t launch_tree(const Launch& l, const KernelArgs& a, hipStream_t stream);
 
-// The persistent ring (ar_persistent_kernels.hip): a cooperative launch on
-// at most as many blocks as the device holds at once.  Refuses
-// (hipErrorStreamCaptureUnsupported) while `stream` is capturing.
+// The ring in one launch (ar_persistent_kernels.hip).  kRingPersistent: a
+// cooperative launch on at most as many blocks as the device holds at once;
+// refuses (hipErrorStreamCaptureUnsupported) while `stream` is capturing.
+// kRingPipelined: an ordinary launch, one block per slice.
 hipError_t launch_persistent(const Launch& l, const KernelArgs& a, hipStream_t stream);
 
 }  // namespace arimpl

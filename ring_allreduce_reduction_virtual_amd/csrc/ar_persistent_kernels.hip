@@ -1,18 +1,30 @@
 // The ring AllReduce in one launch (gfx950): the 2(N-1) steps of tirogla.com
-// "Ring all-reduce" ("How it works") run inside a single persistent grid,
-// separated by grid-wide barriers instead of kernel boundaries.
+// "Ring all-reduce" ("How it works") without a launch per step, in two
+// forms.
 //
-// Each step is exactly the work of the one-launch-per-step ring
-// (ring_reduce_tiles, ring_copy_tiles): the blocks stride over every chunk's
-// tiles, then all of them meet at a barrier before the next step reads what
-// this one wrote.  The barrier is the cooperative-groups grid barrier, which
-// needs every block resident at once: the kernel is only ever started with
+// k_ring_persistent runs the steps inside a single persistent grid,
+// separated by grid-wide barriers instead of kernel boundaries.  Each step
+// is exactly the work of the one-launch-per-step ring (ring_reduce_tiles,
+// ring_copy_tiles): the blocks stride over every chunk's tiles, then all of
+// them meet at a barrier before the next step reads what this one wrote.
+// The barrier is the cooperative-groups grid barrier, which needs every
+// block resident at once: the kernel is only ever started with
 // hipLaunchCooperativeKernel, on a grid no larger than the number of blocks
 // the device can hold at once (the runtime refuses a larger one), and every
 // block runs the same sequence of barriers (no block leaves early).  The
 // barrier's agent-scope fences make one step's stores visible to the next
 // step's loads on every XCD.
-
+//
+// k_ring_pipelined instead pipelines slices of the chunks through the ring,
+// as "AllReduce, All the Way Down" describes the tensor being divided into
+// chunks that are pipelined: a block takes one slice (one tile: 8 KiB per
+// rank) of one chunk and carries it through all 2(N-1) steps in order.  A
+// step of the ring reads only what the previous step wrote at the same
+// positions, and each thread keeps the same positions in every step, so a
+// thread only ever reads back its own earlier stores: no barrier, no
+// flag, no cross-block ordering.  Every step still goes through memory:
+// the incoming partial is loaded from the sender's buffer, not forwarded
+// in registers.
 #include <hip/hip_cooperative_groups.h>
 
 #include <atomic>
@@ -35,6 +47,101 @@ __global__ __launch_bounds__(kThreads) void k_ring_persistent(const KernelArgs a
         ring_copy_tiles<DT, VEC>(a, s, 0);
         if (s + 1 < n - 1) grid.sync();
     }
+}
+
+// A unit stored with a cache-allocating store: the next step of the
+// same thread reads it back.
+template <int DT, int VEC>
+__device__ __forceinline__ void store_unit_cached(char* tb, uint32_t off, typename Unit<DT, VEC>::T x) {
+    if constexpr (VEC > 1) {
+        *reinterpret_cast<u32x4*>(tb + off) = x;
+    } else if constexpr (elem_size<DT>() == 2) {
+        *reinterpret_cast<uint16_t*>(tb + off) = static_cast<uint16_t>(x);
+    } else {
+        *reinterpret_cast<uint32_t*>(tb + off) = x;
+    }
+}
+
+// Keeps the compiler from forwarding a step's stores to the next step's
+// loads: each step receives its partial from the sender's buffer.
+__device__ __forceinline__ void step_boundary() { __asm__ __volatile__("" ::: "memory"); }
+
+// The slice of chunk c that a block owns, through the ring's reduce-scatter
+// (step s: rank c+s+1 adds its own value to the partial of rank c+s, the
+// last step completing the chunk) and all-gather (step s: rank c+s copies
+// the finished chunk from rank c+s-1).  The chunk's head and tail elements
+// go through the same steps, one element per thread, in the chunk's first
+// block.
+template <int DT, int OP, int VEC>
+__global__ __launch_bounds__(kThreads) void k_ring_pipelined(const KernelArgs a) {
+    static_assert(!acc_f32<DT>(), "float32 partials have no pipelined form");
+    using U = Unit<DT, VEC>;                 // the send buffers: read once, nontemporal
+    using UC = Unit<DT, VEC, false>;         // partials: read back from the cache
+    using F = Fold<DT, OP, VEC>;
+    using F1 = Fold<DT, OP, 1>;
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            const uint64_t b = i * ESZ;
+            for (int s = 0; s < n - 1; ++s) {
+                const int r = ring_rank(c, s + 1, n);
+                const int p = ring_rank(c, s, n);
+                const uint32_t in = load_elem<ESZ>((s == 0 ? a.send[p] : a.recv[p]) + b);
+                uint32_t v = F1::add(load_elem<ESZ>(a.send[r] + b), in);
+                if (s == n - 2) v = F1::done(v, n);
+                store_unit_cached<DT, 1>(a.recv[r] + b, 0u, v);
+                step_boundary();
+            }
+            for (int s = 0; s < n - 1; ++s) {
+                const int r = ring_rank(c, s, n);
+                const int p = ring_rank(r, n - 1, n);
+                store_unit_cached<DT, 1>(a.recv[r] + b, 0u, load_elem<ESZ>(a.recv[p] + b));
+                step_boundary();
+            }
+        }
+    }
+    for (int s = 0; s < n - 1; ++s) {        // reduce-scatter
+        const int r = ring_rank(c, s + 1, n);
+        const int p = ring_rank(c, s, n);
+        const char* tl = U::tile(a.send[r] - adj, tv0);
+        const char* ti = UC::tile((s == 0 ? a.send[p] : a.recv[p]) - adj, tv0);
+        typename U::T x[kUnroll], y[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) {
+                x[u] = U::load(tl, U::lane_off(u));
+                y[u] = UC::load(ti, U::lane_off(u));
+            }
+        }
+        char* to = U::tile(a.recv[r] - adj, tv0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (!live[u]) continue;
+            typename U::T z = F::add(x[u], y[u]);
+            if (s == n - 2) z = F::done(z, n);
+            store_unit_cached<DT, VEC>(to, U::lane_off(u), z);
+        }
+        step_boundary();
+    }
+    for (int s = 0; s < n - 1; ++s) {        // all-gather
+        const int r = ring_rank(c, s, n);
+        const int p = ring_rank(r, n - 1, n);
+        const char* ts = UC::tile(a.recv[p] - adj, tv0);
+        typename U::T x[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) x[u] = UC::load(ts, U::lane_off(u));
+        }
+        char* td = U::tile(a.recv[r] - adj, tv0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) store_unit_cached<DT, VEC>(td, U::lane_off(u), x[u]);
+        }
+        step_boundary();
+    }
+    AR_TILE_LOOP_END
 }
 
 constexpr int kMaxDevices = 64;
@@ -74,6 +181,10 @@ hipError_t resident_blocks(int* out) {
 
 template <int DT, int OP, int VEC>
 hipError_t launch_t(const Launch& l, const KernelArgs& a, hipStream_t s) {
+    if (l.kind == Kind::kRingPipelined) {    // an ordinary launch: one block per slice
+        hipLaunchKernelGGL((k_ring_pipelined<DT, OP, VEC>), dim3(l.blocks), dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+    }
     int resident = 0;
     hipError_t e = resident_blocks<DT, OP, VEC>(&resident);
     if (e != hipSuccess) return e;
@@ -105,18 +216,22 @@ hipError_t by_op(const Launch& l, const KernelArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_persistent(const Launch& l, const KernelArgs& a, hipStream_t stream) {
-    // Never inside a stream capture: a captured launch could replay without
-    // the cooperative guarantees the grid barrier depends on.
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    hipError_t e = hipStreamIsCapturing(stream, &cap);
-    if (e != hipSuccess) return e;
-    if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+    if (l.kind == Kind::kRingPersistent) {
+        // Never inside a stream capture: a captured launch could replay without
+        // the cooperative guarantees the grid barrier depends on.
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(stream, &cap);
+        if (e != hipSuccess) return e;
+        if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+    } else if (l.kind != Kind::kRingPipelined) {
+        return hipErrorInvalidValue;
+    }
     switch (l.dtype) {
         case AR_FLOAT32: return by_op<AR_FLOAT32>(l, a, stream);
         case AR_BFLOAT16: return by_op<AR_BFLOAT16>(l, a, stream);
         case AR_INT32: return by_op<AR_INT32>(l, a, stream);
         case AR_FLOAT16: return by_op<AR_FLOAT16>(l, a, stream);
-        default: return hipErrorInvalidValue;   // float32 partials have no persistent form
+        default: return hipErrorInvalidValue;   // float32 partials have no one-launch form
     }
 }
 

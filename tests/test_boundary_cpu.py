@@ -273,13 +273,15 @@ def test_tree_algorithm_host_rules(lib):
     assert rc == 1 and b"workspace" in lib.ar_get_last_error_detail()
 
 
-def test_persistent_ring_host_rules(lib):
-    """The persistent ring: AllReduce only, no float32-partials form, no workspace."""
+@pytest.mark.parametrize("name", ["ring_persistent", "ring_pipelined"])
+def test_one_launch_ring_host_rules(lib, name):
+    """The ring in one launch (persistent or pipelined): AllReduce only, no
+    float32-partials form, no workspace."""
     import ring_allreduce_reduction_virtual_amd as ar
     from ring_allreduce_reduction_virtual_amd import _lib
 
-    algo = _lib.ALGOS["ring_persistent"]
-    assert ar.ar_workspace_bytes("allreduce", "ring_persistent", 1000, "bf16", 8) == 0
+    algo = _lib.ALGOS[name]
+    assert ar.ar_workspace_bytes("allreduce", name, 1000, "bf16", 8) == 0
     S = 1 << 20
     sends = [BASE + r * S for r in range(8)]
     recvs = [BASE + (16 + r) * S for r in range(8)]

@@ -1,7 +1,10 @@
-"""GPU parity for the persistent ring (all 2(N-1) steps in one cooperative
-launch with grid barriers): the ring's bits for every dtype and operator,
-rank counts up to 128, layouts, persistent plans with workgroup caps, the
-full headline workload (sampled), and the refusal to be captured into a graph.
+"""GPU parity for the ring in one launch, in both forms: the persistent ring
+(all 2(N-1) steps in one cooperative launch with grid barriers) and the
+pipelined ring (each slice of each chunk carried through all steps by one
+workgroup, no barrier).  The ring's bits for every dtype and operator, rank
+counts up to 128, layouts, persistent plans with workgroup caps, the full
+headline workload (sampled); the persistent ring refuses graph capture, the
+pipelined ring replays from a graph.
 
 Every launch here runs alone on the device, as the grid barrier requires."""
 
@@ -16,6 +19,8 @@ from oracle.ring import f32_to_bf16_bits, f32_to_f16_bits, same_bits
 from gpu_util import from_dev, require_gpu, sample_positions, to_dev
 
 pytestmark = pytest.mark.gpu
+
+ONE_LAUNCH = ["ring_persistent", "ring_pipelined"]
 
 TORCH_OF = {"f16": "float16", "bf16": "bfloat16", "f32": "float32", "i32": "int32"}
 
@@ -66,7 +71,8 @@ def _empty(n, length, dtype):
                                       ("i32", "sum"), ("i32", "max"), ("i32", "avg")])
 @pytest.mark.parametrize("n,length", [(1, 9), (2, 1001), (3, 7), (5, 1003), (8, 8 * 4096 + 13), (17, 4099),
                                       (64, 64 * 300 + 5), (128, 128 * 40 + 3)])
-def test_persistent_ring_matches_the_oracle(n, length, dtype, op):
+@pytest.mark.parametrize("algo", ONE_LAUNCH)
+def test_one_launch_ring_matches_the_oracle(algo, n, length, dtype, op):
     import torch
 
     ar = _ar()
@@ -74,14 +80,15 @@ def test_persistent_ring_matches_the_oracle(n, length, dtype, op):
     want, _ = oracle.ring_allreduce(xs, op=op, dtype=dtype)
     sends = [_dev(x, dtype) for x in xs]
     recvs = _empty(n, length, dtype)
-    ar.ar_allreduce_ex(sends, recvs, op=op, algo="ring_persistent", dtype=dtype)
+    ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo, dtype=dtype)
     torch.cuda.synchronize()
     for r in range(n):
         assert same_bits(_host(recvs[r], dtype), want[r], dtype), f"rank {r}"
 
 
 @pytest.mark.parametrize("layout", ["in_place", "common_offset", "mixed_offsets"])
-def test_persistent_ring_layouts(layout):
+@pytest.mark.parametrize("algo", ONE_LAUNCH)
+def test_one_launch_ring_layouts(algo, layout):
     import torch
 
     ar = _ar()
@@ -101,13 +108,14 @@ def test_persistent_ring_layouts(layout):
             sends.append(v)
             off2 = 1 if layout == "common_offset" else (r + 1) % 3
             recvs.append(torch.empty(length + 8, device="cuda:0")[off2:off2 + length])
-    ar.ar_allreduce_ex(sends, recvs, algo="ring_persistent")
+    ar.ar_allreduce_ex(sends, recvs, algo=algo)
     torch.cuda.synchronize()
     for r in range(n):
         assert same_bits(_host(recvs[r], "f32"), want[r], "f32"), f"rank {r}"
 
 
-def test_persistent_ring_plan_one_launch_and_caps():
+@pytest.mark.parametrize("algo", ONE_LAUNCH)
+def test_one_launch_ring_plan_and_caps(algo):
     import torch
 
     ar = _ar()
@@ -116,7 +124,7 @@ def test_persistent_ring_plan_one_launch_and_caps():
     want, _ = oracle.ring_allreduce(xs, dtype="bf16")
     sends = [_dev(x, "bf16") for x in xs]
     recvs = _empty(n, length, "bf16")
-    plan = ar.ar_allreduce_init(sends, recvs, algo="ring_persistent")
+    plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
     assert plan.num_launches == 1
     for cap in (0, 1, 5, 64, 0):
         plan.limit_blocks(cap)
@@ -150,7 +158,43 @@ def test_persistent_ring_refuses_graph_capture():
     plan.close()
 
 
-def test_persistent_ring_headline_full_size_sampled():
+def test_pipelined_ring_replays_from_a_graph():
+    """Capture 3 starts of a pipelined-ring plan; replay 4 times with eager input
+    changes in between, checking every replay against the oracle."""
+    import torch
+
+    ar = _ar()
+    n, length = 8, 8 * 2048 + 3
+    xs = _draw("f32", n, length, seed=51)
+    sends = [_dev(x, "f32") for x in xs]
+    recvs = _empty(n, length, "f32")
+    plan = ar.ar_allreduce_init(sends, recvs, algo="ring_pipelined")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.start(side)                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            plan.start()
+    for rep in range(4):
+        xs = [x + np.float32(rep + 1) * np.float32(0.5) for x in xs]
+        for r in range(n):
+            sends[r].copy_(_dev(xs[r], "f32"))   # eager work between replays
+        for t in recvs:
+            t.fill_(-3.0)
+        g.replay()
+        torch.cuda.synchronize()
+        want, _ = oracle.ring_allreduce(xs)
+        for r in range(n):
+            assert same_bits(_host(recvs[r], "f32"), want[r], "f32"), (rep, r)
+    plan.close()
+
+
+@pytest.mark.parametrize("algo", ONE_LAUNCH)
+def test_one_launch_ring_headline_full_size_sampled(algo):
     import torch
 
     from inputs import WORKLOADS, make_inputs
@@ -161,7 +205,7 @@ def test_persistent_ring_headline_full_size_sampled():
     xs = make_inputs(w)
     sends = [_dev(x, "f32") for x in xs]
     recvs = _empty(w.nranks, w.count, "f32")
-    ar.ar_allreduce_ex(sends, recvs, algo="ring_persistent")
+    ar.ar_allreduce_ex(sends, recvs, algo=algo)
     torch.cuda.synchronize()
     pos = sample_positions(w.count, w.nranks, seed=12)
     want = oracle.ring_order_fold_columns(np.stack([x[pos] for x in xs]), chunk_owner(pos, w.nranks, w.count))
