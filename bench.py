@@ -791,6 +791,11 @@ def main():
         ring_ms = time_calls(lambda: ar.ar_allreduce_ex(sends, recvs, algo="ring"), max(3, args.steps // 10), 1, stream)
         extra["ring_mode_ms"] = round(ring_ms, 4)
         extra["ring_mode_hbm_gbps_of_minimum"] = round(algo_bytes / (ring_ms / 1e3) / 1e9, 1)
+        # the same steps pipelined slice by slice in one launch
+        pipe_ms = time_calls(lambda: ar.ar_allreduce_ex(sends, recvs, algo="ring_pipelined"),
+                             max(3, args.steps // 10), 1, stream)
+        extra["ring_pipelined_ms"] = round(pipe_ms, 4)
+        extra["ring_pipelined_hbm_gbps_of_minimum"] = round(algo_bytes / (pipe_ms / 1e3) / 1e9, 1)
         shards = [recvs[r][slice(*chunk(r, n, count))] for r in range(n)]
         rs_ms = time_calls(lambda: ar.ar_reduce_scatter(sends, shards), 20, 2, stream)
         ag_ms = time_calls(lambda: ar.ar_all_gather(shards, sends), 20, 2, stream)
@@ -816,7 +821,8 @@ def main():
                 "mix_probe_us": round(pt["mix"], 1),
                 "fused_frac_of_read_plus_write": round((pt["read"] + pt["write"]) / (ms * 1e3), 4),
                 "fused_speed_vs_mix_probe": round(pt["mix"] / (ms * 1e3), 4)}
-        log(f"[bench] ring mode {ring_ms:.3f} ms; reduce-scatter {rs_ms:.3f} ms; all-gather {ag_ms:.3f} ms; "
+        log(f"[bench] ring mode {ring_ms:.3f} ms; pipelined ring {pipe_ms:.3f} ms; reduce-scatter {rs_ms:.3f} ms; "
+            f"all-gather {ag_ms:.3f} ms; "
             f"torch copy {extra['torch_copy_2x2GiB_hbm_gbps']} GB/s")
         # restore the inputs overwritten by the all-gather above
         for r in range(n):
