@@ -205,7 +205,7 @@ def run_configs(args):
         oracle_s = time.perf_counter() - t0
         steps = 200 if s_bytes < (1 << 24) else 20
         for op in w.ops:
-            for algo in ("fused", "phases", "ring"):
+            for algo in ("fused", "phases", "ring", "ring_pipelined"):
                 fn = (lambda: ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo))
                 med, mn = median_call_ms(fn, steps, 3, stream)
                 ok = _sampled_parity(xs, recvs, dt, op, pos)
@@ -232,7 +232,7 @@ def run_configs(args):
             shards = [torch.empty(chunk(r, n, count)[1] - chunk(r, n, count)[0], dtype=tdt[dt], device=dev)
                       for r in range(n)]
             rs_bytes = algorithmic_bytes("reduce_scatter", n, s_bytes)
-            for algo in ("fused", "ring"):
+            for algo in ("fused", "ring", "ring_pipelined"):
                 med, mn = median_call_ms(lambda: ar.ar_reduce_scatter_ex(sends, shards, algo=algo), steps, 3, stream)
                 print(json.dumps({"config": name, "collective": "reduce_scatter", "algo": algo, "op": "sum",
                                   "dtype": dt, "nranks": n, "count": count, "median_us": round(med * 1e3, 2),
@@ -241,7 +241,7 @@ def run_configs(args):
                                   "busbw_gbps": round(s_bytes / (med / 1e3) / 1e9 * busbw_factor("reduce_scatter", n), 2),
                                   "hbm_gbps_of_minimum": round(rs_bytes / (med / 1e3) / 1e9, 1),
                                   "hbm_frac": round(rs_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}), flush=True)
-            for algo in ("fused", "ring"):
+            for algo in ("fused", "ring", "ring_pipelined"):
                 med, mn = median_call_ms(lambda: ar.ar_all_gather_ex(shards, recvs, algo=algo), steps, 3, stream)
                 print(json.dumps({"config": name, "collective": "all_gather", "algo": algo, "dtype": dt,
                                   "nranks": n, "count": count, "median_us": round(med * 1e3, 2),
@@ -287,7 +287,7 @@ def run_variants(args):
         rng = np.random.default_rng(3)
         pos = np.unique(np.concatenate([rng.integers(0, count, 1024)] +
                                        [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1]) for c in range(n)]))
-        for algo in ("fused", "phases", "ring"):
+        for algo in ("fused", "phases", "ring", "ring_pipelined"):
             med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo, dtype=dt), 20, 3, stream)
             ok = _sampled_parity(xs, recvs, dt, op, pos)
             algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)

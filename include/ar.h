@@ -145,14 +145,13 @@ typedef enum {
  *   while the stream is being captured into a graph (AR_ERR_UNSUPPORTED),
  *   and, since its blocks must all be resident at once, it should not
  *   overlap other kernels on the device.
- * AR_ALGO_RING_PIPELINED: the ring's 2(N-1) steps in one ordinary launch,
- *   slices of the chunks pipelined through the ring ("AllReduce, All the Way
- *   Down": the tensor divided into chunks that are pipelined).  One
- *   workgroup carries one slice of one chunk through every step in order,
- *   loading the sender's partial from its buffer and storing its own, so
- *   the steps need no barrier.  The same bits as AR_ALGO_RING.  AllReduce
- *   only; not for AR_BFLOAT16_ACC_F32 (AR_ERR_UNSUPPORTED); can be captured
- *   into a graph. */
+ * AR_ALGO_RING_PIPELINED: the ring's steps in one ordinary launch, slices
+ *   of the chunks pipelined through the ring ("AllReduce, All the Way Down":
+ *   the tensor divided into chunks that are pipelined).  One workgroup
+ *   carries one slice of one chunk through every step in order, loading the
+ *   sender's partial and storing its own, so the steps need no barrier.  The
+ *   same bits as AR_ALGO_RING, for all three collectives and every dtype,
+ *   with the same workspace as AR_ALGO_RING; can be captured into a graph. */
 typedef enum {
     AR_ALGO_FUSED = 0,
     AR_ALGO_RING = 1,
@@ -209,7 +208,8 @@ ar_result_t ar_all_gather(const void* const* sendbufs, void* const* recvbufs, si
  * `workspace` is device memory of at least ar_workspace_bytes(...) bytes
  * owned by the caller (NULL when that size is 0); it must not overlap any
  * buffer and must stay valid until the stream work completes.  Only the ring
- * algorithm needs one, for nranks >= 3: the reduce-scatter keeps the partial
+ * algorithms (AR_ALGO_RING and AR_ALGO_RING_PIPELINED) need one, for
+ * nranks >= 3: the reduce-scatter keeps the partial
  * sums in flight between steps in it, since its receive buffers are only one
  * shard long, and so does the AllReduce of AR_BFLOAT16_ACC_F32, whose float32
  * partials do not fit the bf16 buffers.  Other ring AllReduces and the ring

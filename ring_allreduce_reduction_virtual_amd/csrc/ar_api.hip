@@ -255,11 +255,13 @@ bool algo_known(ar_algo_t algo) {
     return algo >= AR_ALGO_FUSED && algo <= AR_ALGO_RING_PIPELINED;
 }
 
-// AllReduce-only algorithms: the tree orders and the ring in one launch.
+// AllReduce-only algorithms: the tree orders and the persistent ring.
 bool allreduce_only_algo(ar_algo_t algo) {
-    return (algo >= AR_ALGO_TREE && algo <= AR_ALGO_HALVING_DOUBLING_STEPS) || algo == AR_ALGO_RING_PERSISTENT ||
-           algo == AR_ALGO_RING_PIPELINED;
+    return (algo >= AR_ALGO_TREE && algo <= AR_ALGO_HALVING_DOUBLING_STEPS) || algo == AR_ALGO_RING_PERSISTENT;
 }
+
+// The ring's own schedule, step by step: launched per step or pipelined in one launch.
+bool ring_steps_algo(ar_algo_t algo) { return algo == AR_ALGO_RING || algo == AR_ALGO_RING_PIPELINED; }
 
 // The AllReduce-only algorithms that bracket the reduction as a tree.
 bool tree_algo(ar_algo_t algo) { return algo >= AR_ALGO_TREE && algo <= AR_ALGO_HALVING_DOUBLING_STEPS; }
@@ -356,6 +358,8 @@ const char* kind_name(Kind kd) {
         case Kind::kTreeCopyStep: return "tree_copy_step";
         case Kind::kRingPersistent: return "ring_persistent";
         case Kind::kRingPipelined: return "ring_pipelined";
+        case Kind::kRingPipelinedWs: return "ring_pipelined_ws";
+        case Kind::kRingPipelinedGather: return "ring_pipelined_gather";
         case Kind::kSmallAllReduce: return "small_allreduce";
         case Kind::kSmallTree: return "small_tree";
     }
@@ -409,9 +413,10 @@ private:
 
 // ---------------------------------------------------------------------------
 
-// Workspace of the ring algorithm: one full-length buffer of partial sums
-// for the reduce-scatter, and for the AllReduce of AR_BFLOAT16_ACC_F32; none
-// with fewer than 3 ranks, where the only reduce step is also the last.  The
+// Workspace of the ring algorithm (launched per step or pipelined): one
+// full-length buffer of partial sums for the reduce-scatter, and for the
+// AllReduce of AR_BFLOAT16_ACC_F32; none with fewer than 3 ranks, where the
+// only reduce step is also the last.  The
 // staged tree AllReduces of AR_BFLOAT16_ACC_F32 keep one float32 slab of
 // `count` elements per rank (each slab rounded up to 256 bytes).  The extra
 // 1024 bytes cover placing the partials at the senders' residue: up to 255
@@ -425,7 +430,7 @@ uint64_t ring_workspace_bytes(ar_coll_t coll, uint64_t count, ar_dtype_t dt, int
     if (count == 0) return 0;
     if (coll == AR_COLL_ALLREDUCE && tree_steps_algo(algo) && dt == AR_BFLOAT16_ACC_F32 && n >= 2)
         return static_cast<uint64_t>(n) * slab_bytes(count) + kWorkspaceSlack;
-    if (algo != AR_ALGO_RING || n < 3) return 0;
+    if (!ring_steps_algo(algo) || n < 3) return 0;
     if (coll == AR_COLL_REDUCE_SCATTER || (coll == AR_COLL_ALLREDUCE && dt == AR_BFLOAT16_ACC_F32))
         return count * partial_size(dt) + kWorkspaceSlack;
     return 0;
@@ -546,8 +551,8 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         algo = (k.n >= phases_min_ranks() && k.count * k.esz >= AR_PHASES_MIN_BYTES && !small_message(k))
                    ? AR_ALGO_PHASES
                    : AR_ALGO_FUSED;
-    if ((algo == AR_ALGO_RING_PERSISTENT || algo == AR_ALGO_RING_PIPELINED) && k.dtype == AR_BFLOAT16_ACC_F32)
-        return fail(AR_ERR_UNSUPPORTED, "the ring in one launch has no form with float32 partials");
+    if (algo == AR_ALGO_RING_PERSISTENT && k.dtype == AR_BFLOAT16_ACC_F32)
+        return fail(AR_ERR_UNSUPPORTED, "the persistent ring has no form with float32 partials");
     if (power_of_two_algo(algo) && (k.n & (k.n - 1)) != 0)
         return fail(AR_ERR_UNSUPPORTED, "algo %d needs a power-of-two number of ranks, not %d",
                     static_cast<int>(algo), k.n);
@@ -597,7 +602,13 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         return sink.emit(l, Kind::kFusedAllReduce, a, k);
     }
     if (algo == AR_ALGO_RING_PERSISTENT) return sink.emit(l, Kind::kRingPersistent, a, k);
-    if (algo == AR_ALGO_RING_PIPELINED) return sink.emit(l, Kind::kRingPipelined, a, k);
+    if (algo == AR_ALGO_RING_PIPELINED) {
+        if (k.dtype != AR_BFLOAT16_ACC_F32) return sink.emit(l, Kind::kRingPipelined, a, k);
+        // float32 partials travel through the workspace, as in the ring's launches
+        if ((rc = use_workspace(a, k, AR_COLL_ALLREDUCE, algo, ws, ws_bytes, nullptr)) != AR_SUCCESS) return rc;
+        a.mode = 1;
+        return sink.emit(l, Kind::kRingPipelinedWs, a, k);
+    }
     if (k.dtype == AR_BFLOAT16_ACC_F32) {
         // float32 partials travel through the workspace; the last step leaves
         // finished chunk c in chunk c of rank c-1's own buffer, as the ring does
@@ -629,7 +640,7 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
     if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
     if (allreduce_only_algo(algo))
         return fail(AR_ERR_UNSUPPORTED, "algo %d is defined for AllReduce only", static_cast<int>(algo));
-    if (algo != AR_ALGO_RING) algo = AR_ALGO_FUSED;
+    if (!ring_steps_algo(algo)) algo = AR_ALGO_FUSED;
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;
     const uint64_t bytes = k.count * k.esz;
@@ -662,6 +673,10 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
     if ((rc = plan(a, l, k, residue)) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_FUSED || k.n == 1) return sink.emit(l, Kind::kFusedReduceScatter, a, k);
     if ((rc = use_workspace(a, k, AR_COLL_REDUCE_SCATTER, algo, ws, ws_bytes, nullptr)) != AR_SUCCESS) return rc;
+    if (algo == AR_ALGO_RING_PIPELINED) {
+        a.mode = 0;
+        return sink.emit(l, Kind::kRingPipelinedWs, a, k);
+    }
     for (int s = 0; s < k.n - 1; ++s) {
         a.step = s;
         if ((rc = sink.emit(l, Kind::kRingReduceStepWs, a, k)) != AR_SUCCESS) return rc;
@@ -675,7 +690,7 @@ ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, Sink& sink) {
     if (!algo_known(algo)) return fail(AR_ERR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
     if (allreduce_only_algo(algo))
         return fail(AR_ERR_UNSUPPORTED, "algo %d is defined for AllReduce only", static_cast<int>(algo));
-    if (algo != AR_ALGO_RING) algo = AR_ALGO_FUSED;
+    if (!ring_steps_algo(algo)) algo = AR_ALGO_FUSED;
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;
     const uint64_t bytes = k.count * k.esz;
@@ -702,6 +717,7 @@ ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, Sink& sink) {
     fill_tables(a, k);
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_FUSED || k.n == 1) return sink.emit(l, Kind::kFusedAllGather, a, k);
+    if (algo == AR_ALGO_RING_PIPELINED) return sink.emit(l, Kind::kRingPipelinedGather, a, k);
     if ((rc = sink.emit(l, Kind::kPlaceShards, a, k)) != AR_SUCCESS) return rc;
     for (int s = 0; s < k.n - 1; ++s) {
         a.step = s;

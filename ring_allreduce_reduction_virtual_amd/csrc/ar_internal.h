@@ -25,6 +25,9 @@ enum class Kind : int {
     kTreeCopyStep,         // one distributing stage of a tree-shaped schedule (`mode`, `step`)
     kRingPersistent,       // all 2(N-1) ring steps in one cooperative launch
     kRingPipelined,        // all 2(N-1) ring steps in one launch, slice by slice
+    kRingPipelinedWs,      // the same with the reduce-scatter partials in the workspace (`mode` 0:
+                           // reduce-scatter into the shards; 1: AllReduce, then the all-gather steps)
+    kRingPipelinedGather,  // the all-gather ring in one launch, slice by slice
     kSmallAllReduce,       // the fused AllReduce of a small message, staged through LDS
     kSmallTree,            // kFusedTree for a small message, staged through LDS
 };
@@ -116,7 +119,8 @@ hipError_t launch_tree(const Launch& l, const KernelArgs& a, hipStream_t stream)
 // The ring in one launch (ar_persistent_kernels.hip).  kRingPersistent: a
 // cooperative launch on at most as many blocks as the device holds at once;
 // refuses (hipErrorStreamCaptureUnsupported) while `stream` is capturing.
-// kRingPipelined: an ordinary launch, one block per slice.
+// kRingPipelined, kRingPipelinedWs, kRingPipelinedGather: ordinary launches,
+// one block per slice.
 hipError_t launch_persistent(const Launch& l, const KernelArgs& a, hipStream_t stream);
 
 }  // namespace arimpl

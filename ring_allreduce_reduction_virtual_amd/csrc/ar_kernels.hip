@@ -344,7 +344,9 @@ hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream) {
     if (l.kind == Kind::kFusedTree || l.kind == Kind::kTreeReduceStep || l.kind == Kind::kTreeCopyStep ||
         l.kind == Kind::kSmallTree)
         return launch_tree(l, a, stream);
-    if (l.kind == Kind::kRingPersistent || l.kind == Kind::kRingPipelined) return launch_persistent(l, a, stream);
+    if (l.kind == Kind::kRingPersistent || l.kind == Kind::kRingPipelined || l.kind == Kind::kRingPipelinedWs ||
+        l.kind == Kind::kRingPipelinedGather)
+        return launch_persistent(l, a, stream);
     const bool copy = l.kind == Kind::kFusedAllGather || l.kind == Kind::kPlaceShards ||
                       l.kind == Kind::kRingCopyStep;
     if (copy) {

@@ -144,6 +144,167 @@ __global__ __launch_bounds__(kThreads) void k_ring_pipelined(const KernelArgs a)
     AR_TILE_LOOP_END
 }
 
+// The pipelined ring with its reduce-scatter partials in the workspace: one
+// partial per position, which every step of the slice's owner reads and
+// overwrites (the ring's reduce-scatter as k_ring_reduce_step_ws runs it,
+// slice by slice).  mode 0, reduce-scatter: the last step writes the
+// finished value into shard c of rank c.  mode 1, AllReduce (float32
+// partials of bf16): the last step writes it, rounded, into chunk c of rank
+// c-1's own buffer, and the all-gather steps follow as in k_ring_pipelined.
+template <int DT, int OP, int VEC>
+__global__ __launch_bounds__(kThreads) void k_ring_pipelined_ws(const KernelArgs a) {
+    using U = Unit<DT, VEC>;
+    using UC = Unit<DT, VEC, false>;
+    using F = Fold<DT, OP, VEC>;
+    using F1 = Fold<DT, OP, 1>;
+    using P = Partials<DT, VEC>;
+    using P1 = Partials<DT, 1>;
+    constexpr int ESZ = elem_size<DT>();
+    const bool allreduce = a.mode == 1;
+    const char* ws_base = a.ws - static_cast<int64_t>(a.ofs) * P::kElemBytes;
+    AR_TILE_LOOP_BEGIN
+    char* shard = a.recv[c];
+    const int owner = ring_rank(c, n - 1, n);    // rank c-1 finishes chunk c
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            const uint64_t b = i * ESZ;
+            for (int s = 0; s < n - 1; ++s) {
+                const int r = ring_rank(c, s + 1, n);
+                const typename F1::A in = (s == 0) ? F1::first(load_elem<ESZ>(a.send[c] + b)) : P1::load(a.ws, i);
+                const typename F1::A v = F1::add_acc(F1::first(load_elem<ESZ>(a.send[r] + b)), in);
+                if (s < n - 2) {
+                    P1::store(const_cast<char*>(a.ws), i, v);
+                } else if (allreduce) {
+                    store_unit_cached<DT, 1>(a.recv[owner] + b, 0u, F1::done(v, n));
+                } else {
+                    store_elem<ESZ>(shard + (i - sp.s) * ESZ, F1::done(v, n));
+                }
+                step_boundary();
+            }
+            if (allreduce) {
+                for (int s = 0; s < n - 1; ++s) {
+                    const int r = ring_rank(c, s, n);
+                    const int p = ring_rank(r, n - 1, n);
+                    store_unit_cached<DT, 1>(a.recv[r] + b, 0u, load_elem<ESZ>(a.recv[p] + b));
+                    step_boundary();
+                }
+            }
+        }
+    }
+    const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
+    for (int s = 0; s < n - 1; ++s) {        // reduce-scatter, partials in the workspace
+        const int r = ring_rank(c, s + 1, n);
+        const char* tl = U::tile(a.send[r] - adj, tv0);
+        const char* ts = UC::tile(a.send[c] - adj, tv0);
+        typename U::T x[kUnroll];
+        typename F::A y[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) {
+                x[u] = U::load(tl, U::lane_off(u));
+                y[u] = (s == 0) ? F::first(UC::load(ts, U::lane_off(u))) : P::load(ws_base, tv0 + U::lane_unit(u));
+            }
+        }
+        char* to = allreduce ? U::tile(a.recv[owner] - adj, tv0) : nullptr;   // rank c-1's own chunk c
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (!live[u]) continue;
+            const typename F::A z = F::add_acc(F::first(x[u]), y[u]);
+            if (s < n - 2) {
+                P::store(const_cast<char*>(ws_base), tv0 + U::lane_unit(u), z);
+            } else if (allreduce) {
+                store_unit_cached<DT, VEC>(to, U::lane_off(u), F::done(z, n));
+            } else {
+                store_shard_unit<DT, VEC>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u), F::done(z, n));
+            }
+        }
+        step_boundary();
+    }
+    if (allreduce) {
+        for (int s = 0; s < n - 1; ++s) {    // all-gather
+            const int r = ring_rank(c, s, n);
+            const int p = ring_rank(r, n - 1, n);
+            const char* ts = UC::tile(a.recv[p] - adj, tv0);
+            typename U::T x[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (live[u]) x[u] = UC::load(ts, U::lane_off(u));
+            }
+            char* td = U::tile(a.recv[r] - adj, tv0);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (live[u]) store_unit_cached<DT, VEC>(td, U::lane_off(u), x[u]);
+            }
+            step_boundary();
+        }
+    }
+    AR_TILE_LOOP_END
+}
+
+// The ring all-gather pipelined: shard c is placed at position start(c) of
+// rank c, then copied from rank c+s to rank c+s+1 at step s (the standalone
+// all-gather ring of ramchalamkr.github.io "NCCL Primitives Deep Dive",
+// section "Ring All-Gather"), slice by slice.
+template <int DT, int VEC>
+__global__ __launch_bounds__(kThreads) void k_ring_pipelined_gather(const KernelArgs a) {
+    using U = Unit<DT, VEC, AR_NT_LOADS_COPY>;
+    using UC = Unit<DT, VEC, false>;
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    const char* shard = a.send[c];
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            const uint64_t b = i * ESZ;
+            char* first = a.recv[c] + b;
+            const char* src = shard + (i - sp.s) * ESZ;
+            if (first != src) store_unit_cached<DT, 1>(first, 0u, load_elem<ESZ>(src));
+            step_boundary();
+            for (int s = 0; s < n - 1; ++s) {
+                const int p = ring_rank(c, s, n);
+                const int r = ring_rank(c, s + 1, n);
+                store_unit_cached<DT, 1>(a.recv[r] + b, 0u, load_elem<ESZ>(a.recv[p] + b));
+                step_boundary();
+            }
+        }
+    }
+    {
+        const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
+        const bool in_place = a.recv[c] + sp.s * ESZ == shard;
+        typename U::T x[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) x[u] = load_shard_unit<DT, VEC, AR_NT_LOADS_COPY>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u));
+        }
+        if (!in_place) {
+            char* td = U::tile(a.recv[c] - adj, tv0);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (live[u]) store_unit_cached<DT, VEC>(td, U::lane_off(u), x[u]);
+            }
+        }
+        step_boundary();
+    }
+    for (int s = 0; s < n - 1; ++s) {
+        const int p = ring_rank(c, s, n);
+        const int r = ring_rank(c, s + 1, n);
+        const char* ts = UC::tile(a.recv[p] - adj, tv0);
+        typename U::T x[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) x[u] = UC::load(ts, U::lane_off(u));
+        }
+        char* td = U::tile(a.recv[r] - adj, tv0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) store_unit_cached<DT, VEC>(td, U::lane_off(u), x[u]);
+        }
+        step_boundary();
+    }
+    AR_TILE_LOOP_END
+}
+
 constexpr int kMaxDevices = 64;
 
 // Blocks per compute unit the persistent grid uses.  Every block pays for
@@ -180,11 +341,7 @@ hipError_t resident_blocks(int* out) {
 }
 
 template <int DT, int OP, int VEC>
-hipError_t launch_t(const Launch& l, const KernelArgs& a, hipStream_t s) {
-    if (l.kind == Kind::kRingPipelined) {    // an ordinary launch: one block per slice
-        hipLaunchKernelGGL((k_ring_pipelined<DT, OP, VEC>), dim3(l.blocks), dim3(kThreads), 0, s, a);
-        return hipGetLastError();
-    }
+hipError_t launch_cooperative(const Launch& l, const KernelArgs& a, hipStream_t s) {
     int resident = 0;
     hipError_t e = resident_blocks<DT, OP, VEC>(&resident);
     if (e != hipSuccess) return e;
@@ -193,6 +350,35 @@ hipError_t launch_t(const Launch& l, const KernelArgs& a, hipStream_t s) {
     void* params[] = {&copy};
     return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_ring_persistent<DT, OP, VEC>),
                                       dim3(blocks > 0 ? blocks : 1), dim3(kThreads), params, 0, s);
+}
+
+template <int DT, int OP, int VEC>
+hipError_t launch_t(const Launch& l, const KernelArgs& a, hipStream_t s) {
+    // the pipelined forms are ordinary launches: one block per slice
+    if (l.kind == Kind::kRingPipelinedWs) {
+        hipLaunchKernelGGL((k_ring_pipelined_ws<DT, OP, VEC>), dim3(l.blocks), dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+    }
+    if constexpr (acc_f32<DT>()) {
+        return hipErrorInvalidValue;         // float32 partials need the workspace form
+    } else {
+        if (l.kind == Kind::kRingPipelined) {
+            hipLaunchKernelGGL((k_ring_pipelined<DT, OP, VEC>), dim3(l.blocks), dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        }
+        return launch_cooperative<DT, OP, VEC>(l, a, s);
+    }
+}
+
+template <int DT>
+hipError_t launch_gather(const Launch& l, const KernelArgs& a, hipStream_t s) {
+    constexpr int V = 16 / elem_size<DT>();
+    if (l.vec) {
+        hipLaunchKernelGGL((k_ring_pipelined_gather<DT, V>), dim3(l.blocks), dim3(kThreads), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((k_ring_pipelined_gather<DT, 1>), dim3(l.blocks), dim3(kThreads), 0, s, a);
+    }
+    return hipGetLastError();
 }
 
 template <int DT, int OP>
@@ -223,7 +409,11 @@ hipError_t launch_persistent(const Launch& l, const KernelArgs& a, hipStream_t s
         hipError_t e = hipStreamIsCapturing(stream, &cap);
         if (e != hipSuccess) return e;
         if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
-    } else if (l.kind != Kind::kRingPipelined) {
+    } else if (l.kind == Kind::kRingPipelinedGather) {
+        // copies move bit patterns: the 2-byte types as bf16, the 4-byte ones as float32
+        const bool two_bytes = l.dtype == AR_BFLOAT16 || l.dtype == AR_FLOAT16 || l.dtype == AR_BFLOAT16_ACC_F32;
+        return two_bytes ? launch_gather<AR_BFLOAT16>(l, a, stream) : launch_gather<AR_FLOAT32>(l, a, stream);
+    } else if (l.kind != Kind::kRingPipelined && l.kind != Kind::kRingPipelinedWs) {
         return hipErrorInvalidValue;
     }
     switch (l.dtype) {
@@ -231,8 +421,9 @@ hipError_t launch_persistent(const Launch& l, const KernelArgs& a, hipStream_t s
         case AR_BFLOAT16: return by_op<AR_BFLOAT16>(l, a, stream);
         case AR_INT32: return by_op<AR_INT32>(l, a, stream);
         case AR_FLOAT16: return by_op<AR_FLOAT16>(l, a, stream);
-        default: return hipErrorInvalidValue;   // float32 partials have no one-launch form
+        case AR_BFLOAT16_ACC_F32: return by_op<AR_BFLOAT16_ACC_F32>(l, a, stream);   // workspace form only
     }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace arimpl

@@ -273,10 +273,40 @@ def test_tree_algorithm_host_rules(lib):
     assert rc == 1 and b"workspace" in lib.ar_get_last_error_detail()
 
 
-@pytest.mark.parametrize("name", ["ring_persistent", "ring_pipelined"])
+def test_pipelined_ring_host_rules(lib):
+    """The pipelined ring takes every collective and needs the ring's workspace
+    where the ring's launches do (reduce-scatter; AllReduce of float32 partials),
+    none elsewhere; a missing workspace is refused before anything launches."""
+    import ring_allreduce_reduction_virtual_amd as ar
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    for coll, dt in (("allreduce", "f32"), ("allreduce", "bf16"), ("allreduce", "bf16acc32"),
+                     ("reduce_scatter", "f32"), ("reduce_scatter", "bf16acc32"), ("all_gather", "bf16")):
+        for n in (2, 3, 8, 64):
+            assert (ar.ar_workspace_bytes(coll, "ring_pipelined", 1000, dt, n)
+                    == ar.ar_workspace_bytes(coll, "ring", 1000, dt, n)), (coll, dt, n)
+    algo = _lib.ALGOS["ring_pipelined"]
+    S = 1 << 20
+    sends = [BASE + r * S for r in range(8)]
+    recvs = [BASE + (16 + r) * S for r in range(8)]
+    rc = lib.ar_reduce_scatter_ex(_ptrs(sends), _ptrs(recvs), 100, 0, 0, 8, algo, None, 0, None)
+    assert rc == 1 and b"workspace" in lib.ar_get_last_error_detail()
+    rc = lib.ar_allreduce_ex(_ptrs(sends), _ptrs(recvs), 100, 4, 0, 8, algo, None, 0, None)
+    assert rc == 1 and b"workspace" in lib.ar_get_last_error_detail()
+    for init in ("ar_allreduce_init", "ar_reduce_scatter_init"):
+        plan = ctypes.c_void_p()
+        assert getattr(lib, init)(_ptrs(sends), _ptrs(recvs), 0, 0, 0, 8, algo, None, 0, ctypes.byref(plan)) == 0
+        assert lib.ar_plan_num_launches(plan) == 0
+        assert lib.ar_plan_free(plan) == 0
+    plan = ctypes.c_void_p()
+    assert lib.ar_all_gather_init(_ptrs(sends), _ptrs(recvs), 0, 0, 8, algo, None, 0, ctypes.byref(plan)) == 0
+    assert lib.ar_plan_num_launches(plan) == 0
+    assert lib.ar_plan_free(plan) == 0
+
+
+@pytest.mark.parametrize("name", ["ring_persistent"])
 def test_one_launch_ring_host_rules(lib, name):
-    """The ring in one launch (persistent or pipelined): AllReduce only, no
-    float32-partials form, no workspace."""
+    """The persistent ring: AllReduce only, no float32-partials form, no workspace."""
     import ring_allreduce_reduction_virtual_amd as ar
     from ring_allreduce_reduction_virtual_amd import _lib
 

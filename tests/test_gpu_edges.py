@@ -77,7 +77,7 @@ def test_allreduce_shapes_f32_sum(n, length, algo):
     _allreduce_case(n, length, "f32", "sum", algo, seed=n * 7 + length)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
 @pytest.mark.parametrize("dtype,op", [(d, o) for d in ("f32", "bf16", "i32") for o in ("sum", "prod", "min", "max")])
 @pytest.mark.parametrize("n,length", [(3, 1001), (8, 8 * 64 + 5), (17, 4099)])
 def test_allreduce_dtypes_and_ops(n, length, dtype, op, algo):
@@ -91,7 +91,7 @@ def test_special_values(dtype, op, algo):
     _allreduce_case(6, 3001, dtype, op, algo, special=True, seed=5)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
 @pytest.mark.parametrize("n,length", [(1, 5), (2, 3), (4, 4), (5, 1003), (8, 4101), (64, 64 * 9 + 5), (128, 300)])
 def test_reduce_scatter_and_all_gather(n, length, dtype, algo):
@@ -114,7 +114,7 @@ def test_reduce_scatter_and_all_gather(n, length, dtype, algo):
         assert same_bits(from_dev(outs[r], dtype), want[r], dtype), f"rank {r}"
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_in_place(dtype, algo):
     import torch
@@ -149,7 +149,7 @@ def test_in_place(dtype, algo):
         assert same_bits(from_dev(outs[r], dtype), gathered[r], dtype)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("layout", ["common_offset", "mixed_offsets"])
 def test_misaligned_buffers(layout, dtype, algo):

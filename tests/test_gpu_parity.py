@@ -61,7 +61,7 @@ def _check_whole(xs, dtype, op, algo):
 # workloads at sizes the executed schedule finishes in seconds
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
 def test_c1_small_integers_exact(algo):
     w = WORKLOADS["c1"]
     xs = make_inputs(w)
@@ -72,28 +72,28 @@ def test_c1_small_integers_exact(algo):
         assert np.array_equal(from_dev(t, "f32").astype(np.int64), exact)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
 def test_c2_gradient_bucket(algo):
     _check_whole(make_inputs(WORKLOADS["c2"]), "f32", "sum", algo)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
 def test_c3_bf16_reduced_length(algo):
     _check_whole(make_inputs(WORKLOADS["c3"], count=(1 << 18) + 13), "bf16", "sum", algo)
 
 
 @pytest.mark.parametrize("op", ["sum", "min", "max", "prod"])
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
 def test_c4_int32_reduced_length(op, algo):
     _check_whole(make_inputs(WORKLOADS["c4"], count=(1 << 16) + 5), "i32", op, algo)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
 def test_c5_uneven_64_ranks_reduced_length(algo):
     _check_whole(make_inputs(WORKLOADS["c5"], count=64 * 1024 + 7), "f32", "sum", algo)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
 def test_c5_reduce_scatter_and_all_gather_reduced_length(algo):
     import torch
 
