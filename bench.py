@@ -598,7 +598,7 @@ def run_size_sweep(args):
     stream = torch.cuda.current_stream()
     n = 8
     rows = []
-    for k in range(0, 27, 2):
+    for k in range(0, 29, 2):               # 1 element to 2^28 (1 GiB) per rank
         count = 1 << k
         sends = [torch.randn(count, device=dev) for _ in range(n)]
         recvs = [torch.empty(count, device=dev) for _ in range(n)]
@@ -697,8 +697,8 @@ def main():
                     help="instead of the headline line: HBM read-only, write-only, copy and AllReduce-shaped "
                          "probes beside the fused AllReduce (the bound its traffic allows)")
     ap.add_argument("--size-sweep", action="store_true",
-                    help="instead of the headline line: AllReduce time against message size (8 ranks, f32), "
-                         "fused and ring, with an alpha-beta fit")
+                    help="instead of the headline line: AllReduce time against message size (8 ranks, f32, 1 element "
+                         "to 1 GiB per rank), every schedule, with an alpha-beta fit")
     ap.add_argument("--cache-sweep", action="store_true",
                     help="instead of the headline line: the fused AllReduce at 32-512 MiB of inputs and 8, 16, "
                          "64 ranks, per call in a replayed graph (around the bound of its cache-allocating loads)")
