@@ -9,8 +9,10 @@ memory and the stream.
 ``sendbufs`` / ``recvbufs`` are sequences of one tensor per virtual rank.
 ``count`` is always the full per-rank length (see include/ar.h): for
 reduce-scatter the receive tensors hold one chunk each, for all-gather the
-send tensors do.  ``algo`` is one of "fused", "ring", "phases", "auto";
-``op`` one of "sum", "prod", "min", "max", "avg".  The element type follows
+send tensors do.  ``algo`` names an ``ar_algo_t`` in lower case ("fused",
+"ring", "phases", "auto", "ring_persistent", "ring_pipelined", and the tree
+orders "tree", "tree_steps", "recursive_doubling", "halving_doubling",
+"halving_doubling_steps"); ``op`` one of "sum", "prod", "min", "max", "avg".  The element type follows
 the tensors (float32, bfloat16, float16, int32); ``dtype="bf16acc32"`` with
 bfloat16 tensors keeps the partial sums in float32.
 
@@ -183,9 +185,10 @@ def ar_allreduce_ex(sendbufs, recvbufs=None, op: str = "sum", algo: str = "fused
                     dtype=None):
     """AllReduce with the algorithm chosen by the caller; in place when recvbufs is None.
 
-    Algorithms that keep float32 partials between launches (the ring, and the
-    staged tree algorithms, for bf16acc32) need a workspace; when none is
-    given one is taken from torch's allocator on the stream of the call.
+    Algorithms that keep float32 partials between steps (the ring, launched
+    per step or pipelined, and the staged tree algorithms, for bf16acc32)
+    need a workspace; when none is given one is taken from torch's allocator
+    on the stream of the call.
     """
     recvbufs = sendbufs if recvbufs is None else recvbufs
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
@@ -214,8 +217,9 @@ def ar_reduce_scatter_ex(sendbufs, recvbufs, op: str = "sum", algo: str = "fused
                          dtype=None):
     """Reduce-scatter with the algorithm chosen by the caller.
 
-    The ring algorithm needs a workspace (ar_workspace_bytes); when none is
-    given one is taken from torch's allocator on the stream of the call.
+    The ring algorithms ("ring", "ring_pipelined") need a workspace
+    (ar_workspace_bytes); when none is given one is taken from torch's
+    allocator on the stream of the call.
     """
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
     count = _check_counts("reduce_scatter", sendbufs, recvbufs)
@@ -284,6 +288,9 @@ class Plan:
         _lib.check("ar_plan_limit_blocks", _lib.lib().ar_plan_limit_blocks(self._handle, int(max_blocks)))
 
     def close(self):
+        """Free the plan and drop its references to the tensors.  Work it has
+        enqueued still reads and writes them: close it after that work has
+        completed, or keep the tensors alive until then."""
         if self._handle is not None:
             _lib.lib().ar_plan_free(self._handle)
             self._handle = None
