@@ -39,7 +39,7 @@ def _small(n, length):
 
 
 @pytest.mark.parametrize("algo,launches", [("fused", lambda n, m: 1), ("phases", lambda n, m: 2),
-                                           ("ring", lambda n, m: 2 * (n - 1)),
+                                           ("ring", lambda n, m: 2 * (n - 1)), ("ring_pipelined", lambda n, m: 1),
                                            ("auto", lambda n, m: 1 if n < 24 or _small(n, m) or m * 4 < (4 << 20) else 2)])
 @pytest.mark.parametrize("n,length", [(5, 1003), (8, 8 * 4096 + 5), (32, 32 * 257 + 3), (32, 32 * 4100 + 3),
                                       (24, (1 << 20) + 3)])
@@ -66,7 +66,7 @@ def test_allreduce_plan_matches_and_follows_inputs(n, length, algo, launches):
     plan.close()
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "ring_pipelined"])
 def test_phase_plans(algo):
     import torch
 
@@ -79,8 +79,8 @@ def test_phase_plans(algo):
     outs = [torch.empty(length, dtype=torch.bfloat16, device="cuda:0") for _ in range(n)]
     rs = ar.ar_reduce_scatter_init(sends, shards, algo=algo)
     ag = ar.ar_all_gather_init(shards, outs, algo=algo)
-    assert rs.num_launches == (1 if algo == "fused" else n - 1)
-    assert ag.num_launches == (1 if algo == "fused" else n)
+    assert rs.num_launches == (n - 1 if algo == "ring" else 1)
+    assert ag.num_launches == (n if algo == "ring" else 1)
     ar.ar_plan_start(rs)
     ar.ar_plan_start(ag)
     torch.cuda.synchronize()
@@ -91,7 +91,7 @@ def test_phase_plans(algo):
     ar.ar_plan_free(ag)
 
 
-@pytest.mark.parametrize("algo", ["fused", "phases", "ring"])
+@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined"])
 def test_graph_capture_replays(algo):
     """Capture 3 starts of a plan in a HIP graph; replay it 4 times with eager input
     changes in between, checking every replay against the oracle."""
@@ -126,7 +126,8 @@ def test_graph_capture_replays(algo):
             assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32"), (rep, r)
 
 
-@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "tree", "tree_steps", "halving_doubling_steps"])
+@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined", "tree", "tree_steps",
+                                  "halving_doubling_steps"])
 def test_block_limits_keep_the_bits(algo):
     """A plan capped at 1, 3, 64 blocks (the kernels stride over their tiles), then
     uncapped again, gives the oracle's bits every time."""
@@ -139,7 +140,7 @@ def test_block_limits_keep_the_bits(algo):
     xs = _draw(n, length, seed=21)
     sends = [to_dev(x, "f32") for x in xs]
     recvs = [torch.empty(length, device="cuda:0") for _ in range(n)]
-    if algo in ("fused", "phases", "ring"):
+    if algo in ("fused", "phases", "ring", "ring_pipelined"):
         want, _ = oracle.ring_allreduce(xs)
     else:
         want, _ = order_allreduce({"tree": "tree", "tree_steps": "tree",
