@@ -151,35 +151,57 @@ def _to_device(x, dtype, dev):
     return torch.from_numpy(x).to(dev)
 
 
-def _sampled_parity(xs, outs, dtype, op, positions):
-    """Outputs at chosen positions against the oracle's fold there (all ranks)."""
-    import numpy as np
-    import torch
-
+def cpu_baseline_headline(xs, s_bytes):
+    """The headline line's cpu_baseline: the oracle's executed ring schedule on the
+    whole workload, single-threaded (up to 3 runs or 10 s), and beside it the
+    oracle's one-thread-per-rank ring when the host has a core per rank."""
     import oracle
-    from oracle.ring import chunk_owner, same_bits
+    from oracle.threaded import ring_allreduce_threaded
 
-    n, count = len(xs), len(xs[0])
-    want = oracle.ring_order_fold_columns(np.stack([x[positions] for x in xs]),
-                                          chunk_owner(positions, n, count), op=op, dtype=dtype)
-    idx = torch.from_numpy(positions).to(outs[0].device)
-    for t in outs:
-        got = t[idx].cpu()
-        got = got.view(torch.int16).numpy().view(np.uint16) if dtype in ("bf16", "bf16acc32", "f16") else got.numpy()
-        if not same_bits(got, want, dtype):
-            return False
-    return True
+    n = len(xs)
+    reps, spent = 0, 0.0
+    while reps < 3 and spent < 10.0:
+        t = time.perf_counter()
+        oracle.ring_allreduce(xs, check=False)
+        spent += time.perf_counter() - t
+        reps += 1
+    per = spent / reps
+    cpu = {"value": round(s_bytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"the whole workload ({n} ranks x {len(xs[0])} f32) through the oracle's executed ring schedule, "
+                     f"{reps} run(s), {per:.2f} s each, single-threaded numpy; host {cpu_model()}, "
+                     f"{len(os.sched_getaffinity(0))} cores available"}
+    log(f"[bench] CPU oracle: {per:.2f} s per AllReduce -> algbw {cpu['value']} GB/s (1 core)")
+    # numpy releases the GIL in its array work, so the threads overlap
+    if min(n, len(os.sched_getaffinity(0))) == n:
+        t = time.perf_counter()
+        ring_allreduce_threaded(xs, timeout=600.0)
+        tt = time.perf_counter() - t
+        cpu["threaded"] = {"value": round(s_bytes / tt / 1e9, 4), "unit": "GB/s", "threads": n,
+                           "sample": f"the same workload, one thread per rank, 1 run of {tt:.2f} s"}
+        log(f"[bench] CPU oracle, one thread per rank: {tt:.2f} s -> algbw {cpu['threaded']['value']} GB/s")
+    return cpu
+
+
+def cpu_baseline_on_prefix(xs, op, dtype, sample):
+    """Seconds the oracle's executed ring schedule takes on the first `sample`
+    elements of every rank, single-threaded: the CPU baseline beside each
+    workload.  With cpu_baseline_headline, the only use bench.py makes of the
+    oracle: parity is the GPU tests' job."""
+    import oracle
+
+    t0 = time.perf_counter()
+    oracle.ring_allreduce([x[:sample] for x in xs], op=op, dtype=dtype, check=False)
+    return time.perf_counter() - t0
 
 
 def run_configs(args):
-    """Every workload, fused and ring, timed per call (median of K), with sampled parity."""
-    import numpy as np
+    """Every workload with every ring-order algorithm, timed per call (median of K), with
+    the CPU oracle timed on a bounded prefix beside it.  Parity at these sizes is
+    checked by the GPU tests (tests/test_gpu_parity.py), not here."""
     import torch
 
-    import oracle
     import ring_allreduce_reduction_virtual_amd as ar
     from inputs import WORKLOADS, make_inputs
-    from oracle.ring import chunk
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -194,21 +216,13 @@ def run_configs(args):
         xs = make_inputs(w)
         sends = [_to_device(x, dt, dev) for x in xs]
         recvs = [torch.empty(count, dtype=tdt[dt], device=dev) for _ in range(n)]
-        rng = np.random.default_rng(7)
-        pos = np.unique(np.concatenate([rng.integers(0, count, 1024)] +
-                                       [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1])
-                                        for c in range(n) if chunk(c, n, count)[1] > chunk(c, n, count)[0]]))
-        # the oracle's executed schedule on a bounded prefix of the workload, single-threaded
         sample = min(count, 1 << 20)
-        t0 = time.perf_counter()
-        oracle.ring_allreduce([x[:sample] for x in xs], op=w.ops[0], dtype=dt, check=False)
-        oracle_s = time.perf_counter() - t0
+        oracle_s = cpu_baseline_on_prefix(xs, w.ops[0], dt, sample)
         steps = 200 if s_bytes < (1 << 24) else 20
         for op in w.ops:
             for algo in ("fused", "phases", "ring", "ring_pipelined"):
                 fn = (lambda: ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo))
                 med, mn = median_call_ms(fn, steps, 3, stream)
-                ok = _sampled_parity(xs, recvs, dt, op, pos)
                 algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
                 latency = {}
                 if s_bytes * n <= (64 << 20):
@@ -225,12 +239,11 @@ def run_configs(args):
                     "busbw_gbps": round(s_bytes / (med / 1e3) / 1e9 * busbw_factor("allreduce", n), 2),
                     "hbm_gbps_of_minimum": round(algo_bytes / (med / 1e3) / 1e9, 1),
                     "hbm_frac": round(algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
-                    "parity_sampled": "pass" if ok else "fail",
                     "oracle_s_on_prefix": round(oracle_s, 3), "oracle_prefix_elems": sample, "oracle_cores": 1,
                 }), flush=True)
         if "reduce_scatter" in w.phases:
-            shards = [torch.empty(chunk(r, n, count)[1] - chunk(r, n, count)[0], dtype=tdt[dt], device=dev)
-                      for r in range(n)]
+            shards = [torch.empty(ar.ar_chunk_range(r, count, n)[1] - ar.ar_chunk_range(r, count, n)[0],
+                                  dtype=tdt[dt], device=dev) for r in range(n)]
             rs_bytes = algorithmic_bytes("reduce_scatter", n, s_bytes)
             for algo in ("fused", "ring", "ring_pipelined"):
                 med, mn = median_call_ms(lambda: ar.ar_reduce_scatter_ex(sends, shards, algo=algo), steps, 3, stream)
@@ -258,19 +271,19 @@ def run_configs(args):
 def run_variants(args):
     """The precision and operator variants at full size: the bf16 workload (8 x 2^26)
     with float32 partials and with avg, the headline workload with avg, and
-    an 8 x 2^26 binary16 AllReduce of N(0,1) values; sampled parity each."""
+    an 8 x 2^26 binary16 AllReduce of N(0,1) values.  Parity at these sizes is
+    checked by the GPU tests (tests/test_gpu_variants.py), not here."""
     import numpy as np
     import torch
 
     import ring_allreduce_reduction_virtual_amd as ar
     from inputs import WORKLOADS, make_inputs
-    from oracle.ring import chunk, f32_to_f16_bits
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     c3 = make_inputs(WORKLOADS["c3"])
     head = make_inputs(WORKLOADS["headline"])
-    f16 = [f32_to_f16_bits(x) for x in head]          # the headline draws, rounded to binary16
+    f16 = [x.astype(np.float16).view(np.uint16) for x in head]   # the headline draws, rounded to binary16
     cases = [("c3 8 x 2^26 bf16", c3, "bf16acc32", "sum", torch.bfloat16),
              ("c3 8 x 2^26 bf16", c3, "bf16acc32", "avg", torch.bfloat16),
              ("c3 8 x 2^26 bf16", c3, "bf16", "avg", torch.bfloat16),
@@ -284,58 +297,33 @@ def run_variants(args):
             sends = [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(tdt) for x in xs]
         recvs = [torch.empty(count, dtype=tdt, device=dev) for _ in range(n)]
         s_bytes = count * sends[0].element_size()
-        rng = np.random.default_rng(3)
-        pos = np.unique(np.concatenate([rng.integers(0, count, 1024)] +
-                                       [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1]) for c in range(n)]))
         for algo in ("fused", "phases", "ring", "ring_pipelined"):
             med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo, dtype=dt), 20, 3, stream)
-            ok = _sampled_parity(xs, recvs, dt, op, pos)
             algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
             print(json.dumps({"workload": label, "dtype": dt, "op": op, "algo": algo, "nranks": n, "count": count,
                               "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
                               "algbw_gbps": round(s_bytes / (med / 1e3) / 1e9, 2),
                               "busbw_gbps": round(s_bytes / (med / 1e3) / 1e9 * busbw_factor("allreduce", n), 2),
                               "hbm_gbps_of_minimum": round(algo_bytes / (med / 1e3) / 1e9, 1),
-                              "hbm_frac": round(algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
-                              "parity_sampled": "pass" if ok else "fail"}), flush=True)
+                              "hbm_frac": round(algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}), flush=True)
         del sends, recvs
         torch.cuda.empty_cache()
 
 
-# the algorithms that fold in the ring's association order (the ring's bits)
-RING_ORDER_ALGOS = ("fused", "phases", "ring", "ring_persistent", "ring_pipelined")
-
-
 def run_orders(args):
-    """The tree-shaped orders beside the ring: full workloads timed with sampled
-    parity against the bracketing's evaluation, and small messages timed as
-    one-shot calls, persistent plans and HIP graph replays (the latency
-    regime, where the pages expect 2 log2 N stages to beat the ring's 2(N-1))."""
-    import numpy as np
+    """The tree-shaped orders beside the ring: full workloads timed, and small
+    messages timed as one-shot calls, persistent plans and HIP graph replays
+    (the latency regime, where the pages expect 2 log2 N stages to beat the
+    ring's 2(N-1)).  Parity of every order at these sizes is checked by the
+    GPU tests (tests/test_gpu_orders.py, tests/test_gpu_persistent.py)."""
     import torch
 
     import ring_allreduce_reduction_virtual_amd as ar
     from inputs import WORKLOADS, make_inputs
-    from oracle.orders import order_bracketing, tree_order_fold_columns
-    from oracle.ring import chunk, same_bits
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}
-    order_of = {"tree": "tree", "tree_steps": "tree", "recursive_doubling": "recursive_doubling",
-                "halving_doubling": "halving_doubling", "halving_doubling_steps": "halving_doubling"}
-
-    def parity(xs, outs, dt, algo, pos):
-        want = tree_order_fold_columns(np.stack([x[pos] for x in xs]), order_bracketing(order_of[algo], len(xs)),
-                                       "sum", dt)
-        idx = torch.from_numpy(pos).to(dev)
-        for t in outs:
-            got = t[idx].cpu()
-            got = got.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else got.numpy()
-            if not same_bits(got, want, dt):
-                return False
-        return True
-
     for name in ("headline", "c3", "c4", "c5"):
         w = WORKLOADS[name]
         n, count, dt = w.nranks, w.count, w.dtype
@@ -343,21 +331,15 @@ def run_orders(args):
         sends = [_to_device(x, dt, dev) for x in xs]
         recvs = [torch.empty(count, dtype=tdt[dt], device=dev) for _ in range(n)]
         s_bytes = count * sends[0].element_size()
-        rng = np.random.default_rng(9)
-        pos = np.unique(np.concatenate([rng.integers(0, count, 1024)] +
-                                       [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1]) for c in range(n)]))
         for algo in ("fused", "ring", "ring_persistent", "ring_pipelined", "tree", "halving_doubling", "tree_steps",
                      "recursive_doubling", "halving_doubling_steps"):
             med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 10, 2, stream)
-            ok = (_sampled_parity(xs, recvs, dt, "sum", pos) if algo in RING_ORDER_ALGOS
-                  else parity(xs, recvs, dt, algo, pos))
             algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
             print(json.dumps({"orders": name, "algo": algo, "dtype": dt, "nranks": n, "count": count,
                               "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
                               "algbw_gbps": round(s_bytes / (med / 1e3) / 1e9, 2),
                               "hbm_gbps_of_minimum": round(algo_bytes / (med / 1e3) / 1e9, 1),
-                              "hbm_frac": round(algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
-                              "parity_sampled": "pass" if ok else "fail"}), flush=True)
+                              "hbm_frac": round(algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}), flush=True)
         del sends, recvs, xs
         torch.cuda.empty_cache()
 
@@ -689,7 +671,7 @@ def main():
                          "(float32 partials for bf16, avg, binary16) at full size, one JSON line each")
     ap.add_argument("--orders", action="store_true",
                     help="instead of the headline line: the tree-shaped orders beside the ring at full size "
-                         "(sampled parity) and in the latency regime (one-shot, plan, graph)")
+                         "and in the latency regime (one-shot, plan, graph)")
     ap.add_argument("--interference", action="store_true",
                     help="instead of the headline line: the fused AllReduce overlapping a bf16 GEMM, "
                          "with the AllReduce's workgroups capped at several sizes")
@@ -773,18 +755,6 @@ def main():
     log(f"[bench] fused AllReduce: {ms * 1e3:.1f} us/call (wall {wall_ms * 1e3:.1f} us), algbw {algbw:.1f} GB/s, "
         f"busbw {busbw:.1f} GB/s, HBM {hbm_gbps:.0f} GB/s = {hbm_gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s")
 
-    # parity of the timed output: sampled positions against the oracle's fold
-    import oracle
-    from oracle.ring import chunk, chunk_owner, same_bits
-
-    rng = np.random.default_rng(12345)
-    pos = np.unique(np.concatenate([rng.integers(0, count, 2048)] +
-                                   [np.array([chunk(c, n, count)[0], chunk(c, n, count)[1] - 1]) for c in range(n)]))
-    want = oracle.ring_order_fold_columns(np.stack([x[pos] for x in xs]), chunk_owner(pos, n, count))
-    idx = torch.from_numpy(pos).to(dev)
-    parity = all(same_bits(recvs[r][idx].cpu().numpy(), want, "f32") for r in range(n))
-    log(f"[bench] parity against the oracle at {len(pos)} sampled positions: {'pass' if parity else 'FAIL'}")
-
     extra = {"wall_ms_per_step": round(wall_ms, 4)}
     if not args.no_extra:
         # the step-faithful ring mode and the phases alone, on the same buffers
@@ -796,7 +766,7 @@ def main():
                              max(3, args.steps // 10), 1, stream)
         extra["ring_pipelined_ms"] = round(pipe_ms, 4)
         extra["ring_pipelined_hbm_gbps_of_minimum"] = round(algo_bytes / (pipe_ms / 1e3) / 1e9, 1)
-        shards = [recvs[r][slice(*chunk(r, n, count))] for r in range(n)]
+        shards = [recvs[r][slice(*ar.ar_chunk_range(r, count, n))] for r in range(n)]
         rs_ms = time_calls(lambda: ar.ar_reduce_scatter(sends, shards), 20, 2, stream)
         ag_ms = time_calls(lambda: ar.ar_all_gather(shards, sends), 20, 2, stream)
         rs_bytes = algorithmic_bytes("reduce_scatter", n, s_bytes)
@@ -835,31 +805,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        reps, spent = 0, 0.0
-        while reps < 3 and spent < 10.0:
-            t = time.perf_counter()
-            oracle.ring_allreduce(xs, check=False)
-            spent += time.perf_counter() - t
-            reps += 1
-        per = spent / reps
-        cpu = {"value": round(s_bytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"the whole workload (8 ranks x 2^26 f32) through the oracle's executed ring schedule, "
-                         f"{reps} run(s), {per:.2f} s each, single-threaded numpy; host {cpu_model()}, "
-                         f"{len(os.sched_getaffinity(0))} cores available"}
-        log(f"[bench] CPU oracle: {per:.2f} s per AllReduce -> algbw {cpu['value']} GB/s (1 core)")
-        # beside it, the oracle's one-thread-per-rank ring (numpy releases the GIL in its array work)
-        from oracle.threaded import ring_allreduce_threaded
-
-        threads = min(n, len(os.sched_getaffinity(0)))
-        if threads == n:
-            t = time.perf_counter()
-            ring_allreduce_threaded(xs, timeout=600.0)
-            tt = time.perf_counter() - t
-            cpu["threaded"] = {"value": round(s_bytes / tt / 1e9, 4), "unit": "GB/s", "threads": n,
-                               "sample": f"the same workload, one thread per rank, 1 run of {tt:.2f} s"}
-            log(f"[bench] CPU oracle, one thread per rank: {tt:.2f} s -> algbw {cpu['threaded']['value']} GB/s")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_headline(xs, s_bytes)
 
     traffic = measured_traffic(algo_bytes)
     out = {
@@ -886,12 +832,9 @@ def main():
                      "kernel": "k_fused_allreduce<f32,sum,vec16>",
                      "algorithmic_bytes_per_launch": algo_bytes},
         "cpu_baseline": cpu,
-        "parity": "pass" if parity else "fail",
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
-    if not parity:
-        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -153,6 +153,23 @@ def test_product_and_oracle_do_not_import_each_other():
             assert not re.search(r"^\s*(from|import)\s+inputs\b", src, flags=re.M), f
 
 
+def test_bench_uses_the_oracle_only_for_its_cpu_baseline():
+    """bench.py imports the oracle only inside its cpu_baseline_* functions, which
+    time it; results are checked by the GPU tests, never by the benchmark."""
+    import ast
+
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    allowed = set()
+    for fn in ast.walk(tree):
+        if isinstance(fn, ast.FunctionDef) and fn.name.startswith("cpu_baseline_"):
+            allowed.update(id(n) for n in ast.walk(fn))
+    for node in ast.walk(tree):
+        names = ([a.name for a in node.names] if isinstance(node, ast.Import)
+                 else [node.module or ""] if isinstance(node, ast.ImportFrom) else [])
+        if any(n == "oracle" or n.startswith("oracle.") for n in names):
+            assert id(node) in allowed, f"bench.py imports the oracle at line {node.lineno}"
+
+
 def test_input_generators_are_seeded_and_prefix_stable():
     from inputs import WORKLOADS, make_inputs, make_rank
 

@@ -10,8 +10,9 @@ integer work and min/max are exact anyway.
 * at the full sizes (launch configuration as in the benchmark): sampled
   positions against the oracle's fold at those positions (random positions
   plus every chunk's edges), and properties that hold at any size: all ranks
-  bit-identical, fused == ring bit for bit, int32 results equal to their
-  closed forms.
+  bit-identical, every ring-order algorithm (fused, phases, the ring's
+  launches, the pipelined ring) bit for bit equal to the fused result, int32
+  results equal to their closed forms.
 """
 
 import numpy as np
@@ -185,11 +186,26 @@ def test_fused_loads_either_side_of_the_cache_bound(count):
         assert torch.equal(bits(recvs[r]), first), f"rank {r}"
 
 
+def _same_as(reference, sends, dtype, op, algos):
+    """Each algorithm's AllReduce of `sends`, bit for bit equal to `reference` on every rank."""
+    import torch
+
+    ar = _ar()
+    for algo in algos:
+        other = _alloc(len(sends), sends[0].numel(), dtype)
+        ar.ar_allreduce_ex(sends, other, op=op, algo=algo)
+        torch.cuda.synchronize()
+        for r in range(len(sends)):
+            assert torch.equal(bits(other[r]), bits(reference[0])), (algo, r)
+        del other
+
+
 def test_c3_bf16_full_size():
     w = WORKLOADS["c3"]
     xs = make_inputs(w)
-    _, recvs = _run_allreduce(xs, "bf16", "sum", "fused")
+    sends, recvs = _run_allreduce(xs, "bf16", "sum", "fused")
     _sampled_check(xs, recvs, "bf16", "sum", seed=102)
+    _same_as(recvs, sends, "bf16", "sum", ("ring", "ring_pipelined"))
 
 
 @pytest.mark.parametrize("op", ["sum", "min", "max"])
@@ -198,7 +214,7 @@ def test_c4_int32_full_size_closed_forms(op):
 
     w = WORKLOADS["c4"]
     xs = make_inputs(w)
-    _, recvs = _run_allreduce(xs, "i32", op, "fused")
+    sends, recvs = _run_allreduce(xs, "i32", op, "fused")
     st = np.stack(xs)
     if op == "sum":
         want = np.zeros(w.count, np.uint32)
@@ -214,6 +230,7 @@ def test_c4_int32_full_size_closed_forms(op):
     for r in range(1, w.nranks):
         assert torch.equal(recvs[r], recvs[0])
     _sampled_check(xs, recvs, "i32", op, seed=103)
+    _same_as(recvs, sends, "i32", op, ("ring", "ring_pipelined"))
 
 
 def test_c5_full_size_allreduce_reduce_scatter_all_gather():
@@ -234,6 +251,7 @@ def test_c5_full_size_allreduce_reduce_scatter_all_gather():
     for r in range(n):
         assert torch.equal(bits(one_pass[r]), bits(recvs[0])), f"one-pass rank {r}"
     del one_pass
+    _same_as(recvs, sends, "f32", "sum", ("ring", "ring_pipelined"))
     # reduce-scatter: shard c equals chunk c of the AllReduce, bit for bit
     shards = []
     for c in range(n):
@@ -244,6 +262,13 @@ def test_c5_full_size_allreduce_reduce_scatter_all_gather():
     for c in range(n):
         s, e = chunk(c, n, length)
         assert torch.equal(bits(shards[c]), bits(recvs[0][s:e])), f"shard {c}"
+    for algo in ("ring", "ring_pipelined"):
+        other = [torch.empty_like(t) for t in shards]
+        ar.ar_reduce_scatter_ex(sends, other, algo=algo)
+        torch.cuda.synchronize()
+        for c in range(n):
+            assert torch.equal(bits(other[c]), bits(shards[c])), (algo, c)
+        del other
     del sends
     # all-gather of those shards reproduces the AllReduce on every rank
     outs = recvs          # overwrite the AllReduce outputs after keeping one copy
@@ -254,3 +279,10 @@ def test_c5_full_size_allreduce_reduce_scatter_all_gather():
     torch.cuda.synchronize()
     for r in range(n):
         assert torch.equal(bits(outs[r]), bits(keep)), f"rank {r}"
+    for algo in ("ring", "ring_pipelined"):
+        for t in outs:
+            t.zero_()
+        ar.ar_all_gather_ex(shards, outs, algo=algo)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert torch.equal(bits(outs[r]), bits(keep)), (algo, r)

@@ -181,9 +181,16 @@ def test_c3_workload_full_size_with_float32_partials_and_avg():
     idx = torch.from_numpy(pos).to("cuda:0")
     cols = np.stack([x[pos] for x in xs])
     owners = chunk_owner(pos, w.nranks, w.count)
+    other = _empty(w.nranks, w.count, "bf16")
     for dtype, op in (("bf16acc32", "sum"), ("bf16acc32", "avg"), ("bf16", "avg")):
         ar.ar_allreduce(sends, recvs, op=op, dtype=dtype)
         torch.cuda.synchronize()
         want = oracle.ring_order_fold_columns(cols, owners, op=op, dtype=dtype)
         for r in range(w.nranks):
             assert same_bits(_host(recvs[r][idx], dtype), want, dtype), (dtype, op, r)
+        # the ring's launches and the pipelined ring give the same bits everywhere
+        for algo in ("ring", "ring_pipelined"):
+            ar.ar_allreduce_ex(sends, other, op=op, algo=algo, dtype=dtype)
+            torch.cuda.synchronize()
+            for r in range(w.nranks):
+                assert torch.equal(other[r].view(torch.int16), recvs[0].view(torch.int16)), (dtype, op, algo, r)
