@@ -205,6 +205,10 @@ ar_result_t ar_all_gather(const void* const* sendbufs, void* const* recvbufs, si
                           ar_dtype_t dtype, int nranks, hipStream_t stream);
 
 /* The same three collectives with the algorithm chosen by the caller.
+ * Reduce-scatter and all-gather take AR_ALGO_RING (one launch per step) and
+ * AR_ALGO_RING_PIPELINED (the steps in one launch); AR_ALGO_FUSED,
+ * AR_ALGO_PHASES and AR_ALGO_AUTO all mean their fused kernel; the tree
+ * orders and AR_ALGO_RING_PERSISTENT are AllReduce only (AR_ERR_UNSUPPORTED).
  * `workspace` is device memory of at least ar_workspace_bytes(...) bytes
  * owned by the caller (NULL when that size is 0); it must not overlap any
  * buffer and must stay valid until the stream work completes.  Only the ring
