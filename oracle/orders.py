@@ -15,7 +15,7 @@ Sources (the pages on AllReduce algorithms):
   a recursive-doubling all-gather, for a power-of-two number of ranks, with
   2 log2 N latency terms and the ring's 2(N-1)/N * S bandwidth term.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 
 * the tree is the binomial tree rooted at rank 0: in reduction stage k
   (k = 0, 1, ...) rank r with r mod 2^(k+1) = 0 receives the partial of rank

@@ -19,7 +19,7 @@ Sources (the pages on ring AllReduce):
 * "2.1 Collective communication primitives in detail", section 3.5
   (ReduceScatter): rank i keeps the reduced shard i.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 
 * standalone reduce-scatter returns shard c to rank c.  The ring finishes
   chunk c on rank c-1; the oracle takes the finished chunk from there, so
