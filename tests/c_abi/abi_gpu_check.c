@@ -47,8 +47,8 @@ int main(void) {
     }
 
     const ar_algo_t algos[] = {AR_ALGO_FUSED, AR_ALGO_RING, AR_ALGO_PHASES, AR_ALGO_TREE, AR_ALGO_TREE_STEPS,
-                               AR_ALGO_RING_PERSISTENT};
-    const char* names[] = {"fused", "ring", "phases", "tree", "tree_steps", "ring_persistent"};
+                               AR_ALGO_RING_PERSISTENT, AR_ALGO_RING_PIPELINED};
+    const char* names[] = {"fused", "ring", "phases", "tree", "tree_steps", "ring_persistent", "ring_pipelined"};
     for (size_t k = 0; k < sizeof(algos) / sizeof(algos[0]); ++k) {
         if (check_ar(ar_allreduce_ex((const void* const*)send, recv, COUNT, AR_FLOAT32, AR_SUM, N, algos[k], NULL, 0,
                                      stream), names[k]))
@@ -113,6 +113,38 @@ int main(void) {
         }
     }
     printf("reduce_scatter + all_gather ok\n");
+
+    /* the pipelined ring's reduce-scatter keeps its partials in a caller-owned workspace */
+    size_t ws_bytes = ar_workspace_bytes(AR_COLL_REDUCE_SCATTER, AR_ALGO_RING_PIPELINED, COUNT, AR_FLOAT32, N);
+    void* ws = NULL;
+    if (ws_bytes == (size_t)-1 || ws_bytes == 0) {
+        fprintf(stderr, "ar_workspace_bytes: %zu\n", ws_bytes);
+        return 1;
+    }
+    if ((e = hipMalloc(&ws, ws_bytes)) != hipSuccess) return fail_hip(e, "hipMalloc");
+    for (int r = 0; r < N; ++r)
+        if ((e = hipMemset(recv[r], 0, sizeof(float) * COUNT)) != hipSuccess) return fail_hip(e, "hipMemset");
+    if (check_ar(ar_reduce_scatter_ex((const void* const*)send, shard, COUNT, AR_FLOAT32, AR_SUM, N,
+                                      AR_ALGO_RING_PIPELINED, ws, ws_bytes, stream), "rs pipelined"))
+        return 1;
+    if (check_ar(ar_all_gather_ex((const void* const*)shard, recv, COUNT, AR_FLOAT32, N, AR_ALGO_RING_PIPELINED,
+                                  NULL, 0, stream), "ag pipelined"))
+        return 1;
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+    for (int r = 0; r < N; ++r) {
+        e = hipMemcpy(back, recv[r], sizeof(float) * COUNT, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail_hip(e, "hipMemcpy");
+        for (int i = 0; i < COUNT; ++i) {
+            float want = 0.0f;
+            for (int q = 0; q < N; ++q) want += host[q * COUNT + i];
+            if (back[i] != want) {
+                fprintf(stderr, "pipelined rs+ag: rank %d element %d: %g, want %g\n", r, i, back[i], want);
+                return 1;
+            }
+        }
+    }
+    hipFree(ws);
+    printf("pipelined reduce_scatter + all_gather ok\n");
 
     for (int r = 0; r < N; ++r) {
         hipFree(send[r]);
