@@ -131,6 +131,11 @@ def ar_dtype_size(dtype: str) -> int:
     return _lib.lib().ar_dtype_size(_lib.DTYPES[dtype])
 
 
+def ar_get_last_error_detail() -> str:
+    """The calling thread's text for the last failed call into the library ("" if none)."""
+    return _lib.lib().ar_get_last_error_detail().decode()
+
+
 def _check_counts(coll, sendbufs, recvbufs):
     n = len(sendbufs)
     if coll == "allreduce":
@@ -358,6 +363,11 @@ def ar_all_gather_init(sendbufs, recvbufs, algo: str = "fused", workspace=None) 
 def ar_plan_start(plan: Plan, stream=None):
     """Enqueue a persistent collective's kernels (same as ``plan.start``)."""
     plan.start(stream)
+
+
+def ar_plan_num_launches(plan: Plan) -> int:
+    """Kernel launches one start of the plan enqueues (same as ``plan.num_launches``)."""
+    return plan.num_launches
 
 
 def ar_plan_free(plan: Plan):

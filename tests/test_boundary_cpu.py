@@ -153,6 +153,18 @@ def test_product_and_oracle_do_not_import_each_other():
             assert not re.search(r"^\s*(from|import)\s+inputs\b", src, flags=re.M), f
 
 
+def test_binding_has_every_c_name():
+    """The Python binding offers a function of the same name for every entry point ar.h declares."""
+    import ring_allreduce_reduction_virtual_amd as ar
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ar.h")).read(), flags=re.S)
+    declared = set(re.findall(r"\b(ar_[a-z_]+)\s*\(", text))
+    assert declared == set(_lib.EXPORTS)
+    assert all(callable(getattr(ar, name, None)) for name in declared), sorted(
+        n for n in declared if not callable(getattr(ar, n, None)))
+
+
 def test_bench_uses_the_oracle_only_for_its_cpu_baseline():
     """bench.py imports the oracle only inside its cpu_baseline_* functions, which
     time it; results are checked by the GPU tests, never by the benchmark."""
