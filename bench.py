@@ -530,12 +530,13 @@ def run_ceiling(args):
         raise SystemExit("libarprobe.so is not built (python -m ring_allreduce_reduction_virtual_amd.build)")
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    for n, count in ((8, 1 << 26), (16, 1 << 24)):
+    for n, count in ((8, 1 << 26), (16, 1 << 24), (64, 1 << 26)):
         s_bytes = count * 4
         src = [torch.randn(count, device=dev) for _ in range(n)]
         dst = [torch.empty(count, device=dev) for _ in range(n)]
         t = probe_times_us(lib, src, dst, stream)
         t["fused"] = median_call_ms(lambda: ar.ar_allreduce_ex(src, dst, algo="fused"), 20, 3, stream)[0] * 1e3
+        t["phases"] = median_call_ms(lambda: ar.ar_allreduce_ex(src, dst, algo="phases"), 20, 3, stream)[0] * 1e3
         nbytes = n * s_bytes
         bound = t["read"] + t["write"]
         print(json.dumps({
@@ -545,6 +546,7 @@ def run_ceiling(args):
             "copy_us": round(t["copy"], 1), "copy_gbps": round(2 * nbytes / t["copy"] / 1e3, 1),
             "mix_us": round(t["mix"], 1), "mix_gbps": round(2 * nbytes / t["mix"] / 1e3, 1),
             "fused_allreduce_us": round(t["fused"], 1), "fused_allreduce_gbps": round(2 * nbytes / t["fused"] / 1e3, 1),
+            "phases_allreduce_us": round(t["phases"], 1),
             "bound_read_plus_write_us": round(bound, 1),
             "bound_frac_of_8tbps": round(2 * nbytes / bound / 1e3 / HBM_PEAK_GBPS, 4),
             "fused_frac_of_bound": round(bound / t["fused"], 4),

@@ -20,7 +20,7 @@
 //   src, dst: n device pointers each, 16-byte aligned, nvec vectors long
 //   (dst unused by kind 0, src by kind 1); sink: 16 bytes of device memory
 //   (kind 0 writes it only if the xor of everything read hits one fixed
-//   value, which keeps the loads alive); n in [1, 16]; nvec a multiple of
+//   value, which keeps the loads alive); n in [1, 128]; nvec a multiple of
 //   512.  Returns 0 on success, 1 for bad arguments, 2 for a launch error.
 
 #include <hip/hip_runtime.h>
@@ -31,7 +31,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kProbeMax = 16;
+constexpr int kProbeMax = 128;   // two tables of 128 pointers: 2 KiB of kernel arguments
 constexpr int kThreads = 256;
 constexpr int kPerThread = 2;
 constexpr uint64_t kTile = kThreads * kPerThread;   // vectors per buffer per block
