@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark: ring AllReduce of 8 virtual ranks x 2^26 float32 (sum) on one MI355X.
 
-One step is one AllReduce through the fused one-pass kernel (the library's
-default algorithm) on synthetic N(0,1) inputs already resident in HBM.
-Prints one JSON line with algbw (S/t, the value), busbw (algbw * 2(N-1)/N),
-the kernel's HBM roofline and the CPU oracle timed on this host.
+One step is one AllReduce through the library's default algorithm, which
+for this shape is the staged form (per segment, a reducing launch into rank
+0, then a broadcasting launch), on synthetic N(0,1) inputs already resident
+in HBM.  Prints one JSON line with algbw (S/t, the value), busbw
+(algbw * 2(N-1)/N), the HBM roofline of the call's kernels, the fused
+one-pass kernel's time beside it, and the CPU oracle timed on this host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -28,8 +30,8 @@ if ROOT not in sys.path:
 
 METRIC = "AllReduce algbw/busbw GB/s + % HBM peak, N=8 ranks x 64M fp32, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "fused_allreduce_headline_counters.md")
-# the sources the fused AllReduce kernel is built from (its counters are only
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "staged_allreduce_headline_counters.md")
+# the sources the AllReduce kernels are built from (their counters are only
 # used while these are unchanged)
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_reduction_virtual_amd", "csrc", f)
                   for f in ("ar_kernels.hip", "ar_device.h", "ar_internal.h")]
@@ -58,9 +60,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(per_launch_algo_bytes: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+def measured_traffic():
+    """HBM bytes per call (all the call's launches) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source;
+    else None."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     text = open(COUNTERS_FILE).read()
@@ -70,7 +73,7 @@ def measured_traffic(per_launch_algo_bytes: int):
     d = json.loads(m.group(1))
     if d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return d.get("bytes_per_launch")
+    return d.get("bytes_per_call")
 
 
 def ensure_library():
@@ -220,7 +223,7 @@ def run_configs(args):
         oracle_s = cpu_baseline_on_prefix(xs, w.ops[0], dt, sample)
         steps = 200 if s_bytes < (1 << 24) else 20
         for op in w.ops:
-            for algo in ("fused", "phases", "ring", "ring_pipelined"):
+            for algo in ("fused", "staged", "phases", "auto", "ring", "ring_pipelined"):
                 fn = (lambda: ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo))
                 med, mn = median_call_ms(fn, steps, 3, stream)
                 algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
@@ -297,7 +300,7 @@ def run_variants(args):
             sends = [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(tdt) for x in xs]
         recvs = [torch.empty(count, dtype=tdt, device=dev) for _ in range(n)]
         s_bytes = count * sends[0].element_size()
-        for algo in ("fused", "phases", "ring", "ring_pipelined"):
+        for algo in ("fused", "staged", "phases", "ring", "ring_pipelined"):
             med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo, dtype=dt), 20, 3, stream)
             algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
             print(json.dumps({"workload": label, "dtype": dt, "op": op, "algo": algo, "nranks": n, "count": count,
@@ -537,6 +540,7 @@ def run_ceiling(args):
         t = probe_times_us(lib, src, dst, stream)
         t["fused"] = median_call_ms(lambda: ar.ar_allreduce_ex(src, dst, algo="fused"), 20, 3, stream)[0] * 1e3
         t["phases"] = median_call_ms(lambda: ar.ar_allreduce_ex(src, dst, algo="phases"), 20, 3, stream)[0] * 1e3
+        t["staged"] = median_call_ms(lambda: ar.ar_allreduce_ex(src, dst, algo="staged"), 20, 3, stream)[0] * 1e3
         nbytes = n * s_bytes
         bound = t["read"] + t["write"]
         print(json.dumps({
@@ -547,6 +551,8 @@ def run_ceiling(args):
             "mix_us": round(t["mix"], 1), "mix_gbps": round(2 * nbytes / t["mix"] / 1e3, 1),
             "fused_allreduce_us": round(t["fused"], 1), "fused_allreduce_gbps": round(2 * nbytes / t["fused"] / 1e3, 1),
             "phases_allreduce_us": round(t["phases"], 1),
+            "staged_allreduce_us": round(t["staged"], 1),
+            "staged_frac_of_bound": round(bound / t["staged"], 4),
             "bound_read_plus_write_us": round(bound, 1),
             "bound_frac_of_8tbps": round(2 * nbytes / bound / 1e3 / HBM_PEAK_GBPS, 4),
             "fused_frac_of_bound": round(bound / t["fused"], 4),
@@ -741,6 +747,21 @@ def main():
     def step():
         ar.ar_allreduce(sends, recvs)
 
+    # which form the library's default (AR_ALGO_AUTO) takes here: compare its
+    # plan with the staged one (2 launches per segment) and the fused one (1)
+    launches = {}
+    for name in ("auto", "staged", "fused"):
+        plan = ar.ar_allreduce_init(sends, recvs, algo=name)
+        launches[name] = plan.num_launches
+        plan.close()
+    default_algo = "staged" if launches["auto"] == launches["staged"] and launches["staged"] > 1 else "fused"
+    if default_algo == "staged":
+        segments = launches["staged"] // 2
+        kernel_name = (f"k_staged_reduce<f32,sum,vec16> + k_staged_broadcast<f32,vec16>, "
+                       f"{segments} segments of {s_bytes // segments >> 20} MiB of results")
+    else:
+        kernel_name = "k_fused_allreduce<f32,sum,vec16>"
+
     # timed region: K AllReduce calls, synchronized on both sides
     ms = time_calls(step, args.steps, args.warmup, stream)
     torch.cuda.synchronize()
@@ -754,11 +775,17 @@ def main():
     busbw = algbw * busbw_factor("allreduce", n)
     algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
     hbm_gbps = algo_bytes / t_s / 1e9
-    log(f"[bench] fused AllReduce: {ms * 1e3:.1f} us/call (wall {wall_ms * 1e3:.1f} us), algbw {algbw:.1f} GB/s, "
+    log(f"[bench] AllReduce ({default_algo}, {launches['auto']} launches): {ms * 1e3:.1f} us/call "
+        f"(wall {wall_ms * 1e3:.1f} us), algbw {algbw:.1f} GB/s, "
         f"busbw {busbw:.1f} GB/s, HBM {hbm_gbps:.0f} GB/s = {hbm_gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s")
 
     extra = {"wall_ms_per_step": round(wall_ms, 4)}
     if not args.no_extra:
+        # the one-pass fused kernel on the same buffers
+        fused_ms = time_calls(lambda: ar.ar_allreduce_ex(sends, recvs, algo="fused"), max(10, args.steps // 2), 2,
+                              stream)
+        extra["fused_ms"] = round(fused_ms, 4)
+        extra["fused_hbm_frac_of_peak"] = round(algo_bytes / (fused_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)
         # the step-faithful ring mode and the phases alone, on the same buffers
         ring_ms = time_calls(lambda: ar.ar_allreduce_ex(sends, recvs, algo="ring"), max(3, args.steps // 10), 1, stream)
         extra["ring_mode_ms"] = round(ring_ms, 4)
@@ -791,9 +818,10 @@ def main():
                 "read_plus_write_us": round(pt["read"] + pt["write"], 1),
                 "read_plus_write_frac_of_8tbps": round(algo_bytes / (pt["read"] + pt["write"]) / 1e3 / HBM_PEAK_GBPS, 4),
                 "mix_probe_us": round(pt["mix"], 1),
-                "fused_frac_of_read_plus_write": round((pt["read"] + pt["write"]) / (ms * 1e3), 4),
-                "fused_speed_vs_mix_probe": round(pt["mix"] / (ms * 1e3), 4)}
-        log(f"[bench] ring mode {ring_ms:.3f} ms; pipelined ring {pipe_ms:.3f} ms; reduce-scatter {rs_ms:.3f} ms; "
+                "allreduce_frac_of_read_plus_write": round((pt["read"] + pt["write"]) / (ms * 1e3), 4),
+                "allreduce_speed_vs_mix_probe": round(pt["mix"] / (ms * 1e3), 4)}
+        log(f"[bench] fused {fused_ms:.3f} ms; ring mode {ring_ms:.3f} ms; pipelined ring {pipe_ms:.3f} ms; "
+            f"reduce-scatter {rs_ms:.3f} ms; "
             f"all-gather {ag_ms:.3f} ms; "
             f"torch copy {extra['torch_copy_2x2GiB_hbm_gbps']} GB/s")
         # restore the inputs overwritten by the all-gather above
@@ -809,7 +837,7 @@ def main():
 
     cpu = None if args.no_cpu_baseline else cpu_baseline_headline(xs, s_bytes)
 
-    traffic = measured_traffic(algo_bytes)
+    traffic = measured_traffic()
     out = {
         "metric": METRIC,
         "value": round(algbw, 2),
@@ -823,16 +851,18 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "ring AllReduce, 8 virtual ranks x 2^26 float32 (256 MiB each), sum, fused kernel",
-                   "nranks": n, "count": count, "op": "sum", "algo": "fused", "inputs": "N(0,1), seed 1"},
+        "config": {"workload": "ring AllReduce, 8 virtual ranks x 2^26 float32 (256 MiB each), sum, "
+                               "the library's default algorithm",
+                   "nranks": n, "count": count, "op": "sum", "algo": f"auto ({default_algo})",
+                   "inputs": "N(0,1), seed 1"},
         "algbw_gbps": round(algbw, 2),
         "busbw_gbps": round(busbw, 2),
         "hbm_gbps": round(hbm_gbps, 1),
         "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "k_fused_allreduce<f32,sum,vec16>",
-                     "algorithmic_bytes_per_launch": algo_bytes},
+                     "kernel": kernel_name, "launches_per_call": launches["auto"],
+                     "algorithmic_bytes_per_call": algo_bytes},
         "cpu_baseline": cpu,
         "extra": extra,
     }

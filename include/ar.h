@@ -110,9 +110,11 @@ typedef enum {
  *   is copied to every other rank.  (2N+1)*S bytes, S more than the fused
  *   kernel, but the read-heavy and the write-heavy halves run apart, which is
  *   faster on MI355X HBM once N is large.
- * AR_ALGO_AUTO: AR_ALGO_PHASES from AR_PHASES_MIN_RANKS ranks when every
- *   rank holds at least AR_PHASES_MIN_BYTES bytes, AR_ALGO_FUSED otherwise
- *   (AllReduce); the fused kernel for the single phases.
+ * AR_ALGO_AUTO: for AllReduce, AR_ALGO_STAGED for large buffers (the
+ *   AR_STAGED_MIN_* bounds below), else AR_ALGO_PHASES from
+ *   AR_PHASES_MIN_RANKS ranks when every rank holds at least
+ *   AR_PHASES_MIN_BYTES bytes, else AR_ALGO_FUSED; the fused kernel for the
+ *   single phases.
  * These four give the same bits: the ring's association order.
  *
  * The remaining algorithms are AllReduce only (AR_ERR_UNSUPPORTED for
@@ -151,7 +153,19 @@ typedef enum {
  *   carries one slice of one chunk through every step in order, loading the
  *   sender's partial and storing its own, so the steps need no barrier.  The
  *   same bits as AR_ALGO_RING, for all three collectives and every dtype,
- *   with the same workspace as AR_ALGO_RING; can be captured into a graph. */
+ *   with the same workspace as AR_ALGO_RING; can be captured into a graph.
+ * AR_ALGO_STAGED: AllReduce as the reduce-then-broadcast form of the same
+ *   collective ("2.1 Collective communication primitives in detail",
+ *   section 3.8: AllReduce as a reduce followed by a broadcast), cut into
+ *   segments of rank 0's results.  Per segment, one launch
+ *   folds every position in ring order and stores the result to recvbufs[0]
+ *   only, then one launch copies it to the other ranks.  The results
+ *   are reread from the device's 256 MB last-level cache, so HBM still moves
+ *   N*S read and N*S written; the reading and the writing launches run apart,
+ *   which MI355X HBM serves faster than the two interleaved.  The same bits
+ *   as AR_ALGO_FUSED.  AllReduce only; 2 launches per segment.  A segment
+ *   holds about 2 GiB / N of results, between 32 and 128 MiB; the
+ *   AR_STAGE_BYTES environment variable sets it in bytes instead. */
 typedef enum {
     AR_ALGO_FUSED = 0,
     AR_ALGO_RING = 1,
@@ -163,9 +177,19 @@ typedef enum {
     AR_ALGO_HALVING_DOUBLING = 7,
     AR_ALGO_HALVING_DOUBLING_STEPS = 8,
     AR_ALGO_RING_PERSISTENT = 9,
-    AR_ALGO_RING_PIPELINED = 10
+    AR_ALGO_RING_PIPELINED = 10,
+    AR_ALGO_STAGED = 11
 } ar_algo_t;
 
+/* AR_ALGO_AUTO takes AR_ALGO_STAGED for an AllReduce over at least
+ * AR_STAGED_MIN_RANKS ranks of at least AR_STAGED_MIN_BYTES bytes each and at
+ * least AR_STAGED_MIN_TOTAL_BYTES bytes in all (measured on MI355X, float32:
+ * 8 ranks x 256 MiB 736 us against 752 fused; 32 x 64 MiB 786 against 822
+ * for either other form; 64 x 256 MiB 5,944 against 6,271 for the phases;
+ * at 8 x 64 MiB and 16 x 16 MiB the fused kernel is faster). */
+#define AR_STAGED_MIN_RANKS 8
+#define AR_STAGED_MIN_BYTES (64ull << 20)
+#define AR_STAGED_MIN_TOTAL_BYTES (2048ull << 20)
 /* Rank count from which AR_ALGO_AUTO runs an AllReduce as two fused phases
  * (measured crossover on MI355X; the AR_PHASES_MIN_RANKS environment variable
  * overrides it). */

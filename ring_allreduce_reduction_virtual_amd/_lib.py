@@ -18,7 +18,8 @@ RESULT_NAMES = {0: "AR_SUCCESS", 1: "AR_ERR_INVALID_ARGUMENT", 2: "AR_ERR_UNSUPP
 DTYPES = {"f32": 0, "bf16": 1, "i32": 2, "f16": 3, "bf16acc32": 4}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
 ALGOS = {"fused": 0, "ring": 1, "phases": 2, "auto": 3, "tree": 4, "tree_steps": 5, "recursive_doubling": 6,
-         "halving_doubling": 7, "halving_doubling_steps": 8, "ring_persistent": 9, "ring_pipelined": 10}
+         "halving_doubling": 7, "halving_doubling_steps": 8, "ring_persistent": 9, "ring_pipelined": 10,
+         "staged": 11}
 # algorithms whose bracketing is a tree, not the ring's (AllReduce only)
 TREE_ALGOS = ("tree", "tree_steps", "recursive_doubling", "halving_doubling", "halving_doubling_steps")
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}

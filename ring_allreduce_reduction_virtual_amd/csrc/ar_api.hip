@@ -252,12 +252,14 @@ ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, Residue res) {
 }
 
 bool algo_known(ar_algo_t algo) {
-    return algo >= AR_ALGO_FUSED && algo <= AR_ALGO_RING_PIPELINED;
+    return algo >= AR_ALGO_FUSED && algo <= AR_ALGO_STAGED;
 }
 
-// AllReduce-only algorithms: the tree orders and the persistent ring.
+// AllReduce-only algorithms: the tree orders, the persistent ring and the
+// staged reduce-then-broadcast.
 bool allreduce_only_algo(ar_algo_t algo) {
-    return (algo >= AR_ALGO_TREE && algo <= AR_ALGO_HALVING_DOUBLING_STEPS) || algo == AR_ALGO_RING_PERSISTENT;
+    return (algo >= AR_ALGO_TREE && algo <= AR_ALGO_HALVING_DOUBLING_STEPS) || algo == AR_ALGO_RING_PERSISTENT ||
+           algo == AR_ALGO_STAGED;
 }
 
 // The ring's own schedule, step by step: launched per step or pipelined in one launch.
@@ -334,6 +336,21 @@ uint64_t cached_loads_max() {
     return v;
 }
 
+// Bytes of rank 0's results per segment of AR_ALGO_STAGED: about
+// AR_STAGE_READ_BYTES of inputs read per segment, between AR_STAGE_BYTES_MIN
+// and AR_STAGE_BYTES_MAX of results.  The AR_STAGE_BYTES environment variable
+// sets it outright; it is read at every call (plans keep what they were built
+// with), so one process can exercise several segment sizes.
+uint64_t stage_bytes(int nranks) {
+    const char* e = std::getenv("AR_STAGE_BYTES");
+    if (e != nullptr && e[0] != '\0') {
+        const uint64_t b = static_cast<uint64_t>(std::strtoull(e, nullptr, 10));
+        if (b > 0) return b;
+    }
+    const uint64_t b = AR_STAGE_READ_BYTES / static_cast<uint64_t>(nranks);
+    return std::min<uint64_t>(AR_STAGE_BYTES_MAX, std::max<uint64_t>(AR_STAGE_BYTES_MIN, b));
+}
+
 // Rank count from which AR_ALGO_AUTO runs AllReduce as two fused phases.
 int phases_min_ranks() {
     static const int v = [] {
@@ -362,6 +379,8 @@ const char* kind_name(Kind kd) {
         case Kind::kRingPipelinedGather: return "ring_pipelined_gather";
         case Kind::kSmallAllReduce: return "small_allreduce";
         case Kind::kSmallTree: return "small_tree";
+        case Kind::kStagedReduce: return "staged_reduce";
+        case Kind::kStagedBroadcast: return "staged_broadcast";
     }
     return "?";
 }
@@ -544,13 +563,20 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         ptrs.push_back(s);
         ptrs.push_back(d);
     }
-    // AUTO: two fused phases from phases_min_ranks() ranks when every rank
-    // holds at least AR_PHASES_MIN_BYTES; below that the one fused kernel wins
-    // (and the small-message kernel for the smallest messages)
-    if (algo == AR_ALGO_AUTO)
-        algo = (k.n >= phases_min_ranks() && k.count * k.esz >= AR_PHASES_MIN_BYTES && !small_message(k))
-                   ? AR_ALGO_PHASES
-                   : AR_ALGO_FUSED;
+    // AUTO: the staged reduce-then-broadcast for large buffers over 8 ranks or
+    // more; otherwise two fused phases from phases_min_ranks() ranks when every
+    // rank holds at least AR_PHASES_MIN_BYTES; below that the one fused kernel
+    // wins (and the small-message kernel for the smallest messages)
+    if (algo == AR_ALGO_AUTO) {
+        const uint64_t per_rank = k.count * k.esz;
+        if (k.n >= AR_STAGED_MIN_RANKS && per_rank >= AR_STAGED_MIN_BYTES &&
+            per_rank * static_cast<uint64_t>(k.n) >= AR_STAGED_MIN_TOTAL_BYTES)
+            algo = AR_ALGO_STAGED;
+        else if (k.n >= phases_min_ranks() && per_rank >= AR_PHASES_MIN_BYTES && !small_message(k))
+            algo = AR_ALGO_PHASES;
+        else
+            algo = AR_ALGO_FUSED;
+    }
     if (algo == AR_ALGO_RING_PERSISTENT && k.dtype == AR_BFLOAT16_ACC_F32)
         return fail(AR_ERR_UNSUPPORTED, "the persistent ring has no form with float32 partials");
     if (power_of_two_algo(algo) && (k.n & (k.n - 1)) != 0)
@@ -600,6 +626,21 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     if (algo == AR_ALGO_FUSED) {
         l.cached = l.vec && static_cast<uint64_t>(k.n) * k.count * k.esz <= cached_loads_max();
         return sink.emit(l, Kind::kFusedAllReduce, a, k);
+    }
+    if (algo == AR_ALGO_STAGED) {
+        // segments of whole tiles, each holding about stage_bytes() of rank 0's
+        // results: reduce into rank 0, then broadcast from it
+        const uint32_t total = a.tile_end;
+        const uint64_t tile_bytes = static_cast<uint64_t>(arimpl::kThreads) * arimpl::kUnroll * (l.vec ? 16 : k.esz);
+        const uint64_t per_seg = std::max<uint64_t>(1, stage_bytes(k.n) / tile_bytes);
+        for (uint64_t t0 = 0; t0 < total; t0 += per_seg) {
+            a.tile_first = static_cast<uint32_t>(t0);
+            a.tile_end = static_cast<uint32_t>(std::min<uint64_t>(total, t0 + per_seg));
+            if ((rc = grid_for(a, l)) != AR_SUCCESS) return rc;
+            if ((rc = sink.emit(l, Kind::kStagedReduce, a, k)) != AR_SUCCESS) return rc;
+            if ((rc = sink.emit(l, Kind::kStagedBroadcast, a, k)) != AR_SUCCESS) return rc;
+        }
+        return AR_SUCCESS;
     }
     if (algo == AR_ALGO_RING_PERSISTENT) return sink.emit(l, Kind::kRingPersistent, a, k);
     if (algo == AR_ALGO_RING_PIPELINED) {

@@ -202,16 +202,16 @@ __device__ __forceinline__ uint32_t load_elem(const char* p) {
     }
 }
 
-template <int ESZ>
+template <int ESZ, bool NT = AR_NT_STORES>
 __device__ __forceinline__ void store_elem(char* p, uint32_t v) {
     if constexpr (ESZ == 2) {
-        if constexpr (AR_NT_STORES) {
+        if constexpr (NT) {
             __builtin_nontemporal_store(static_cast<uint16_t>(v), reinterpret_cast<uint16_t*>(p));
         } else {
             *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(v);
         }
     } else {
-        if constexpr (AR_NT_STORES) {
+        if constexpr (NT) {
             __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
         } else {
             *reinterpret_cast<uint32_t*>(p) = v;
@@ -228,8 +228,9 @@ __device__ __forceinline__ u32x4 load16(const char* p) {
     }
 }
 
+template <bool NT = AR_NT_STORES>
 __device__ __forceinline__ void store16(char* p, u32x4 v) {
-    if constexpr (AR_NT_STORES) {
+    if constexpr (NT) {
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
     } else {
         *reinterpret_cast<u32x4*>(p) = v;
@@ -274,11 +275,14 @@ struct Unit {
             return load_elem<kEsz>(tb + off);
         }
     }
+    // NT: nontemporal store (the default for outputs, written once) or a
+    // cache-allocating one (a result that a later launch reads back)
+    template <bool NT = AR_NT_STORES>
     static __device__ __forceinline__ void store(char* tb, uint32_t off, T x) {
         if constexpr (VEC > 1) {
-            store16(tb + off, x);
+            store16<NT>(tb + off, x);
         } else {
-            store_elem<kEsz>(tb + off, x);
+            store_elem<kEsz, NT>(tb + off, x);
         }
     }
     template <int OP>

@@ -30,6 +30,8 @@ enum class Kind : int {
     kRingPipelinedGather,  // the all-gather ring in one launch, slice by slice
     kSmallAllReduce,       // the fused AllReduce of a small message, staged through LDS
     kSmallTree,            // kFusedTree for a small message, staged through LDS
+    kStagedReduce,         // kFusedAllReduce for tiles [tile_first, tile_end), stored to rank 0 only
+    kStagedBroadcast,      // copy rank 0's result for tiles [tile_first, tile_end) to every other rank
 };
 
 // Stages of the tree-shaped schedules; at stage `step` the partner distance is d.
@@ -107,6 +109,24 @@ constexpr int kUnroll = AR_TILE_UNROLL;
 // win (2^24 per rank: 186.5 against 197 us).
 #ifndef AR_CACHED_LOADS_MAX_BYTES
 #define AR_CACHED_LOADS_MAX_BYTES (256ull << 20)
+#endif
+
+// AR_ALGO_STAGED: rank 0's results per segment (one reducing and one
+// broadcasting launch each) are about AR_STAGE_READ_BYTES / N bytes, kept
+// between AR_STAGE_BYTES_MIN and AR_STAGE_BYTES_MAX.  The broadcast rereads
+// them, so they should stay in MI355X's 256 MB Infinity Cache between the two
+// launches.  Measured on MI355X, float32, 256 MiB per rank, median us per
+// call, 32 MiB / 128 MiB segments: 8 ranks 740 / 736, 16 ranks 1,513 /
+// 1,519, 32 ranks 2,979 / 3,002, 64 ranks 5,944 / 6,028, 128 ranks 11,701 /
+// 11,728.
+#ifndef AR_STAGE_READ_BYTES
+#define AR_STAGE_READ_BYTES (2048ull << 20)
+#endif
+#ifndef AR_STAGE_BYTES_MIN
+#define AR_STAGE_BYTES_MIN (32ull << 20)
+#endif
+#ifndef AR_STAGE_BYTES_MAX
+#define AR_STAGE_BYTES_MAX (128ull << 20)
 #endif
 
 // Enqueue one kernel; returns the HIP error of the launch.

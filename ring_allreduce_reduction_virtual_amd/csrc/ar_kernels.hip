@@ -65,6 +65,64 @@ __global__ __launch_bounds__(kThreads) void k_fused_allreduce(const KernelArgs a
     AR_TILE_LOOP_END
 }
 
+// Staged AllReduce, reducing launch: the fused AllReduce's fold for the
+// launch's tiles, stored to rank 0's receive buffer only.  The stores allocate
+// in the caches (unlike every other output), so the broadcast launch that
+// follows rereads the results from the Infinity Cache instead of HBM.  This
+// launch is then almost all reads, and the broadcast almost all writes: HBM
+// serves each direction faster alone than the two interleaved.
+template <int DT, int OP, int VEC>
+__global__ __launch_bounds__(kThreads) void k_staged_reduce(const KernelArgs a) {
+    using U = Unit<DT, VEC>;
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            store_elem<ESZ, false>(a.recv[0] + i * ESZ, fold_element<DT, OP>(a, c, i));
+        }
+    }
+    typename Fold<DT, OP, VEC>::A acc[kUnroll];
+    fold_units<DT, OP, VEC>(a, c, adj, tv0, live, acc);
+    char* tb = U::tile(a.recv[0] - adj, tv0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) U::template store<false>(tb, U::lane_off(u), Fold<DT, OP, VEC>::done(acc[u], n));
+    }
+    AR_TILE_LOOP_END
+}
+
+// Staged AllReduce, broadcasting launch: rank 0's results for the same tiles
+// (so the same elements, chunk edges included) copied to ranks 1..N-1.
+template <int DT, int VEC>
+__global__ __launch_bounds__(kThreads) void k_staged_broadcast(const KernelArgs a) {
+    using U = Unit<DT, VEC, false>;   // cache-allocating loads: the results sit in the Infinity Cache
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    const char* src = a.recv[0];
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            const uint32_t x = load_elem<ESZ>(src + i * ESZ);
+            for (int q = 1; q < n; ++q) store_elem<ESZ>(a.recv[q] + i * ESZ, x);
+        }
+    }
+    typename U::T x[kUnroll];
+    const char* sb = U::tile(src - adj, tv0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) x[u] = U::load(sb, U::lane_off(u));
+    }
+    for (int q = 1; q < n; ++q) {
+        char* tb = U::tile(a.recv[q] - adj, tv0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) U::store(tb, U::lane_off(u), x[u]);
+        }
+    }
+    AR_TILE_LOOP_END
+}
+
 // Reduce-scatter: the fold of chunk c goes to rank c's shard only.  Reads N*S,
 // writes S bytes.
 template <int DT, int OP, int VEC>
@@ -274,6 +332,9 @@ hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
         case Kind::kFusedReduceScatter:
             hipLaunchKernelGGL((k_fused_reduce_scatter<DT, OP, VEC>), grid, block, 0, s, a);
             break;
+        case Kind::kStagedReduce:
+            hipLaunchKernelGGL((k_staged_reduce<DT, OP, VEC>), grid, block, 0, s, a);
+            break;
         case Kind::kRingReduceStep:
             if constexpr (acc_f32<DT>()) {
                 return hipErrorInvalidValue;   // float32 partials always take the workspace step
@@ -307,6 +368,9 @@ hipError_t launch_copy(const Launch& l, const KernelArgs& a, hipStream_t s) {
             break;
         case Kind::kRingCopyStep:
             hipLaunchKernelGGL((k_ring_copy_step<DT, VEC>), grid, block, 0, s, a);
+            break;
+        case Kind::kStagedBroadcast:
+            hipLaunchKernelGGL((k_staged_broadcast<DT, VEC>), grid, block, 0, s, a);
             break;
         default:
             return hipErrorInvalidValue;
@@ -348,7 +412,7 @@ hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream) {
         l.kind == Kind::kRingPipelinedGather)
         return launch_persistent(l, a, stream);
     const bool copy = l.kind == Kind::kFusedAllGather || l.kind == Kind::kPlaceShards ||
-                      l.kind == Kind::kRingCopyStep;
+                      l.kind == Kind::kRingCopyStep || l.kind == Kind::kStagedBroadcast;
     if (copy) {
         const bool two_bytes = l.dtype == AR_BFLOAT16 || l.dtype == AR_FLOAT16 || l.dtype == AR_BFLOAT16_ACC_F32;
         return two_bytes ? copy_by_vec<AR_BFLOAT16>(l, a, stream) : copy_by_vec<AR_FLOAT32>(l, a, stream);

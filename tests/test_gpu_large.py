@@ -67,7 +67,7 @@ def test_rank_buffers_beyond_2p31_elements():
     recvs = [torch.empty(count, device="cuda:0") for _ in range(n)]
     edge = 1 << 31
     pos = _positions(n, count, seed=5, extra=range(edge - 5, edge + 5))
-    for algo in ("fused", "phases", "ring", "ring_pipelined"):
+    for algo in ("fused", "phases", "ring", "ring_pipelined", "staged"):
         print(f"[large] {algo}", flush=True)
         for t in recvs:
             t.fill_(-1.0)
@@ -78,7 +78,8 @@ def test_rank_buffers_beyond_2p31_elements():
 
 
 def test_128_ranks_at_a_large_size():
-    """128 ranks x (2^25 + 3) float32 (128 MiB per buffer): the default (two phases) and the one-pass kernel."""
+    """128 ranks x (2^25 + 3) float32 (128 MiB per buffer): the default (the staged form), the two
+    phases and the one-pass kernel."""
     import torch
 
     ar = _ar()
@@ -91,7 +92,9 @@ def test_128_ranks_at_a_large_size():
     torch.cuda.synchronize()
     _check(sends, recvs, pos)
     first = recvs[0].clone()
-    ar.ar_allreduce_ex(sends, recvs, algo="fused")
-    torch.cuda.synchronize()
-    for r in range(n):
-        assert torch.equal(recvs[r], first), f"rank {r}"
+    for algo in ("fused", "phases"):
+        print(f"[large] {algo}", flush=True)
+        ar.ar_allreduce_ex(sends, recvs, algo=algo)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert torch.equal(recvs[r], first), f"{algo} rank {r}"

@@ -11,7 +11,8 @@ integer work and min/max are exact anyway.
   positions against the oracle's fold at those positions (random positions
   plus every chunk's edges), and properties that hold at any size: all ranks
   bit-identical, every ring-order algorithm (fused, phases, the ring's
-  launches, the pipelined ring) bit for bit equal to the fused result, int32
+  launches, the pipelined ring, the staged reduce-then-broadcast) bit for
+  bit equal to the fused result, int32
   results equal to their closed forms.
 """
 
@@ -62,7 +63,7 @@ def _check_whole(xs, dtype, op, algo):
 # workloads at sizes the executed schedule finishes in seconds
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined", "staged"])
 def test_c1_small_integers_exact(algo):
     w = WORKLOADS["c1"]
     xs = make_inputs(w)
@@ -73,23 +74,23 @@ def test_c1_small_integers_exact(algo):
         assert np.array_equal(from_dev(t, "f32").astype(np.int64), exact)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined", "staged"])
 def test_c2_gradient_bucket(algo):
     _check_whole(make_inputs(WORKLOADS["c2"]), "f32", "sum", algo)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined", "staged"])
 def test_c3_bf16_reduced_length(algo):
     _check_whole(make_inputs(WORKLOADS["c3"], count=(1 << 18) + 13), "bf16", "sum", algo)
 
 
 @pytest.mark.parametrize("op", ["sum", "min", "max", "prod"])
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined", "staged"])
 def test_c4_int32_reduced_length(op, algo):
     _check_whole(make_inputs(WORKLOADS["c4"], count=(1 << 16) + 5), "i32", op, algo)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined", "staged"])
 def test_c5_uneven_64_ranks_reduced_length(algo):
     _check_whole(make_inputs(WORKLOADS["c5"], count=64 * 1024 + 7), "f32", "sum", algo)
 
@@ -147,7 +148,7 @@ def test_headline_8_ranks_2p26_float32_full_size():
     xs = make_inputs(w)
     sends, fused = _run_allreduce(xs, "f32", "sum", "fused")
     _sampled_check(xs, fused, "f32", "sum", seed=101)
-    for algo in ("ring", "phases"):
+    for algo in ("ring", "phases", "staged"):
         other = _alloc(w.nranks, w.count, "f32")
         ar.ar_allreduce_ex(sends, other, algo=algo)
         torch.cuda.synchronize()
@@ -242,7 +243,7 @@ def test_c5_full_size_allreduce_reduce_scatter_all_gather():
     xs = make_inputs(w)
     sends = [to_dev(x, "f32") for x in xs]
     recvs = _alloc(n, length, "f32")
-    ar.ar_allreduce(sends, recvs)          # 64 ranks: the default runs the two fused phases
+    ar.ar_allreduce(sends, recvs)          # 64 ranks x 256 MiB: the default runs the staged form
     torch.cuda.synchronize()
     _sampled_check(xs, recvs, "f32", "sum", seed=104)
     one_pass = _alloc(n, length, "f32")
@@ -251,7 +252,7 @@ def test_c5_full_size_allreduce_reduce_scatter_all_gather():
     for r in range(n):
         assert torch.equal(bits(one_pass[r]), bits(recvs[0])), f"one-pass rank {r}"
     del one_pass
-    _same_as(recvs, sends, "f32", "sum", ("ring", "ring_pipelined"))
+    _same_as(recvs, sends, "f32", "sum", ("ring", "ring_pipelined", "phases"))
     # reduce-scatter: shard c equals chunk c of the AllReduce, bit for bit
     shards = []
     for c in range(n):
