@@ -154,10 +154,12 @@ typedef enum {
  *   sender's partial and storing its own, so the steps need no barrier.  The
  *   same bits as AR_ALGO_RING, for all three collectives and every dtype,
  *   with the same workspace as AR_ALGO_RING; can be captured into a graph.
- * AR_ALGO_STAGED: AllReduce as the reduce-then-broadcast form of the same
- *   collective ("2.1 Collective communication primitives in detail",
- *   section 3.8: AllReduce as a reduce followed by a broadcast), cut into
- *   segments of rank 0's results.  Per segment, one launch
+ * AR_ALGO_STAGED: AllReduce moved as a reduce followed by a broadcast
+ *   (bitfern.com "AllReduce Explained", section "Reduce Followed by
+ *   Broadcast"; "2.1 Collective communication primitives in detail",
+ *   section 3.3, the note that AllReduce is Reduce plus Broadcast), with the
+ *   ring's association order kept, cut into segments of rank 0's results.
+ *   Per segment, one launch
  *   folds every position in ring order and stores the result to recvbufs[0]
  *   only, then one launch copies it to the other ranks.  The results
  *   are reread from the device's 256 MB last-level cache, so HBM still moves

@@ -65,8 +65,11 @@ __global__ __launch_bounds__(kThreads) void k_fused_allreduce(const KernelArgs a
     AR_TILE_LOOP_END
 }
 
-// Staged AllReduce, reducing launch: the fused AllReduce's fold for the
-// launch's tiles, stored to rank 0's receive buffer only.  The stores allocate
+// Staged AllReduce: the data moves as a reduce onto rank 0 followed by a
+// broadcast from it (bitfern.com "AllReduce Explained", section "Reduce
+// Followed by Broadcast"), while every value keeps the ring's association
+// order.  Reducing launch: the fused AllReduce's fold for the launch's tiles,
+// stored to rank 0's receive buffer only.  The stores allocate
 // in the caches (unlike every other output), so the broadcast launch that
 // follows rereads the results from the Infinity Cache instead of HBM.  This
 // launch is then almost all reads, and the broadcast almost all writes: HBM
