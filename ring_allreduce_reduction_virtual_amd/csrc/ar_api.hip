@@ -211,14 +211,15 @@ void fill_tables(KernelArgs& a, const Common& k) {
 }
 
 // Grid for the tiles [tile_first, tile_end) of a launch.
-ar_result_t grid_for(const KernelArgs& a, Launch& l) {
+ar_result_t grid_for(const KernelArgs& a, Launch& l, unsigned blocks_per_tile = 1) {
     int cus = 0;
     const ar_result_t rc = cu_count(&cus);
     if (rc != AR_SUCCESS) return rc;
-    const uint64_t tiles = a.tile_end - a.tile_first;
+    const uint64_t tiles = static_cast<uint64_t>(a.tile_end - a.tile_first) * blocks_per_tile;
     const unsigned bpc = blocks_per_cu();
     const uint64_t blocks = bpc == 0 ? tiles : std::min<uint64_t>(tiles, static_cast<uint64_t>(cus) * bpc);
-    l.blocks = static_cast<unsigned>(std::max<uint64_t>(blocks, 1));
+    // the kernels stride over what one grid (at most 2^31 - 1 blocks) leaves
+    l.blocks = static_cast<unsigned>(std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 0x7fffffffu));
     return AR_SUCCESS;
 }
 
@@ -638,6 +639,8 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
             a.tile_end = static_cast<uint32_t>(std::min<uint64_t>(total, t0 + per_seg));
             if ((rc = grid_for(a, l)) != AR_SUCCESS) return rc;
             if ((rc = sink.emit(l, Kind::kStagedReduce, a, k)) != AR_SUCCESS) return rc;
+            // the broadcast: one block per unit row of a tile (kUnroll per tile)
+            if ((rc = grid_for(a, l, arimpl::kUnroll)) != AR_SUCCESS) return rc;
             if ((rc = sink.emit(l, Kind::kStagedBroadcast, a, k)) != AR_SUCCESS) return rc;
         }
         return AR_SUCCESS;
