@@ -71,20 +71,20 @@ SHAPES = [(1, 0), (1, 7), (2, 1), (2, 9), (3, 2), (3, 1000), (4, 3), (5, 1003), 
           (8, 4097), (16, 15), (16, 65541), (64, 63), (64, 64 * 33 + 7), (128, 127), (128, 128 * 20 + 3)]
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_persistent", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_persistent", "ring_pipelined", "staged"])
 @pytest.mark.parametrize("n,length", SHAPES)
 def test_allreduce_shapes_f32_sum(n, length, algo):
     _allreduce_case(n, length, "f32", "sum", algo, seed=n * 7 + length)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_pipelined", "staged"])
 @pytest.mark.parametrize("dtype,op", [(d, o) for d in ("f32", "bf16", "i32") for o in ("sum", "prod", "min", "max")])
 @pytest.mark.parametrize("n,length", [(3, 1001), (8, 8 * 64 + 5), (17, 4099)])
 def test_allreduce_dtypes_and_ops(n, length, dtype, op, algo):
     _allreduce_case(n, length, dtype, op, algo, seed=zlib.crc32(f"{dtype}{op}".encode()) % 1000)
 
 
-@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_persistent", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "ring", "phases", "ring_persistent", "ring_pipelined", "staged"])
 @pytest.mark.parametrize("dtype,op", [("f32", "sum"), ("f32", "min"), ("f32", "max"), ("f32", "prod"),
                                       ("bf16", "sum"), ("bf16", "max"), ("i32", "sum"), ("i32", "prod")])
 def test_special_values(dtype, op, algo):

@@ -91,12 +91,15 @@ def test_phase_plans(algo):
     ar.ar_plan_free(ag)
 
 
-@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined"])
-def test_graph_capture_replays(algo):
+@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined", "staged"])
+def test_graph_capture_replays(algo, monkeypatch):
     """Capture 3 starts of a plan in a HIP graph; replay it 4 times with eager input
-    changes in between, checking every replay against the oracle."""
+    changes in between, checking every replay against the oracle.  The staged form
+    runs with one tile of results per segment (8 segments, 16 launches per start)."""
     import torch
 
+    if algo == "staged":
+        monkeypatch.setenv("AR_STAGE_BYTES", "8192")
     ar = _ar()
     n, length = 8, 8 * 2048 + 3
     xs = _draw(n, length, seed=11)
@@ -126,26 +129,31 @@ def test_graph_capture_replays(algo):
             assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32"), (rep, r)
 
 
-@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined", "tree", "tree_steps",
+@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined", "staged", "tree", "tree_steps",
                                   "halving_doubling_steps"])
-def test_block_limits_keep_the_bits(algo):
+def test_block_limits_keep_the_bits(algo, monkeypatch):
     """A plan capped at 1, 3, 64 blocks (the kernels stride over their tiles), then
-    uncapped again, gives the oracle's bits every time."""
+    uncapped again, gives the oracle's bits every time.  The staged form runs with
+    one tile of results per segment (16 segments)."""
     import torch
 
     from oracle.orders import order_allreduce
 
+    if algo == "staged":
+        monkeypatch.setenv("AR_STAGE_BYTES", "8192")
     ar = _ar()
     n, length = 8, 8 * 4096 + 5
     xs = _draw(n, length, seed=21)
     sends = [to_dev(x, "f32") for x in xs]
     recvs = [torch.empty(length, device="cuda:0") for _ in range(n)]
-    if algo in ("fused", "phases", "ring", "ring_pipelined"):
+    if algo in ("fused", "phases", "ring", "ring_pipelined", "staged"):
         want, _ = oracle.ring_allreduce(xs)
     else:
         want, _ = order_allreduce({"tree": "tree", "tree_steps": "tree",
                                    "halving_doubling_steps": "halving_doubling"}[algo], xs)
     plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
+    if algo == "staged":
+        assert plan.num_launches == 2 * 16
     for cap in (1, 3, 64, 0):
         plan.limit_blocks(cap)
         for r in range(n):

@@ -73,7 +73,7 @@ CASES = [(d, o) for d in ("f16", "bf16acc32") for o in ("sum", "prod", "min", "m
         [("f32", "avg"), ("bf16", "avg"), ("i32", "avg")]
 
 
-@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined", "staged"])
 @pytest.mark.parametrize("dtype,op", CASES)
 @pytest.mark.parametrize("n,length", [(1, 9), (2, 1001), (3, 7), (5, 1003), (8, 8 * 512 + 13), (17, 4099)])
 def test_allreduce_variants(n, length, dtype, op, algo):
@@ -115,7 +115,7 @@ def test_reduce_scatter_and_all_gather_variants(n, length, dtype, op, algo):
         assert same_bits(_host(outs[r], dtype), want[r], dtype), f"rank {r}"
 
 
-@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined", "staged"])
 @pytest.mark.parametrize("dtype,op", [("f16", "sum"), ("f16", "prod"), ("f16", "min"), ("f16", "avg"),
                                       ("bf16acc32", "sum"), ("bf16acc32", "avg"), ("f32", "avg")])
 def test_special_values_variants(dtype, op, algo):
@@ -133,7 +133,7 @@ def test_special_values_variants(dtype, op, algo):
         assert same_bits(_host(recvs[r], dtype), want[r], dtype), f"rank {r}"
 
 
-@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined", "staged"])
 @pytest.mark.parametrize("layout", ["in_place", "common_offset", "mixed_offsets"])
 def test_bf16acc32_layouts(layout, algo):
     """Float32 partials with in-place buffers and views 1..3 elements into allocations."""
