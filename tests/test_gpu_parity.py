@@ -206,7 +206,7 @@ def test_c3_bf16_full_size():
     xs = make_inputs(w)
     sends, recvs = _run_allreduce(xs, "bf16", "sum", "fused")
     _sampled_check(xs, recvs, "bf16", "sum", seed=102)
-    _same_as(recvs, sends, "bf16", "sum", ("ring", "ring_pipelined"))
+    _same_as(recvs, sends, "bf16", "sum", ("ring", "ring_pipelined", "staged"))
 
 
 @pytest.mark.parametrize("op", ["sum", "min", "max"])
@@ -231,7 +231,7 @@ def test_c4_int32_full_size_closed_forms(op):
     for r in range(1, w.nranks):
         assert torch.equal(recvs[r], recvs[0])
     _sampled_check(xs, recvs, "i32", op, seed=103)
-    _same_as(recvs, sends, "i32", op, ("ring", "ring_pipelined"))
+    _same_as(recvs, sends, "i32", op, ("ring", "ring_pipelined", "staged"))
 
 
 def test_c5_full_size_allreduce_reduce_scatter_all_gather():

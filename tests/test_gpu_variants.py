@@ -188,8 +188,8 @@ def test_c3_workload_full_size_with_float32_partials_and_avg():
         want = oracle.ring_order_fold_columns(cols, owners, op=op, dtype=dtype)
         for r in range(w.nranks):
             assert same_bits(_host(recvs[r][idx], dtype), want, dtype), (dtype, op, r)
-        # the ring's launches and the pipelined ring give the same bits everywhere
-        for algo in ("ring", "ring_pipelined"):
+        # the ring's launches, the pipelined ring and the staged form give the same bits everywhere
+        for algo in ("ring", "ring_pipelined", "staged"):
             ar.ar_allreduce_ex(sends, other, op=op, algo=algo, dtype=dtype)
             torch.cuda.synchronize()
             for r in range(w.nranks):
