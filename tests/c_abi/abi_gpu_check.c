@@ -4,6 +4,7 @@
  * Integer-valued inputs make every result a closed form (exact sums in any
  * order), so the program needs no reference implementation.  Prints one
  * line per check and exits non-zero on the first mismatch. */
+#define _POSIX_C_SOURCE 200112L   /* setenv */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -37,6 +38,8 @@ int main(void) {
     hipStream_t stream;
     hipError_t e;
     if (host == NULL || back == NULL) return 1;
+    /* the staged form with one tile of results per segment: 6 segments, 12 launches */
+    if (setenv("AR_STAGE_BYTES", "8192", 1) != 0) return 1;
     if ((e = hipStreamCreate(&stream)) != hipSuccess) return fail_hip(e, "hipStreamCreate");
     for (int r = 0; r < N; ++r) {
         if ((e = hipMalloc(&send[r], sizeof(float) * COUNT)) != hipSuccess) return fail_hip(e, "hipMalloc");
@@ -47,8 +50,9 @@ int main(void) {
     }
 
     const ar_algo_t algos[] = {AR_ALGO_FUSED, AR_ALGO_RING, AR_ALGO_PHASES, AR_ALGO_TREE, AR_ALGO_TREE_STEPS,
-                               AR_ALGO_RING_PERSISTENT, AR_ALGO_RING_PIPELINED};
-    const char* names[] = {"fused", "ring", "phases", "tree", "tree_steps", "ring_persistent", "ring_pipelined"};
+                               AR_ALGO_RING_PERSISTENT, AR_ALGO_RING_PIPELINED, AR_ALGO_STAGED};
+    const char* names[] = {"fused", "ring", "phases", "tree", "tree_steps", "ring_persistent", "ring_pipelined",
+                           "staged"};
     for (size_t k = 0; k < sizeof(algos) / sizeof(algos[0]); ++k) {
         if (check_ar(ar_allreduce_ex((const void* const*)send, recv, COUNT, AR_FLOAT32, AR_SUM, N, algos[k], NULL, 0,
                                      stream), names[k]))
