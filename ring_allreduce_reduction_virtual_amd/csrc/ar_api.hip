@@ -352,6 +352,20 @@ uint64_t stage_bytes(int nranks) {
     return std::min<uint64_t>(AR_STAGE_BYTES_MAX, std::max<uint64_t>(AR_STAGE_BYTES_MIN, b));
 }
 
+// Grid of a launch that copies one value to many ranks (fused all-gather,
+// staged broadcast): one block per unit row of a tile (kUnroll per tile)
+// except for many large buffers, where whole tiles per block are faster.
+// The AR_HALF_TILES environment variable (read at every call) forces one form:
+// 0 whole tiles, 1 unit rows.
+ar_result_t copy_grid(const KernelArgs& a, Launch& l, const Common& k) {
+    const char* e = std::getenv("AR_HALF_TILES");
+    if (e != nullptr && (e[0] == '0' || e[0] == '1') && e[1] == '\0')
+        l.half = e[0] == '1';
+    else
+        l.half = !(k.n >= AR_HALF_TILES_MAX_RANKS && k.count * k.esz >= AR_HALF_TILES_MAX_BYTES);
+    return grid_for(a, l, l.half ? arimpl::kUnroll : 1);
+}
+
 // Rank count from which AR_ALGO_AUTO runs AllReduce as two fused phases.
 int phases_min_ranks() {
     static const int v = [] {
@@ -617,7 +631,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
             recvs.push_back(reinterpret_cast<uintptr_t>(k.recv[r]));
         }
         if ((rc = plan(g, lg, k, common_residue(recvs))) != AR_SUCCESS) return rc;
-        return sink.emit(lg, Kind::kFusedAllGather, g, k);
+        return sink.emit(lg, Kind::kFusedAllGather, g, k);   // whole tiles: measured faster in place
     }
     if (algo == AR_ALGO_FUSED && small_message(k)) {
         plan_small(a, l, k);
@@ -639,9 +653,9 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
             a.tile_end = static_cast<uint32_t>(std::min<uint64_t>(total, t0 + per_seg));
             if ((rc = grid_for(a, l)) != AR_SUCCESS) return rc;
             if ((rc = sink.emit(l, Kind::kStagedReduce, a, k)) != AR_SUCCESS) return rc;
-            // the broadcast: one block per unit row of a tile (kUnroll per tile)
-            if ((rc = grid_for(a, l, arimpl::kUnroll)) != AR_SUCCESS) return rc;
+            if ((rc = copy_grid(a, l, k)) != AR_SUCCESS) return rc;
             if ((rc = sink.emit(l, Kind::kStagedBroadcast, a, k)) != AR_SUCCESS) return rc;
+            l.half = false;
         }
         return AR_SUCCESS;
     }
@@ -760,7 +774,10 @@ ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, Sink& sink) {
     Launch l{};
     fill_tables(a, k);
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
-    if (algo == AR_ALGO_FUSED || k.n == 1) return sink.emit(l, Kind::kFusedAllGather, a, k);
+    if (algo == AR_ALGO_FUSED || k.n == 1) {
+        if ((rc = copy_grid(a, l, k)) != AR_SUCCESS) return rc;
+        return sink.emit(l, Kind::kFusedAllGather, a, k);
+    }
     if (algo == AR_ALGO_RING_PIPELINED) return sink.emit(l, Kind::kRingPipelinedGather, a, k);
     if ((rc = sink.emit(l, Kind::kPlaceShards, a, k)) != AR_SUCCESS) return rc;
     for (int s = 0; s < k.n - 1; ++s) {

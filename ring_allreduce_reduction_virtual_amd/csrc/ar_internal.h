@@ -80,6 +80,7 @@ struct Launch {
     ar_op_t op;
     bool vec;                  // 16-byte vector path (all streamed buffers share a residue)
     bool cached;               // kFusedAllReduce on the vector path: cache-allocating loads
+    bool half;                 // kFusedAllGather, kStagedBroadcast: one unit row of a tile per block
     unsigned blocks;
     int depth;                 // kFusedTree: partial slots, 2^depth > N (4, 6 or 8)
     unsigned actors;           // kTree*Step: actors per chunk in the stage (the grid's y extent)
@@ -127,6 +128,22 @@ constexpr int kUnroll = AR_TILE_UNROLL;
 #endif
 #ifndef AR_STAGE_BYTES_MAX
 #define AR_STAGE_BYTES_MAX (128ull << 20)
+#endif
+
+// The copy launches that write one value to many ranks (the fused all-gather
+// and the staged AllReduce's broadcast) give each block one of a tile's
+// kUnroll unit rows, unless there are at least AR_HALF_TILES_MAX_RANKS ranks
+// of at least AR_HALF_TILES_MAX_BYTES bytes each.  Measured on MI355X,
+// float32, same box, whole / half tiles, staged AllReduce and all-gather in
+// us: 8 x 256 MiB 736 / 723 and 396 / 390; 16 x 256 MiB 1,509 / 1,461 and
+// 785 / 736; 64 x 128 MiB 3,031 / 2,981 and 1,532 / 1,509; 128 x 64 MiB
+// 3,080 / 3,040 and 1,618 / 1,561; but 32 x 256 MiB 2,984 / 3,046 and
+// 1,546 / 1,564; 64 x 256 MiB 5,928 / 6,341 and 3,186 / 3,392.
+#ifndef AR_HALF_TILES_MAX_RANKS
+#define AR_HALF_TILES_MAX_RANKS 32
+#endif
+#ifndef AR_HALF_TILES_MAX_BYTES
+#define AR_HALF_TILES_MAX_BYTES (256ull << 20)
 #endif
 
 // Enqueue one kernel; returns the HIP error of the launch.

@@ -98,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void k_staged_reduce(const KernelArgs a) 
 // Staged AllReduce, broadcasting launch: rank 0's results for the same tiles
 // (so the same elements, chunk edges included) copied to ranks 1..N-1.  Each
 // block takes one of a tile's kUnroll units per thread, so a wave issues half
-// the stores of a whole tile; HBM takes the writes faster that way (write
-// probes on MI355X: fewer stores per wave, faster writes).
+// the stores of a whole tile; HBM mostly takes the writes faster that way
+// (the host picks this form or k_staged_broadcast_tiles by measured shape).
 template <int DT, int VEC>
 __global__ __launch_bounds__(kThreads) void k_staged_broadcast(const KernelArgs a) {
     using U = Unit<DT, VEC, false>;   // cache-allocating loads: the results sit in the Infinity Cache
@@ -128,6 +128,37 @@ __global__ __launch_bounds__(kThreads) void k_staged_broadcast(const KernelArgs 
             for (int q = 1; q < n; ++q) U::store(U::tile(a.recv[q] - adj, tv0), U::lane_off(u), x);
         }
     }
+}
+
+// The same broadcast with whole tiles per block (kUnroll unit rows): faster
+// for many large buffers.
+template <int DT, int VEC>
+__global__ __launch_bounds__(kThreads) void k_staged_broadcast_tiles(const KernelArgs a) {
+    using U = Unit<DT, VEC, false>;   // cache-allocating loads: the results sit in the Infinity Cache
+    constexpr int ESZ = elem_size<DT>();
+    AR_TILE_LOOP_BEGIN
+    const char* src = a.recv[0];
+    if (VEC > 1 && t == 0) {
+        uint64_t i;
+        if (edge_element(sp, threadIdx.x, &i)) {
+            const uint32_t x = load_elem<ESZ>(src + i * ESZ);
+            for (int q = 1; q < n; ++q) store_elem<ESZ>(a.recv[q] + i * ESZ, x);
+        }
+    }
+    typename U::T x[kUnroll];
+    const char* sb = U::tile(src - adj, tv0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (live[u]) x[u] = U::load(sb, U::lane_off(u));
+    }
+    for (int q = 1; q < n; ++q) {
+        char* tb = U::tile(a.recv[q] - adj, tv0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (live[u]) U::store(tb, U::lane_off(u), x[u]);
+        }
+    }
+    AR_TILE_LOOP_END
 }
 
 // Reduce-scatter: the fold of chunk c goes to rank c's shard only.  Reads N*S,
@@ -190,6 +221,47 @@ __global__ __launch_bounds__(kThreads) void k_gather_shards(const KernelArgs a) 
         }
     }
     AR_TILE_LOOP_END
+}
+
+// k_gather_shards with one of a tile's kUnroll unit rows per block (grid of
+// kUnroll blocks per tile): each wave issues half the stores, which HBM
+// mostly takes faster (the host picks the form by measured shape).
+template <int DT, int VEC, bool ALL>
+__global__ __launch_bounds__(kThreads) void k_gather_shards_half(const KernelArgs a) {
+    using U = Unit<DT, VEC, AR_NT_LOADS_COPY>;
+    constexpr int ESZ = elem_size<DT>();
+    const int n = a.nranks;
+    const uint32_t tpc = a.tiles_per_chunk;
+    const int64_t adj = (VEC > 1) ? static_cast<int64_t>(a.ofs) * ESZ : 0;
+    const uint64_t parts = static_cast<uint64_t>(a.tile_end - a.tile_first) * kUnroll;
+    for (uint64_t w = blockIdx.x; w < parts; w += gridDim.x) {
+        const uint32_t tile = a.tile_first + static_cast<uint32_t>(w / kUnroll);
+        const int u = static_cast<int>(w % kUnroll);
+        const int c = static_cast<int>(tile / tpc);
+        const uint64_t t = tile - static_cast<uint32_t>(c) * tpc;
+        const Span sp = chunk_span<VEC>(c, a);
+        const uint64_t tv0 = sp.vb + t * (kThreads * kUnroll);
+        const char* shard = a.send[c];
+        if (VEC > 1 && t == 0 && u == 0) {
+            uint64_t i;
+            if (edge_element(sp, threadIdx.x, &i)) {
+                const uint32_t x = load_elem<ESZ>(shard + (i - sp.s) * ESZ);
+                for (int q = ALL ? 0 : c; q < (ALL ? n : c + 1); ++q) {
+                    char* dst = a.recv[q] + i * ESZ;
+                    if (dst != shard + (i - sp.s) * ESZ) store_elem<ESZ>(dst, x);
+                }
+            }
+        }
+        if (tv0 + U::lane_unit(u) < sp.ve) {
+            const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
+            const typename U::T x =
+                load_shard_unit<DT, VEC, AR_NT_LOADS_COPY>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u));
+            for (int q = ALL ? 0 : c; q < (ALL ? n : c + 1); ++q) {
+                if (a.recv[q] + sp.s * ESZ == shard) continue;   // the shard already sits there
+                U::store(U::tile(a.recv[q] - adj, tv0), U::lane_off(u), x);
+            }
+        }
+    }
 }
 
 // AllReduce of a small message: the ring-order fold of P = kThreads / N
@@ -368,7 +440,10 @@ hipError_t launch_copy(const Launch& l, const KernelArgs& a, hipStream_t s) {
     const dim3 grid(l.blocks), block(kThreads);
     switch (l.kind) {
         case Kind::kFusedAllGather:
-            hipLaunchKernelGGL((k_gather_shards<DT, VEC, true>), grid, block, 0, s, a);
+            if (l.half)
+                hipLaunchKernelGGL((k_gather_shards_half<DT, VEC, true>), grid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((k_gather_shards<DT, VEC, true>), grid, block, 0, s, a);
             break;
         case Kind::kPlaceShards:
             hipLaunchKernelGGL((k_gather_shards<DT, VEC, false>), grid, block, 0, s, a);
@@ -377,7 +452,10 @@ hipError_t launch_copy(const Launch& l, const KernelArgs& a, hipStream_t s) {
             hipLaunchKernelGGL((k_ring_copy_step<DT, VEC>), grid, block, 0, s, a);
             break;
         case Kind::kStagedBroadcast:
-            hipLaunchKernelGGL((k_staged_broadcast<DT, VEC>), grid, block, 0, s, a);
+            if (l.half)
+                hipLaunchKernelGGL((k_staged_broadcast<DT, VEC>), grid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((k_staged_broadcast_tiles<DT, VEC>), grid, block, 0, s, a);
             break;
         default:
             return hipErrorInvalidValue;

@@ -136,6 +136,53 @@ def test_staged_equals_fused_bits_and_segments(stage_env):
     plan.close()
 
 
+@pytest.mark.parametrize("half", ["0", "1"])
+@pytest.mark.parametrize("n,length,dtype,op", [(5, 1003, "f32", "sum"), (8, 8 * 4096 + 5, "bf16", "sum"),
+                                               (17, 4099, "i32", "max"), (64, 64 * 333 + 7, "f32", "sum"),
+                                               (7, 7 * 3000 + 5, "bf16acc32", "avg")])
+def test_staged_both_broadcast_forms(n, length, dtype, op, half, stage_env, monkeypatch):
+    """The broadcast with whole tiles per block and with one unit row per block
+    (the host picks by shape; AR_HALF_TILES forces either), over several segments."""
+    require_gpu()
+    stage_env(3 * 8192)
+    monkeypatch.setenv("AR_HALF_TILES", half)
+    print(f"[staged] broadcast form half={half} n={n} len={length} {dtype} {op}", flush=True)
+    for layout in ("fresh", "offset", "in_place"):
+        _run(n, length, dtype, op, layout, 3 * 8192, seed=n + length)
+
+
+@pytest.mark.parametrize("half", ["0", "1"])
+@pytest.mark.parametrize("n,length,dtype", [(1, 7, "f32"), (3, 1000, "i32"), (5, 1003, "f32"), (8, 8 * 4096 + 5, "bf16"),
+                                            (64, 64 * 333 + 7, "f32"), (128, 300, "f16")])
+def test_all_gather_both_forms(n, length, dtype, half, monkeypatch):
+    """The fused all-gather with whole tiles per block and with one unit row per
+    block, out of place and in place, against the oracle."""
+    import torch
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    require_gpu()
+    monkeypatch.setenv("AR_HALF_TILES", half)
+    xs = _draw(dtype, n, length, seed=n * 5 + length)
+    shards_want, _ = oracle.reduce_scatter(xs, dtype=dtype)
+    want, _ = oracle.all_gather(shards_want, length, dtype=dtype)
+    for layout in ("fresh", "offset", "in_place"):
+        so = 1 if layout == "offset" else 0
+        if layout == "in_place":
+            outs = [_empty(length, dtype) for _ in range(n)]
+            shards = []
+            for r in range(n):
+                b, e = ar.ar_chunk_range(r, length, n)
+                outs[r][b:e].copy_(_tensor(shards_want[r], dtype))
+                shards.append(outs[r][b:e])
+        else:
+            shards = [_tensor(sh, dtype, so) for sh in shards_want]
+            outs = [_empty(length, dtype, so) for _ in range(n)]
+        ar.ar_all_gather_ex(shards, outs, algo="fused")
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert same_bits(_host(outs[r], dtype), want[r], dtype), (layout, r)
+
+
 def test_staged_is_allreduce_only():
     import ring_allreduce_reduction_virtual_amd as ar
 
