@@ -620,6 +620,8 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
             sends.push_back(reinterpret_cast<uintptr_t>(k.send[r]));
         }
         if ((rc = plan(a, l, k, common_residue(sends))) != AR_SUCCESS) return rc;
+        // cache-allocating stores: the all-gather that follows rereads these chunks
+        l.cached_store = true;
         if ((rc = sink.emit(l, Kind::kFusedReduceScatter, a, k)) != AR_SUCCESS) return rc;
         // ... then all-gather in place: chunk c of recv[c] to every other rank
         KernelArgs g{};

@@ -538,20 +538,20 @@ __device__ __forceinline__ void store_elem_all(const KernelArgs& a, int n, uint6
 // Store unit v of a result into a shard that starts at element `s` of the
 // full buffer (reduce-scatter output).  `aligned` says whether the shard's
 // 16-byte vectors line up with the source's.
-template <int DT, int VEC>
+template <int DT, int VEC, bool NT = AR_NT_STORES>
 __device__ __forceinline__ void store_shard_unit(char* shard, uint64_t s, int32_t ofs, bool aligned,
                                                  uint64_t v, typename Unit<DT, VEC>::T x) {
     constexpr int ESZ = elem_size<DT>();
     if constexpr (VEC > 1) {
         const uint64_t first = v * VEC - static_cast<uint64_t>(ofs);   // element index in the full buffer
         if (aligned) {
-            store16(shard + (first - s) * ESZ, x);
+            store16<NT>(shard + (first - s) * ESZ, x);
         } else {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) store_elem<ESZ>(shard + (first + e - s) * ESZ, vec_elem<ESZ>(x, e));
+            for (int e = 0; e < VEC; ++e) store_elem<ESZ, NT>(shard + (first + e - s) * ESZ, vec_elem<ESZ>(x, e));
         }
     } else {
-        store_elem<ESZ>(shard + (v - s) * ESZ, x);
+        store_elem<ESZ, NT>(shard + (v - s) * ESZ, x);
     }
 }
 

@@ -81,6 +81,8 @@ struct Launch {
     bool vec;                  // 16-byte vector path (all streamed buffers share a residue)
     bool cached;               // kFusedAllReduce on the vector path: cache-allocating loads
     bool half;                 // kFusedAllGather, kStagedBroadcast: one unit row of a tile per block
+    bool cached_store;         // kFusedReduceScatter: cache-allocating stores of the shards (the
+                               // phases' AllReduce, whose all-gather rereads them)
     unsigned blocks;
     int depth;                 // kFusedTree: partial slots, 2^depth > N (4, 6 or 8)
     unsigned actors;           // kTree*Step: actors per chunk in the stage (the grid's y extent)
