@@ -354,15 +354,17 @@ uint64_t stage_bytes(int nranks) {
 
 // Grid of a launch that copies one value to many ranks (fused all-gather,
 // staged broadcast): one block per unit row of a tile (kUnroll per tile)
-// except for many large buffers, where whole tiles per block are faster.
+// inside the measured band of total sizes, whole tiles per block outside it.
 // The AR_HALF_TILES environment variable (read at every call) forces one form:
 // 0 whole tiles, 1 unit rows.
 ar_result_t copy_grid(const KernelArgs& a, Launch& l, const Common& k) {
     const char* e = std::getenv("AR_HALF_TILES");
-    if (e != nullptr && (e[0] == '0' || e[0] == '1') && e[1] == '\0')
+    if (e != nullptr && (e[0] == '0' || e[0] == '1') && e[1] == '\0') {
         l.half = e[0] == '1';
-    else
-        l.half = !(k.n >= AR_HALF_TILES_MAX_RANKS && k.count * k.esz >= AR_HALF_TILES_MAX_BYTES);
+    } else {
+        const uint64_t total = k.count * k.esz * static_cast<uint64_t>(k.n);
+        l.half = total >= AR_HALF_TILES_MIN_TOTAL && total < AR_HALF_TILES_MAX_TOTAL;
+    }
     return grid_for(a, l, l.half ? arimpl::kUnroll : 1);
 }
 

@@ -134,18 +134,20 @@ constexpr int kUnroll = AR_TILE_UNROLL;
 
 // The copy launches that write one value to many ranks (the fused all-gather
 // and the staged AllReduce's broadcast) give each block one of a tile's
-// kUnroll unit rows, unless there are at least AR_HALF_TILES_MAX_RANKS ranks
-// of at least AR_HALF_TILES_MAX_BYTES bytes each.  Measured on MI355X,
-// float32, same box, whole / half tiles, staged AllReduce and all-gather in
-// us: 8 x 256 MiB 736 / 723 and 396 / 390; 16 x 256 MiB 1,509 / 1,461 and
-// 785 / 736; 64 x 128 MiB 3,031 / 2,981 and 1,532 / 1,509; 128 x 64 MiB
-// 3,080 / 3,040 and 1,618 / 1,561; but 32 x 256 MiB 2,984 / 3,046 and
-// 1,546 / 1,564; 64 x 256 MiB 5,928 / 6,341 and 3,186 / 3,392.
-#ifndef AR_HALF_TILES_MAX_RANKS
-#define AR_HALF_TILES_MAX_RANKS 32
+// kUnroll unit rows when the ranks' buffers hold between
+// AR_HALF_TILES_MIN_TOTAL and AR_HALF_TILES_MAX_TOTAL bytes in all (N * S);
+// outside that band whole tiles per block are faster.  Measured on MI355X,
+// float32, same box, staged AllReduce whole / half tiles in us: inside the
+// band 8 x 256 MiB 736 / 723, 16 x 256 MiB 1,509 / 1,461, 64 x 64 MiB
+// 1,559 / 1,527, 32 x 128 MiB 1,519 / 1,495; below it 8 x 4 MiB 19.1 / 21.3,
+// 16 x 64 MiB 396 / 415, 64 x 16 MiB 419 / 473; above it 32 x 256 MiB
+// 2,984 / 3,046, 64 x 256 MiB 5,928 / 6,341.  The all-gather follows the
+// same band (64 x 16 MiB 235 / 284 us; 16 x 256 MiB 785 / 736 us).
+#ifndef AR_HALF_TILES_MIN_TOTAL
+#define AR_HALF_TILES_MIN_TOTAL (2048ull << 20)
 #endif
-#ifndef AR_HALF_TILES_MAX_BYTES
-#define AR_HALF_TILES_MAX_BYTES (256ull << 20)
+#ifndef AR_HALF_TILES_MAX_TOTAL
+#define AR_HALF_TILES_MAX_TOTAL (8192ull << 20)
 #endif
 
 // Enqueue one kernel; returns the HIP error of the launch.
