@@ -111,7 +111,7 @@ typedef enum {
  *   kernel, but the read-heavy and the write-heavy halves run apart, which is
  *   faster on MI355X HBM once N is large.
  * AR_ALGO_AUTO: for AllReduce, AR_ALGO_STAGED for large buffers (the
- *   AR_STAGED_MIN_* bounds below), else AR_ALGO_PHASES from
+ *   AR_STAGED_MIN_* bounds below, lower for 16-bit types), else AR_ALGO_PHASES from
  *   AR_PHASES_MIN_RANKS ranks when every rank holds at least
  *   AR_PHASES_MIN_BYTES bytes, else AR_ALGO_FUSED; the fused kernel for the
  *   single phases.
@@ -192,6 +192,13 @@ typedef enum {
 #define AR_STAGED_MIN_RANKS 8
 #define AR_STAGED_MIN_BYTES (64ull << 20)
 #define AR_STAGED_MIN_TOTAL_BYTES (2048ull << 20)
+/* The same bounds for the 16-bit element types (bf16, binary16, bf16 with
+ * float32 partials), whose fused kernel spends more of its time converting:
+ * measured on MI355X, bf16, fused / staged in us: 8 x 64 MiB 204.6 / 201.7,
+ * 8 x 128 MiB 397.6 / 383.2, 16 x 32 MiB 211.5 / 206.1, 32 x 32 MiB
+ * 444.1 / 405.0; but 8 x 32 MiB 85.8 / 106.1. */
+#define AR_STAGED_MIN_BYTES_16BIT (32ull << 20)
+#define AR_STAGED_MIN_TOTAL_BYTES_16BIT (512ull << 20)
 /* Rank count from which AR_ALGO_AUTO runs an AllReduce as two fused phases
  * (measured crossover on MI355X; the AR_PHASES_MIN_RANKS environment variable
  * overrides it). */

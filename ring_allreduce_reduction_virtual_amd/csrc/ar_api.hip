@@ -586,8 +586,10 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     // wins (and the small-message kernel for the smallest messages)
     if (algo == AR_ALGO_AUTO) {
         const uint64_t per_rank = k.count * k.esz;
-        if (k.n >= AR_STAGED_MIN_RANKS && per_rank >= AR_STAGED_MIN_BYTES &&
-            per_rank * static_cast<uint64_t>(k.n) >= AR_STAGED_MIN_TOTAL_BYTES)
+        const bool narrow = k.esz == 2;   // 16-bit types: lower bounds (measured)
+        const uint64_t min_rank = narrow ? AR_STAGED_MIN_BYTES_16BIT : AR_STAGED_MIN_BYTES;
+        const uint64_t min_total = narrow ? AR_STAGED_MIN_TOTAL_BYTES_16BIT : AR_STAGED_MIN_TOTAL_BYTES;
+        if (k.n >= AR_STAGED_MIN_RANKS && per_rank >= min_rank && per_rank * static_cast<uint64_t>(k.n) >= min_total)
             algo = AR_ALGO_STAGED;
         else if (k.n >= phases_min_ranks() && per_rank >= AR_PHASES_MIN_BYTES && !small_message(k))
             algo = AR_ALGO_PHASES;

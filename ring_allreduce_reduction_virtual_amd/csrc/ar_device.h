@@ -106,14 +106,37 @@ __device__ __forceinline__ uint32_t i32_apply(uint32_t a, uint32_t b) {
 // bf16 bits are the upper half of the float32 with the same value.
 __device__ __forceinline__ float bf16_widen(uint32_t h) { return as_f(h << 16); }
 
-// float32 -> bf16, nearest with ties to even: adding 0x7FFF plus the last
-// kept bit carries into the upper half exactly when the dropped half is above
-// one half ulp, or equal to it with an odd last bit.  NaN -> quiet NaN.
+// float32 -> bf16, nearest with ties to even.  AR_BF16_HW_CVT (default 1)
+// uses gfx950's conversion instruction (v_cvt_pk_bf16_f32, two values per
+// instruction, in the default round-to-nearest-even mode, subnormals kept);
+// 0 uses the integer formula: adding 0x7FFF plus the last kept bit carries
+// into the upper half exactly when the dropped half is above one half ulp, or
+// equal to it with an odd last bit.  Either way NaN -> a quiet NaN.
+#ifndef AR_BF16_HW_CVT
+#define AR_BF16_HW_CVT 1
+#endif
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t bf16_round(float f) {
-    const uint32_t u = as_u(f);
-    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    const uint32_t quiet = (u >> 16) | 0x40u;
-    return ((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded;
+    if constexpr (AR_BF16_HW_CVT) {
+        return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+    } else {
+        const uint32_t u = as_u(f);
+        const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+        const uint32_t quiet = (u >> 16) | 0x40u;
+        return ((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded;
+    }
+}
+
+// Two values rounded to bf16 and packed: lo in bits 0-15, hi in bits 16-31.
+__device__ __forceinline__ uint32_t bf16_round2(float lo, float hi) {
+    if constexpr (AR_BF16_HW_CVT) {
+        const f32x2_t v = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    } else {
+        return bf16_round(lo) | (bf16_round(hi) << 16);
+    }
 }
 
 // IEEE binary16 <-> float32 with the hardware conversions (exact widening;
@@ -144,7 +167,10 @@ struct Red {
     }
     // one 32-bit word: one 4-byte element or two 2-byte elements
     static __device__ __forceinline__ uint32_t word(uint32_t a, uint32_t b) {
-        if constexpr (elem_size<DT>() == 2) {
+        if constexpr (DT == AR_BFLOAT16 || DT == AR_BFLOAT16_ACC_F32) {
+            return bf16_round2(f32_apply<kOp>(bf16_widen(a & 0xffffu), bf16_widen(b & 0xffffu)),
+                               f32_apply<kOp>(bf16_widen(a >> 16), bf16_widen(b >> 16)));
+        } else if constexpr (elem_size<DT>() == 2) {
             return elem(a, b) | (elem(a >> 16, b >> 16) << 16);
         } else {
             return elem(a, b);
@@ -369,7 +395,7 @@ struct Fold {
                     lo = lo / static_cast<float>(n);
                     hi = hi / static_cast<float>(n);
                 }
-                r[k] = bf16_round(lo) | (bf16_round(hi) << 16);
+                r[k] = bf16_round2(lo, hi);
             }
             return r;
         } else {
