@@ -163,3 +163,25 @@ def test_block_limits_keep_the_bits(algo, monkeypatch):
         for r in range(n):
             assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32"), (cap, r)
     plan.close()
+
+
+@pytest.mark.parametrize("n,count,dtype,launches", [
+    (8, 48 << 20, "float32", 1),      # 192 MiB per rank, 1.5 GiB in all: below the 4-byte bounds -> fused
+    (8, 96 << 20, "bfloat16", 4),     # the same bytes in bf16: staged (16-bit bounds), 2 segments of 128 MiB
+    (8, 1 << 26, "float32", 4),       # the headline: staged, 2 segments
+    (8, 1 << 24, "bfloat16", 1),      # 32 MiB per rank, 256 MiB in all: below the 16-bit total -> fused
+    (4, 1 << 27, "float32", 1),       # 4 ranks: below the staged rank bound -> fused
+    (64, 1 << 20, "float32", 2),      # 64 ranks x 4 MiB: the two phases
+])
+def test_auto_choice(n, count, dtype, launches):
+    """Which form AR_ALGO_AUTO plans at shapes on both sides of its bounds
+    (validation and planning only: nothing is launched)."""
+    import torch
+
+    ar = _ar()
+    tdt = getattr(torch, dtype)
+    sends = [torch.empty(count, dtype=tdt, device="cuda:0") for _ in range(n)]
+    recvs = [torch.empty(count, dtype=tdt, device="cuda:0") for _ in range(n)]
+    plan = ar.ar_allreduce_init(sends, recvs, algo="auto")
+    assert plan.num_launches == launches
+    plan.close()
