@@ -207,6 +207,24 @@ typedef enum {
  * on MI355X: below it the single fused kernel is faster at every rank count). */
 #define AR_PHASES_MIN_BYTES (4u << 20)
 
+/* Environment variables.  They tune speed only; no setting changes a
+ * result's bits.
+ *   AR_STAGE_BYTES       AR_ALGO_STAGED: bytes of results per segment (read
+ *                        at every call; a plan keeps what it was built with)
+ *   AR_HALF_TILES        0 or 1: the fused all-gather and the staged broadcast
+ *                        with whole tiles or half tiles per workgroup
+ *                        (read at every call; unset: chosen by size)
+ *   AR_PHASES_MIN_RANKS  AR_ALGO_AUTO's rank bound for AR_ALGO_PHASES
+ *   AR_SMALL_CHUNK_MAX   chunk length (elements) below which the one-pass
+ *                        kernels stage a few positions in LDS; 0: never
+ *   AR_CACHED_LOADS_MAX  input bytes (N*S) up to which the fused AllReduce
+ *                        reads with cache-allocating loads; 0: never
+ *   AR_BLOCKS_PER_CU     cap the tiled kernels' grids at this many workgroups
+ *                        per compute unit (they stride over the rest); 0:
+ *                        one workgroup per tile
+ *   AR_DEBUG             nonzero: print every planned launch to stderr
+ * All but the first two are read once per process. */
+
 typedef enum {
     AR_COLL_ALLREDUCE = 0,
     AR_COLL_REDUCE_SCATTER = 1,
