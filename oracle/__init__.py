@@ -22,7 +22,10 @@ What it holds, each piece written from the pages on ring AllReduce:
                 halving and doubling), executed the same way, and the
                 bracketings they compute written from their definitions;
 * ``explore``   brute force for tiny rings: every interleaving of the ranks'
-                send/receive events, and every bracketing of an N-term sum.
+                send/receive events, and every bracketing of an N-term sum;
+* ``staged``    AllReduce as a reduce onto a root followed by a broadcast
+                (bitfern.com "AllReduce Explained", section "Reduce Followed
+                by Broadcast"), the root folding in the ring's order.
 
 Pins (what each part is checked against) are in ``tests/test_oracle_*.py``.
 Every function has a pin; none is "parity unpinned".
@@ -59,3 +62,4 @@ from .orders import (  # noqa: F401,E402
     tree_order_fold,
     tree_order_fold_columns,
 )
+from .staged import reduce_then_broadcast, reduce_to_root  # noqa: F401,E402

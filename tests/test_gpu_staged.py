@@ -1,5 +1,5 @@
 """AR_ALGO_STAGED (reduce into rank 0, then broadcast, segment by segment)
-against the oracle.
+against the oracle's reduce-then-broadcast schedule (oracle/staged.py).
 
 The staged AllReduce gives the ring's bits: its reducing launch folds in the
 ring's association order, its broadcasting launch copies.  These tests cut
@@ -32,7 +32,9 @@ def _run(n, length, dtype, op, layout, stage, seed):
     import ring_allreduce_reduction_virtual_amd as ar
 
     xs = _draw(dtype, n, length, seed=seed)
-    want, _ = oracle.ring_allreduce(xs, op=op, dtype=dtype)
+    # the staged form's own oracle (reduce onto rank 0, then broadcast, in the ring's
+    # association order); its equality with the executed ring is pinned on the CPU
+    want, _ = oracle.reduce_then_broadcast(xs, op=op, dtype=dtype, root=0)
     so, ro = _offsets(layout, n)
     sends = [_tensor(x, dtype, so[r]) for r, x in enumerate(xs)]
     recvs = None if layout == "in_place" else [_empty(length, dtype, ro[r]) for r in range(n)]

@@ -296,3 +296,100 @@ def test_orders_mutant_fails_a_pin(label, mutation):
     O = _load("oracle/orders.py", mutation, name="orders_mutant")
     results = _orders_pins(O)
     assert any(ok is not True for _, ok in results), f"mutant {label!r} passed every pin"
+
+
+# --------------------------------------------------------------------------
+# pins against oracle/staged.py
+# --------------------------------------------------------------------------
+
+def _staged_pins(S):
+    """(name, ok) for each pin of the reduce-then-broadcast oracle."""
+    out = []
+
+    def pin(name, fn):
+        try:
+            out.append((name, bool(fn())))
+        except Exception as e:  # noqa: BLE001 - a raising mutant is a caught mutant
+            out.append((name, e))
+
+    with open(os.path.join(GOLDEN, "p4_worked_examples.json")) as f:
+        gold = json.load(f)
+
+    # the Reduce example of "2.1 ..." section 3.3: GPU0 gets the sum, the others keep their vectors
+    def reduce_example():
+        ex = gold["reduce_sum_3_4_onto_gpu0"]
+        xs = [np.array(v, np.float32) for v in ex["inputs"]]
+        got, _ = S.reduce_to_root(xs, root=ex["root"])
+        return all(np.array_equal(g, np.array(w, np.float32)) for g, w in zip(got, ex["expected"]))
+    pin("reduce example", reduce_example)
+
+    # the AllReduce example of section 3.4 from every root
+    def allreduce_example():
+        ex = gold["allreduce_sum_3_4"]
+        xs = [np.array(v, np.float32) for v in ex["inputs"]]
+        for root in range(4):
+            got, _ = S.reduce_then_broadcast(xs, root=root)
+            if not all(np.array_equal(g, np.array(ex["expected"], np.float32)) for g in got):
+                return False
+        return True
+    pin("allreduce example", allreduce_example)
+
+    # the ring's bracketing, typed by hand for 4 ranks x 4 elements: element i starts at rank i
+    def ring_order():
+        base = np.array([1e8, 1.0, -1e8, 1.0], np.float32)
+        xs = [np.roll(base, -r) for r in range(4)]
+        want = []
+        for i in range(4):
+            acc = xs[i][i]
+            for k in range(1, 4):
+                acc = np.float32(acc + xs[(i + k) % 4][i])
+            want.append(acc)
+        got, _ = S.reduce_then_broadcast(xs, root=2)
+        return all(np.array_equal(g, np.array(want, np.float32)) for g in got)
+    pin("ring order", ring_order)
+
+    # ragged chunks and avg, against integer closed forms: sum, then one truncating division
+    def ragged_avg():
+        rng = np.random.default_rng(7)
+        xs = [rng.integers(-1000, 1000, size=1003).astype(np.int32) for _ in range(5)]
+        got, _ = S.reduce_then_broadcast(xs, op="avg", dtype="i32", root=1)
+        tot = np.sum(np.stack(xs).astype(np.int64), axis=0)
+        want = np.where(tot >= 0, tot // 5, -((-tot) // 5)).astype(np.int32)
+        return all(np.array_equal(g, want) for g in got)
+    pin("ragged avg", ragged_avg)
+
+    # bytes: the root receives and sends N-1 buffers, every other rank one each way
+    def traffic():
+        xs = [np.ones(10, np.float32) for _ in range(4)]
+        _, st = S.reduce_then_broadcast(xs, root=3)
+        return st.received == [40, 40, 40, 120] and st.sent == [40, 40, 40, 120]
+    pin("traffic", traffic)
+    return out
+
+
+STAGED_MUTANTS = [
+    ("root folds every chunk from rank 0",
+     ("acc = to_work(have[c][a:b], dtype)", "acc = to_work(have[0][a:b], dtype)")),
+    ("root folds from its own rank",
+     ("acc = reduce_op(op, wd, acc, to_work(have[(c + k) % n][a:b], dtype))",
+      "acc = reduce_op(op, wd, acc, to_work(have[(root + k) % n][a:b], dtype))")),
+    ("avg left undivided", ("out[a:b] = finish(op, dtype, acc, n)", "out[a:b] = acc.astype(_STORAGE[dtype])")),
+    ("broadcast skips the last rank", ("    for r in range(n):\n        if r != root:\n            msg = mailbox[r].popleft()",
+                                       "    for r in range(n - 1):\n        if r != root:\n            msg = mailbox[r].popleft()")),
+    ("other ranks' buffers taken from the result", ("bufs = [np.array(x, dtype=_STORAGE[dtype], copy=True) for x in xs]",
+                                                    "bufs = [out.copy() for x in xs]")),
+    ("root's sends not counted", ("            stats.sent[root] += length * esz\n", "")),
+]
+
+
+def test_staged_oracle_passes_every_pin():
+    S = _load("oracle/staged.py", name="staged_unmutated")
+    bad = [(name, ok) for name, ok in _staged_pins(S) if ok is not True]
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("label,mutation", STAGED_MUTANTS, ids=[m[0] for m in STAGED_MUTANTS])
+def test_staged_mutant_fails_a_pin(label, mutation):
+    S = _load("oracle/staged.py", mutation, name="staged_mutant")
+    results = _staged_pins(S)
+    assert any(ok is not True for _, ok in results), f"mutant {label!r} passed every pin"
