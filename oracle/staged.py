@@ -3,9 +3,9 @@
 Sources:
 
 * bitfern.com "AllReduce Explained", section "Reduce Followed by Broadcast":
-  the simplest AllReduce sends every process's data toward a root, which
-  combines it; the root then broadcasts the completed result to every other
-  process.  The page warns that the root carries most of the traffic.
+  the plainest way to an AllReduce.  Each process's values go to one chosen
+  process, which adds them up and then sends the finished sum out to all the
+  others.  The page notes the load this puts on that one process.
 * "2.1 Collective communication primitives in detail", section 3.3
   (Reduce): the reduced result lands on the root only and the other ranks'
   buffers stay as they were; the section's note states that AllReduce is a
