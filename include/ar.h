@@ -106,10 +106,11 @@ typedef enum {
  *   works").
  * AR_ALGO_PHASES: AllReduce as reduce-scatter followed by all-gather ("2.1
  *   Collective communication primitives in detail", section 3.8), each phase
- *   one fused pass: the reduced chunk c lands in chunk c of recvbufs[c], then
- *   is copied to every other rank.  (2N+1)*S bytes, S more than the fused
- *   kernel, but the read-heavy and the write-heavy halves run apart, which is
- *   faster on MI355X HBM once N is large.
+ *   one fused pass: the reduced chunk c lands in chunk c of recvbufs[c]
+ *   (cache-allocating stores), then is copied to every other rank.  The copy
+ *   rereads S bytes, partly from the last-level cache, beyond the fused
+ *   kernel's 2N*S, but the read-heavy and the write-heavy halves run apart,
+ *   which is faster on MI355X HBM once N is large.
  * AR_ALGO_AUTO: for AllReduce, AR_ALGO_STAGED for large buffers (the
  *   AR_STAGED_MIN_* bounds below, lower for 16-bit types), else AR_ALGO_PHASES from
  *   AR_PHASES_MIN_RANKS ranks when every rank holds at least
@@ -159,15 +160,15 @@ typedef enum {
  *   Broadcast"; "2.1 Collective communication primitives in detail",
  *   section 3.3, the note that AllReduce is Reduce plus Broadcast), with the
  *   ring's association order kept, cut into segments of rank 0's results.
- *   Per segment, one launch
- *   folds every position in ring order and stores the result to recvbufs[0]
- *   only, then one launch copies it to the other ranks.  The results
- *   are reread from the device's 256 MB last-level cache, so HBM still moves
- *   N*S read and N*S written; the reading and the writing launches run apart,
- *   which MI355X HBM serves faster than the two interleaved.  The same bits
- *   as AR_ALGO_FUSED.  AllReduce only; 2 launches per segment.  A segment
- *   holds about 2 GiB / N of results, between 32 and 128 MiB; the
- *   AR_STAGE_BYTES environment variable sets it in bytes instead. */
+ *   Per segment, one launch folds every position in ring order and stores
+ *   the result to recvbufs[0] only, then one launch copies it to the other
+ *   ranks.  The results are reread from the device's 256 MB last-level
+ *   cache, so HBM still moves N*S read and N*S written; the reading and the
+ *   writing launches run apart, which MI355X HBM serves faster than the two
+ *   interleaved.  The same bits as AR_ALGO_FUSED.  AllReduce only; 2
+ *   launches per segment.  A segment holds about 2 GiB / N of results,
+ *   between 32 and 128 MiB; the AR_STAGE_BYTES environment variable sets it
+ *   in bytes instead. */
 typedef enum {
     AR_ALGO_FUSED = 0,
     AR_ALGO_RING = 1,
