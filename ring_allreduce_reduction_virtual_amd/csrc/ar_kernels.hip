@@ -69,8 +69,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_allreduce(const KernelArgs a
 // broadcast from it (bitfern.com "AllReduce Explained", section "Reduce
 // Followed by Broadcast"), while every value keeps the ring's association
 // order.  Reducing launch: the fused AllReduce's fold for the launch's tiles,
-// stored to rank 0's receive buffer only.  The stores allocate
-// in the caches (unlike every other output), so the broadcast launch that
+// stored to rank 0's receive buffer only.  The stores allocate in the caches
+// (the one-pass kernels' outputs do not), so the broadcast launch that
 // follows rereads the results from the Infinity Cache instead of HBM.  This
 // launch is then almost all reads, and the broadcast almost all writes: HBM
 // serves each direction faster alone than the two interleaved.
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void k_staged_broadcast(const KernelArgs 
 }
 
 // The same broadcast with whole tiles per block (kUnroll unit rows): faster
-// for many large buffers.
+// when all ranks' buffers hold less than 2 GiB or more than 8 GiB in all.
 template <int DT, int VEC>
 __global__ __launch_bounds__(kThreads) void k_staged_broadcast_tiles(const KernelArgs a) {
     using U = Unit<DT, VEC, false>;   // cache-allocating loads: the results sit in the Infinity Cache
