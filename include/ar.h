@@ -186,13 +186,14 @@ typedef enum {
 
 /* AR_ALGO_AUTO takes AR_ALGO_STAGED for an AllReduce over at least
  * AR_STAGED_MIN_RANKS ranks of at least AR_STAGED_MIN_BYTES bytes each and at
- * least AR_STAGED_MIN_TOTAL_BYTES bytes in all (measured on MI355X, float32:
- * 8 ranks x 256 MiB 736 us against 752 fused; 32 x 64 MiB 786 against 822
- * for either other form; 64 x 256 MiB 5,944 against 6,271 for the phases;
- * at 8 x 64 MiB and 16 x 16 MiB the fused kernel is faster). */
+ * least AR_STAGED_MIN_TOTAL_BYTES bytes in all (measured on MI355X, float32,
+ * fused / phases / staged in us: 8 x 256 MiB 752 / 823 / 736; 64 x 256 MiB
+ * 6,685 / 6,271 / 5,944; 16 x 96 MiB 600 / 581 / 583; 32 x 32 MiB
+ * 425 / 412 / 408; 16 x 64 MiB int32 395 / 391 / 393; at 8 x 128 MiB the
+ * three tie; at 8 x 64 MiB and 16 x 16 MiB the fused kernel is faster). */
 #define AR_STAGED_MIN_RANKS 8
-#define AR_STAGED_MIN_BYTES (64ull << 20)
-#define AR_STAGED_MIN_TOTAL_BYTES (2048ull << 20)
+#define AR_STAGED_MIN_BYTES (32ull << 20)
+#define AR_STAGED_MIN_TOTAL_BYTES (1024ull << 20)
 /* The same bounds for the 16-bit element types (bf16, binary16, bf16 with
  * float32 partials), whose fused kernel spends more of its time converting:
  * measured on MI355X, bf16, fused / staged in us: 8 x 64 MiB 204.6 / 201.7,

@@ -166,8 +166,9 @@ def test_block_limits_keep_the_bits(algo, monkeypatch):
 
 
 @pytest.mark.parametrize("n,count,dtype,launches", [
-    (8, 48 << 20, "float32", 1),      # 192 MiB per rank, 1.5 GiB in all: below the 4-byte bounds -> fused
-    (8, 96 << 20, "bfloat16", 4),     # the same bytes in bf16: staged (16-bit bounds), 2 segments of 128 MiB
+    (8, 24 << 20, "float32", 1),      # 96 MiB per rank, 768 MiB in all: below the 4-byte total -> fused
+    (8, 48 << 20, "bfloat16", 2),     # the same bytes in bf16: staged (16-bit bounds), one segment
+    (8, 48 << 20, "float32", 4),      # 192 MiB per rank, 1.5 GiB in all: staged, 2 segments of 128 MiB
     (8, 1 << 26, "float32", 4),       # the headline: staged, 2 segments
     (8, 1 << 24, "bfloat16", 1),      # 32 MiB per rank, 256 MiB in all: below the 16-bit total -> fused
     (4, 1 << 27, "float32", 1),       # 4 ranks: below the staged rank bound -> fused
