@@ -190,8 +190,11 @@ typedef enum {
  * fused / phases / staged in us: 8 x 256 MiB 752 / 823 / 736; 64 x 256 MiB
  * 6,685 / 6,271 / 5,944; 16 x 96 MiB 600 / 581 / 583; 32 x 32 MiB
  * 425 / 412 / 408; 16 x 64 MiB int32 395 / 391 / 393; at 8 x 128 MiB the
- * three tie; at 8 x 64 MiB and 16 x 16 MiB the fused kernel is faster). */
-#define AR_STAGED_MIN_RANKS 8
+ * three tie; at 8 x 64 MiB and 16 x 16 MiB the fused kernel is faster).  At
+ * 6 ranks, fused / staged: 6 x 256 MiB 563 / 554, 6 x 512 MiB 1,175 / 1,132;
+ * at 2-4 ranks the fused kernel wins or ties (2 x 512 MiB 367 / 422,
+ * 4 x 512 MiB 770 / 771). */
+#define AR_STAGED_MIN_RANKS 6
 #define AR_STAGED_MIN_BYTES (32ull << 20)
 #define AR_STAGED_MIN_TOTAL_BYTES (1024ull << 20)
 /* The same bounds for the 16-bit element types (bf16, binary16, bf16 with

@@ -651,9 +651,13 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     if (algo == AR_ALGO_STAGED) {
         // segments of whole tiles, each holding about stage_bytes() of rank 0's
         // results: reduce into rank 0, then broadcast from it
+        // the nearest whole number of segments, tiles spread evenly over them (so
+        // chunks rounded up to whole tiles do not leave a sliver of a segment)
         const uint32_t total = a.tile_end;
         const uint64_t tile_bytes = static_cast<uint64_t>(arimpl::kThreads) * arimpl::kUnroll * (l.vec ? 16 : k.esz);
-        const uint64_t per_seg = std::max<uint64_t>(1, stage_bytes(k.n) / tile_bytes);
+        const uint64_t stage = stage_bytes(k.n);
+        const uint64_t nseg = std::max<uint64_t>(1, (total * tile_bytes + stage / 2) / stage);
+        const uint64_t per_seg = (total + nseg - 1) / nseg;
         for (uint64_t t0 = 0; t0 < total; t0 += per_seg) {
             a.tile_first = static_cast<uint32_t>(t0);
             a.tile_end = static_cast<uint32_t>(std::min<uint64_t>(total, t0 + per_seg));

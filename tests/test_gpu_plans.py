@@ -172,6 +172,7 @@ def test_block_limits_keep_the_bits(algo, monkeypatch):
     (8, 1 << 26, "float32", 4),       # the headline: staged, 2 segments
     (8, 1 << 24, "bfloat16", 1),      # 32 MiB per rank, 256 MiB in all: below the 16-bit total -> fused
     (4, 1 << 27, "float32", 1),       # 4 ranks: below the staged rank bound -> fused
+    (6, 1 << 26, "float32", 4),       # 6 ranks x 256 MiB: staged, 2 segments of 128 MiB
     (64, 1 << 20, "float32", 2),      # 64 ranks x 4 MiB: the two phases
 ])
 def test_auto_choice(n, count, dtype, launches):
