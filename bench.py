@@ -30,7 +30,9 @@ if ROOT not in sys.path:
 
 METRIC = "AllReduce algbw/busbw GB/s + % HBM peak, N=8 ranks x 64M fp32, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "staged_allreduce_headline_counters.md")
+# rocprofv3 counter summaries of the headline call, by the form it runs
+COUNTERS_FILES = {"staged": os.path.join(ROOT, "profiles", "staged_allreduce_headline_counters.md"),
+                  "fused": os.path.join(ROOT, "profiles", "fused_allreduce_headline_counters.md")}
 # the sources the AllReduce kernels are built from (their counters are only
 # used while these are unchanged)
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_reduction_virtual_amd", "csrc", f)
@@ -60,20 +62,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per call (all the call's launches) from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source;
-    else None."""
-    if not os.path.exists(COUNTERS_FILE):
+def measured_traffic(form: str):
+    """HBM bytes per call (all the call's launches) of the given form from the
+    committed rocprofv3 counter summary, if it was taken on the current kernel
+    source; else None."""
+    path = COUNTERS_FILES.get(form)
+    if path is None or not os.path.exists(path):
         return None
-    text = open(COUNTERS_FILE).read()
+    text = open(path).read()
     m = re.search(r"^traffic_json: (\{.*\})\s*$", text, flags=re.M)
     if not m:
         return None
     d = json.loads(m.group(1))
     if d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return d.get("bytes_per_call")
+    return d.get("bytes_per_call", d.get("bytes_per_launch"))
 
 
 def ensure_library():
@@ -668,6 +671,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--algo", default="auto", choices=("auto", "fused", "staged"),
+                    help="the AllReduce form the step runs (default: the library's default)")
     ap.add_argument("--no-extra", action="store_true", help="skip the ring / phase / copy side measurements")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
@@ -745,16 +750,24 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        ar.ar_allreduce(sends, recvs)
+        if args.algo == "auto":
+            ar.ar_allreduce(sends, recvs)
+        else:
+            ar.ar_allreduce_ex(sends, recvs, algo=args.algo)
 
-    # which form the library's default (AR_ALGO_AUTO) takes here: compare its
-    # plan with the staged one (2 launches per segment) and the fused one (1)
+    # which form the timed call takes here (the library's default, AR_ALGO_AUTO,
+    # unless --algo names one): compare its plan with the staged one (2
+    # launches per segment) and the fused one (1)
     launches = {}
     for name in ("auto", "staged", "fused"):
         plan = ar.ar_allreduce_init(sends, recvs, algo=name)
         launches[name] = plan.num_launches
         plan.close()
-    default_algo = "staged" if launches["auto"] == launches["staged"] and launches["staged"] > 1 else "fused"
+    if args.algo == "auto":
+        default_algo = "staged" if launches["auto"] == launches["staged"] and launches["staged"] > 1 else "fused"
+    else:
+        default_algo = args.algo
+    launches["timed"] = launches[default_algo]
     if default_algo == "staged":
         segments = launches["staged"] // 2
         kernel_name = (f"k_staged_reduce<f32,sum,vec16> + k_staged_broadcast<f32,vec16>, "
@@ -775,7 +788,7 @@ def main():
     busbw = algbw * busbw_factor("allreduce", n)
     algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
     hbm_gbps = algo_bytes / t_s / 1e9
-    log(f"[bench] AllReduce ({default_algo}, {launches['auto']} launches): {ms * 1e3:.1f} us/call "
+    log(f"[bench] AllReduce ({default_algo}, {launches['timed']} launches): {ms * 1e3:.1f} us/call "
         f"(wall {wall_ms * 1e3:.1f} us), algbw {algbw:.1f} GB/s, "
         f"busbw {busbw:.1f} GB/s, HBM {hbm_gbps:.0f} GB/s = {hbm_gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s")
 
@@ -837,7 +850,7 @@ def main():
 
     cpu = None if args.no_cpu_baseline else cpu_baseline_headline(xs, s_bytes)
 
-    traffic = measured_traffic()
+    traffic = measured_traffic(default_algo)
     out = {
         "metric": METRIC,
         "value": round(algbw, 2),
@@ -852,8 +865,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "ring AllReduce, 8 virtual ranks x 2^26 float32 (256 MiB each), sum, "
-                               "the library's default algorithm",
-                   "nranks": n, "count": count, "op": "sum", "algo": f"auto ({default_algo})",
+                               + ("the library's default algorithm" if args.algo == "auto"
+                                  else f"the {args.algo} form"),
+                   "nranks": n, "count": count, "op": "sum",
+                   "algo": f"auto ({default_algo})" if args.algo == "auto" else args.algo,
                    "inputs": "N(0,1), seed 1"},
         "algbw_gbps": round(algbw, 2),
         "busbw_gbps": round(busbw, 2),
@@ -861,7 +876,7 @@ def main():
         "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": kernel_name, "launches_per_call": launches["auto"],
+                     "kernel": kernel_name, "launches_per_call": launches["timed"],
                      "algorithmic_bytes_per_call": algo_bytes},
         "cpu_baseline": cpu,
         "extra": extra,
