@@ -76,7 +76,7 @@ def measured_traffic(form: str):
     d = json.loads(m.group(1))
     if d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return d.get("bytes_per_call", d.get("bytes_per_launch"))
+    return d.get("bytes_per_call")
 
 
 def ensure_library():
