@@ -52,3 +52,13 @@ def test_traffic_withheld_for_other_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("stale") is None
     assert bench.measured_traffic("none") is None
     assert bench.measured_traffic("unknown") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py --gpus N with N above 1 exits with a message, before touching a GPU."""
+    import subprocess
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
