@@ -193,7 +193,10 @@ typedef enum {
  * three tie; at 8 x 64 MiB and 16 x 16 MiB the fused kernel is faster).  At
  * 6 ranks, fused / staged: 6 x 256 MiB 563 / 554, 6 x 512 MiB 1,175 / 1,132;
  * at 2-4 ranks the fused kernel wins or ties (2 x 512 MiB 367 / 422,
- * 4 x 512 MiB 770 / 771). */
+ * 4 x 512 MiB 770 / 771).  These are the common MI355X boxes, whose HBM
+ * writes 2 GiB in 371-396 us; on the few whose HBM writes almost as fast as
+ * it reads, the fused kernel is ahead at 8 x 256 MiB (659 / 680 and
+ * 696 / 734).  Either choice gives the same bits. */
 #define AR_STAGED_MIN_RANKS 6
 #define AR_STAGED_MIN_BYTES (32ull << 20)
 #define AR_STAGED_MIN_TOTAL_BYTES (1024ull << 20)
