@@ -3,18 +3,18 @@
 large size.
 
 Inputs are drawn on the device from a seeded torch generator (N(0,1)
-float32), so tens of GiB need no host copy.  The oracle sees the sampled
-columns: random positions, every chunk's first and last element, and the
-elements around 2^31, copied back to the host.
+float32), then copied to the host, where the oracle folds the whole buffers
+in the ring's order.  Its result goes back to the device once, and every
+element of every rank's output is compared with it there, bit for bit.
 """
 
 import numpy as np
 import pytest
 
 import oracle
-from oracle.ring import chunk, chunk_owner, same_bits
+from oracle.ring import same_bits
 
-from gpu_util import require_gpu
+from gpu_util import assert_every_rank_equals, poison, require_gpu, want_on_device
 
 pytestmark = pytest.mark.gpu
 
@@ -33,27 +33,11 @@ def _inputs(n, count, seed):
     return [torch.randn(count, generator=g, device="cuda:0") for _ in range(n)]
 
 
-def _positions(n, count, seed, extra=()):
-    rng = np.random.default_rng(seed)
-    edges = []
-    for c in range(n):
-        b, e = chunk(c, n, count)
-        if e > b:
-            edges += [b, e - 1]
-    pos = np.concatenate([rng.integers(0, count, 2048), np.array(edges, dtype=np.int64),
-                          np.array([p for p in extra if 0 <= p < count], dtype=np.int64)])
-    return np.unique(pos)
-
-
-def _check(sends, recvs, pos):
-    import torch
-
-    n, count = len(sends), sends[0].numel()
-    idx = torch.from_numpy(pos).to("cuda:0")
-    cols = np.stack([t[idx].cpu().numpy() for t in sends])
-    want = oracle.ring_order_fold_columns(cols, chunk_owner(pos, n, count))
-    for r, t in enumerate(recvs):
-        assert same_bits(t[idx].cpu().numpy(), want, "f32"), f"rank {r}"
+def _oracle_whole(sends):
+    """The oracle's AllReduce of the device inputs, on the host, back on the device."""
+    xs = [t.cpu().numpy() for t in sends]
+    want = oracle.ring_order_fold(xs)
+    return want, want_on_device(want, "f32")
 
 
 def test_rank_buffers_beyond_2p31_elements():
@@ -64,17 +48,16 @@ def test_rank_buffers_beyond_2p31_elements():
     n, count = 2, (1 << 31) + 37
     print(f"[large] {n} x {count} f32", flush=True)
     sends = _inputs(n, count, seed=31)
+    want, want_dev = _oracle_whole(sends)
     recvs = [torch.empty(count, device="cuda:0") for _ in range(n)]
-    edge = 1 << 31
-    pos = _positions(n, count, seed=5, extra=range(edge - 5, edge + 5))
     for algo in ("fused", "phases", "ring", "ring_pipelined", "staged"):
         print(f"[large] {algo}", flush=True)
-        for t in recvs:
-            t.fill_(-1.0)
+        poison(recvs)
         ar.ar_allreduce_ex(sends, recvs, algo=algo)
         torch.cuda.synchronize()
-        _check(sends, recvs, pos)
-        assert torch.equal(recvs[0], recvs[1])
+        assert_every_rank_equals(recvs, want_dev, algo)
+    edge = 1 << 31                          # the elements around 2^31, also on the host
+    assert same_bits(recvs[1][edge - 5:edge + 5].cpu().numpy(), want[edge - 5:edge + 5], "f32")
 
 
 def test_128_ranks_at_a_large_size():
@@ -86,15 +69,14 @@ def test_128_ranks_at_a_large_size():
     n, count = 128, (1 << 25) + 3
     print(f"[large] {n} x {count} f32", flush=True)
     sends = _inputs(n, count, seed=128)
+    _, want_dev = _oracle_whole(sends)
     recvs = [torch.empty(count, device="cuda:0") for _ in range(n)]
-    pos = _positions(n, count, seed=6)
-    ar.ar_allreduce(sends, recvs)
-    torch.cuda.synchronize()
-    _check(sends, recvs, pos)
-    first = recvs[0].clone()
-    for algo in ("fused", "phases"):
+    for algo in ("auto", "fused", "phases"):
         print(f"[large] {algo}", flush=True)
-        ar.ar_allreduce_ex(sends, recvs, algo=algo)
+        poison(recvs)
+        if algo == "auto":
+            ar.ar_allreduce(sends, recvs)
+        else:
+            ar.ar_allreduce_ex(sends, recvs, algo=algo)
         torch.cuda.synchronize()
-        for r in range(n):
-            assert torch.equal(recvs[r], first), f"{algo} rank {r}"
+        assert_every_rank_equals(recvs, want_dev, algo)

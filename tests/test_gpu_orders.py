@@ -2,17 +2,17 @@
 staged), recursive doubling, and recursive halving/doubling (fused and staged),
 against the oracle's schedules (oracle/orders.py) bit for bit, over every
 dtype and operator, in-place and offset layouts, special values, persistent
-plans and HIP graph replays, and sampled at the full workload sizes."""
+plans and HIP graph replays, and every element at the full workload sizes."""
 
 import zlib
 
 import numpy as np
 import pytest
 
-from oracle.orders import order_allreduce, order_bracketing, tree_order_fold_columns
+from oracle.orders import order_allreduce, order_bracketing, tree_order_fold
 from oracle.ring import f32_to_bf16_bits, f32_to_f16_bits, ring_order_fold, same_bits
 
-from gpu_util import from_dev, require_gpu, sample_positions, to_dev
+from gpu_util import assert_every_rank_equals, from_dev, poison, require_gpu, to_dev, want_on_device
 
 pytestmark = pytest.mark.gpu
 
@@ -239,8 +239,9 @@ def test_tree_order_graph_replays(algo):
     ("c5", ["tree", "halving_doubling"]),
     ("c3", ["tree", "halving_doubling_steps"]),
 ])
-def test_tree_orders_full_size_sampled(workload, algos):
-    """The full workloads, checked at sampled positions against the bracketing evaluated there."""
+def test_tree_orders_full_size_every_element(workload, algos):
+    """The full workloads: every element of every rank against the order's
+    bracketing evaluated over the whole buffers on the host."""
     import torch
 
     from inputs import WORKLOADS, make_inputs
@@ -251,15 +252,13 @@ def test_tree_orders_full_size_sampled(workload, algos):
     xs = make_inputs(w)
     sends = [_dev(x, dtype) for x in xs]
     recvs = _empty(w.nranks, w.count, dtype)
-    pos = sample_positions(w.count, w.nranks, seed=7)
-    idx = torch.from_numpy(pos).to("cuda:0")
-    cols = np.stack([x[pos] for x in xs])
+    wants = {}
     for algo in algos:
         print(f"[full size] {workload} {algo}", flush=True)
+        order = ORDER_OF[algo]
+        if order not in wants:
+            wants[order] = want_on_device(tree_order_fold(xs, order_bracketing(order, w.nranks), "sum", dtype), dtype)
+        poison(recvs)
         ar.ar_allreduce_ex(sends, recvs, algo=algo, dtype=dtype)
         torch.cuda.synchronize()
-        want = tree_order_fold_columns(cols, order_bracketing(ORDER_OF[algo], w.nranks), "sum", dtype)
-        for r in range(w.nranks):
-            assert same_bits(_host(recvs[r][idx], dtype), want, dtype), (algo, r)
-        for r in range(w.nranks):
-            recvs[r].fill_(0)
+        assert_every_rank_equals(recvs, wants[order], f"{workload} {algo}")

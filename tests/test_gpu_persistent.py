@@ -3,7 +3,7 @@
 pipelined ring (each slice of each chunk carried through all steps by one
 workgroup, no barrier).  The ring's bits for every dtype and operator, rank
 counts up to 128, layouts, persistent plans with workgroup caps, the full
-headline workload (sampled); the persistent ring refuses graph capture, the
+headline workload (every element); the persistent ring refuses graph capture, the
 pipelined ring replays from a graph.
 
 Every launch here runs alone on the device, as the grid barrier requires."""
@@ -16,7 +16,7 @@ import pytest
 import oracle
 from oracle.ring import f32_to_bf16_bits, f32_to_f16_bits, same_bits
 
-from gpu_util import from_dev, require_gpu, sample_positions, to_dev
+from gpu_util import assert_every_rank_equals, from_dev, poison, require_gpu, to_dev, want_on_device
 
 pytestmark = pytest.mark.gpu
 
@@ -194,21 +194,18 @@ def test_pipelined_ring_replays_from_a_graph():
 
 
 @pytest.mark.parametrize("algo", ONE_LAUNCH)
-def test_one_launch_ring_headline_full_size_sampled(algo):
+def test_one_launch_ring_headline_full_size_every_element(algo):
     import torch
 
     from inputs import WORKLOADS, make_inputs
-    from oracle.ring import chunk_owner
 
     ar = _ar()
     w = WORKLOADS["headline"]
     xs = make_inputs(w)
+    want = want_on_device(oracle.ring_order_fold(xs), "f32")
     sends = [_dev(x, "f32") for x in xs]
     recvs = _empty(w.nranks, w.count, "f32")
+    poison(recvs)
     ar.ar_allreduce_ex(sends, recvs, algo=algo)
     torch.cuda.synchronize()
-    pos = sample_positions(w.count, w.nranks, seed=12)
-    want = oracle.ring_order_fold_columns(np.stack([x[pos] for x in xs]), chunk_owner(pos, w.nranks, w.count))
-    idx = torch.from_numpy(pos).to("cuda:0")
-    for r in range(w.nranks):
-        assert same_bits(recvs[r][idx].cpu().numpy(), want, "f32"), r
+    assert_every_rank_equals(recvs, want, algo)

@@ -165,32 +165,26 @@ def test_bf16acc32_layouts(layout, algo):
 
 
 def test_c3_workload_full_size_with_float32_partials_and_avg():
-    """8 x 2^26 bf16 (the c3 workload) with float32 partials, and its average, sampled."""
+    """8 x 2^26 bf16 (the c3 workload) with float32 partials, and its average:
+    every element of every rank, for the default and every ring-order algorithm."""
     import torch
 
-    from gpu_util import sample_positions
+    from gpu_util import assert_every_rank_equals, poison, want_on_device
     from inputs import WORKLOADS, make_inputs
-    from oracle.ring import chunk_owner
 
     ar = _ar()
     w = WORKLOADS["c3"]
     xs = make_inputs(w)
     sends = [_dev(x, "bf16") for x in xs]
     recvs = _empty(w.nranks, w.count, "bf16")
-    pos = sample_positions(w.count, w.nranks, seed=5)
-    idx = torch.from_numpy(pos).to("cuda:0")
-    cols = np.stack([x[pos] for x in xs])
-    owners = chunk_owner(pos, w.nranks, w.count)
-    other = _empty(w.nranks, w.count, "bf16")
     for dtype, op in (("bf16acc32", "sum"), ("bf16acc32", "avg"), ("bf16", "avg")):
-        ar.ar_allreduce(sends, recvs, op=op, dtype=dtype)
-        torch.cuda.synchronize()
-        want = oracle.ring_order_fold_columns(cols, owners, op=op, dtype=dtype)
-        for r in range(w.nranks):
-            assert same_bits(_host(recvs[r][idx], dtype), want, dtype), (dtype, op, r)
-        # the ring's launches, the pipelined ring and the staged form give the same bits everywhere
-        for algo in ("ring", "ring_pipelined", "staged"):
-            ar.ar_allreduce_ex(sends, other, op=op, algo=algo, dtype=dtype)
+        want = want_on_device(oracle.ring_order_fold(xs, op=op, dtype=dtype), dtype)
+        for algo in ("auto", "fused", "ring", "ring_pipelined", "staged", "phases"):
+            print(f"[full size] c3 {dtype} {op} {algo}", flush=True)
+            poison(recvs)
+            if algo == "auto":
+                ar.ar_allreduce(sends, recvs, op=op, dtype=dtype)
+            else:
+                ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo, dtype=dtype)
             torch.cuda.synchronize()
-            for r in range(w.nranks):
-                assert torch.equal(other[r].view(torch.int16), recvs[0].view(torch.int16)), (dtype, op, algo, r)
+            assert_every_rank_equals(recvs, want, f"{dtype} {op} {algo}")

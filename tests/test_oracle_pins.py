@@ -489,6 +489,8 @@ def test_schedule_equals_definition(dtype, op, n, length):
         assert R.same_bits(o, want, dtype)
     # reduce-scatter followed by all-gather is AllReduce, bit for bit
     shards, _ = oracle.reduce_scatter(xs, op=op, dtype=dtype)
+    for c in range(n):                     # shard c is chunk c of the AllReduce result
+        assert R.same_bits(shards[c], want[slice(*R.chunk(c, n, length))], dtype)
     again, _ = oracle.all_gather(shards, length, dtype=dtype)
     for o in again:
         assert R.same_bits(o, want, dtype)
