@@ -291,6 +291,27 @@ ar_result_t ar_all_gather_ex(const void* const* sendbufs, void* const* recvbufs,
                              ar_dtype_t dtype, int nranks, ar_algo_t algo,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Reduce-scatter that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The same call, rules, errors and results as
+ * ar_reduce_scatter_ex with `algo`, except that the workspace the ring
+ * algorithms need (ar_workspace_bytes) is not passed in: it is a fixed array
+ * of AR_NOALLOC_SCRATCH_BYTES in device memory inside the library.  Each
+ * device holds its own copy from the first call on it until the process ends;
+ * that first call looks its address up (hipGetSymbolAddress), so make it
+ * outside a graph capture.  A call whose workspace would exceed
+ * AR_NOALLOC_SCRATCH_BYTES fails with AR_ERR_INVALID_ARGUMENT and launches
+ * nothing (float32 ring: up to 16M - 256 elements per rank).  Nothing in the
+ * array needs to start at zero, and each call overwrites what it uses, but
+ * every call on one device shares the one array: calls whose work overlaps
+ * on the same GPU (other streams, or concurrent host threads) race and give
+ * wrong results.  Algorithms that need no workspace touch the array not at
+ * all.  No call here allocates device memory. */
+#define AR_NOALLOC_SCRATCH_BYTES (64ull << 20)
+ar_result_t ar_reduce_scatter_noalloc(const void* const* sendbufs, void* const* recvbufs, size_t count,
+                                      ar_dtype_t dtype, ar_op_t op, int nranks, ar_algo_t algo,
+                                      hipStream_t stream);
+
 /* Persistent collectives, in the manner of MPI's persistent AllReduce request
  * (bitfern.com "AllReduce Explained", section "MPI_Allreduce"): *_init
  * validates the arguments and plans the launches once, with the same

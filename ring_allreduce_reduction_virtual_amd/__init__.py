@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     ar_reduce_scatter,
     ar_reduce_scatter_ex,
     ar_reduce_scatter_init,
+    ar_reduce_scatter_noalloc,
     ar_workspace_bytes,
 )
 
@@ -35,5 +36,5 @@ __all__ = [
     "ar_all_gather", "ar_all_gather_ex", "ar_workspace_bytes", "ar_chunk_range",
     "ar_get_error_string", "ar_get_last_error_detail", "ar_dtype_size",
     "ar_allreduce_init", "ar_reduce_scatter_init", "ar_all_gather_init", "ar_plan_start", "ar_plan_free",
-    "ar_plan_limit_blocks", "ar_plan_num_launches",
+    "ar_plan_limit_blocks", "ar_plan_num_launches", "ar_reduce_scatter_noalloc",
 ]

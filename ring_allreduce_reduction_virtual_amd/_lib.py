@@ -33,7 +33,10 @@ EXPORTS = (
     "ar_get_last_error_detail", "ar_dtype_size",
     "ar_allreduce_init", "ar_reduce_scatter_init", "ar_all_gather_init",
     "ar_plan_start", "ar_plan_num_launches", "ar_plan_free", "ar_plan_limit_blocks",
+    "ar_reduce_scatter_noalloc",
 )
+# bytes of the fixed device array behind ar_reduce_scatter_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -63,6 +66,7 @@ def _declare(lib):
         "ar_plan_num_launches": (_int, [_vp]),
         "ar_plan_free": (_int, [_vp]),
         "ar_plan_limit_blocks": (_int, [_vp, ctypes.c_uint]),
+        "ar_reduce_scatter_noalloc": (_int, [_vpp, _vpp, _sz, _int, _int, _int, _int, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -238,6 +238,18 @@ def ar_reduce_scatter_ex(sendbufs, recvbufs, op: str = "sum", algo: str = "fused
     return recvbufs
 
 
+def ar_reduce_scatter_noalloc(sendbufs, recvbufs, op: str = "sum", algo: str = "ring", stream=None, dtype=None):
+    """Reduce-scatter as :func:`ar_reduce_scatter_ex`, with the ring's workspace
+    taken from the library's fixed device array: no device memory is allocated."""
+    dev, dtype, sp, rp = _marshal(sendbufs, recvbufs, dtype)
+    count = _check_counts("reduce_scatter", sendbufs, recvbufs)
+    with _on_device(dev):
+        rc = _lib.lib().ar_reduce_scatter_noalloc(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
+                                                  _lib.ALGOS[algo], _stream_handle(stream))
+    _lib.check("ar_reduce_scatter_noalloc", rc)
+    return recvbufs
+
+
 def ar_all_gather(sendbufs, recvbufs, stream=None):
     """All-gather with the fused kernel: every recvbufs[r] receives all shards in rank order."""
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)

@@ -800,6 +800,8 @@ ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, Sink& sink) {
 
 }  // namespace
 
+void arimpl::set_error_detail(const char* text) { g_detail = text; }
+
 // A persistent collective: the launches one call makes, validated and planned.
 struct ar_plan_s {
     std::vector<Step> steps;

@@ -150,6 +150,10 @@ constexpr int kUnroll = AR_TILE_UNROLL;
 #define AR_HALF_TILES_MAX_TOTAL (8192ull << 20)
 #endif
 
+// Replace the calling thread's error text (what ar_get_last_error_detail
+// returns) for a failure found outside ar_api.hip.
+void set_error_detail(const char* text);
+
 // Enqueue one kernel; returns the HIP error of the launch.
 hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream);
 

@@ -107,6 +107,29 @@ def test_argument_errors_are_caught_on_the_host(lib):
     assert lib.ar_get_last_error_detail() == b""
 
 
+def test_noalloc_refuses_an_oversized_workspace_on_the_host(lib):
+    """ar_reduce_scatter_noalloc checks the workspace a call needs against its fixed
+    array before anything else: too large is an argument error, with no GPU touched."""
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    text = open(os.path.join(ROOT, "include", "ar.h")).read()
+    m = re.search(r"#define\s+AR_NOALLOC_SCRATCH_BYTES\s+\((\d+)ull\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+    n = 3
+    count = (_lib.NOALLOC_SCRATCH_BYTES - 1024) // 4 + 1           # float32 ring: one element too many
+    sends = [BASE + r * (1 << 30) for r in range(n)]
+    recvs = [BASE + (8 + r) * (1 << 30) for r in range(n)]
+    for algo in ("ring", "ring_pipelined"):
+        rc = lib.ar_reduce_scatter_noalloc(_ptrs(sends), _ptrs(recvs), count, 0, 0, n, _lib.ALGOS[algo], None)
+        assert rc == 1 and b"scratch" in lib.ar_get_last_error_detail()
+    # arguments the ordinary validation rejects are reported as it reports them
+    assert lib.ar_reduce_scatter_noalloc(_ptrs(sends), _ptrs(recvs), 10, 0, 9, n, _lib.ALGOS["ring"], None) == 1
+    assert b"op" in lib.ar_get_last_error_detail()
+    assert lib.ar_reduce_scatter_noalloc(_ptrs(sends), _ptrs(recvs), 10, 0, 0, n, _lib.ALGOS["tree"], None) == 2
+    # empty work succeeds without a device
+    assert lib.ar_reduce_scatter_noalloc(_ptrs(sends), _ptrs(recvs), 0, 0, 0, n, _lib.ALGOS["ring"], None) == 0
+
+
 def test_in_place_layouts_are_accepted_others_rejected(lib):
     """Validation of the aliasing rules, stopped before any launch by count checks."""
     n, count = 4, 1000
