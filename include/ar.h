@@ -1,9 +1,9 @@
 /*
  * ar.h — ring AllReduce over N virtual ranks resident in one GPU's HBM.
  *
- * C ABI of libar.so.  Every call is stateless ("State: none between calls",
- * tirogla.com "Ring all-reduce", section "How it works", In/Out/State line)
- * and asynchronous: it validates its arguments on the host, enqueues kernels
+ * C ABI of libar.so.  Calls keep no state from one to the next (tirogla.com
+ * "Ring all-reduce", section "How it works", the line that states the
+ * collective's inputs, outputs and state), and every call is asynchronous: it validates its arguments on the host, enqueues kernels
  * on `stream` and returns.  The arguments follow the collective's statement
  * on arjunsriva.com "AllReduce, All the Way Down", section "The Contract"
  * (send buffer, receive buffer, count, datatype, reduction, participants,
@@ -20,7 +20,7 @@
  * travels the ring from rank c: ((x_c (op) x_{c+1}) (op) x_{c+2}) ... with
  * ranks taken mod N and the result rounded to the buffer type after every
  * operation (arjunsriva.com, figure "Ring AllReduce · follow chunk 0";
- * tirogla.com "Ring all-reduce", "How it works").  Both algorithms below give
+ * tirogla.com "Ring all-reduce", "How it works").  The ring-order algorithms below give
  * these bits exactly, and every rank receives identical bits.
  *
  * Pointers.  `sendbufs` and `recvbufs` are HOST arrays of `nranks` DEVICE
@@ -350,7 +350,11 @@ ar_result_t ar_plan_limit_blocks(ar_plan_t plan, unsigned max_blocks);
 ar_result_t ar_plan_free(ar_plan_t plan);
 
 /* Workspace in bytes that a call with these arguments needs (0: none).
- * Returns (size_t)-1 for invalid arguments. */
+ * Returns (size_t)-1 for invalid arguments.  The leading `coll` names the
+ * collective: the size depends on it (only the ring reduce-scatter, whose
+ * receive buffers are one shard long, and the float32-partial variants keep
+ * partial sums in a workspace), so this takes one argument more than a
+ * per-algorithm size would. */
 size_t ar_workspace_bytes(ar_coll_t coll, ar_algo_t algo, size_t count, ar_dtype_t dtype, int nranks);
 
 /* Bounds of chunk c: *begin = c*count/nranks, *end = (c+1)*count/nranks

@@ -10,8 +10,7 @@ Sources (the pages on ring AllReduce):
   sends chunk (r+1-s) mod N, receives chunk (r-s) mod N and overwrites.  The
   same page's "Code" section fixes the chunk bounds as
   [c*len/N, (c+1)*len/N) with integer (floor) division, uneven on purpose,
-  and the receiving rank adds the incoming values to its own
-  ("local += incoming").
+  and the receiving rank adds the incoming values into its own buffer.
 * ramchalamkr.github.io "NCCL Primitives Deep Dive", section "Ring
   All-Gather": the standalone all-gather in which rank r starts with shard r
   in slot r and at step s sends slot (r-s) mod N and receives slot

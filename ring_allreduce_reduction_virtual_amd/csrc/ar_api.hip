@@ -580,10 +580,11 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         ptrs.push_back(s);
         ptrs.push_back(d);
     }
-    // AUTO: the staged reduce-then-broadcast for large buffers over 8 ranks or
-    // more; otherwise two fused phases from phases_min_ranks() ranks when every
-    // rank holds at least AR_PHASES_MIN_BYTES; below that the one fused kernel
-    // wins (and the small-message kernel for the smallest messages)
+    // AUTO: the staged reduce-then-broadcast for large buffers over
+    // AR_STAGED_MIN_RANKS ranks or more; otherwise two fused phases from
+    // phases_min_ranks() ranks when every rank holds at least
+    // AR_PHASES_MIN_BYTES; below that the one fused kernel wins (and the
+    // small-message kernel for the smallest messages)
     if (algo == AR_ALGO_AUTO) {
         const uint64_t per_rank = k.count * k.esz;
         const bool narrow = k.esz == 2;   // 16-bit types: lower bounds (measured)

@@ -83,9 +83,9 @@ def test_cancelling_rotations_single_out_the_ring_order():
         assert out[0][c] == np.float32(1.0)
 
 
+@pytest.mark.parametrize("n,length", [(1, 7), (2, 5), (3, 1), (6, 1001), (8, 8 * 64 + 3)])
 @pytest.mark.parametrize("dtype,op", [("f32", "sum"), ("bf16", "sum"), ("i32", "max")])
-def test_threaded_ring_equals_lockstep(dtype, op):
-    n, length = 6, 1001
+def test_threaded_ring_equals_lockstep(dtype, op, n, length):
     rng = np.random.default_rng(4)
     if dtype == "f32":
         xs = [rng.standard_normal(length).astype(np.float32) for _ in range(n)]
