@@ -492,7 +492,173 @@ def load_probe_library():
     lib.arprobe_stream.restype = ctypes.c_int
     lib.arprobe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.arprobe_pattern.restype = ctypes.c_int
+    lib.arprobe_pattern.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.arprobe_xcd.restype = ctypes.c_int
+    lib.arprobe_xcd.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
+                                ctypes.c_void_p]
     return lib
+
+
+def run_xcd_patterns(lib, steps=20):
+    """Whether the fast write pattern is about XCDs: writes in which XCD x
+    writes buffer x only (8 buffers, and 7 with one XCD idle), against the
+    tile-major order over 7 and 16 buffers, where XCDs and buffers do not
+    line up; then the staged broadcast's shape (a just-written source copied
+    to 7 destinations) with one workgroup per tile storing to all 7, against
+    XCD x copying to destination x only, for 128 MiB and 32 MiB sources.
+    One JSON line each; median of `steps` event-timed calls."""
+    import ctypes
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, before=None):
+        ts = []
+        for i in range(steps + 3):
+            if before is not None:
+                before()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            if i >= 3:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: error {rc}")
+
+    def emit(direction, pattern, nbytes, us, buffers):
+        row = {"ceiling_pattern": pattern, "direction": direction, "buffers": buffers, "bytes": nbytes,
+               "us": round(us, 1), "tbps": round(nbytes / us / 1e6, 3),
+               "frac_of_8tbps": round(nbytes / us / 1e6 / (HBM_PEAK_GBPS / 1e3), 4)}
+        print(json.dumps(row), flush=True)
+
+    mib = 1 << 20
+    for n, size in ((8, 256 * mib), (7, 256 * mib)):
+        bufs = [torch.empty(size // 4, device=dev) for _ in range(n)]
+        bp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in bufs])
+        nvec = size // 16
+        emit("write", f"XCD x writes buffer x only ({n} buffers; {8 - n} XCDs idle), 8 KiB per workgroup, plain",
+             n * size, timed(lambda: check(lib.arprobe_xcd(0, None, bp, n, nvec, stream.cuda_stream), "xcd")),
+             f"{n} x {size >> 20} MiB")
+        if n == 7:
+            emit("write", "one buffer per workgroup, 8 KiB runs, tile-major over 7 buffers, plain", n * size,
+                 timed(lambda: check(lib.arprobe_pattern(1, 0, 1, 512, bp, n, nvec, None, stream.cuda_stream),
+                                     "pattern")), f"{n} x {size >> 20} MiB")
+        del bufs
+    n, size = 16, 128 * mib
+    bufs = [torch.empty(size // 4, device=dev) for _ in range(n)]
+    bp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in bufs])
+    emit("write", "one buffer per workgroup, 8 KiB runs, tile-major over 16 buffers, plain", n * size,
+         timed(lambda: check(lib.arprobe_pattern(1, 0, 1, 512, bp, n, size // 16, None, stream.cuda_stream),
+                             "pattern")), f"{n} x {size >> 20} MiB")
+    del bufs
+    for g in (128 * mib, 32 * mib):
+        src = torch.empty(g // 4, device=dev)
+        sp = (ctypes.c_void_p * 1)(src.data_ptr())
+        dst = [torch.empty(g // 4, device=dev) for _ in range(7)]
+        dp = (ctypes.c_void_p * 7)(*[t.data_ptr() for t in dst])
+        nvec = g // 16
+
+        def produce():
+            check(lib.arprobe_pattern(1, 0, 1, 512, sp, 1, nvec, None, stream.cuda_stream), "produce")
+
+        for kind, name in ((1, "one workgroup per tile storing to all 7"), (2, "XCD x copies to destination x")):
+            us = timed(lambda: check(lib.arprobe_xcd(kind, src.data_ptr(), dp, 7, nvec, stream.cuda_stream), "bcast"),
+                       before=produce)
+            emit("write", f"broadcast of a just-written {g >> 20} MiB source to 7 destinations: {name}", 7 * g, us,
+                 f"1 + 7 x {g >> 20} MiB")
+        del src, dst
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def run_ceiling_patterns(lib, n=8, count=1 << 26, steps=20):
+    """Read and write rates of HBM for access patterns other than the kernels'
+    own, over n buffers of `count` float32 (the headline's 8 x 256 MiB by
+    default), one JSON line per pattern: the kernels' pattern (each workgroup
+    one 8 KiB tile of every buffer) with nontemporal and plain stores; one
+    buffer per workgroup with contiguous runs of 8, 64 and 256 KiB, in
+    buffer-major and tile-major block order, nontemporal and plain; reads the
+    same ways; and torch's fill_ and hipMemsetD32Async on one 2 GiB tensor.
+    Median of `steps` single calls, event-timed."""
+    import ctypes
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    bufs = [torch.empty(count, device=dev) for _ in range(n)]
+    for t in bufs:
+        t.fill_(0.5)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    bp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in bufs])
+    nvec = count * 4 // 16
+    nbytes = n * count * 4
+    rows = []
+
+    def emit(direction, pattern, us):
+        row = {"ceiling_pattern": pattern, "direction": direction, "buffers": f"{n} x {count * 4 >> 20} MiB",
+               "bytes": nbytes, "us": round(us, 1), "tbps": round(nbytes / us / 1e6, 3),
+               "frac_of_8tbps": round(nbytes / us / 1e6 / (HBM_PEAK_GBPS / 1e3), 4)}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+
+    def timed(fn):
+        return median_call_ms(fn, steps, 3, stream)[0] * 1e3
+
+    def stream_probe(kind):
+        rc = lib.arprobe_stream(kind, bp, bp, n, nvec, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"arprobe_stream {kind}: {rc}")
+
+    def pattern_probe(write, nt, order, run):
+        rc = lib.arprobe_pattern(write, nt, order, run, bp, n, nvec, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"arprobe_pattern {write} {nt} {order} {run}: {rc}")
+
+    emit("write", "kernels' pattern: 8 KiB of every buffer per workgroup, nontemporal", timed(lambda: stream_probe(1)))
+    emit("write", "kernels' pattern: 8 KiB of every buffer per workgroup, plain stores",
+         timed(lambda: pattern_probe(1, 0, 0, 0)))
+    for run_kib in (8, 64, 256):
+        run = run_kib * 1024 // 16
+        for order, oname in ((0, "buffer-major"), (1, "tile-major")):
+            for nt in (1, 0):
+                emit("write", f"one buffer per workgroup, {run_kib} KiB runs, {oname}, "
+                              f"{'nontemporal' if nt else 'plain stores'}",
+                     timed(lambda: pattern_probe(1, nt, order, run)))
+    emit("read", "kernels' pattern: 8 KiB of every buffer per workgroup, nontemporal", timed(lambda: stream_probe(0)))
+    for run_kib in (64, 256):
+        run = run_kib * 1024 // 16
+        for order, oname in ((0, "buffer-major"), (1, "tile-major")):
+            emit("read", f"one buffer per workgroup, {run_kib} KiB runs, {oname}, nontemporal",
+                 timed(lambda: pattern_probe(0, 1, order, run)))
+    del bufs
+    torch.cuda.empty_cache()
+    big = torch.empty(n * count, device=dev)
+    emit("write", "torch fill_ of one 2 GiB tensor", timed(lambda: big.fill_(1.0)))
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipMemsetD32Async.restype = ctypes.c_int
+    hip.hipMemsetD32Async.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p]
+
+    def memset():
+        rc = hip.hipMemsetD32Async(big.data_ptr(), 7, big.numel(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipMemsetD32Async: {rc}")
+
+    emit("write", "hipMemsetD32Async of one 2 GiB tensor", timed(memset))
+    del big
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rows
 
 
 def probe_times_us(lib, src, dst, stream, kinds=(("read", 0), ("write", 1), ("copy", 2), ("mix", 3)), steps=20):
@@ -536,6 +702,10 @@ def run_ceiling(args):
         raise SystemExit("libarprobe.so is not built (python -m ring_allreduce_reduction_virtual_amd.build)")
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    run_ceiling_patterns(lib)
+    run_xcd_patterns(lib)
+    if args.patterns_only:
+        return
     for n, count in ((8, 1 << 26), (16, 1 << 24), (64, 1 << 26)):
         s_bytes = count * 4
         src = [torch.randn(count, device=dev) for _ in range(n)]
@@ -691,6 +861,8 @@ def main():
     ap.add_argument("--ceiling", action="store_true",
                     help="instead of the headline line: HBM read-only, write-only, copy and AllReduce-shaped "
                          "probes beside the fused AllReduce (the bound its traffic allows)")
+    ap.add_argument("--patterns-only", action="store_true",
+                    help="with --ceiling: only the table of read and write patterns (8 x 256 MiB)")
     ap.add_argument("--size-sweep", action="store_true",
                     help="instead of the headline line: AllReduce time against message size (8 ranks, f32, 1 element "
                          "to 1 GiB per rank), every schedule, with an alpha-beta fit")

@@ -100,7 +100,168 @@ __global__ __launch_bounds__(kThreads) void k_mix(const Table t) {
     }
 }
 
+// Patterned streams: each block moves one contiguous run of `run` vectors of
+// ONE buffer, so a wave reads or writes long stretches of a single buffer.
+// order 0 (buffer-major): consecutive blocks walk buffer 0's runs, then
+// buffer 1's; order 1 (tile-major): consecutive blocks take run j of
+// buffers 0, 1, ..., n-1 in turn.  Each thread moves 4 vectors per pass of
+// the block over its run (16 KiB per block per pass).  Block b's run lies in
+// [0, nvec) of one buffer by construction: runs = nvec / run, blocks = n * runs.
+template <bool WRITE, bool NT>
+__global__ __launch_bounds__(kThreads) void k_pattern(const Table t, uint64_t run, uint64_t runs, int order,
+                                                      u32x4* sink) {
+    const uint64_t b = blockIdx.x;
+    const int q = order == 0 ? static_cast<int>(b / runs) : static_cast<int>(b % static_cast<uint64_t>(t.n));
+    const uint64_t j = order == 0 ? b % runs : b / static_cast<uint64_t>(t.n);
+    const uint64_t first = j * run;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    const u32x4 v = {static_cast<uint32_t>(b), 1u, 2u, 3u};
+    for (uint64_t k = threadIdx.x; k < run; k += 4 * kThreads) {
+        if constexpr (WRITE) {
+            u32x4* d = t.dst[q] + first + k;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (k + u * kThreads < run) {
+                    if constexpr (NT) {
+                        st(d + u * kThreads, v);
+                    } else {
+                        d[u * kThreads] = v;
+                    }
+                }
+            }
+        } else {
+            const u32x4* p = t.src[q] + first + k;
+            u32x4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (k + u * kThreads < run) x[u] = NT ? ld(p + u * kThreads) : p[u * kThreads];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (k + u * kThreads < run) acc ^= x[u];
+            }
+        }
+    }
+    if constexpr (!WRITE) {
+        if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) *sink = acc;
+    }
+}
+
+// The kernels' write pattern with plain (cache-allocating) stores: k_write
+// without the nontemporal hint.
+__global__ __launch_bounds__(kThreads) void k_write_plain(const Table t) {
+    const uint64_t v0 = blockIdx.x * kTile + threadIdx.x;
+    const u32x4 v = {static_cast<uint32_t>(v0), 1u, 2u, 3u};
+    for (int r = 0; r < t.n; ++r) {
+        t.dst[r][v0] = v;
+        t.dst[r][v0 + kThreads] = v;
+    }
+}
+
+// Writes in which XCD x (workgroups are handed to MI355X's 8 XCDs in turn,
+// block b to XCD b mod 8) writes buffer x only: block b writes tile b / 8
+// (8 KiB) of buffer b mod 8, and blocks whose b mod 8 >= n do nothing, so
+// with n < 8 some XCDs idle.  Grid: 8 * tiles blocks.
+__global__ __launch_bounds__(kThreads) void k_xcd_write(const Table t) {
+    const uint64_t b = blockIdx.x;
+    const int x = static_cast<int>(b % 8);
+    if (x >= t.n) return;
+    const uint64_t v0 = (b / 8) * kTile + threadIdx.x;
+    const u32x4 v = {static_cast<uint32_t>(b), 1u, 2u, 3u};
+    t.dst[x][v0] = v;
+    t.dst[x][v0 + kThreads] = v;
+}
+
+// Broadcast shapes: src (one buffer, just written) copied to n destinations.
+// mode 0: one block per 8 KiB tile, loading it once and storing it to every
+//   destination (the staged broadcast's shape);
+// mode 1: XCD x copies to destination x only: block b copies tile b / 8 of
+//   src to destination b mod 8 (blocks with b mod 8 >= n idle), so each tile
+//   is loaded by n blocks on n XCDs.  Grid: 8 * tiles blocks.
+// Plain loads (the source sits in the last-level cache) and plain stores.
+__global__ __launch_bounds__(kThreads) void k_bcast(const Table t, int mode) {
+    const uint64_t b = blockIdx.x;
+    if (mode == 0) {
+        const uint64_t v0 = b * kTile + threadIdx.x;
+        const u32x4 a = t.src[0][v0], c = t.src[0][v0 + kThreads];
+        for (int q = 0; q < t.n; ++q) {
+            t.dst[q][v0] = a;
+            t.dst[q][v0 + kThreads] = c;
+        }
+        return;
+    }
+    const int x = static_cast<int>(b % 8);
+    if (x >= t.n) return;
+    const uint64_t v0 = (b / 8) * kTile + threadIdx.x;
+    const u32x4 a = t.src[0][v0], c = t.src[0][v0 + kThreads];
+    t.dst[x][v0] = a;
+    t.dst[x][v0 + kThreads] = c;
+}
+
 }  // namespace
+
+// extern "C" int arprobe_xcd(int kind, const void* src, void* const* dst, int n,
+//     uint64_t nvec, hipStream_t s)
+//   kind 0: k_xcd_write over the n (<= 8) buffers dst of nvec vectors;
+//   kind 1, 2: k_bcast mode 0, 1 from src (nvec vectors) to the n (<= 8)
+//   destinations.  nvec a multiple of 512.  Returns 0, 1 (bad arguments) or 2.
+extern "C" int arprobe_xcd(int kind, const void* src, void* const* dst, int n, uint64_t nvec, hipStream_t s) {
+    if (n < 1 || n > 8 || nvec == 0 || nvec % kTile != 0 || nvec / kTile > 0x0fffffffull || dst == nullptr) return 1;
+    if (kind < 0 || kind > 2 || (kind > 0 && (src == nullptr || reinterpret_cast<uintptr_t>(src) % 16 != 0))) return 1;
+    Table t{};
+    t.n = n;
+    t.src[0] = static_cast<const u32x4*>(src);
+    for (int r = 0; r < n; ++r) {
+        if (dst[r] == nullptr || reinterpret_cast<uintptr_t>(dst[r]) % 16 != 0) return 1;
+        t.dst[r] = static_cast<u32x4*>(dst[r]);
+    }
+    const uint64_t tiles = nvec / kTile;
+    const dim3 block(kThreads);
+    if (kind == 0) hipLaunchKernelGGL(k_xcd_write, dim3(static_cast<unsigned>(8 * tiles)), block, 0, s, t);
+    else if (kind == 1) hipLaunchKernelGGL(k_bcast, dim3(static_cast<unsigned>(tiles)), block, 0, s, t, 0);
+    else hipLaunchKernelGGL(k_bcast, dim3(static_cast<unsigned>(8 * tiles)), block, 0, s, t, 1);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// extern "C" int arprobe_pattern(int write, int nt, int order, uint64_t run,
+//     const void* const* bufs, int n, uint64_t nvec, void* sink, hipStream_t s)
+//   One patterned stream (k_pattern) over n buffers of nvec 16-byte vectors:
+//   write != 0 stores, else loads (sink as for arprobe_stream); nt picks the
+//   nontemporal hint; order 0 buffer-major, 1 tile-major; run vectors per
+//   block, a divisor of nvec.  With run == 0 it is the kernels' own write
+//   pattern with plain stores (k_write_plain; nvec a multiple of 512).
+//   Returns 0 on success, 1 for bad arguments, 2 for a launch error.
+extern "C" int arprobe_pattern(int write, int nt, int order, uint64_t run, const void* const* bufs, int n,
+                               uint64_t nvec, void* sink, hipStream_t s) {
+    if (n < 1 || n > kProbeMax || nvec == 0 || bufs == nullptr || (order != 0 && order != 1)) return 1;
+    Table t{};
+    t.n = n;
+    for (int r = 0; r < n; ++r) {
+        if (bufs[r] == nullptr || reinterpret_cast<uintptr_t>(bufs[r]) % 16 != 0) return 1;
+        t.src[r] = static_cast<const u32x4*>(bufs[r]);
+        t.dst[r] = static_cast<u32x4*>(const_cast<void*>(bufs[r]));
+    }
+    const dim3 block(kThreads);
+    if (run == 0) {
+        if (!write || nvec % kTile != 0 || nvec / kTile > 0x7fffffffull) return 1;
+        hipLaunchKernelGGL(k_write_plain, dim3(static_cast<unsigned>(nvec / kTile)), block, 0, s, t);
+        return hipGetLastError() == hipSuccess ? 0 : 2;
+    }
+    if (nvec % run != 0) return 1;
+    const uint64_t runs = nvec / run;
+    const uint64_t blocks = runs * static_cast<uint64_t>(n);
+    if (blocks > 0x7fffffffull || (!write && sink == nullptr)) return 1;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    u32x4* sk = static_cast<u32x4*>(sink);
+    if (write) {
+        if (nt) hipLaunchKernelGGL((k_pattern<true, true>), grid, block, 0, s, t, run, runs, order, sk);
+        else hipLaunchKernelGGL((k_pattern<true, false>), grid, block, 0, s, t, run, runs, order, sk);
+    } else {
+        if (nt) hipLaunchKernelGGL((k_pattern<false, true>), grid, block, 0, s, t, run, runs, order, sk);
+        else hipLaunchKernelGGL((k_pattern<false, false>), grid, block, 0, s, t, run, runs, order, sk);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 extern "C" int arprobe_stream(int kind, const void* const* src, void* const* dst, int n, uint64_t nvec, void* sink,
                               hipStream_t s) {
