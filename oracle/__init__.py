@@ -14,13 +14,18 @@ What it holds, each piece written from the pages on ring AllReduce:
                 all-gather, the element operators, bf16 round-to-nearest-even,
                 and the closed definition of the result (the ring's
                 association order) used for sampled checks at full size;
-* ``threaded``  one thread per rank with queue channels, the same program
-                the Rust listing on that page runs, with a receive time-out
-                that turns a stuck ring into an error;
+* ``threaded``  one thread per rank, each a state machine that answers
+                arrivals and forwards the chunk it just completed, with a
+                receive time-out that turns a stuck ring into an error;
 * ``orders``    the tree-shaped schedules (binomial tree reduce and
                 distribution, recursive doubling, and Rabenseifner's recursive
                 halving and doubling), executed the same way, and the
                 bracketings they compute written from their definitions;
+* ``dbt``       the double binary tree: each half of the buffer reduced up
+                one of two in-order binary trees and sent back down it, no
+                rank an inner node of both (the two-tree construction of
+                Sanders, Speck and Träff, 2009), executed stage by stage,
+                and each half's bracketing evaluated directly;
 * ``explore``   brute force for tiny rings: every interleaving of the ranks'
                 send/receive events, and every bracketing of an N-term sum;
 * ``staged``    AllReduce as a reduce onto a root followed by a broadcast
@@ -63,3 +68,4 @@ from .orders import (  # noqa: F401,E402
     tree_order_fold_columns,
 )
 from .staged import reduce_then_broadcast, reduce_to_root  # noqa: F401,E402
+from .dbt import double_binary_tree_allreduce, double_binary_tree_fold, double_binary_trees  # noqa: F401,E402

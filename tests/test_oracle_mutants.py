@@ -393,3 +393,100 @@ def test_staged_mutant_fails_a_pin(label, mutation):
     S = _load("oracle/staged.py", mutation, name="staged_mutant")
     results = _staged_pins(S)
     assert any(ok is not True for _, ok in results), f"mutant {label!r} passed every pin"
+
+
+# --------------------------------------------------------------------------
+# pins against oracle/dbt.py
+# --------------------------------------------------------------------------
+
+# the two trees typed by hand from the construction (as in test_oracle_dbt.py)
+DBT0 = {4: (((0, 1), 2), 3), 6: ((((0, 1), 2), 3), (4, 5)), 8: (((((0, 1), 2), 3), ((4, 5), 6)), 7)}
+DBT1 = {4: (((1, 2), 3), 0), 6: ((((1, 2), 3), 4), (5, 0)), 8: (((((1, 2), 3), 4), ((5, 6), 7)), 0)}
+
+
+def _dbt_pins(D):
+    from oracle.explore import evaluate
+    from oracle.ring import same_bits
+
+    out = []
+
+    def pin(name, fn):
+        try:
+            out.append((name, bool(fn())))
+        except Exception as e:  # noqa: BLE001
+            out.append((name, e))
+
+    def spread(n, m, seed):
+        rng = np.random.default_rng(seed)
+        return [(rng.choice([-1.0, 1.0], m) * rng.uniform(1, 2, m) * np.exp2(rng.integers(-20, 21, m)))
+                .astype(np.float32) for _ in range(n)]
+
+    def bracket():
+        for n in DBT0:
+            m = 257                                   # odd: the halves are 128 and 129 elements
+            xs = spread(n, m, n)
+            got, _ = D.double_binary_tree_allreduce(xs)
+            want = np.concatenate([evaluate(DBT0[n], [x[:128] for x in xs]),
+                                   evaluate(DBT1[n], [x[128:] for x in xs])])
+            if not all(same_bits(g, want, "f32") for g in got):
+                return False
+        return True
+    pin("hand-typed trees on each half", bracket)
+    pin("definitions", lambda: all(D.double_binary_trees(n) == (DBT0[n], DBT1[n]) for n in DBT0))
+
+    def exact():
+        rng = np.random.default_rng(11)
+        for n in (2, 3, 5, 6, 7, 9, 16):
+            for length in (1, 5, 3 * n + 2):
+                ints = [rng.integers(-8, 9, size=length) for _ in range(n)]
+                got, _ = D.double_binary_tree_allreduce([x.astype(np.float32) for x in ints])
+                if not all(np.array_equal(g, np.sum(ints, axis=0).astype(np.float32)) for g in got):
+                    return False
+                got, _ = D.double_binary_tree_allreduce([x.astype(np.int32) for x in ints], "avg", "i32")
+                s = np.sum(ints, axis=0)
+                if not all(np.array_equal(g, (np.sign(s) * (np.abs(s) // n)).astype(np.int32)) for g in got):
+                    return False
+        return True
+    pin("exact sums and int avg", exact)
+
+    def cost():
+        for n in (5, 8, 13):
+            length = 64 * n
+            S = 4 * length
+            _, st = D.double_binary_tree_allreduce([np.ones(length, np.float32) for _ in range(n)])
+            if st.stages != 2 * (n.bit_length() - 1) or sum(st.sent) != 2 * (n - 1) * S or max(st.sent) > 2 * S + 8:
+                return False
+        return True
+    pin("stages and bytes", cost)
+    return out
+
+
+DBT_MUTANTS = [
+    ("second tree not moved on", ("    return (p - 1 + tree) % n", "    return (p - 1) % n")),
+    ("right child takes the smallest step", ("    for j in range(h - 1, -1, -1):", "    for j in range(0, h):")),
+    ("own value joins after both children", [
+        ("                v = reduce_op(op, wd, mail.take(me, rank_of(left, t, n), (t, \"up\", left), _ITEMSIZE[wd]),\n                              val[t][p])",
+         "                v = mail.take(me, rank_of(left, t, n), (t, \"up\", left), _ITEMSIZE[wd])"),
+        ("                val[t][p] = v\n                up(t, p, v)",
+         "                v = reduce_op(op, wd, v, val[t][p])\n                val[t][p] = v\n                up(t, p, v)")]),
+    ("halves split by ceiling", ("    return chunk(0, 2, length), chunk(1, 2, length)",
+                                 "    return (0, (length + 1) // 2), ((length + 1) // 2, length)")),
+    ("root left unfinished", ("        final[t][top] = finish(op, dtype, val[t][top], n)",
+                              "        final[t][top] = finish(op, dtype, val[t][top], 1)")),
+    ("distribution skips right children", ("                    for c in children(p, n):\n                        if c is not None:\n                            mail.send(",
+                                           "                    for c in children(p, n)[:1]:\n                        if c is not None:\n                            mail.send(")),
+    ("root one level too low", ("    while 2 * r <= n:", "    while 2 * r < n:")),
+]
+
+
+def test_dbt_oracle_passes_every_pin():
+    D = _load("oracle/dbt.py", name="dbt_unmutated")
+    bad = [(name, ok) for name, ok in _dbt_pins(D) if ok is not True]
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("label,mutation", DBT_MUTANTS, ids=[m[0] for m in DBT_MUTANTS])
+def test_dbt_mutant_fails_a_pin(label, mutation):
+    D = _load("oracle/dbt.py", mutation, name="dbt_mutant")
+    results = _dbt_pins(D)
+    assert any(ok is not True for _, ok in results), f"mutant {label!r} passed every pin"
