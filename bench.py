@@ -338,7 +338,9 @@ def run_orders(args):
         recvs = [torch.empty(count, dtype=tdt[dt], device=dev) for _ in range(n)]
         s_bytes = count * sends[0].element_size()
         for algo in ("fused", "ring", "ring_persistent", "ring_pipelined", "tree", "halving_doubling", "tree_steps",
-                     "recursive_doubling", "halving_doubling_steps"):
+                     "recursive_doubling", "halving_doubling_steps", "double_binary_tree", "double_binary_tree_steps"):
+            if algo in ("recursive_doubling", "halving_doubling", "halving_doubling_steps") and n & (n - 1):
+                continue
             med, mn = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 10, 2, stream)
             algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
             print(json.dumps({"orders": name, "algo": algo, "dtype": dt, "nranks": n, "count": count,
@@ -349,13 +351,13 @@ def run_orders(args):
         del sends, recvs, xs
         torch.cuda.empty_cache()
 
-    # latency regime: 4 KiB per rank at 4, 8 and 64 ranks
-    for n in (4, 8, 64):
+    # latency regime: 4 KiB per rank at 4, 8, 64 and 128 ranks
+    for n in (4, 8, 64, 128):
         count = 1024
         sends = [torch.randn(count, device=dev) for _ in range(n)]
         recvs = [torch.empty(count, device=dev) for _ in range(n)]
         for algo in ("fused", "ring", "ring_persistent", "ring_pipelined", "tree", "tree_steps", "recursive_doubling",
-                     "halving_doubling_steps"):
+                     "halving_doubling_steps", "double_binary_tree", "double_binary_tree_steps"):
             med, _ = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 200, 5, stream)
             plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
             pmed, _ = median_call_ms(plan.start, 200, 5, stream)
@@ -735,7 +737,19 @@ def run_ceiling(args):
 
 
 SWEEP_ALGOS = ("fused", "ring", "ring_persistent", "ring_pipelined", "tree", "tree_steps", "recursive_doubling",
-               "halving_doubling_steps")
+               "halving_doubling_steps", "double_binary_tree", "double_binary_tree_steps")
+
+
+def dbt_steps_bytes_factor(n: int) -> int:
+    """HBM bytes of the double binary tree's level-by-level schedule in units of S.
+
+    Per tree (half the buffer): each of the floor(N/2) inner nodes reads its
+    own half and one partial per child (N - 1 children in all) and writes its
+    partial; going down, each inner node reads its half once and writes it to
+    every child.  Reads 2 floor(N/2) + N - 1 halves and writes
+    floor(N/2) + N - 1; the two trees together 3 floor(N/2) + 2 (N - 1) times S.
+    """
+    return 3 * (n // 2) + 2 * (n - 1)
 
 
 def run_size_sweep(args):
@@ -782,7 +796,10 @@ def run_size_sweep(args):
                                          ("ring_pipelined", 5 * (n - 1), 1),
                                          ("tree", 2 * n, 1), ("tree_steps", 5 * (n - 1), 2 * L),
                                          ("recursive_doubling", 2 * n * L, L),
-                                         ("halving_doubling_steps", 5 * (n - 1), 2 * L)):
+                                         ("halving_doubling_steps", 5 * (n - 1), 2 * L),
+                                         ("double_binary_tree", 2 * n, 1),
+                                         ("double_binary_tree_steps", dbt_steps_bytes_factor(n),
+                                          2 * (n.bit_length() - 1))):
         pts = [(c * 4 * bytes_factor, t / 1e3) for a, c, t in rows if a == algo]
         A = np.array([[launches, b] for b, _ in pts], dtype=np.float64)
         y = np.array([t for _, t in pts])
@@ -835,7 +852,30 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
+def release():
+    """Close what a run leaves alive and wait for the GPU before the interpreter
+    exits: plans and captured graphs dropped, the caching allocator emptied,
+    the device synchronized.  The HIP runtime and a profiler attached to the
+    process then tear down with nothing of the run still pending."""
+    import gc
+
+    gc.collect()
+    if "torch" in sys.modules:
+        import torch
+
+        if torch.cuda.is_initialized():
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
+
 def main():
+    try:
+        _main()
+    finally:
+        release()
+
+
+def _main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)

@@ -168,7 +168,25 @@ typedef enum {
  *   interleaved.  The same bits as AR_ALGO_FUSED.  AllReduce only; 2
  *   launches per segment.  A segment holds about 2 GiB / N of results,
  *   between 32 and 128 MiB; the AR_STAGE_BYTES environment variable sets it
- *   in bytes instead. */
+ *   in bytes instead.
+ * AR_ALGO_DOUBLE_BINARY_TREE: the double binary tree (tirogla.com "Ring
+ *   all-reduce", "How it works", cost model: about 2 log2 N latency terms
+ *   and 2 S/B; NCCL's choice for small messages at large N), built as
+ *   Sanders, Speck and Traff's two trees ("Two-tree algorithms for full
+ *   bandwidth broadcast, reduction and scan", 2009): the buffer's floor
+ *   halves [0, count/2) and [count/2, count) are reduced in two binary trees
+ *   over the ranks, no rank an inner node of both.  Tree 0 is the in-order
+ *   tree over positions 1..N holding ranks 0..N-1 (position p's height is its
+ *   trailing zero bits; an inner node p of height h has children
+ *   p - 2^(h-1) and p + 2^j for the largest j < h with p + 2^j <= N); tree 1
+ *   is the same with every rank moved on by one.  A node combines
+ *   ((left (op) own) (op) right): at N = 8 half 0 is
+ *   ((((((x0 x1) x2) x3) ((x4 x5) x6)) x7) and half 1 the same over ranks
+ *   1, 2, ..., 7, 0.  One fused pass (2*N*S bytes), any N.
+ * AR_ALGO_DOUBLE_BINARY_TREE_STEPS: the same trees level by level:
+ *   floor(log2 N) reducing launches up both trees at once, then as many
+ *   distributing launches down them.  AR_BFLOAT16_ACC_F32 keeps its float32
+ *   partials in a workspace, one count-element slab per rank. */
 typedef enum {
     AR_ALGO_FUSED = 0,
     AR_ALGO_RING = 1,
@@ -181,7 +199,9 @@ typedef enum {
     AR_ALGO_HALVING_DOUBLING_STEPS = 8,
     AR_ALGO_RING_PERSISTENT = 9,
     AR_ALGO_RING_PIPELINED = 10,
-    AR_ALGO_STAGED = 11
+    AR_ALGO_STAGED = 11,
+    AR_ALGO_DOUBLE_BINARY_TREE = 12,
+    AR_ALGO_DOUBLE_BINARY_TREE_STEPS = 13
 } ar_algo_t;
 
 /* AR_ALGO_AUTO takes AR_ALGO_STAGED for an AllReduce over at least
@@ -278,7 +298,8 @@ ar_result_t ar_all_gather(const void* const* sendbufs, void* const* recvbufs, si
  * partials do not fit the bf16 buffers.  Other ring AllReduces and the ring
  * all-gather work in recvbufs.  The staged tree algorithms
  * (AR_ALGO_TREE_STEPS, AR_ALGO_RECURSIVE_DOUBLING,
- * AR_ALGO_HALVING_DOUBLING_STEPS) keep their partials in recvbufs too,
+ * AR_ALGO_HALVING_DOUBLING_STEPS, AR_ALGO_DOUBLE_BINARY_TREE_STEPS) keep
+ * their partials in recvbufs too,
  * except for AR_BFLOAT16_ACC_F32, whose float32 partials take one
  * count-element float32 slab per rank in the workspace (nranks >= 2). */
 ar_result_t ar_allreduce_ex(const void* const* sendbufs, void* const* recvbufs, size_t count,

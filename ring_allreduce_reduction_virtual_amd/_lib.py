@@ -19,9 +19,10 @@ DTYPES = {"f32": 0, "bf16": 1, "i32": 2, "f16": 3, "bf16acc32": 4}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
 ALGOS = {"fused": 0, "ring": 1, "phases": 2, "auto": 3, "tree": 4, "tree_steps": 5, "recursive_doubling": 6,
          "halving_doubling": 7, "halving_doubling_steps": 8, "ring_persistent": 9, "ring_pipelined": 10,
-         "staged": 11}
+         "staged": 11, "double_binary_tree": 12, "double_binary_tree_steps": 13}
 # algorithms whose bracketing is a tree, not the ring's (AllReduce only)
-TREE_ALGOS = ("tree", "tree_steps", "recursive_doubling", "halving_doubling", "halving_doubling_steps")
+TREE_ALGOS = ("tree", "tree_steps", "recursive_doubling", "halving_doubling", "halving_doubling_steps",
+              "double_binary_tree", "double_binary_tree_steps")
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
 MAX_RANKS = 128
 

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libar.so")
 
-SOURCES = ("ar_api.hip", "ar_kernels.hip", "ar_tree_kernels.hip", "ar_persistent_kernels.hip", "ar_noalloc.hip")
+SOURCES = ("ar_api.hip", "ar_kernels.hip", "ar_tree_kernels.hip", "ar_persistent_kernels.hip", "ar_dbt_kernels.hip",
+           "ar_noalloc.hip")
 
 # -ffp-contract=off: no fused multiply-add, every add/mul rounds on its own.
 # -fno-fast-math: IEEE semantics (NaN, signed zero, no reassociation).

@@ -223,22 +223,24 @@ ar_result_t grid_for(const KernelArgs& a, Launch& l, unsigned blocks_per_tile = 
     return AR_SUCCESS;
 }
 
-// Tiles per chunk and grid size for a launch on the current device.
-ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, Residue res) {
+// Tiles per chunk and grid size for a launch on the current device.  The
+// buffer is cut into `parts` floor parts (0: one per rank, the ring's chunks).
+ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, Residue res, int parts = 0) {
+    const int np = parts > 0 ? parts : k.n;
     l.vec = res.bytes >= 0;
     const uint64_t block = l.vec ? static_cast<uint64_t>(res.align) / k.esz : 1;   // A elements
     a.ofs = l.vec ? static_cast<int32_t>(res.bytes / static_cast<int>(k.esz)) : 0;
     int shift = 0;
     while ((1ull << shift) < block) ++shift;
     a.align_shift = shift;
-    const uint64_t n = static_cast<uint64_t>(k.n);
+    const uint64_t n = static_cast<uint64_t>(np);
     // the largest chunk body in units (16-byte vectors or elements), as the
     // kernels count it: whole aligned blocks of A elements inside [start, end)
     const uint64_t per_unit = l.vec ? 16 / k.esz : 1;
     const uint64_t ofs = static_cast<uint64_t>(a.ofs);
     uint64_t units = 0;
-    for (int c = 0; c < k.n; ++c) {
-        const uint64_t s = chunk_start(c, k.count, k.n), e = chunk_start(c + 1, k.count, k.n);
+    for (int c = 0; c < np; ++c) {
+        const uint64_t s = chunk_start(c, k.count, np), e = chunk_start(c + 1, k.count, np);
         const uint64_t fb = (s + ofs + block - 1) / block, eb = (e + ofs) / block;
         units = std::max(units, eb > fb ? (eb - fb) * block / per_unit : 0);
     }
@@ -253,14 +255,19 @@ ar_result_t plan(KernelArgs& a, Launch& l, const Common& k, Residue res) {
 }
 
 bool algo_known(ar_algo_t algo) {
-    return algo >= AR_ALGO_FUSED && algo <= AR_ALGO_STAGED;
+    return algo >= AR_ALGO_FUSED && algo <= AR_ALGO_DOUBLE_BINARY_TREE_STEPS;
 }
 
-// AllReduce-only algorithms: the tree orders, the persistent ring and the
-// staged reduce-then-broadcast.
+// The double binary tree, fused or level by level.
+bool dbt_algo(ar_algo_t algo) {
+    return algo == AR_ALGO_DOUBLE_BINARY_TREE || algo == AR_ALGO_DOUBLE_BINARY_TREE_STEPS;
+}
+
+// AllReduce-only algorithms: the tree orders, the persistent ring, the
+// staged reduce-then-broadcast and the double binary tree.
 bool allreduce_only_algo(ar_algo_t algo) {
     return (algo >= AR_ALGO_TREE && algo <= AR_ALGO_HALVING_DOUBLING_STEPS) || algo == AR_ALGO_RING_PERSISTENT ||
-           algo == AR_ALGO_STAGED;
+           algo == AR_ALGO_STAGED || dbt_algo(algo);
 }
 
 // The ring's own schedule, step by step: launched per step or pipelined in one launch.
@@ -271,7 +278,8 @@ bool tree_algo(ar_algo_t algo) { return algo >= AR_ALGO_TREE && algo <= AR_ALGO_
 
 // The tree algorithms that run stage by stage (and keep partials between stages).
 bool tree_steps_algo(ar_algo_t algo) {
-    return algo == AR_ALGO_TREE_STEPS || algo == AR_ALGO_RECURSIVE_DOUBLING || algo == AR_ALGO_HALVING_DOUBLING_STEPS;
+    return algo == AR_ALGO_TREE_STEPS || algo == AR_ALGO_RECURSIVE_DOUBLING || algo == AR_ALGO_HALVING_DOUBLING_STEPS ||
+           algo == AR_ALGO_DOUBLE_BINARY_TREE_STEPS;
 }
 
 // The ones defined for a power-of-two number of ranks only.
@@ -398,6 +406,10 @@ const char* kind_name(Kind kd) {
         case Kind::kSmallTree: return "small_tree";
         case Kind::kStagedReduce: return "staged_reduce";
         case Kind::kStagedBroadcast: return "staged_broadcast";
+        case Kind::kFusedDbt: return "fused_dbt";
+        case Kind::kDbtReduceStep: return "dbt_reduce_step";
+        case Kind::kDbtCopyStep: return "dbt_copy_step";
+        case Kind::kSmallDbt: return "small_dbt";
     }
     return "?";
 }
@@ -561,6 +573,53 @@ ar_result_t tree_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     }
 }
 
+int floor_log2(int n) {
+    int l = 0;
+    while ((2 << l) <= n) ++l;
+    return l;
+}
+
+// Positions of height j (2^j times an odd number) among 1..n.
+unsigned dbt_actors(int j, int n) { return static_cast<unsigned>(((n >> j) + 1) / 2); }
+
+// AllReduce over the double binary tree: the buffer cut in two halves, half c
+// reduced in binary tree c's bracketing.  The fused kernel evaluates both in
+// one pass; the stage kernels climb the trees' floor(log2 N) levels, then
+// descend them.
+ar_result_t dbt_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_bytes,
+                          const std::vector<uintptr_t>& ptrs, Sink& sink) {
+    KernelArgs a{};
+    Launch l{};
+    fill_tables(a, k);
+    ar_result_t rc = plan(a, l, k, common_residue(ptrs), 2);
+    if (rc != AR_SUCCESS) return rc;
+    a.count_q = k.count / 2;
+    a.count_r = static_cast<uint32_t>(k.count % 2);
+    if (algo == AR_ALGO_DOUBLE_BINARY_TREE) {
+        l.depth = k.n < 16 ? 4 : 6;   // the deepest stack the trees need: 3 below 16 ranks, 6 up to 128
+        if (small_message(k)) {
+            plan_small(a, l, k);
+            return sink.emit(l, Kind::kSmallDbt, a, k);
+        }
+        return sink.emit(l, Kind::kFusedDbt, a, k);
+    }
+    if ((rc = use_workspace(a, k, AR_COLL_ALLREDUCE, algo, ws, ws_bytes, nullptr)) != AR_SUCCESS) return rc;
+    const int levels = floor_log2(k.n);
+    for (int j = 1; j <= levels; ++j) {
+        a.step = j;
+        a.last = j == levels ? 1 : 0;
+        l.actors = dbt_actors(j, k.n);
+        if ((rc = sink.emit(l, Kind::kDbtReduceStep, a, k)) != AR_SUCCESS) return rc;
+    }
+    for (int j = levels; j >= 1; --j) {
+        a.step = j;
+        a.last = 0;
+        l.actors = dbt_actors(j, k.n);
+        if ((rc = sink.emit(l, Kind::kDbtCopyStep, a, k)) != AR_SUCCESS) return rc;
+    }
+    return AR_SUCCESS;
+}
+
 ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_bytes, Sink& sink) {
     ar_result_t rc = check_common(k, true);
     if (rc != AR_SUCCESS) return rc;
@@ -614,6 +673,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     if (k.count == 0) return AR_SUCCESS;
 
     if (tree_algo(algo)) return tree_allreduce(k, algo, ws, ws_bytes, ptrs, sink);
+    if (dbt_algo(algo)) return dbt_allreduce(k, algo, ws, ws_bytes, ptrs, sink);
     KernelArgs a{};
     Launch l{};
     fill_tables(a, k);

@@ -417,12 +417,14 @@ struct Span {
     uint64_t tb, te;  // tail elements [tb, te)
 };
 
+// Part c of `parts` floor parts of the buffer: [c*count/parts, (c+1)*count/parts),
+// with a.count_q = count / parts and a.count_r = count % parts.
 template <int VEC>
-__device__ __forceinline__ Span chunk_span(int c, const KernelArgs& a) {
+__device__ __forceinline__ Span part_span(int c, int parts, const KernelArgs& a) {
     Span sp;
     // c*count/n = c*(count/n) + c*(count%n)/n; the last product is below 128^2,
     // so only a 32-bit division is left
-    const uint32_t n = static_cast<uint32_t>(a.nranks);
+    const uint32_t n = static_cast<uint32_t>(parts);
     const uint32_t cu = static_cast<uint32_t>(c);
     sp.s = static_cast<uint64_t>(cu) * a.count_q + (cu * a.count_r) / n;
     sp.e = static_cast<uint64_t>(cu + 1) * a.count_q + ((cu + 1) * a.count_r) / n;
@@ -451,6 +453,12 @@ __device__ __forceinline__ Span chunk_span(int c, const KernelArgs& a) {
         sp.hb = sp.he = sp.tb = sp.te = sp.s;
     }
     return sp;
+}
+
+// Chunk c of the ring's plan: one part per rank.
+template <int VEC>
+__device__ __forceinline__ Span chunk_span(int c, const KernelArgs& a) {
+    return part_span<VEC>(c, a.nranks, a);
 }
 
 // Element handled by thread j among the chunk's edge elements, or false.

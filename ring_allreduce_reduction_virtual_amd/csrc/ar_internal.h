@@ -32,6 +32,11 @@ enum class Kind : int {
     kSmallTree,            // kFusedTree for a small message, staged through LDS
     kStagedReduce,         // kFusedAllReduce for tiles [tile_first, tile_end), stored to rank 0 only
     kStagedBroadcast,      // copy rank 0's result for tiles [tile_first, tile_end) to every other rank
+    kFusedDbt,             // reduce each half of the buffer in its binary tree's bracketing (the
+                           // double binary tree), store to every rank
+    kDbtReduceStep,        // one reducing level of the double binary tree (`step` = height)
+    kDbtCopyStep,          // one distributing level of the double binary tree (`step` = height)
+    kSmallDbt,             // kFusedDbt for a small message, staged through LDS
 };
 
 // Stages of the tree-shaped schedules; at stage `step` the partner distance is d.
@@ -84,8 +89,9 @@ struct Launch {
     bool cached_store;         // kFusedReduceScatter: cache-allocating stores of the shards (the
                                // phases' AllReduce, whose all-gather rereads them)
     unsigned blocks;
-    int depth;                 // kFusedTree: partial slots, 2^depth > N (4, 6 or 8)
-    unsigned actors;           // kTree*Step: actors per chunk in the stage (the grid's y extent)
+    int depth;                 // kFusedTree: partial slots, 2^depth > N (4, 6 or 8); kFusedDbt: stack
+                               // slots (4 below 16 ranks, else 6)
+    unsigned actors;           // kTree*Step, kDbt*Step: actors per chunk in the stage (the grid's y extent)
 };
 
 // Vectors of 16 bytes each thread handles per rank per tile.
@@ -160,6 +166,11 @@ hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream);
 // The kernels of the tree-shaped schedules (ar_tree_kernels.hip); `launch`
 // forwards the kFusedTree, kTreeReduceStep and kTreeCopyStep kinds here.
 hipError_t launch_tree(const Launch& l, const KernelArgs& a, hipStream_t stream);
+
+// The double binary tree (ar_dbt_kernels.hip); `launch` forwards the
+// kFusedDbt, kSmallDbt, kDbtReduceStep and kDbtCopyStep kinds here.  Their tile loop
+// cuts the buffer in two parts (count_q = count / 2, count_r = count % 2).
+hipError_t launch_dbt(const Launch& l, const KernelArgs& a, hipStream_t stream);
 
 // The ring in one launch (ar_persistent_kernels.hip).  kRingPersistent: a
 // cooperative launch on at most as many blocks as the device holds at once;

@@ -498,6 +498,9 @@ hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream) {
     if (l.kind == Kind::kFusedTree || l.kind == Kind::kTreeReduceStep || l.kind == Kind::kTreeCopyStep ||
         l.kind == Kind::kSmallTree)
         return launch_tree(l, a, stream);
+    if (l.kind == Kind::kFusedDbt || l.kind == Kind::kSmallDbt || l.kind == Kind::kDbtReduceStep ||
+        l.kind == Kind::kDbtCopyStep)
+        return launch_dbt(l, a, stream);
     if (l.kind == Kind::kRingPersistent || l.kind == Kind::kRingPipelined || l.kind == Kind::kRingPipelinedWs ||
         l.kind == Kind::kRingPipelinedGather)
         return launch_persistent(l, a, stream);

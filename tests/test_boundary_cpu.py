@@ -293,12 +293,12 @@ def test_tree_algorithm_host_rules(lib):
     from ring_allreduce_reduction_virtual_amd import _lib
 
     slab = ((1000 * 4 + 255) // 256) * 256
-    for algo in ("tree_steps", "recursive_doubling", "halving_doubling_steps"):
+    for algo in ("tree_steps", "recursive_doubling", "halving_doubling_steps", "double_binary_tree_steps"):
         assert ar.ar_workspace_bytes("allreduce", algo, 1000, "bf16acc32", 8) == 8 * slab + 1024
         assert ar.ar_workspace_bytes("allreduce", algo, 1000, "bf16acc32", 1) == 0
         assert ar.ar_workspace_bytes("allreduce", algo, 1000, "bf16", 8) == 0
         assert ar.ar_workspace_bytes("allreduce", algo, 0, "bf16acc32", 8) == 0
-    for algo in ("tree", "halving_doubling"):
+    for algo in ("tree", "halving_doubling", "double_binary_tree"):
         assert ar.ar_workspace_bytes("allreduce", algo, 1000, "bf16acc32", 8) == 0
     S = 1 << 20
     sends = [BASE + r * S for r in range(8)]
@@ -309,9 +309,9 @@ def test_tree_algorithm_host_rules(lib):
         assert lib.ar_reduce_scatter_ex(_ptrs(sends), _ptrs(recvs), 100, 0, 0, 8, algo, None, 0, None) == 2
         assert b"AllReduce only" in lib.ar_get_last_error_detail()
         assert lib.ar_all_gather_ex(_ptrs(sends), _ptrs(recvs), 100, 0, 8, algo, None, 0, None) == 2
-        # six ranks: only the binomial tree is defined
+        # six ranks: the binomial tree and the double binary tree are defined, the rest need a power of two
         rc = lib.ar_allreduce_ex(_ptrs(sends[:6]), _ptrs(recvs[:6]), 100, 0, 0, 6, algo, None, 0, None)
-        if name in ("tree", "tree_steps"):
+        if name in ("tree", "tree_steps", "double_binary_tree", "double_binary_tree_steps"):
             assert rc in (0, 3)   # valid: reaches the device (none here) or succeeds
         else:
             assert rc == 2 and b"power-of-two" in lib.ar_get_last_error_detail()
@@ -321,8 +321,9 @@ def test_tree_algorithm_host_rules(lib):
         assert lib.ar_plan_num_launches(plan) == 0
         assert lib.ar_plan_free(plan) == 0
     # the staged forms of bf16acc32 need their workspace
-    rc = lib.ar_allreduce_ex(_ptrs(sends), _ptrs(recvs), 100, 4, 0, 8, _lib.ALGOS["tree_steps"], None, 0, None)
-    assert rc == 1 and b"workspace" in lib.ar_get_last_error_detail()
+    for name in ("tree_steps", "double_binary_tree_steps"):
+        rc = lib.ar_allreduce_ex(_ptrs(sends), _ptrs(recvs), 100, 4, 0, 8, _lib.ALGOS[name], None, 0, None)
+        assert rc == 1 and b"workspace" in lib.ar_get_last_error_detail()
 
 
 def test_pipelined_ring_host_rules(lib):

@@ -1,6 +1,7 @@
 """GPU parity for the tree-shaped AllReduce orders: the binomial tree (fused and
-staged), recursive doubling, and recursive halving/doubling (fused and staged),
-against the oracle's schedules (oracle/orders.py) bit for bit, over every
+staged), recursive doubling, recursive halving/doubling (fused and staged) and
+the double binary tree (fused and level by level), against the oracle's
+schedules (oracle/orders.py, oracle/dbt.py) bit for bit, over every
 dtype and operator, in-place and offset layouts, special values, persistent
 plans and HIP graph replays, and every element at the full workload sizes."""
 
@@ -9,7 +10,9 @@ import zlib
 import numpy as np
 import pytest
 
-from oracle.orders import order_allreduce, order_bracketing, tree_order_fold
+from oracle import dbt
+from oracle.orders import order_allreduce as _order_allreduce
+from oracle.orders import order_bracketing, tree_order_fold
 from oracle.ring import f32_to_bf16_bits, f32_to_f16_bits, ring_order_fold, same_bits
 
 from gpu_util import assert_every_rank_equals, from_dev, poison, require_gpu, to_dev, want_on_device
@@ -17,9 +20,24 @@ from gpu_util import assert_every_rank_equals, from_dev, poison, require_gpu, to
 pytestmark = pytest.mark.gpu
 
 ORDER_OF = {"tree": "tree", "tree_steps": "tree", "recursive_doubling": "recursive_doubling",
-            "halving_doubling": "halving_doubling", "halving_doubling_steps": "halving_doubling"}
+            "halving_doubling": "halving_doubling", "halving_doubling_steps": "halving_doubling",
+            "double_binary_tree": "double_binary_tree", "double_binary_tree_steps": "double_binary_tree"}
 POW2 = ("recursive_doubling", "halving_doubling", "halving_doubling_steps")
 TORCH_OF = {"f16": "float16", "bf16acc32": "bfloat16", "bf16": "bfloat16", "f32": "float32", "i32": "int32"}
+
+
+def order_allreduce(order, xs, op="sum", dtype="f32"):
+    """The oracle's executed schedule of an order: (outputs, stats)."""
+    if order == "double_binary_tree":
+        return dbt.double_binary_tree_allreduce(xs, op, dtype)
+    return _order_allreduce(order, xs, op, dtype)
+
+
+def order_fold(order, xs, op="sum", dtype="f32"):
+    """The order's result as a definition: its bracketing evaluated on the whole buffers."""
+    if order == "double_binary_tree":
+        return dbt.double_binary_tree_fold(xs, op, dtype)
+    return tree_order_fold(xs, order_bracketing(order, len(xs)), op, dtype)
 
 
 def _ar():
@@ -169,16 +187,18 @@ def test_tree_orders_layouts(layout, dtype, algo):
         assert same_bits(_host(recvs[r], dtype), want[r], dtype), f"rank {r}"
 
 
-LAUNCHES = {"tree": lambda n: 1, "halving_doubling": lambda n: 1,
+LAUNCHES = {"tree": lambda n: 1, "halving_doubling": lambda n: 1, "double_binary_tree": lambda n: 1,
             "tree_steps": lambda n: 2 * (n - 1).bit_length(), "recursive_doubling": lambda n: (n - 1).bit_length(),
-            "halving_doubling_steps": lambda n: 2 * (n - 1).bit_length()}
+            "halving_doubling_steps": lambda n: 2 * (n - 1).bit_length(),
+            "double_binary_tree_steps": lambda n: 2 * (n.bit_length() - 1)}
 
 
-@pytest.mark.parametrize("algo", list(ORDER_OF))
-@pytest.mark.parametrize("n", [4, 8, 16])
+@pytest.mark.parametrize("n,algo", [(n, algo) for n in (4, 8, 13, 16) for algo in ORDER_OF
+                                    if algo not in POW2 or not n & (n - 1)])
 def test_tree_order_plans_and_launch_counts(n, algo):
     """Stage counts of the pages' cost statements: 2 ceil(log2 N) for the tree and for
-    halving/doubling, log2 N for recursive doubling; one launch for the fused forms."""
+    halving/doubling, log2 N for recursive doubling, 2 floor(log2 N) for the double
+    binary tree; one launch for the fused forms."""
     import torch
 
     ar = _ar()
@@ -200,7 +220,8 @@ def test_tree_order_plans_and_launch_counts(n, algo):
     plan.close()
 
 
-@pytest.mark.parametrize("algo", ["tree_steps", "recursive_doubling", "halving_doubling_steps"])
+@pytest.mark.parametrize("algo", ["tree_steps", "recursive_doubling", "halving_doubling_steps",
+                                  "double_binary_tree_steps"])
 def test_tree_order_graph_replays(algo):
     """Staged schedules captured in a HIP graph: 4 replays with eager input changes between."""
     import torch
@@ -235,9 +256,11 @@ def test_tree_order_graph_replays(algo):
 
 
 @pytest.mark.parametrize("workload,algos", [
-    ("headline", ["tree", "halving_doubling", "tree_steps", "recursive_doubling", "halving_doubling_steps"]),
-    ("c5", ["tree", "halving_doubling"]),
-    ("c3", ["tree", "halving_doubling_steps"]),
+    ("headline", ["tree", "halving_doubling", "tree_steps", "recursive_doubling", "halving_doubling_steps",
+                  "double_binary_tree", "double_binary_tree_steps"]),
+    ("c5", ["tree", "halving_doubling", "double_binary_tree", "double_binary_tree_steps"]),
+    ("c3", ["tree", "halving_doubling_steps", "double_binary_tree"]),
+    ("c4", ["double_binary_tree_steps"]),
 ])
 def test_tree_orders_full_size_every_element(workload, algos):
     """The full workloads: every element of every rank against the order's
@@ -257,7 +280,7 @@ def test_tree_orders_full_size_every_element(workload, algos):
         print(f"[full size] {workload} {algo}", flush=True)
         order = ORDER_OF[algo]
         if order not in wants:
-            wants[order] = want_on_device(tree_order_fold(xs, order_bracketing(order, w.nranks), "sum", dtype), dtype)
+            wants[order] = want_on_device(order_fold(order, xs, "sum", dtype), dtype)
         poison(recvs)
         ar.ar_allreduce_ex(sends, recvs, algo=algo, dtype=dtype)
         torch.cuda.synchronize()

@@ -1,7 +1,8 @@
 """GPU parity for the small-message kernels (chunks shorter than the
 small-message threshold: every rank's values of a few positions staged through
-LDS), across the threshold, for the ring order and the tree orders, every
-dtype class and several operators, rank counts from 2 to 128."""
+LDS), across the threshold, for the ring order, the tree orders and the double
+binary tree, every dtype class and several operators, rank counts from 2 to
+128."""
 
 import zlib
 
@@ -9,6 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle.dbt import double_binary_tree_allreduce
 from oracle.orders import order_allreduce
 from oracle.ring import f32_to_bf16_bits, f32_to_f16_bits, same_bits
 
@@ -53,8 +55,8 @@ def _host(t, dtype):
 
 
 # halving/doubling is defined for power-of-two rank counts only
-VALID = [(algo, n) for algo in ("fused", "tree", "halving_doubling") for n in (2, 3, 8, 16, 64, 128)
-         if algo != "halving_doubling" or not n & (n - 1)]
+VALID = [(algo, n) for algo in ("fused", "tree", "halving_doubling", "double_binary_tree")
+         for n in (2, 3, 8, 16, 64, 128) if algo != "halving_doubling" or not n & (n - 1)]
 
 
 @pytest.mark.parametrize("dtype,op", [("f32", "sum"), ("f32", "max"), ("bf16", "sum"), ("f16", "avg"),
@@ -73,6 +75,8 @@ def test_small_messages_across_the_threshold(algo, n, dtype, op):
         xs = _draw(dtype, n, length, seed=zlib.crc32(f"{dtype}{op}{n}{length}".encode()))
         if algo == "fused":
             want, _ = oracle.ring_allreduce(xs, op=op, dtype=dtype)
+        elif algo == "double_binary_tree":
+            want, _ = double_binary_tree_allreduce(xs, op, dtype)
         else:
             want, _ = order_allreduce(algo, xs, op, dtype)
         sends = [_dev(x, dtype) for x in xs]
