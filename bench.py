@@ -497,6 +497,9 @@ def load_probe_library():
     lib.arprobe_pattern.restype = ctypes.c_int
     lib.arprobe_pattern.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p,
                                     ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.arprobe_copy_order.restype = ctypes.c_int
+    lib.arprobe_copy_order.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_uint64, ctypes.c_void_p]
     lib.arprobe_xcd.restype = ctypes.c_int
     lib.arprobe_xcd.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
                                 ctypes.c_void_p]
@@ -544,6 +547,26 @@ def run_xcd_patterns(lib, steps=20):
         print(json.dumps(row), flush=True)
 
     mib = 1 << 20
+    # reads and writes together: copies of 8 x 256 MiB in the kernels' order and the write-friendly orders,
+    # each timed twice, interleaved, on the same buffers
+    n, size = 8, 256 * mib
+    src = [torch.ones(size // 4, device=dev) for _ in range(n)]
+    dst = [torch.empty(size // 4, device=dev) for _ in range(n)]
+    sp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in src])
+    dp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dst])
+    nvec = size // 16
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for rep in range(2):
+        emit("copy", "kernels' pattern: 8 KiB of every buffer per workgroup, nontemporal", 2 * n * size,
+             timed(lambda: check(lib.arprobe_stream(2, sp, dp, n, nvec, sink.data_ptr(), stream.cuda_stream),
+                                 "copy")), f"{n} x {size >> 20} MiB")
+        for order, oname in ((1, "tile-major"), (0, "buffer-major")):
+            for nt in (0, 1):
+                emit("copy", f"one buffer per workgroup, 8 KiB, {oname}, "
+                             f"{'nontemporal' if nt else 'plain'} stores", 2 * n * size,
+                     timed(lambda: check(lib.arprobe_copy_order(order, nt, sp, dp, n, nvec, stream.cuda_stream),
+                                         "copy order")), f"{n} x {size >> 20} MiB")
+    del src, dst
     for n, size in ((8, 256 * mib), (7, 256 * mib)):
         bufs = [torch.empty(size // 4, device=dev) for _ in range(n)]
         bp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in bufs])

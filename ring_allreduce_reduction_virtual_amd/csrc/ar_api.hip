@@ -376,6 +376,57 @@ ar_result_t copy_grid(const KernelArgs& a, Launch& l, const Common& k) {
     return grid_for(a, l, l.half ? arimpl::kUnroll : 1);
 }
 
+// The staged broadcast's form: one destination rank per block with a tile's
+// blocks grouped on one XCD (form 3, k_staged_broadcast_xcd), unless
+// AR_BCAST_FORM=0 (read at every call) asks for the tile forms of copy_grid
+// (a whole or half tile to every rank per block).  The grid is
+// 8 * ceil(tiles / 8) * (N-1) blocks, capped by AR_BLOCKS_PER_CU like the
+// others (the kernel then strides).
+ar_result_t broadcast_form(const KernelArgs& a, Launch& l, const Common& k) {
+    const char* e = std::getenv("AR_BCAST_FORM");
+    if ((e != nullptr && e[0] == '0' && e[1] == '\0') || k.n < 2) {
+        l.form = 0;
+        return AR_SUCCESS;
+    }
+    int cus = 0;
+    const ar_result_t rc = cu_count(&cus);
+    if (rc != AR_SUCCESS) return rc;
+    const uint64_t tiles = a.tile_end - a.tile_first;
+    uint64_t blocks = 8 * ((tiles + 7) / 8) * static_cast<uint64_t>(k.n - 1);
+    const unsigned bpc = blocks_per_cu();
+    if (bpc != 0) blocks = std::min<uint64_t>(blocks, static_cast<uint64_t>(cus) * bpc);
+    l.form = 3;
+    l.blocks = static_cast<unsigned>(std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 0x7fffffffu));
+    return AR_SUCCESS;
+}
+
+// The fused all-gather's form: one destination rank per block with a tile's
+// blocks grouped on one XCD (form 3, k_gather_shards_xcd), unless
+// AR_GATHER_FORM=0 (read at every call) asks for the tile forms of
+// copy_grid.  Measured on MI355X, whole or half tiles to every rank per block
+// against form 3, us: all-gather 8 x 256 MiB 395-400 / 347-359, 16 x 64 MiB
+// 229-233 / 190, 64 x (2^26+7) 3,253-3,338 / 3,084-3,097, 8 x 16 MiB 44 / 41;
+// the phases' AllReduce 8 x 256 MiB 742-745 / 721-722, 16 x 64 MiB 402-403 /
+// 369-371.  The grid is 8 * ceil(tiles / 8) * N blocks, capped by
+// AR_BLOCKS_PER_CU like the others (the kernel then strides).
+ar_result_t gather_form(const KernelArgs& a, Launch& l, const Common& k) {
+    const char* e = std::getenv("AR_GATHER_FORM");
+    if (e != nullptr && e[0] == '0' && e[1] == '\0') {
+        l.form = 0;
+        return AR_SUCCESS;
+    }
+    int cus = 0;
+    const ar_result_t rc = cu_count(&cus);
+    if (rc != AR_SUCCESS) return rc;
+    const uint64_t tiles = a.tile_end - a.tile_first;
+    uint64_t blocks = 8 * ((tiles + 7) / 8) * static_cast<uint64_t>(k.n);
+    const unsigned bpc = blocks_per_cu();
+    if (bpc != 0) blocks = std::min<uint64_t>(blocks, static_cast<uint64_t>(cus) * bpc);
+    l.form = 3;
+    l.blocks = static_cast<unsigned>(std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 0x7fffffffu));
+    return AR_SUCCESS;
+}
+
 // Rank count from which AR_ALGO_AUTO runs AllReduce as two fused phases.
 int phases_min_ranks() {
     static const int v = [] {
@@ -698,6 +749,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
             recvs.push_back(reinterpret_cast<uintptr_t>(k.recv[r]));
         }
         if ((rc = plan(g, lg, k, common_residue(recvs))) != AR_SUCCESS) return rc;
+        if ((rc = gather_form(g, lg, k)) != AR_SUCCESS) return rc;
         return sink.emit(lg, Kind::kFusedAllGather, g, k);   // whole tiles: measured faster in place
     }
     if (algo == AR_ALGO_FUSED && small_message(k)) {
@@ -725,7 +777,9 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
             if ((rc = grid_for(a, l)) != AR_SUCCESS) return rc;
             if ((rc = sink.emit(l, Kind::kStagedReduce, a, k)) != AR_SUCCESS) return rc;
             if ((rc = copy_grid(a, l, k)) != AR_SUCCESS) return rc;
+            if ((rc = broadcast_form(a, l, k)) != AR_SUCCESS) return rc;
             if ((rc = sink.emit(l, Kind::kStagedBroadcast, a, k)) != AR_SUCCESS) return rc;
+            l.form = 0;
             l.half = false;
         }
         return AR_SUCCESS;
@@ -847,6 +901,7 @@ ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, Sink& sink) {
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_FUSED || k.n == 1) {
         if ((rc = copy_grid(a, l, k)) != AR_SUCCESS) return rc;
+        if ((rc = gather_form(a, l, k)) != AR_SUCCESS) return rc;
         return sink.emit(l, Kind::kFusedAllGather, a, k);
     }
     if (algo == AR_ALGO_RING_PIPELINED) return sink.emit(l, Kind::kRingPipelinedGather, a, k);

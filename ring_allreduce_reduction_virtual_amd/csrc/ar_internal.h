@@ -86,6 +86,8 @@ struct Launch {
     bool vec;                  // 16-byte vector path (all streamed buffers share a residue)
     bool cached;               // kFusedAllReduce on the vector path: cache-allocating loads
     bool half;                 // kFusedAllGather, kStagedBroadcast: one unit row of a tile per block
+    int form;                  // kStagedBroadcast: 3 one destination per block, a tile's blocks grouped
+                               // on one XCD; 0 the tile forms above
     bool cached_store;         // kFusedReduceScatter: cache-allocating stores of the shards (the
                                // phases' AllReduce, whose all-gather rereads them)
     unsigned blocks;

@@ -161,6 +161,57 @@ __global__ __launch_bounds__(kThreads) void k_staged_broadcast_tiles(const Kerne
     AR_TILE_LOOP_END
 }
 
+// Staged AllReduce, broadcasting launch, one destination rank per block with
+// a tile's N-1 blocks on one XCD: workgroups go to MI355X's 8 XCDs in turn,
+// so block b = x + 8 m, on XCD x, copies tile tile_first + 8 (m / (N-1)) + x
+// of rank 0's results to rank 1 + m mod (N-1).  The source tile is fetched
+// into that XCD's L2 once for its N-1 destinations, and neighbouring blocks
+// on an XCD write the same tile of neighbouring ranks.  Measured on MI355X
+// against whole or half tiles to every rank per block, staged AllReduce in
+// us: 8 x 256 MiB 725 / 732, 16 x 64 MiB 378 / 402, 64 x 256 MiB 5,814 /
+// 5,885; sending every destination's copy from its own XCD instead (each
+// tile loaded N-1 times) was slower everywhere (8 x 256 MiB: 944 us).  The
+// planned grid is 8 * ceil(tiles / 8) * (N-1) blocks; a capped grid strides
+// over the same numbering (same results, the XCD grouping then approximate).
+template <int DT, int VEC>
+__global__ __launch_bounds__(kThreads) void k_staged_broadcast_xcd(const KernelArgs a) {
+    using U = Unit<DT, VEC, false>;   // cache-allocating loads: the results sit in the Infinity Cache
+    constexpr int ESZ = elem_size<DT>();
+    const int n = a.nranks;
+    const uint32_t tpc = a.tiles_per_chunk;
+    const int64_t adj = (VEC > 1) ? static_cast<int64_t>(a.ofs) * ESZ : 0;
+    const char* src = a.recv[0];
+    const uint64_t dests = static_cast<uint64_t>(n - 1);
+    const uint64_t groups = (static_cast<uint64_t>(a.tile_end - a.tile_first) + 7) / 8;
+    const uint64_t total = 8 * groups * dests;
+    for (uint64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const uint64_t m = b / 8;
+        const uint64_t tile64 = a.tile_first + 8 * (m / dests) + (b % 8);
+        if (tile64 >= a.tile_end) continue;
+        const uint32_t tile = static_cast<uint32_t>(tile64);
+        const int q = 1 + static_cast<int>(m % dests);
+        const int c = static_cast<int>(tile / tpc);
+        const uint64_t t = tile - static_cast<uint32_t>(c) * tpc;
+        const Span sp = chunk_span<VEC>(c, a);
+        const uint64_t tv0 = sp.vb + t * (kThreads * kUnroll);
+        if (VEC > 1 && t == 0) {
+            uint64_t i;
+            if (edge_element(sp, threadIdx.x, &i)) store_elem<ESZ>(a.recv[q] + i * ESZ, load_elem<ESZ>(src + i * ESZ));
+        }
+        typename U::T x[kUnroll];
+        const char* sb = U::tile(src - adj, tv0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (tv0 + U::lane_unit(u) < sp.ve) x[u] = U::load(sb, U::lane_off(u));
+        }
+        char* tb = U::tile(a.recv[q] - adj, tv0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (tv0 + U::lane_unit(u) < sp.ve) U::store(tb, U::lane_off(u), x[u]);
+        }
+    }
+}
+
 // Reduce-scatter: the fold of chunk c goes to rank c's shard only.  Reads N*S,
 // writes S bytes.  NT_STORE: nontemporal stores (a standalone reduce-scatter)
 // or cache-allocating ones (the phases' AllReduce, whose all-gather rereads
@@ -262,6 +313,53 @@ __global__ __launch_bounds__(kThreads) void k_gather_shards_half(const KernelArg
                 if (a.recv[q] + sp.s * ESZ == shard) continue;   // the shard already sits there
                 U::store(U::tile(a.recv[q] - adj, tv0), U::lane_off(u), x);
             }
+        }
+    }
+}
+
+// The fused all-gather with one destination rank per block and a tile's N
+// blocks on one XCD (as k_staged_broadcast_xcd): block b = x + 8 m copies tile
+// tile_first + 8 (m / N) + x of its chunk's shard to rank m mod N, skipping
+// the rank the shard already sits in (in place).  Strides over the same
+// numbering when the grid is capped.
+template <int DT, int VEC>
+__global__ __launch_bounds__(kThreads) void k_gather_shards_xcd(const KernelArgs a) {
+    using U = Unit<DT, VEC, AR_NT_LOADS_COPY>;
+    constexpr int ESZ = elem_size<DT>();
+    const int n = a.nranks;
+    const uint32_t tpc = a.tiles_per_chunk;
+    const int64_t adj = (VEC > 1) ? static_cast<int64_t>(a.ofs) * ESZ : 0;
+    const uint64_t dests = static_cast<uint64_t>(n);
+    const uint64_t groups = (static_cast<uint64_t>(a.tile_end - a.tile_first) + 7) / 8;
+    const uint64_t total = 8 * groups * dests;
+    for (uint64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const uint64_t m = b / 8;
+        const uint64_t tile64 = a.tile_first + 8 * (m / dests) + (b % 8);
+        if (tile64 >= a.tile_end) continue;
+        const uint32_t tile = static_cast<uint32_t>(tile64);
+        const int q = static_cast<int>(m % dests);
+        const int c = static_cast<int>(tile / tpc);
+        const uint64_t t = tile - static_cast<uint32_t>(c) * tpc;
+        const Span sp = chunk_span<VEC>(c, a);
+        const uint64_t tv0 = sp.vb + t * (kThreads * kUnroll);
+        const char* shard = a.send[c];
+        if (a.recv[q] + sp.s * ESZ == shard) continue;   // the shard already sits there
+        if (VEC > 1 && t == 0) {
+            uint64_t i;
+            if (edge_element(sp, threadIdx.x, &i))
+                store_elem<ESZ>(a.recv[q] + i * ESZ, load_elem<ESZ>(shard + (i - sp.s) * ESZ));
+        }
+        const bool aligned = shard_aligned<DT>(shard, sp.s, a.ofs);
+        typename U::T x[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (tv0 + U::lane_unit(u) < sp.ve)
+                x[u] = load_shard_unit<DT, VEC, AR_NT_LOADS_COPY>(shard, sp.s, a.ofs, aligned, tv0 + U::lane_unit(u));
+        }
+        char* tb = U::tile(a.recv[q] - adj, tv0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (tv0 + U::lane_unit(u) < sp.ve) U::store(tb, U::lane_off(u), x[u]);
         }
     }
 }
@@ -445,7 +543,9 @@ hipError_t launch_copy(const Launch& l, const KernelArgs& a, hipStream_t s) {
     const dim3 grid(l.blocks), block(kThreads);
     switch (l.kind) {
         case Kind::kFusedAllGather:
-            if (l.half)
+            if (l.form == 3)
+                hipLaunchKernelGGL((k_gather_shards_xcd<DT, VEC>), grid, block, 0, s, a);
+            else if (l.half)
                 hipLaunchKernelGGL((k_gather_shards_half<DT, VEC, true>), grid, block, 0, s, a);
             else
                 hipLaunchKernelGGL((k_gather_shards<DT, VEC, true>), grid, block, 0, s, a);
@@ -457,7 +557,9 @@ hipError_t launch_copy(const Launch& l, const KernelArgs& a, hipStream_t s) {
             hipLaunchKernelGGL((k_ring_copy_step<DT, VEC>), grid, block, 0, s, a);
             break;
         case Kind::kStagedBroadcast:
-            if (l.half)
+            if (l.form == 3)
+                hipLaunchKernelGGL((k_staged_broadcast_xcd<DT, VEC>), grid, block, 0, s, a);
+            else if (l.half)
                 hipLaunchKernelGGL((k_staged_broadcast<DT, VEC>), grid, block, 0, s, a);
             else
                 hipLaunchKernelGGL((k_staged_broadcast_tiles<DT, VEC>), grid, block, 0, s, a);

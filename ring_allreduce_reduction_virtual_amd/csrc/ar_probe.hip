@@ -198,7 +198,51 @@ __global__ __launch_bounds__(kThreads) void k_bcast(const Table t, int mode) {
     t.dst[x][v0 + kThreads] = c;
 }
 
+// Copies of n buffers (src[q] -> dst[q], 8 KiB per workgroup) in the block
+// orders of k_pattern: order 0 buffer-major, 1 tile-major.  Nontemporal loads;
+// stores nontemporal (nt) or plain.  Grid: n * tiles blocks.
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void k_copy_order(const Table t, uint64_t tiles, int order) {
+    const uint64_t b = blockIdx.x;
+    const int q = order == 0 ? static_cast<int>(b / tiles) : static_cast<int>(b % static_cast<uint64_t>(t.n));
+    const uint64_t j = order == 0 ? b % tiles : b / static_cast<uint64_t>(t.n);
+    const uint64_t v0 = j * kTile + threadIdx.x;
+    const u32x4 a = ld(t.src[q] + v0), c = ld(t.src[q] + v0 + kThreads);
+    if constexpr (NT) {
+        st(t.dst[q] + v0, a);
+        st(t.dst[q] + v0 + kThreads, c);
+    } else {
+        t.dst[q][v0] = a;
+        t.dst[q][v0 + kThreads] = c;
+    }
+}
+
 }  // namespace
+
+// extern "C" int arprobe_copy_order(int order, int nt, const void* const* src,
+//     void* const* dst, int n, uint64_t nvec, hipStream_t s)
+//   k_copy_order over n buffers of nvec vectors (a multiple of 512).
+//   Returns 0, 1 (bad arguments) or 2 (launch error).
+extern "C" int arprobe_copy_order(int order, int nt, const void* const* src, void* const* dst, int n, uint64_t nvec,
+                                  hipStream_t s) {
+    if (n < 1 || n > kProbeMax || nvec == 0 || nvec % kTile != 0 || src == nullptr || dst == nullptr) return 1;
+    if (order != 0 && order != 1) return 1;
+    const uint64_t tiles = nvec / kTile;
+    if (tiles * static_cast<uint64_t>(n) > 0x7fffffffull) return 1;
+    Table t{};
+    t.n = n;
+    for (int r = 0; r < n; ++r) {
+        if (src[r] == nullptr || dst[r] == nullptr || reinterpret_cast<uintptr_t>(src[r]) % 16 != 0 ||
+            reinterpret_cast<uintptr_t>(dst[r]) % 16 != 0)
+            return 1;
+        t.src[r] = static_cast<const u32x4*>(src[r]);
+        t.dst[r] = static_cast<u32x4*>(dst[r]);
+    }
+    const dim3 grid(static_cast<unsigned>(tiles * static_cast<uint64_t>(n))), block(kThreads);
+    if (nt) hipLaunchKernelGGL((k_copy_order<true>), grid, block, 0, s, t, tiles, order);
+    else hipLaunchKernelGGL((k_copy_order<false>), grid, block, 0, s, t, tiles, order);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // extern "C" int arprobe_xcd(int kind, const void* src, void* const* dst, int n,
 //     uint64_t nvec, hipStream_t s)

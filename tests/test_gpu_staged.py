@@ -138,32 +138,43 @@ def test_staged_equals_fused_bits_and_segments(stage_env):
     plan.close()
 
 
-@pytest.mark.parametrize("half", ["0", "1"])
+# the copy forms: one destination per block grouped on an XCD (the default), whole tiles to
+# every rank per block, one unit row of a tile to every rank per block
+COPY_FORMS = {"xcd": {}, "whole": {"AR_BCAST_FORM": "0", "AR_GATHER_FORM": "0", "AR_HALF_TILES": "0"},
+              "half": {"AR_BCAST_FORM": "0", "AR_GATHER_FORM": "0", "AR_HALF_TILES": "1"}}
+
+
+@pytest.mark.parametrize("form", sorted(COPY_FORMS))
 @pytest.mark.parametrize("n,length,dtype,op", [(5, 1003, "f32", "sum"), (8, 8 * 4096 + 5, "bf16", "sum"),
                                                (17, 4099, "i32", "max"), (64, 64 * 333 + 7, "f32", "sum"),
-                                               (7, 7 * 3000 + 5, "bf16acc32", "avg")])
-def test_staged_both_broadcast_forms(n, length, dtype, op, half, stage_env, monkeypatch):
-    """The broadcast with whole tiles per block and with one unit row per block
-    (the host picks by shape; AR_HALF_TILES forces either), over several segments."""
+                                               (7, 7 * 3000 + 5, "bf16acc32", "avg"), (2, 9000, "f16", "min")])
+def test_staged_every_broadcast_form(n, length, dtype, op, form, stage_env, monkeypatch):
+    """The broadcast with one destination rank per block grouped on an XCD (the
+    default), with whole tiles per block and with one unit row per block
+    (AR_BCAST_FORM=0 and AR_HALF_TILES force those), over several segments."""
     require_gpu()
     stage_env(3 * 8192)
-    monkeypatch.setenv("AR_HALF_TILES", half)
-    print(f"[staged] broadcast form half={half} n={n} len={length} {dtype} {op}", flush=True)
+    for k, v in COPY_FORMS[form].items():
+        monkeypatch.setenv(k, v)
+    print(f"[staged] broadcast form {form} n={n} len={length} {dtype} {op}", flush=True)
     for layout in ("fresh", "offset", "in_place"):
         _run(n, length, dtype, op, layout, 3 * 8192, seed=n + length)
 
 
-@pytest.mark.parametrize("half", ["0", "1"])
+@pytest.mark.parametrize("form", sorted(COPY_FORMS))
 @pytest.mark.parametrize("n,length,dtype", [(1, 7, "f32"), (3, 1000, "i32"), (5, 1003, "f32"), (8, 8 * 4096 + 5, "bf16"),
-                                            (64, 64 * 333 + 7, "f32"), (128, 300, "f16")])
-def test_all_gather_both_forms(n, length, dtype, half, monkeypatch):
-    """The fused all-gather with whole tiles per block and with one unit row per
-    block, out of place and in place, against the oracle."""
+                                            (64, 64 * 333 + 7, "f32"), (128, 300, "f16"), (9, 9 * 4096 * 3 + 1, "f32")])
+def test_all_gather_every_form(n, length, dtype, form, monkeypatch):
+    """The fused all-gather with one destination rank per block grouped on an XCD
+    (the default), whole tiles and unit rows to every rank per block, out of
+    place and in place, against the oracle; and the phases' AllReduce, whose
+    all-gather runs in place."""
     import torch
     import ring_allreduce_reduction_virtual_amd as ar
 
     require_gpu()
-    monkeypatch.setenv("AR_HALF_TILES", half)
+    for k, v in COPY_FORMS[form].items():
+        monkeypatch.setenv(k, v)
     xs = _draw(dtype, n, length, seed=n * 5 + length)
     shards_want, _ = oracle.reduce_scatter(xs, dtype=dtype)
     want, _ = oracle.all_gather(shards_want, length, dtype=dtype)
@@ -183,6 +194,12 @@ def test_all_gather_both_forms(n, length, dtype, half, monkeypatch):
         torch.cuda.synchronize()
         for r in range(n):
             assert same_bits(_host(outs[r], dtype), want[r], dtype), (layout, r)
+    sends = [_tensor(x, dtype) for x in xs]
+    outs = [_empty(length, dtype) for _ in range(n)]
+    ar.ar_allreduce_ex(sends, outs, algo="phases")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(_host(outs[r], dtype), want[r], dtype), ("phases", r)
 
 
 def test_staged_is_allreduce_only():
