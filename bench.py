@@ -32,7 +32,8 @@ METRIC = "AllReduce algbw/busbw GB/s + % HBM peak, N=8 ranks x 64M fp32, 1 MI355
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 # rocprofv3 counter summaries of the headline call, by the form it runs
 COUNTERS_FILES = {"staged": os.path.join(ROOT, "profiles", "staged_allreduce_headline_counters.md"),
-                  "fused": os.path.join(ROOT, "profiles", "fused_allreduce_headline_counters.md")}
+                  "fused": os.path.join(ROOT, "profiles", "fused_allreduce_headline_counters.md"),
+                  "phases": os.path.join(ROOT, "profiles", "phases_allreduce_headline_counters.md")}
 # the sources the AllReduce kernels are built from (their counters are only
 # used while these are unchanged)
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_reduction_virtual_amd", "csrc", f)
@@ -831,6 +832,48 @@ def run_size_sweep(args):
     print(json.dumps({"sweep_fit": fits, "model": "t = launches*alpha + hbm_bytes/B"}), flush=True)
 
 
+FORM_SWEEP = ((8, 256, "float32"), (8, 128, "float32"), (8, 64, "float32"), (8, 32, "float32"),
+              (8, 16, "float32"), (8, 4, "float32"), (16, 256, "float32"), (16, 64, "float32"),
+              (16, 16, "float32"), (32, 128, "float32"), (32, 32, "float32"), (64, 256, "float32"),
+              (64, 64, "float32"), (64, 16, "float32"), (128, 64, "float32"), (4, 256, "float32"),
+              (6, 256, "float32"), (2, 512, "float32"), (8, 128, "bfloat16"), (8, 64, "bfloat16"),
+              (16, 64, "bfloat16"), (16, 64, "int32"))
+
+
+def run_form_sweep(args):
+    """The three ring-order forms of a large AllReduce side by side (fused,
+    phases, staged) over rank counts and sizes: the measurements behind
+    AR_ALGO_AUTO's bounds.  Median of 10 single calls each, the three forms
+    interleaved, one JSON line per shape (MiB per rank, element type)."""
+    import torch
+
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    for n, mib, dt in FORM_SWEEP:
+        tdt = getattr(torch, dt)
+        count = (mib << 20) // torch.empty(0, dtype=tdt).element_size()
+        if dt == "int32":
+            sends = [torch.randint(-2**31, 2**31 - 1, (count,), dtype=tdt, device=dev) for _ in range(n)]
+        else:
+            sends = [torch.randn(count, device=dev).to(tdt) for _ in range(n)]
+        recvs = [torch.empty(count, dtype=tdt, device=dev) for _ in range(n)]
+        us = {}
+        for rep in range(2):
+            for algo in ("fused", "phases", "staged"):
+                med, _ = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo), 10, 2, stream)
+                us.setdefault(algo, []).append(med * 1e3)
+        plan = ar.ar_allreduce_init(sends, recvs, algo="auto")
+        auto_launches = plan.num_launches
+        plan.close()
+        row = {"form_sweep": f"{n} x {mib} MiB {dt}", "nranks": n, "mib_per_rank": mib, "dtype": dt,
+               "us": {k: round(min(v), 1) for k, v in us.items()}, "auto_launches": auto_launches}
+        print(json.dumps(row), flush=True)
+        del sends, recvs
+        torch.cuda.empty_cache()
+
+
 def run_cache_sweep(args):
     """The fused AllReduce around the bound of its cache-allocating loads.
 
@@ -904,7 +947,7 @@ def _main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--algo", default="auto", choices=("auto", "fused", "staged"),
+    ap.add_argument("--algo", default="auto", choices=("auto", "fused", "phases", "staged"),
                     help="the AllReduce form the step runs (default: the library's default)")
     ap.add_argument("--no-extra", action="store_true", help="skip the ring / phase / copy side measurements")
     ap.add_argument("--copy-probe", action="store_true",
@@ -929,6 +972,9 @@ def _main():
     ap.add_argument("--size-sweep", action="store_true",
                     help="instead of the headline line: AllReduce time against message size (8 ranks, f32, 1 element "
                          "to 1 GiB per rank), every schedule, with an alpha-beta fit")
+    ap.add_argument("--form-sweep", action="store_true",
+                    help="instead of the headline line: fused, phases and staged AllReduce side by side over rank "
+                         "counts and sizes (the measurements behind the default's choice)")
     ap.add_argument("--cache-sweep", action="store_true",
                     help="instead of the headline line: the fused AllReduce at 32-512 MiB of inputs and 8, 16, "
                          "64 ranks, per call in a replayed graph (around the bound of its cache-allocating loads)")
@@ -972,6 +1018,9 @@ def _main():
     if args.cache_sweep:
         run_cache_sweep(args)
         return
+    if args.form_sweep:
+        run_form_sweep(args)
+        return
     w = WORKLOADS["headline"]
     n, count = w.nranks, w.count
     s_bytes = count * 4
@@ -991,22 +1040,17 @@ def _main():
             ar.ar_allreduce_ex(sends, recvs, algo=args.algo)
 
     # which form the timed call takes here (the library's default, AR_ALGO_AUTO,
-    # unless --algo names one): compare its plan with the staged one (2
-    # launches per segment) and the fused one (1)
-    launches = {}
-    for name in ("auto", "staged", "fused"):
-        plan = ar.ar_allreduce_init(sends, recvs, algo=name)
-        launches[name] = plan.num_launches
-        plan.close()
-    if args.algo == "auto":
-        default_algo = "staged" if launches["auto"] == launches["staged"] and launches["staged"] > 1 else "fused"
-    else:
-        default_algo = args.algo
-    launches["timed"] = launches[default_algo]
+    # unless --algo names one), as the plan of the same call reports it
+    plan = ar.ar_allreduce_init(sends, recvs, algo=args.algo)
+    default_algo, timed_launches = plan.algo, plan.num_launches
+    plan.close()
+    launches = {"timed": timed_launches}
     if default_algo == "staged":
-        segments = launches["staged"] // 2
-        kernel_name = (f"k_staged_reduce<f32,sum,vec16> + k_staged_broadcast<f32,vec16>, "
+        segments = timed_launches // 2
+        kernel_name = (f"k_staged_reduce<f32,sum,vec16> + k_staged_broadcast_xcd<f32,vec16>, "
                        f"{segments} segments of {s_bytes // segments >> 20} MiB of results")
+    elif default_algo == "phases":
+        kernel_name = "k_fused_reduce_scatter<f32,sum,vec16> + k_gather_shards_xcd<f32,vec16> (in place)"
     else:
         kernel_name = "k_fused_allreduce<f32,sum,vec16>"
 
@@ -1034,6 +1078,11 @@ def _main():
                               stream)
         extra["fused_ms"] = round(fused_ms, 4)
         extra["fused_hbm_frac_of_peak"] = round(algo_bytes / (fused_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)
+        # the other large-buffer forms on the same buffers (the same bits)
+        for form in ("phases", "staged"):
+            f_ms = time_calls(lambda: ar.ar_allreduce_ex(sends, recvs, algo=form), max(10, args.steps // 2), 2, stream)
+            extra[f"{form}_ms"] = round(f_ms, 4)
+            extra[f"{form}_hbm_frac_of_peak"] = round(algo_bytes / (f_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)
         # the step-faithful ring mode and the phases alone, on the same buffers
         ring_ms = time_calls(lambda: ar.ar_allreduce_ex(sends, recvs, algo="ring"), max(3, args.steps // 10), 1, stream)
         extra["ring_mode_ms"] = round(ring_ms, 4)
@@ -1068,7 +1117,8 @@ def _main():
                 "mix_probe_us": round(pt["mix"], 1),
                 "allreduce_frac_of_read_plus_write": round((pt["read"] + pt["write"]) / (ms * 1e3), 4),
                 "allreduce_speed_vs_mix_probe": round(pt["mix"] / (ms * 1e3), 4)}
-        log(f"[bench] fused {fused_ms:.3f} ms; ring mode {ring_ms:.3f} ms; pipelined ring {pipe_ms:.3f} ms; "
+        log(f"[bench] fused {fused_ms:.3f} ms; phases {extra['phases_ms']:.3f} ms; staged {extra['staged_ms']:.3f} ms; "
+            f"ring mode {ring_ms:.3f} ms; pipelined ring {pipe_ms:.3f} ms; "
             f"reduce-scatter {rs_ms:.3f} ms; "
             f"all-gather {ag_ms:.3f} ms; "
             f"torch copy {extra['torch_copy_2x2GiB_hbm_gbps']} GB/s")

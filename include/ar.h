@@ -107,15 +107,14 @@ typedef enum {
  * AR_ALGO_PHASES: AllReduce as reduce-scatter followed by all-gather ("2.1
  *   Collective communication primitives in detail", section 3.8), each phase
  *   one fused pass: the reduced chunk c lands in chunk c of recvbufs[c]
- *   (cache-allocating stores), then is copied to every other rank.  The copy
- *   rereads S bytes, partly from the last-level cache, beyond the fused
+ *   (cache-allocating stores), then is copied to every other rank, each
+ *   destination by its own workgroup, a tile's workgroups on one XCD.  The
+ *   copy rereads S bytes, partly from the last-level cache, beyond the fused
  *   kernel's 2N*S, but the read-heavy and the write-heavy halves run apart,
- *   which is faster on MI355X HBM once N is large.
- * AR_ALGO_AUTO: for AllReduce, AR_ALGO_STAGED for large buffers (the
- *   AR_STAGED_MIN_* bounds below, lower for 16-bit types), else AR_ALGO_PHASES from
- *   AR_PHASES_MIN_RANKS ranks when every rank holds at least
- *   AR_PHASES_MIN_BYTES bytes, else AR_ALGO_FUSED; the fused kernel for the
- *   single phases.
+ *   which MI355X HBM serves faster for large buffers.
+ * AR_ALGO_AUTO: for AllReduce, by shape (rules below): AR_ALGO_PHASES or
+ *   AR_ALGO_STAGED for large buffers, AR_ALGO_PHASES at many ranks,
+ *   AR_ALGO_FUSED otherwise; the fused kernel for the single phases.
  * These four give the same bits: the ring's association order.
  *
  * The remaining algorithms are AllReduce only (AR_ERR_UNSUPPORTED for
@@ -162,7 +161,8 @@ typedef enum {
  *   ring's association order kept, cut into segments of rank 0's results.
  *   Per segment, one launch folds every position in ring order and stores
  *   the result to recvbufs[0] only, then one launch copies it to the other
- *   ranks.  The results are reread from the device's 256 MB last-level
+ *   ranks, each destination by its own workgroup, a tile's workgroups on one
+ *   XCD (AR_BCAST_FORM=0: whole or half tiles to every rank per workgroup).  The results are reread from the device's 256 MB last-level
  *   cache, so HBM still moves N*S read and N*S written; the reading and the
  *   writing launches run apart, which MI355X HBM serves faster than the two
  *   interleaved.  The same bits as AR_ALGO_FUSED.  AllReduce only; 2
@@ -204,27 +204,36 @@ typedef enum {
     AR_ALGO_DOUBLE_BINARY_TREE_STEPS = 13
 } ar_algo_t;
 
-/* AR_ALGO_AUTO takes AR_ALGO_STAGED for an AllReduce over at least
- * AR_STAGED_MIN_RANKS ranks of at least AR_STAGED_MIN_BYTES bytes each and at
- * least AR_STAGED_MIN_TOTAL_BYTES bytes in all (measured on MI355X, float32,
- * fused / phases / staged in us: 8 x 256 MiB 752 / 823 / 736; 64 x 256 MiB
- * 6,685 / 6,271 / 5,944; 16 x 96 MiB 600 / 581 / 583; 32 x 32 MiB
- * 425 / 412 / 408; 16 x 64 MiB int32 395 / 391 / 393; at 8 x 128 MiB the
- * three tie; at 8 x 64 MiB and 16 x 16 MiB the fused kernel is faster).  At
- * 6 ranks, fused / staged: 6 x 256 MiB 563 / 554, 6 x 512 MiB 1,175 / 1,132;
- * at 2-4 ranks the fused kernel wins or ties (2 x 512 MiB 367 / 422,
- * 4 x 512 MiB 770 / 771).  These are the common MI355X boxes, whose HBM
- * writes 2 GiB in 371-396 us; on the few whose HBM writes almost as fast as
- * it reads, the fused kernel is ahead at 8 x 256 MiB (659 / 680 and
- * 696 / 734).  Either choice gives the same bits. */
+/* AR_ALGO_AUTO's choice for an AllReduce, from side-by-side timings of the
+ * three forms on MI355X (bench.py --form-sweep; median us of three processes,
+ * fused / phases / staged, float32 unless noted):
+ *   8 x 256 MiB 753 / 718 / 722; 8 x 128 MiB 372 / 359 / 368; 8 x 64 MiB
+ *   188 / 184 / 196; 8 x 32 MiB 83 / 96 / 97; 16 x 256 MiB 1,587 / 1,417 /
+ *   1,470; 16 x 64 MiB 392 / 362 / 362; 16 x 16 MiB 87 / 95 / 94; 32 x 32 MiB
+ *   421 / 374 / 387; 64 x 64 MiB 1,677 / 1,549 / 1,564; 64 x 16 MiB 415 / 398
+ *   / 400; 128 x 64 MiB 3,367 / 2,981 / 3,012; 6 x 256 MiB 547 / 561 / 536;
+ *   4 x 256 MiB 362 / 370 / 363; 2 x 512 MiB 382 / 484 / 429; bf16 8 x 128
+ *   MiB 403 / 368 / 365, 8 x 64 MiB 201 / 190 / 186, 16 x 64 MiB 410 / 356 /
+ *   365; int32 16 x 64 MiB 389 / 359 / 354.
+ * Rules, in order:
+ *   1. AR_ALGO_PHASES from AR_BIG_PHASES_MIN_RANKS ranks with at least
+ *      AR_BIG_PHASES_MIN_BYTES per rank, or from twice that many ranks with
+ *      half as many bytes (16-bit types: from AR_BIG_PHASES_MIN_RANKS_16BIT
+ *      ranks with AR_BIG_PHASES_MIN_BYTES_16BIT per rank);
+ *   2. AR_ALGO_STAGED from AR_STAGED_MIN_RANKS ranks with at least
+ *      AR_STAGED_MIN_BYTES per rank and AR_STAGED_MIN_TOTAL_BYTES in all
+ *      (16-bit types: the _16BIT bounds);
+ *   3. AR_ALGO_PHASES from AR_PHASES_MIN_RANKS ranks with at least
+ *      AR_PHASES_MIN_BYTES per rank;
+ *   4. AR_ALGO_FUSED.
+ * Every choice gives the same bits. */
+#define AR_BIG_PHASES_MIN_RANKS 8
+#define AR_BIG_PHASES_MIN_BYTES (64ull << 20)
+#define AR_BIG_PHASES_MIN_RANKS_16BIT 16
+#define AR_BIG_PHASES_MIN_BYTES_16BIT (32ull << 20)
 #define AR_STAGED_MIN_RANKS 6
 #define AR_STAGED_MIN_BYTES (32ull << 20)
 #define AR_STAGED_MIN_TOTAL_BYTES (1024ull << 20)
-/* The same bounds for the 16-bit element types (bf16, binary16, bf16 with
- * float32 partials), whose fused kernel spends more of its time converting:
- * measured on MI355X, bf16, fused / staged in us: 8 x 64 MiB 204.6 / 201.7,
- * 8 x 128 MiB 397.6 / 383.2, 16 x 32 MiB 211.5 / 206.1, 32 x 32 MiB
- * 444.1 / 405.0; but 8 x 32 MiB 85.8 / 106.1. */
 #define AR_STAGED_MIN_BYTES_16BIT (32ull << 20)
 #define AR_STAGED_MIN_TOTAL_BYTES_16BIT (512ull << 20)
 /* Rank count from which AR_ALGO_AUTO runs an AllReduce as two fused phases
@@ -239,9 +248,14 @@ typedef enum {
  * result's bits.
  *   AR_STAGE_BYTES       AR_ALGO_STAGED: bytes of results per segment (read
  *                        at every call; a plan keeps what it was built with)
- *   AR_HALF_TILES        0 or 1: the fused all-gather and the staged broadcast
- *                        with whole tiles or half tiles per workgroup
- *                        (read at every call; unset: chosen by size)
+ *   AR_BCAST_FORM        0: the staged broadcast with whole or half tiles
+ *                        to every rank per workgroup instead of one
+ *                        destination per workgroup (read at every call)
+ *   AR_GATHER_FORM       0: the same for the fused all-gather (read at
+ *                        every call)
+ *   AR_HALF_TILES        0 or 1: with AR_BCAST_FORM=0 or AR_GATHER_FORM=0,
+ *                        whole tiles or half tiles per workgroup (read at
+ *                        every call; unset: chosen by size)
  *   AR_PHASES_MIN_RANKS  AR_ALGO_AUTO's rank bound for AR_ALGO_PHASES
  *   AR_SMALL_CHUNK_MAX   chunk length (elements) below which the one-pass
  *                        kernels stage a few positions in LDS; 0: never
@@ -251,7 +265,7 @@ typedef enum {
  *                        per compute unit (they stride over the rest); 0:
  *                        one workgroup per tile
  *   AR_DEBUG             nonzero: print every planned launch to stderr
- * All but the first two are read once per process. */
+ * All but the first four are read once per process. */
 
 typedef enum {
     AR_COLL_ALLREDUCE = 0,
@@ -358,6 +372,10 @@ ar_result_t ar_all_gather_init(const void* const* sendbufs, void* const* recvbuf
 ar_result_t ar_plan_start(ar_plan_t plan, hipStream_t stream);
 /* Kernel launches one start enqueues (0 for count == 0), or -1 for NULL. */
 int ar_plan_num_launches(ar_plan_t plan);
+/* The algorithm (an ar_algo_t) the planned call runs: AR_ALGO_AUTO's choice
+ * for the plan's shape, AR_ALGO_FUSED for the fused forms of reduce-scatter
+ * and all-gather and for a single rank; -1 for NULL. */
+int ar_plan_algo(ar_plan_t plan);
 /* Cap the workgroups of every launch of the plan at `max_blocks` (each
  * launch keeps at least one block per acting rank of its stage); the
  * kernels then stride over their tiles, with the same results.  0 restores

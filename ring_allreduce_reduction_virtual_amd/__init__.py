@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     ar_dtype_size,
     ar_get_error_string,
     ar_get_last_error_detail,
+    ar_plan_algo,
     ar_plan_free,
     ar_plan_limit_blocks,
     ar_plan_num_launches,
@@ -36,5 +37,5 @@ __all__ = [
     "ar_all_gather", "ar_all_gather_ex", "ar_workspace_bytes", "ar_chunk_range",
     "ar_get_error_string", "ar_get_last_error_detail", "ar_dtype_size",
     "ar_allreduce_init", "ar_reduce_scatter_init", "ar_all_gather_init", "ar_plan_start", "ar_plan_free",
-    "ar_plan_limit_blocks", "ar_plan_num_launches", "ar_reduce_scatter_noalloc",
+    "ar_plan_limit_blocks", "ar_plan_num_launches", "ar_reduce_scatter_noalloc", "ar_plan_algo",
 ]

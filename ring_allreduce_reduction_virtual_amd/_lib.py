@@ -34,7 +34,7 @@ EXPORTS = (
     "ar_get_last_error_detail", "ar_dtype_size",
     "ar_allreduce_init", "ar_reduce_scatter_init", "ar_all_gather_init",
     "ar_plan_start", "ar_plan_num_launches", "ar_plan_free", "ar_plan_limit_blocks",
-    "ar_reduce_scatter_noalloc",
+    "ar_reduce_scatter_noalloc", "ar_plan_algo",
 )
 # bytes of the fixed device array behind ar_reduce_scatter_noalloc
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -65,6 +65,7 @@ def _declare(lib):
         "ar_all_gather_init": (_int, [_vpp, _vpp, _sz, _int, _int, _int, _vp, _sz, _vpp]),
         "ar_plan_start": (_int, [_vp, _vp]),
         "ar_plan_num_launches": (_int, [_vp]),
+        "ar_plan_algo": (_int, [_vp]),
         "ar_plan_free": (_int, [_vp]),
         "ar_plan_limit_blocks": (_int, [_vp, ctypes.c_uint]),
         "ar_reduce_scatter_noalloc": (_int, [_vpp, _vpp, _sz, _int, _int, _int, _int, _vp]),

@@ -293,6 +293,12 @@ class Plan:
     def num_launches(self) -> int:
         return _lib.lib().ar_plan_num_launches(self._handle)
 
+    @property
+    def algo(self) -> str:
+        """The algorithm the plan runs (the default's choice for its shape), by name."""
+        code = _lib.lib().ar_plan_algo(self._handle)
+        return {v: k for k, v in _lib.ALGOS.items()}.get(code, str(code))
+
     def start(self, stream=None):
         if self._handle is None:
             raise ValueError("plan is closed")
@@ -380,6 +386,11 @@ def ar_plan_start(plan: Plan, stream=None):
 def ar_plan_num_launches(plan: Plan) -> int:
     """Kernel launches one start of the plan enqueues (same as ``plan.num_launches``)."""
     return plan.num_launches
+
+
+def ar_plan_algo(plan: Plan) -> str:
+    """The algorithm a persistent collective runs, by name (same as ``plan.algo``)."""
+    return plan.algo
 
 
 def ar_plan_free(plan: Plan):

@@ -483,7 +483,12 @@ ar_result_t launch_step(const Launch& l, const KernelArgs& a, hipStream_t stream
 class Sink {
 public:
     explicit Sink(hipStream_t stream) : stream_(stream) {}
-    explicit Sink(std::vector<Step>* steps) : steps_(steps) {}
+    Sink(std::vector<Step>* steps, ar_algo_t* algo) : steps_(steps), algo_(algo) {}
+
+    // The algorithm a call resolved to (AR_ALGO_AUTO's choice), kept by plans.
+    void resolved(ar_algo_t algo) {
+        if (algo_ != nullptr) *algo_ = algo;
+    }
 
     ar_result_t emit(Launch& l, Kind kind, const KernelArgs& a, const Common& k) {
         l.kind = kind;
@@ -508,6 +513,7 @@ public:
 private:
     hipStream_t stream_ = nullptr;
     std::vector<Step>* steps_ = nullptr;
+    ar_algo_t* algo_ = nullptr;
 };
 
 // ---------------------------------------------------------------------------
@@ -690,23 +696,31 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         ptrs.push_back(s);
         ptrs.push_back(d);
     }
-    // AUTO: the staged reduce-then-broadcast for large buffers over
-    // AR_STAGED_MIN_RANKS ranks or more; otherwise two fused phases from
-    // phases_min_ranks() ranks when every rank holds at least
-    // AR_PHASES_MIN_BYTES; below that the one fused kernel wins (and the
-    // small-message kernel for the smallest messages)
+    // AUTO (bounds in ar.h, from bench.py --form-sweep): two fused phases for
+    // large buffers from 8 ranks (4-byte types) or 16 (16-bit types); the
+    // staged reduce-then-broadcast for large buffers over 6 ranks or more
+    // below that; the phases again from AR_PHASES_MIN_RANKS ranks when every
+    // rank holds at least AR_PHASES_MIN_BYTES; else the one fused kernel (and
+    // the small-message kernel for the smallest messages)
     if (algo == AR_ALGO_AUTO) {
         const uint64_t per_rank = k.count * k.esz;
-        const bool narrow = k.esz == 2;   // 16-bit types: lower bounds (measured)
+        const bool narrow = k.esz == 2;   // 16-bit types: other bounds (measured)
         const uint64_t min_rank = narrow ? AR_STAGED_MIN_BYTES_16BIT : AR_STAGED_MIN_BYTES;
         const uint64_t min_total = narrow ? AR_STAGED_MIN_TOTAL_BYTES_16BIT : AR_STAGED_MIN_TOTAL_BYTES;
-        if (k.n >= AR_STAGED_MIN_RANKS && per_rank >= min_rank && per_rank * static_cast<uint64_t>(k.n) >= min_total)
+        const bool big_phases = narrow ? (k.n >= AR_BIG_PHASES_MIN_RANKS_16BIT && per_rank >= AR_BIG_PHASES_MIN_BYTES_16BIT)
+                                       : ((k.n >= AR_BIG_PHASES_MIN_RANKS && per_rank >= AR_BIG_PHASES_MIN_BYTES) ||
+                                          (k.n >= 2 * AR_BIG_PHASES_MIN_RANKS &&
+                                           per_rank >= AR_BIG_PHASES_MIN_BYTES / 2));
+        if (big_phases)
+            algo = AR_ALGO_PHASES;
+        else if (k.n >= AR_STAGED_MIN_RANKS && per_rank >= min_rank && per_rank * static_cast<uint64_t>(k.n) >= min_total)
             algo = AR_ALGO_STAGED;
         else if (k.n >= phases_min_ranks() && per_rank >= AR_PHASES_MIN_BYTES && !small_message(k))
             algo = AR_ALGO_PHASES;
         else
             algo = AR_ALGO_FUSED;
     }
+    sink.resolved(k.n == 1 ? AR_ALGO_FUSED : algo);
     if (algo == AR_ALGO_RING_PERSISTENT && k.dtype == AR_BFLOAT16_ACC_F32)
         return fail(AR_ERR_UNSUPPORTED, "the persistent ring has no form with float32 partials");
     if (power_of_two_algo(algo) && (k.n & (k.n - 1)) != 0)
@@ -824,6 +838,7 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
     if (allreduce_only_algo(algo))
         return fail(AR_ERR_UNSUPPORTED, "algo %d is defined for AllReduce only", static_cast<int>(algo));
     if (!ring_steps_algo(algo)) algo = AR_ALGO_FUSED;
+    sink.resolved(k.n == 1 ? AR_ALGO_FUSED : algo);
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;
     const uint64_t bytes = k.count * k.esz;
@@ -874,6 +889,7 @@ ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, Sink& sink) {
     if (allreduce_only_algo(algo))
         return fail(AR_ERR_UNSUPPORTED, "algo %d is defined for AllReduce only", static_cast<int>(algo));
     if (!ring_steps_algo(algo)) algo = AR_ALGO_FUSED;
+    sink.resolved(k.n == 1 ? AR_ALGO_FUSED : algo);
     std::vector<Interval> iv;
     std::vector<uintptr_t> ptrs;
     const uint64_t bytes = k.count * k.esz;
@@ -921,6 +937,7 @@ void arimpl::set_error_detail(const char* text) { g_detail = text; }
 // A persistent collective: the launches one call makes, validated and planned.
 struct ar_plan_s {
     std::vector<Step> steps;
+    ar_algo_t algo = AR_ALGO_AUTO;   // what the planned call resolved to
 };
 
 namespace {
@@ -934,7 +951,7 @@ ar_result_t make_plan(ar_plan_t* out, Build build) {
     *out = nullptr;
     ar_plan_s* p = new (std::nothrow) ar_plan_s;
     if (p == nullptr) return fail(AR_ERR_INTERNAL, "out of host memory");
-    Sink sink(&p->steps);
+    Sink sink(&p->steps, &p->algo);
     const ar_result_t rc = build(sink);
     if (rc != AR_SUCCESS) {
         delete p;
@@ -1032,6 +1049,10 @@ ar_result_t ar_plan_start(ar_plan_t plan, hipStream_t stream) {
 
 int ar_plan_num_launches(ar_plan_t plan) {
     return plan == nullptr ? -1 : static_cast<int>(plan->steps.size());
+}
+
+int ar_plan_algo(ar_plan_t plan) {
+    return plan == nullptr ? -1 : static_cast<int>(plan->algo);
 }
 
 ar_result_t ar_plan_limit_blocks(ar_plan_t plan, unsigned max_blocks) {

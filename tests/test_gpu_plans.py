@@ -166,10 +166,13 @@ def test_block_limits_keep_the_bits(algo, monkeypatch):
 
 
 @pytest.mark.parametrize("n,count,dtype,launches", [
-    (8, 24 << 20, "float32", 1),      # 96 MiB per rank, 768 MiB in all: below the 4-byte total -> fused
-    (8, 48 << 20, "bfloat16", 2),     # the same bytes in bf16: staged (16-bit bounds), one segment
-    (8, 48 << 20, "float32", 4),      # 192 MiB per rank, 1.5 GiB in all: staged, 2 segments of 128 MiB
-    (8, 1 << 26, "float32", 4),       # the headline: staged, 2 segments
+    (8, 24 << 20, "float32", 2),      # 96 MiB per rank from 8 ranks: the two phases
+    (8, 1 << 26, "float32", 2),       # the headline: the two phases
+    (8, 8 << 20, "float32", 1),       # 32 MiB per rank, 256 MiB in all: fused
+    (16, 8 << 20, "float32", 2),      # 32 MiB per rank from 16 ranks: the two phases
+    (8, 48 << 20, "bfloat16", 2),     # 96 MiB per rank of bf16 at 8 ranks: staged (16-bit bounds), one segment
+    (8, 1 << 26, "bfloat16", 2),      # the bf16 workload (128 MiB per rank): staged, one segment
+    (16, 1 << 25, "bfloat16", 2),     # bf16 from 16 ranks, 64 MiB per rank: the two phases
     (8, 1 << 24, "bfloat16", 1),      # 32 MiB per rank, 256 MiB in all: below the 16-bit total -> fused
     (4, 1 << 27, "float32", 1),       # 4 ranks: below the staged rank bound -> fused
     (6, 1 << 26, "float32", 4),       # 6 ranks x 256 MiB: staged, 2 segments of 128 MiB
@@ -186,4 +189,8 @@ def test_auto_choice(n, count, dtype, launches):
     recvs = [torch.empty(count, dtype=tdt, device="cuda:0") for _ in range(n)]
     plan = ar.ar_allreduce_init(sends, recvs, algo="auto")
     assert plan.num_launches == launches
+    want = {1: "fused", 2: "phases", 4: "staged"}[launches]
+    if (n, dtype) in ((8, "bfloat16"),) and count >= 48 << 20:
+        want = "staged"                   # one segment of the staged form: 2 launches too
+    assert plan.algo == want
     plan.close()
