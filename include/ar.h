@@ -205,8 +205,10 @@ typedef enum {
 } ar_algo_t;
 
 /* AR_ALGO_AUTO's choice for an AllReduce, from side-by-side timings of the
- * three forms on MI355X (bench.py --form-sweep; median us of three processes,
- * fused / phases / staged, float32 unless noted):
+ * three forms on MI355X, fused / phases / staged, in microseconds, float32
+ * unless noted.  Two regimes were measured:
+ * (a) steady state (bench.py --form-sweep; median of three processes, each
+ *     after many calls):
  *   8 x 256 MiB 753 / 718 / 722; 8 x 128 MiB 372 / 359 / 368; 8 x 64 MiB
  *   188 / 184 / 196; 8 x 32 MiB 83 / 96 / 97; 16 x 256 MiB 1,587 / 1,417 /
  *   1,470; 16 x 64 MiB 392 / 362 / 362; 16 x 16 MiB 87 / 95 / 94; 32 x 32 MiB
@@ -215,11 +217,17 @@ typedef enum {
  *   4 x 256 MiB 362 / 370 / 363; 2 x 512 MiB 382 / 484 / 429; bf16 8 x 128
  *   MiB 403 / 368 / 365, 8 x 64 MiB 201 / 190 / 186, 16 x 64 MiB 410 / 356 /
  *   365; int32 16 x 64 MiB 389 / 359 / 354.
- * Rules, in order:
+ * (b) a fresh process, after 2 s idle, mean of calls 6 to 25: the two
+ *     phases' in-place gather runs 3-8 % slow over its first twenty or so
+ *     calls; the other forms do not:
+ *   8 x 256 MiB 753 / 751 / 732; 8 x 64 MiB 197 / 204 / 193; 16 x 64 MiB 405
+ *   / 395 / 381; 32 x 32 MiB 448 / 407 / 398; 16 x 256 MiB 1,575 / 1,420 /
+ *   1,438; 64 x 64 MiB 1,694 / 1,522 / 1,546; bf16 8 x 128 MiB 396 / 413 /
+ *   385, 16 x 64 MiB 415 / 403 / 389, 16 x 32 MiB 220 / 216 / 205, 32 x 32
+ *   MiB 452 / 409 / 413.
+ * The rules follow (b) where the two disagree, in order:
  *   1. AR_ALGO_PHASES from AR_BIG_PHASES_MIN_RANKS ranks with at least
- *      AR_BIG_PHASES_MIN_BYTES per rank, or from twice that many ranks with
- *      half as many bytes (16-bit types: from AR_BIG_PHASES_MIN_RANKS_16BIT
- *      ranks with AR_BIG_PHASES_MIN_BYTES_16BIT per rank);
+ *      AR_BIG_PHASES_MIN_TOTAL_BYTES over all ranks;
  *   2. AR_ALGO_STAGED from AR_STAGED_MIN_RANKS ranks with at least
  *      AR_STAGED_MIN_BYTES per rank and AR_STAGED_MIN_TOTAL_BYTES in all
  *      (16-bit types: the _16BIT bounds);
@@ -227,10 +235,8 @@ typedef enum {
  *      AR_PHASES_MIN_BYTES per rank;
  *   4. AR_ALGO_FUSED.
  * Every choice gives the same bits. */
-#define AR_BIG_PHASES_MIN_RANKS 8
-#define AR_BIG_PHASES_MIN_BYTES (64ull << 20)
-#define AR_BIG_PHASES_MIN_RANKS_16BIT 16
-#define AR_BIG_PHASES_MIN_BYTES_16BIT (32ull << 20)
+#define AR_BIG_PHASES_MIN_RANKS 16
+#define AR_BIG_PHASES_MIN_TOTAL_BYTES (4ull << 30)
 #define AR_STAGED_MIN_RANKS 6
 #define AR_STAGED_MIN_BYTES (32ull << 20)
 #define AR_STAGED_MIN_TOTAL_BYTES (1024ull << 20)

@@ -696,24 +696,23 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         ptrs.push_back(s);
         ptrs.push_back(d);
     }
-    // AUTO (bounds in ar.h, from bench.py --form-sweep): two fused phases for
-    // large buffers from 8 ranks (4-byte types) or 16 (16-bit types); the
-    // staged reduce-then-broadcast for large buffers over 6 ranks or more
-    // below that; the phases again from AR_PHASES_MIN_RANKS ranks when every
-    // rank holds at least AR_PHASES_MIN_BYTES; else the one fused kernel (and
-    // the small-message kernel for the smallest messages)
+    // AUTO (bounds in ar.h, from timings of the three forms): two fused phases
+    // from AR_BIG_PHASES_MIN_RANKS ranks once all ranks together hold
+    // AR_BIG_PHASES_MIN_TOTAL_BYTES; the staged reduce-then-broadcast for large
+    // buffers over 6 ranks or more below that; the phases again from
+    // AR_PHASES_MIN_RANKS ranks when every rank holds at least
+    // AR_PHASES_MIN_BYTES; else the one fused kernel (and the small-message
+    // kernel for the smallest messages)
     if (algo == AR_ALGO_AUTO) {
         const uint64_t per_rank = k.count * k.esz;
+        const uint64_t total = per_rank * static_cast<uint64_t>(k.n);
         const bool narrow = k.esz == 2;   // 16-bit types: other bounds (measured)
         const uint64_t min_rank = narrow ? AR_STAGED_MIN_BYTES_16BIT : AR_STAGED_MIN_BYTES;
         const uint64_t min_total = narrow ? AR_STAGED_MIN_TOTAL_BYTES_16BIT : AR_STAGED_MIN_TOTAL_BYTES;
-        const bool big_phases = narrow ? (k.n >= AR_BIG_PHASES_MIN_RANKS_16BIT && per_rank >= AR_BIG_PHASES_MIN_BYTES_16BIT)
-                                       : ((k.n >= AR_BIG_PHASES_MIN_RANKS && per_rank >= AR_BIG_PHASES_MIN_BYTES) ||
-                                          (k.n >= 2 * AR_BIG_PHASES_MIN_RANKS &&
-                                           per_rank >= AR_BIG_PHASES_MIN_BYTES / 2));
+        const bool big_phases = k.n >= AR_BIG_PHASES_MIN_RANKS && total >= AR_BIG_PHASES_MIN_TOTAL_BYTES;
         if (big_phases)
             algo = AR_ALGO_PHASES;
-        else if (k.n >= AR_STAGED_MIN_RANKS && per_rank >= min_rank && per_rank * static_cast<uint64_t>(k.n) >= min_total)
+        else if (k.n >= AR_STAGED_MIN_RANKS && per_rank >= min_rank && total >= min_total)
             algo = AR_ALGO_STAGED;
         else if (k.n >= phases_min_ranks() && per_rank >= AR_PHASES_MIN_BYTES && !small_message(k))
             algo = AR_ALGO_PHASES;

@@ -165,20 +165,23 @@ def test_block_limits_keep_the_bits(algo, monkeypatch):
     plan.close()
 
 
-@pytest.mark.parametrize("n,count,dtype,launches", [
-    (8, 24 << 20, "float32", 2),      # 96 MiB per rank from 8 ranks: the two phases
-    (8, 1 << 26, "float32", 2),       # the headline: the two phases
-    (8, 8 << 20, "float32", 1),       # 32 MiB per rank, 256 MiB in all: fused
-    (16, 8 << 20, "float32", 2),      # 32 MiB per rank from 16 ranks: the two phases
-    (8, 48 << 20, "bfloat16", 2),     # 96 MiB per rank of bf16 at 8 ranks: staged (16-bit bounds), one segment
-    (8, 1 << 26, "bfloat16", 2),      # the bf16 workload (128 MiB per rank): staged, one segment
-    (16, 1 << 25, "bfloat16", 2),     # bf16 from 16 ranks, 64 MiB per rank: the two phases
-    (8, 1 << 24, "bfloat16", 1),      # 32 MiB per rank, 256 MiB in all: below the 16-bit total -> fused
-    (4, 1 << 27, "float32", 1),       # 4 ranks: below the staged rank bound -> fused
-    (6, 1 << 26, "float32", 4),       # 6 ranks x 256 MiB: staged, 2 segments of 128 MiB
-    (64, 1 << 20, "float32", 2),      # 64 ranks x 4 MiB: the two phases
+@pytest.mark.parametrize("n,count,dtype,want,launches", [
+    (8, 1 << 26, "float32", "staged", 4),     # the headline, 8 x 256 MiB: staged, 2 segments of 128 MiB
+    (8, 24 << 20, "float32", "fused", 1),     # 96 MiB per rank, 768 MiB in all: below the staged total
+    (8, 8 << 20, "float32", "fused", 1),      # 32 MiB per rank, 256 MiB in all: fused
+    (16, 1 << 24, "float32", "staged", 2),    # 16 x 64 MiB, 1 GiB in all: staged, one segment
+    (16, 1 << 26, "float32", "phases", 2),    # 16 x 256 MiB, 4 GiB in all: the two phases
+    (64, 1 << 24, "float32", "phases", 2),    # 64 x 64 MiB, 4 GiB in all: the two phases
+    (16, 8 << 20, "float32", "fused", 1),     # 16 x 32 MiB, 512 MiB in all: fused
+    (8, 48 << 20, "bfloat16", "staged", 2),   # 96 MiB per rank of bf16 at 8 ranks: staged (16-bit total)
+    (8, 1 << 26, "bfloat16", "staged", 2),    # the bf16 workload (128 MiB per rank): staged, one segment
+    (16, 1 << 25, "bfloat16", "staged", 2),   # bf16, 16 x 64 MiB: staged
+    (8, 1 << 24, "bfloat16", "fused", 1),     # 32 MiB per rank, 256 MiB in all: below the 16-bit total
+    (4, 1 << 27, "float32", "fused", 1),      # 4 ranks: below the staged rank bound
+    (6, 1 << 26, "float32", "staged", 4),     # 6 ranks x 256 MiB: staged, 2 segments of 128 MiB
+    (64, 1 << 20, "float32", "phases", 2),    # 64 ranks x 4 MiB: the two phases (many ranks)
 ])
-def test_auto_choice(n, count, dtype, launches):
+def test_auto_choice(n, count, dtype, want, launches):
     """Which form AR_ALGO_AUTO plans at shapes on both sides of its bounds
     (validation and planning only: nothing is launched)."""
     import torch
@@ -188,9 +191,6 @@ def test_auto_choice(n, count, dtype, launches):
     sends = [torch.empty(count, dtype=tdt, device="cuda:0") for _ in range(n)]
     recvs = [torch.empty(count, dtype=tdt, device="cuda:0") for _ in range(n)]
     plan = ar.ar_allreduce_init(sends, recvs, algo="auto")
-    assert plan.num_launches == launches
-    want = {1: "fused", 2: "phases", 4: "staged"}[launches]
-    if (n, dtype) in ((8, "bfloat16"),) and count >= 48 << 20:
-        want = "staged"                   # one segment of the staged form: 2 launches too
     assert plan.algo == want
+    assert plan.num_launches == launches
     plan.close()
