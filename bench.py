@@ -874,6 +874,36 @@ def run_form_sweep(args):
         torch.cuda.empty_cache()
 
 
+RANK_SCALING = ((8, 1 << 26), (16, 1 << 26), (32, 1 << 26), (64, 1 << 26), (64, (1 << 26) + 7))
+
+
+def run_rank_scaling(args):
+    """The fused AllReduce at 8 to 64 ranks of 256 MiB of float32 each (and
+    the 64-rank workload's own length, 2^26 + 7), beside the staged form: the
+    same bytes per rank, more interleaved streams.  Median of --steps single
+    calls after --warmup, one JSON line per shape.  Run under rocprofv3 with
+    address-translation and memory-side counters, it is the command of the
+    fused kernel's rank-count counter summary."""
+    import torch
+
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    for n, count in RANK_SCALING:
+        sends = [torch.randn(count, device=dev) for _ in range(n)]
+        recvs = [torch.empty(count, device=dev) for _ in range(n)]
+        row = {"rank_scaling": f"{n} x {count} f32 sum", "nranks": n, "count": count}
+        for algo in ("fused", "staged"):
+            med, best = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo),
+                                       max(args.steps, 1), args.warmup, stream)
+            row[f"{algo}_us"] = round(med * 1e3, 1)
+            row[f"{algo}_hbm_frac"] = round(2 * n * count * 4 / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        print(json.dumps(row), flush=True)
+        del sends, recvs
+        torch.cuda.empty_cache()
+
+
 def run_cache_sweep(args):
     """The fused AllReduce around the bound of its cache-allocating loads.
 
@@ -978,6 +1008,9 @@ def _main():
     ap.add_argument("--cache-sweep", action="store_true",
                     help="instead of the headline line: the fused AllReduce at 32-512 MiB of inputs and 8, 16, "
                          "64 ranks, per call in a replayed graph (around the bound of its cache-allocating loads)")
+    ap.add_argument("--rank-scaling", action="store_true",
+                    help="instead of the headline line: the fused and staged AllReduce at 8, 16, 32 and 64 ranks "
+                         "of 256 MiB float32 each (the 64-rank workload's length too)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -1020,6 +1053,9 @@ def _main():
         return
     if args.form_sweep:
         run_form_sweep(args)
+        return
+    if args.rank_scaling:
+        run_rank_scaling(args)
         return
     w = WORKLOADS["headline"]
     n, count = w.nranks, w.count

@@ -262,6 +262,11 @@ typedef enum {
  *   AR_HALF_TILES        0 or 1: with AR_BCAST_FORM=0 or AR_GATHER_FORM=0,
  *                        whole tiles or half tiles per workgroup (read at
  *                        every call; unset: chosen by size)
+ *   AR_TILE_XCD          rank count from which the fused AllReduce, the
+ *                        staged reduce and the fused reduce-scatter walk
+ *                        their tiles in one contiguous slab per XCD (fewer
+ *                        pages for each XCD to translate; default 64; 0:
+ *                        never; read at every call)
  *   AR_PHASES_MIN_RANKS  AR_ALGO_AUTO's rank bound for AR_ALGO_PHASES
  *   AR_SMALL_CHUNK_MAX   chunk length (elements) below which the one-pass
  *                        kernels stage a few positions in LDS; 0: never
@@ -271,7 +276,7 @@ typedef enum {
  *                        per compute unit (they stride over the rest); 0:
  *                        one workgroup per tile
  *   AR_DEBUG             nonzero: print every planned launch to stderr
- * All but the first four are read once per process. */
+ * All but the first five are read once per process. */
 
 typedef enum {
     AR_COLL_ALLREDUCE = 0,

@@ -345,6 +345,24 @@ uint64_t cached_loads_max() {
     return v;
 }
 
+// Tile order of a launch that streams every rank's buffer at once (the fused
+// AllReduce, the staged reduce, the phases' reduce-scatter): one contiguous
+// slab of tiles per XCD from AR_TILE_XCD_MIN_RANKS ranks, else consecutive
+// tiles to consecutive blocks.  The AR_TILE_XCD environment variable sets the
+// rank bound (0: never); it is read at every call, as AR_STAGE_BYTES is.
+unsigned tile_xcd_min_ranks() {
+    const char* e = std::getenv("AR_TILE_XCD");
+    if (e != nullptr && e[0] != '\0') return static_cast<unsigned>(std::strtoul(e, nullptr, 10));
+    return AR_TILE_XCD_MIN_RANKS;
+}
+
+void tile_order(KernelArgs& a, Launch& l, const Common& k) {
+    const unsigned from = tile_xcd_min_ranks();
+    a.xcd_slabs = (from != 0 && static_cast<unsigned>(k.n) >= from && l.blocks >= 8) ? 1 : 0;
+    // whole groups of eight blocks, one per XCD (the kernels stride within a slab)
+    if (a.xcd_slabs) l.blocks = static_cast<unsigned>(std::min<uint64_t>((l.blocks + 7ull) / 8 * 8, 0x7ffffff8u));
+}
+
 // Bytes of rank 0's results per segment of AR_ALGO_STAGED: about
 // AR_STAGE_READ_BYTES of inputs read per segment, between AR_STAGE_BYTES_MIN
 // and AR_STAGE_BYTES_MAX of results.  The AR_STAGE_BYTES environment variable
@@ -751,6 +769,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         if ((rc = plan(a, l, k, common_residue(sends))) != AR_SUCCESS) return rc;
         // cache-allocating stores: the all-gather that follows rereads these chunks
         l.cached_store = true;
+        tile_order(a, l, k);
         if ((rc = sink.emit(l, Kind::kFusedReduceScatter, a, k)) != AR_SUCCESS) return rc;
         // ... then all-gather in place: chunk c of recv[c] to every other rank
         KernelArgs g{};
@@ -772,6 +791,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_FUSED) {
         l.cached = l.vec && static_cast<uint64_t>(k.n) * k.count * k.esz <= cached_loads_max();
+        tile_order(a, l, k);
         return sink.emit(l, Kind::kFusedAllReduce, a, k);
     }
     if (algo == AR_ALGO_STAGED) {
@@ -788,6 +808,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
             a.tile_first = static_cast<uint32_t>(t0);
             a.tile_end = static_cast<uint32_t>(std::min<uint64_t>(total, t0 + per_seg));
             if ((rc = grid_for(a, l)) != AR_SUCCESS) return rc;
+            tile_order(a, l, k);
             if ((rc = sink.emit(l, Kind::kStagedReduce, a, k)) != AR_SUCCESS) return rc;
             if ((rc = copy_grid(a, l, k)) != AR_SUCCESS) return rc;
             if ((rc = broadcast_form(a, l, k)) != AR_SUCCESS) return rc;

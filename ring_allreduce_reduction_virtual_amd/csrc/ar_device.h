@@ -620,16 +620,41 @@ __device__ __forceinline__ bool shard_aligned(const void* shard, uint64_t s, int
     return (q & 15u) == 0;
 }
 
+// The tiles a block walks: consecutive tiles to consecutive blocks (the
+// default), or, when the launch sets xcd_slabs, the launch's tiles cut into
+// eight contiguous slabs, slab x walked by the blocks the dispatcher deals to
+// XCD x (blocks x, x + 8, x + 16, ...).  Each XCD then touches one eighth of
+// the address range that all the blocks in flight touch, so its address
+// translation cache holds one eighth of the pages: that matters once many
+// ranks' buffers are streamed at once (measured on MI355X at 32 and more
+// ranks); with few ranks the plain order is as fast.  The host gives such a
+// launch a grid of a multiple of eight blocks; blocks past the last whole
+// group of eight walk nothing.
+struct TileWalk {
+    uint32_t first, end, step;
+};
+
+__device__ __forceinline__ TileWalk tile_walk(const KernelArgs& a) {
+    const uint32_t per = gridDim.x >> 3;   // blocks per XCD
+    if (a.xcd_slabs == 0 || per == 0) return {a.tile_first + blockIdx.x, a.tile_end, gridDim.x};
+    const uint32_t x = blockIdx.x & 7u, m = blockIdx.x >> 3;
+    const uint64_t span = a.tile_end - a.tile_first;
+    const uint32_t s0 = a.tile_first + static_cast<uint32_t>(span * x / 8);
+    const uint32_t s1 = a.tile_first + static_cast<uint32_t>(span * (x + 1) / 8);
+    if (m >= per) return {s1, s1, 1u};
+    return {s0 + m, s1, per};
+}
+
 // Tile loop: tile -> (chunk c, tile t within the chunk); consecutive tiles
 // walk one chunk after another (measured faster on MI355X than cycling over
-// the chunks, or than renumbering tiles per XCD).  A launch covers tiles
-// [tile_first, tile_end); the host keeps N * tiles_per_chunk below 2^31.
+// the chunks).  A launch covers tiles [tile_first, tile_end) in the order of
+// tile_walk; the host keeps N * tiles_per_chunk below 2^31.
 #define AR_TILE_LOOP_BEGIN                                                                   \
     const int n = a.nranks;                                                                  \
     const uint32_t tpc = a.tiles_per_chunk;                                                  \
-    const uint32_t ntiles = a.tile_end;                                                      \
     const int64_t adj = (VEC > 1) ? static_cast<int64_t>(a.ofs) * elem_size<DT>() : 0;       \
-    for (uint32_t tile = a.tile_first + blockIdx.x; tile < ntiles; tile += gridDim.x) {      \
+    const TileWalk walk = tile_walk(a);                                                      \
+    for (uint32_t tile = walk.first; tile < walk.end; tile += walk.step) {                   \
         const int c = static_cast<int>(tile / tpc);                                          \
         const uint64_t t = tile - static_cast<uint32_t>(c) * tpc;                            \
         const Span sp = chunk_span<VEC>(c, a);                                               \

@@ -77,6 +77,7 @@ struct KernelArgs {
     int32_t mode;              // kTree*Step: a TreeMode
     int32_t last;              // kTreeReduceStep: nonzero on the stage that completes the values
     uint64_t ws_stride;        // kTreeReduceStep with float32 partials: bytes between ranks' partials
+    int32_t xcd_slabs;         // tiled kernels: nonzero walks the tiles in one contiguous slab per XCD
 };
 
 struct Launch {
@@ -130,6 +131,16 @@ constexpr int kUnroll = AR_TILE_UNROLL;
 // call, 32 MiB / 128 MiB segments: 8 ranks 740 / 736, 16 ranks 1,513 /
 // 1,519, 32 ranks 2,979 / 3,002, 64 ranks 5,944 / 6,028, 128 ranks 11,701 /
 // 11,728.
+// Rank count from which the launches that stream every rank's buffer at once
+// walk their tiles in one contiguous slab per XCD (tile_walk); 0 never.
+// Measured on MI355X, the same buffers in one process, plain / slabs, us:
+// 64 x 16 MiB float32 fused 427 / 395, staged 386 / 370, phases 378 / 364;
+// 128 x 64 MiB fused 3,351 / 3,285, staged 2,986 / 2,934; 64 x 256 MiB
+// phases 6,412 / 6,096, fused and staged within 1 %; 32 x 256 MiB within
+// 1.5 % (staged slower); 8 x 256 MiB fused 741 / 790 (slower).
+#ifndef AR_TILE_XCD_MIN_RANKS
+#define AR_TILE_XCD_MIN_RANKS 64
+#endif
 #ifndef AR_STAGE_READ_BYTES
 #define AR_STAGE_READ_BYTES (2048ull << 20)
 #endif
