@@ -13,7 +13,8 @@ What it holds, each piece written from the pages on ring AllReduce:
                 section "How it works"), the standalone reduce-scatter and
                 all-gather, the element operators, bf16 round-to-nearest-even,
                 and the closed definition of the result (the ring's
-                association order) used for sampled checks at full size;
+                association order), which the full-size checks compare
+                every output element with;
 * ``threaded``  one thread per rank, each a state machine that answers
                 arrivals and forwards the chunk it just completed, with a
                 receive time-out that turns a stuck ring into an error;
