@@ -3,8 +3,9 @@
  *
  * C ABI of libar.so.  Calls keep no state from one to the next (tirogla.com
  * "Ring all-reduce", section "How it works", the line that states the
- * collective's inputs, outputs and state), and every call is asynchronous: it validates its arguments on the host, enqueues kernels
- * on `stream` and returns.  The arguments follow the collective's statement
+ * collective's inputs, outputs and state), and every call is asynchronous:
+ * it validates its arguments on the host, enqueues kernels on `stream` and
+ * returns.  The arguments follow the collective's statement
  * on arjunsriva.com "AllReduce, All the Way Down", section "The Contract"
  * (send buffer, receive buffer, count, datatype, reduction, participants,
  * stream), with the communicator replaced by the number of virtual ranks and
@@ -162,7 +163,8 @@ typedef enum {
  *   Per segment, one launch folds every position in ring order and stores
  *   the result to recvbufs[0] only, then one launch copies it to the other
  *   ranks, each destination by its own workgroup, a tile's workgroups on one
- *   XCD (AR_BCAST_FORM=0: whole or half tiles to every rank per workgroup).  The results are reread from the device's 256 MB last-level
+ *   XCD (AR_BCAST_FORM=0: whole or half tiles to every rank per
+ *   workgroup).  The results are reread from the device's 256 MB last-level
  *   cache, so HBM still moves N*S read and N*S written; the reading and the
  *   writing launches run apart, which MI355X HBM serves faster than the two
  *   interleaved.  The same bits as AR_ALGO_FUSED.  AllReduce only; 2
