@@ -33,11 +33,35 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 # rocprofv3 counter summaries of the headline call, by the form it runs
 COUNTERS_FILES = {"staged": os.path.join(ROOT, "profiles", "staged_allreduce_headline_counters.md"),
                   "fused": os.path.join(ROOT, "profiles", "fused_allreduce_headline_counters.md"),
-                  "phases": os.path.join(ROOT, "profiles", "phases_allreduce_headline_counters.md")}
+                  "phases": os.path.join(ROOT, "profiles", "phases_allreduce_headline_counters.md"),
+                  "double_binary_tree": os.path.join(ROOT, "profiles", "dbt_allreduce_headline_counters.md"),
+                  "double_binary_tree_steps": os.path.join(ROOT, "profiles",
+                                                           "dbt_steps_allreduce_headline_counters.md")}
 # the sources the AllReduce kernels are built from (their counters are only
 # used while these are unchanged)
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_reduction_virtual_amd", "csrc", f)
                   for f in ("ar_kernels.hip", "ar_device.h", "ar_internal.h")]
+
+
+# the AllReduce algorithms bench.py can time as its step, and the kernels each
+# one launches (float32, sum, 16-byte vectors at the headline shape)
+STEP_ALGOS = ("auto", "fused", "phases", "staged", "ring", "ring_pipelined", "ring_persistent", "tree",
+              "tree_steps", "recursive_doubling", "halving_doubling", "halving_doubling_steps", "double_binary_tree",
+              "double_binary_tree_steps")
+STEP_KERNELS = {
+    "fused": "k_fused_allreduce<f32,sum,vec16>",
+    "phases": "k_fused_reduce_scatter<f32,sum,vec16> + k_gather_shards_xcd<f32,vec16> (in place)",
+    "ring": "k_ring_reduce_step<f32,sum,vec16> + k_ring_copy_step<f32,vec16>, {launches} launches",
+    "ring_pipelined": "k_ring_pipelined<f32,sum,vec16>",
+    "ring_persistent": "k_ring_persistent<f32,sum,vec16>",
+    "tree": "k_fused_tree<f32,sum,vec16>",
+    "halving_doubling": "k_fused_tree<f32,sum,vec16> (bit-reversed ranks)",
+    "tree_steps": "k_tree_reduce_step<f32,sum,vec16> + k_tree_copy_step<f32,vec16>, {launches} launches",
+    "halving_doubling_steps": "k_tree_reduce_step<f32,sum,vec16> + k_tree_copy_step<f32,vec16>, {launches} launches",
+    "recursive_doubling": "k_tree_reduce_step<f32,sum,vec16>, {launches} launches",
+    "double_binary_tree": "k_fused_dbt<f32,sum,vec16>",
+    "double_binary_tree_steps": "k_dbt_reduce_step<f32,sum,vec16> + k_dbt_copy_step<f32,vec16>, {launches} launches",
+}
 
 
 def log(*a):
@@ -55,9 +79,14 @@ def algorithmic_bytes(coll: str, n: int, s_bytes: int) -> int:
     return 2 * n * s_bytes if coll == "allreduce" else (n + 1) * s_bytes
 
 
-def kernel_source_hash() -> str:
+# kernels of other forms live in files of their own, hashed with the shared ones
+FORM_SOURCES = {form: [os.path.join(ROOT, "ring_allreduce_reduction_virtual_amd", "csrc", "ar_dbt_kernels.hip")]
+                for form in ("double_binary_tree", "double_binary_tree_steps")}
+
+
+def kernel_source_hash(form: str = None) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in KERNEL_SOURCES + FORM_SOURCES.get(form, []):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -75,7 +104,7 @@ def measured_traffic(form: str):
     if not m:
         return None
     d = json.loads(m.group(1))
-    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+    if d.get("kernel_source_sha256_16") != kernel_source_hash(form):
         return None
     return d.get("bytes_per_call")
 
@@ -977,8 +1006,10 @@ def _main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--algo", default="auto", choices=("auto", "fused", "phases", "staged"),
-                    help="the AllReduce form the step runs (default: the library's default)")
+    ap.add_argument("--algo", default="auto", choices=STEP_ALGOS,
+                    help="the AllReduce algorithm the step runs (default: the library's default); every one "
+                         "but auto, fused, phases and staged runs another schedule or order, timed against "
+                         "the same 2*N*S minimum")
     ap.add_argument("--no-extra", action="store_true", help="skip the ring / phase / copy side measurements")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
@@ -1085,10 +1116,8 @@ def _main():
         segments = timed_launches // 2
         kernel_name = (f"k_staged_reduce<f32,sum,vec16> + k_staged_broadcast_xcd<f32,vec16>, "
                        f"{segments} segments of {s_bytes // segments >> 20} MiB of results")
-    elif default_algo == "phases":
-        kernel_name = "k_fused_reduce_scatter<f32,sum,vec16> + k_gather_shards_xcd<f32,vec16> (in place)"
     else:
-        kernel_name = "k_fused_allreduce<f32,sum,vec16>"
+        kernel_name = STEP_KERNELS[default_algo].format(launches=timed_launches)
 
     # timed region: K AllReduce calls, synchronized on both sides
     ms = time_calls(step, args.steps, args.warmup, stream)
@@ -1187,7 +1216,7 @@ def _main():
         "data": "synthetic",
         "config": {"workload": "ring AllReduce, 8 virtual ranks x 2^26 float32 (256 MiB each), sum, "
                                + ("the library's default algorithm" if args.algo == "auto"
-                                  else f"the {args.algo} form"),
+                                  else f"algorithm {args.algo}"),
                    "nranks": n, "count": count, "op": "sum",
                    "algo": f"auto ({default_algo})" if args.algo == "auto" else args.algo,
                    "inputs": "N(0,1), seed 1"},

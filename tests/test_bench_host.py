@@ -25,17 +25,26 @@ def test_algorithmic_bytes_and_busbw():
     assert bench.busbw_factor("allreduce", 1) == 0.0
 
 
-@pytest.mark.parametrize("form", ["staged", "fused"])
+# bytes each form names per call at the headline (8 ranks, S = 256 MiB), in units of S
+NAMED = {"staged": 16, "fused": 16, "phases": 17, "double_binary_tree": 16,
+         "double_binary_tree_steps": bench.dbt_steps_bytes_factor(8)}
+
+
+@pytest.mark.parametrize("form", sorted(bench.COUNTERS_FILES))
 def test_committed_counter_summaries_parse(form):
     """Each committed summary holds a traffic line for one call of its form at
-    the headline, between the algorithmic minimum (2N*S) and 10% above it."""
-    text = open(bench.COUNTERS_FILES[form]).read()
+    the headline, between the algorithmic minimum (2N*S) and 10% above the
+    bytes the form names."""
+    path = bench.COUNTERS_FILES[form]
+    if not os.path.exists(path):
+        pytest.skip(f"no counter summary for {form}")
+    text = open(path).read()
     line = [ln for ln in text.splitlines() if ln.startswith("traffic_json: ")]
     assert len(line) == 1
     d = json.loads(line[0][len("traffic_json: "):])
-    assert 2 * 8 * S <= d["bytes_per_call"] <= 1.1 * 2 * 8 * S
+    assert 2 * 8 * S <= d["bytes_per_call"] <= 1.1 * NAMED[form] * S
     assert d["fetch_bytes"] + d["write_bytes"] == d["bytes_per_call"]
-    if d["kernel_source_sha256_16"] == bench.kernel_source_hash():
+    if d["kernel_source_sha256_16"] == bench.kernel_source_hash(form):
         assert bench.measured_traffic(form) == d["bytes_per_call"]
     else:
         assert bench.measured_traffic(form) is None
