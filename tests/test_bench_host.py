@@ -71,3 +71,15 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_every_step_algorithm_names_its_kernels():
+    """bench.py --algo accepts the library's AllReduce algorithms, and names the
+    kernels of each in its line (staged and auto are named from the plan)."""
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    for algo in bench.STEP_ALGOS:
+        assert algo in _lib.ALGOS, algo
+        if algo not in ("auto", "staged"):
+            assert bench.STEP_KERNELS[algo].format(launches=6)
+    assert set(bench.STEP_KERNELS) | {"auto", "staged"} == set(bench.STEP_ALGOS)
