@@ -533,7 +533,70 @@ def load_probe_library():
     lib.arprobe_xcd.restype = ctypes.c_int
     lib.arprobe_xcd.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
                                 ctypes.c_void_p]
+    lib.arprobe_wmap.restype = ctypes.c_int
+    lib.arprobe_wmap.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
+                                 ctypes.c_void_p]
     return lib
+
+
+WMAPS = {0: "grouped per XCD (a tile's workgroups on one XCD, as the staged broadcast)",
+         1: "tile-major (workgroup b: buffer b mod n)",
+         2: "buffer-major",
+         3: "one contiguous buffer-major range per XCD",
+         4: "one contiguous tile-major range per XCD",
+         5: "one contiguous eighth of the tiles per XCD, in runs of 16 tiles buffer by buffer",
+         6: "one contiguous eighth of the tiles per XCD, in runs of 64 tiles buffer by buffer",
+         7: "one contiguous eighth of the tiles per XCD, in runs of 256 tiles buffer by buffer"}
+
+
+def run_write_maps(lib, steps=20, rounds=3):
+    """Writes of 7 and 8 buffers of 128 MiB (the staged broadcast's segment at
+    8 ranks: 7 destinations), one 8 KiB tile per workgroup, nontemporal
+    stores, in each of the workgroup -> (buffer, tile) maps of k_wmap; alone,
+    and with each workgroup loading its tile from one 128 MiB source first, as
+    the broadcast does (the source rewritten by torch just before each call).
+    The maps are interleaved over `rounds` passes on the same buffers and the
+    best median kept.  One JSON line per map and form."""
+    import ctypes
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    mib = 1 << 20
+    size = 128 * mib
+    nvec = size // 16
+    src = torch.ones(size // 4, device=dev)
+    dst = [torch.empty(size // 4, device=dev) for _ in range(8)]
+    best = {}
+    for _ in range(rounds):
+        for n in (7, 8):
+            tbl = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dst[:n]])
+            for with_src in (False, True):
+                for m in WMAPS:
+                    ts = []
+                    for i in range(steps + 3):
+                        if with_src:
+                            src.fill_(float(i))
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        rc = lib.arprobe_wmap(m, src.data_ptr() if with_src else None, tbl, n, nvec,
+                                              ctypes.c_void_p(stream.cuda_stream))
+                        e1.record(stream)
+                        e1.synchronize()
+                        if rc != 0:
+                            raise RuntimeError(f"arprobe_wmap map {m}: error {rc}")
+                        if i >= 3:
+                            ts.append(e0.elapsed_time(e1) * 1e3)
+                    ts.sort()
+                    key = (n, with_src, m)
+                    best[key] = min(best.get(key, 1e18), ts[len(ts) // 2])
+    for (n, with_src, m), us in sorted(best.items()):
+        nbytes = n * size
+        print(json.dumps({"write_map": WMAPS[m], "map": m, "buffers": f"{n} x 128 MiB",
+                          "source": "each tile loaded from a 128 MiB source first" if with_src else "none",
+                          "bytes_written": nbytes, "us": round(us, 1), "write_tbps": round(nbytes / us / 1e6, 3),
+                          "frac_of_8tbps": round(nbytes / us / 1e6 / (HBM_PEAK_GBPS / 1e3), 4)}), flush=True)
 
 
 def run_xcd_patterns(lib, steps=20):
@@ -759,6 +822,7 @@ def run_ceiling(args):
     stream = torch.cuda.current_stream()
     run_ceiling_patterns(lib)
     run_xcd_patterns(lib)
+    run_write_maps(lib)
     if args.patterns_only:
         return
     for n, count in ((8, 1 << 26), (16, 1 << 24), (64, 1 << 26)):

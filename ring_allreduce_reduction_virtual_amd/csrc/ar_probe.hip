@@ -217,6 +217,67 @@ __global__ __launch_bounds__(kThreads) void k_copy_order(const Table t, uint64_t
     }
 }
 
+// Writes of n buffers, one 8 KiB tile per workgroup, in one of five
+// workgroup -> (buffer, tile) maps (T tiles per buffer; workgroups are dealt
+// to the 8 XCDs in turn, so workgroup b runs on XCD b mod 8):
+//   0 grouped per XCD as the staged broadcast: b = x + 8m -> tile
+//     8 floor(m / n) + x, buffer m mod n (a tile's n workgroups on XCD x);
+//   1 tile-major: buffer b mod n, tile floor(b / n);
+//   2 buffer-major: buffer floor(b / T), tile b mod T;
+//   3 one contiguous range per XCD of the n*T (buffer, tile) units taken
+//     buffer-major: XCD x writes units [x nT/8, (x+1) nT/8) in order;
+//   4 the same with the units taken tile-major (each XCD a contiguous range
+//     of tiles, every buffer);
+//   5, 6, 7 each XCD a contiguous eighth of the tiles (T a multiple of 8K),
+//     walked in sub-ranges of K = 16, 64, 256 tiles, each sub-range buffer by
+//     buffer: runs of K tiles per buffer, and a sub-range's source tiles
+//     (K x 8 KiB) reread from that XCD's L2 for every buffer after the first.
+// SRC: each workgroup first loads its tile from src[0] (cache-allocating
+// loads), as a broadcast does, else stores a constant.  Grid: n*T for maps 1
+// and 2, 8 ceil(T/8) n for map 0, 8 ceil(nT/8) for maps 3 and 4; workgroups
+// beyond the units write nothing; maps 5-7 use n*T workgroups.
+template <bool SRC>
+__global__ __launch_bounds__(kThreads) void k_wmap(const Table t, uint64_t tiles, int map) {
+    const uint64_t n = static_cast<uint64_t>(t.n), b = blockIdx.x;
+    uint64_t buf, tile;
+    if (map == 1) {
+        buf = b % n;
+        tile = b / n;
+    } else if (map == 2) {
+        buf = b / tiles;
+        tile = b % tiles;
+    } else if (map == 0) {
+        const uint64_t x = b & 7u, m = b >> 3;
+        tile = 8 * (m / n) + x;
+        buf = m % n;
+    } else if (map <= 4) {
+        const uint64_t units = n * tiles, x = b & 7u, m = b >> 3;
+        const uint64_t u = units * x / 8 + m;
+        if (u >= units * (x + 1) / 8) return;
+        buf = map == 3 ? u / tiles : u % n;
+        tile = map == 3 ? u % tiles : u / n;
+    } else {
+        const uint64_t k = map == 5 ? 16 : (map == 6 ? 64 : 256);
+        const uint64_t per = tiles / 8, x = b & 7u, m = b >> 3;
+        const uint64_t j = m / (n * k), r = m % (n * k);
+        buf = r / k;
+        tile = x * per + j * k + r % k;
+        if (j * k + r % k >= per) return;
+    }
+    if (buf >= n || tile >= tiles) return;
+    const uint64_t v0 = tile * kTile + threadIdx.x;
+    u32x4 a, c;
+    if constexpr (SRC) {
+        a = t.src[0][v0];
+        c = t.src[0][v0 + kThreads];
+    } else {
+        a = u32x4{static_cast<uint32_t>(v0), 1u, 2u, 3u};
+        c = a;
+    }
+    st(t.dst[buf] + v0, a);
+    st(t.dst[buf] + v0 + kThreads, c);
+}
+
 }  // namespace
 
 // extern "C" int arprobe_copy_order(int order, int nt, const void* const* src,
@@ -331,5 +392,32 @@ extern "C" int arprobe_stream(int kind, const void* const* src, void* const* dst
         case 2: hipLaunchKernelGGL(k_copy, grid, block, 0, s, t); break;
         default: hipLaunchKernelGGL(k_mix, grid, block, 0, s, t); break;
     }
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// extern "C" int arprobe_wmap(int map, const void* src, void* const* dst,
+//     int n, uint64_t nvec, hipStream_t s)
+//   k_wmap over the n (<= 8) destinations dst of nvec vectors (a multiple of
+//   512), in map 0-7; src (nvec vectors) loaded by each workgroup first, or
+//   nullptr for writes alone.  Returns 0, 1 (bad arguments) or 2.
+extern "C" int arprobe_wmap(int map, const void* src, void* const* dst, int n, uint64_t nvec, hipStream_t s) {
+    if (n < 1 || n > 8 || nvec == 0 || nvec % kTile != 0 || dst == nullptr || map < 0 || map > 7) return 1;
+    if (src != nullptr && reinterpret_cast<uintptr_t>(src) % 16 != 0) return 1;
+    const uint64_t tiles = nvec / kTile;
+    const uint64_t un = static_cast<uint64_t>(n);
+    if (map >= 5 && tiles % (8 * (map == 5 ? 16u : (map == 6 ? 64u : 256u))) != 0) return 1;
+    const uint64_t blocks = map == 0 ? 8 * ((tiles + 7) / 8) * un
+                            : (map <= 2 || map >= 5 ? un * tiles : 8 * ((un * tiles + 7) / 8));
+    if (blocks > 0x7fffffffull) return 1;
+    Table t{};
+    t.n = n;
+    t.src[0] = static_cast<const u32x4*>(src);
+    for (int r = 0; r < n; ++r) {
+        if (dst[r] == nullptr || reinterpret_cast<uintptr_t>(dst[r]) % 16 != 0) return 1;
+        t.dst[r] = static_cast<u32x4*>(dst[r]);
+    }
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    if (src != nullptr) hipLaunchKernelGGL((k_wmap<true>), grid, block, 0, s, t, tiles, map);
+    else hipLaunchKernelGGL((k_wmap<false>), grid, block, 0, s, t, tiles, map);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
