@@ -227,34 +227,54 @@ __global__ __launch_bounds__(kThreads) void k_fused_dbt(const KernelArgs a) {
 }
 
 // The two trees' bracketings for a small message: P = kThreads / N positions
-// per block staged through LDS (see small_stage), each folded by one thread.
-// A position's half, and with it the rank at each tree position, is the
-// thread's own; the order of the fold depends on positions only, so the
-// machine's control flow is the same for every thread.
-template <int DT, int OP, int D>
+// per block staged through LDS (see small_stage), then evaluated level by
+// level: thread (p - 1) P + j holds tree position p of column j, and at
+// level h = 1 .. H = floor(log2 N) every position of height h combines
+// ((left child (op) own value) (op) right child) from the values of the
+// levels below, kept in LDS, with a barrier between levels.  Those are the
+// in-order machine's operations on the same operands, so the bits are the
+// same, in H dependent steps instead of N.  A column's half, and with it the
+// rank at each position, follows from its element index.
+template <int DT, int OP>
 __global__ __launch_bounds__(kThreads) void k_small_dbt(const KernelArgs a) {
     constexpr int ESZ = elem_size<DT>();
     using F = Fold<DT, OP, 1>;
+    using A = typename F::A;
     __shared__ uint32_t vals[kThreads];
+    __shared__ A acc[kThreads];
     __shared__ uint32_t res[kThreads];
     const int n = a.nranks;
     const int P = kThreads / n;
     const int t = static_cast<int>(threadIdx.x);
-    const bool live[kUnroll] = {true};
+    const uint32_t p = static_cast<uint32_t>(t / P) + 1u;       // this thread's tree position
+    const int col = t - (t / P) * P;                             // its column
+    const bool node = p <= static_cast<uint32_t>(n);
+    const int hp = node ? __builtin_ctz(p) : -1;
+    int levels = 0;
+    while ((2u << levels) <= static_cast<uint32_t>(n)) ++levels;  // floor(log2 N): the root's height
+    const uint32_t root = 1u << levels;
     for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * P; i0 < a.count;
          i0 += static_cast<uint64_t>(gridDim.x) * P) {
         small_stage<ESZ>(a, vals, P, i0);
         __syncthreads();
-        if (t < P && i0 + t < a.count) {
-            const int c = (i0 + t) >= a.count_q ? 1 : 0;     // half 1 starts at count / 2
-            InOrder<DT, OP, 1, D> m;
-            for (int k = 1; k <= n; ++k) {
-                typename F::A x[kUnroll];
-                x[0] = F::first(vals[dbt_rank(static_cast<uint32_t>(k), c, n) * P + t]);
-                m.feed(static_cast<uint32_t>(k), static_cast<uint32_t>(n), x, live);
-            }
-            res[t] = F::done(m.cur[0], n);
+        const bool active = node && i0 + col < a.count;
+        A own{};
+        if (active) {
+            const int c = (i0 + col) >= a.count_q ? 1 : 0;      // half 1 starts at count / 2
+            own = F::first(vals[dbt_rank(p, c, n) * P + col]);
+            if (hp == 0) acc[t] = own;                           // a leaf's value is its own
         }
+        __syncthreads();
+        for (int h = 1; h <= levels; ++h) {
+            if (active && hp == h) {
+                A v = F::add_acc(acc[(p - (1u << (h - 1)) - 1u) * P + col], own);
+                const uint32_t rp = dbt_right(p, h, static_cast<uint32_t>(n));
+                if (rp != 0u) v = F::add_acc(v, acc[(rp - 1u) * P + col]);
+                acc[t] = v;
+            }
+            __syncthreads();
+        }
+        if (t < P && i0 + t < a.count) res[t] = F::done(acc[(root - 1u) * P + t], n);
         __syncthreads();
         small_store<ESZ>(a, res, P, i0);
         __syncthreads();
@@ -431,11 +451,7 @@ hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
             break;
         case Kind::kSmallDbt:
             if constexpr (VEC == 1) {
-                switch (l.depth) {
-                    case 4: hipLaunchKernelGGL((k_small_dbt<DT, OP, 4>), grid, block, 0, s, a); break;
-                    case 6: hipLaunchKernelGGL((k_small_dbt<DT, OP, 6>), grid, block, 0, s, a); break;
-                    default: return hipErrorInvalidValue;
-                }
+                hipLaunchKernelGGL((k_small_dbt<DT, OP>), grid, block, 0, s, a);
             } else {
                 return hipErrorInvalidValue;
             }

@@ -175,31 +175,38 @@ __global__ __launch_bounds__(kThreads) void k_fused_tree(const KernelArgs a) {
 }
 
 // The binomial-tree bracketing for a small message: P = kThreads / N
-// positions per block staged through LDS (see small_stage), each folded by
-// one thread over the leaves in the send table's order.
-template <int DT, int OP, int D>
+// positions per block staged through LDS (see small_stage), then reduced
+// stage by stage: thread r P + j holds leaf r (the send table's r-th rank) of
+// column j, and at stage k every r with r mod 2^(k+1) = 0 adds the partial of
+// r + 2^k when that leaf exists, (own (op) received), a barrier between
+// stages.  That is the binary counter's bracketing with the same operand
+// order, so the bits are the same, in ceil(log2 N) dependent steps instead
+// of N.
+template <int DT, int OP>
 __global__ __launch_bounds__(kThreads) void k_small_tree(const KernelArgs a) {
     constexpr int ESZ = elem_size<DT>();
     using F = Fold<DT, OP, 1>;
+    using A = typename F::A;
     __shared__ uint32_t vals[kThreads];
+    __shared__ A acc[kThreads];
     __shared__ uint32_t res[kThreads];
     const int n = a.nranks;
     const int P = kThreads / n;
     const int t = static_cast<int>(threadIdx.x);
+    const int r = t / P;                                         // this thread's leaf
+    const int col = t - r * P;                                   // its column
     for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * P; i0 < a.count;
          i0 += static_cast<uint64_t>(gridDim.x) * P) {
         small_stage<ESZ>(a, vals, P, i0);
         __syncthreads();
-        if (t < P && i0 + t < a.count) {
-            typename F::A slot[D][kUnroll];
-            const bool live[kUnroll] = {true};
-            for (int k = 0; k < n; ++k) {
-                typename F::A x[kUnroll];
-                x[0] = F::first(vals[k * P + t]);
-                tree_push<DT, OP, 1, D>(slot, static_cast<uint32_t>(k), x, live);
-            }
-            res[t] = F::done(tree_result<DT, OP, 1, D>(slot, static_cast<uint32_t>(n), 0), n);
+        const bool active = r < n && i0 + col < a.count;
+        if (active) acc[t] = F::first(vals[t]);
+        __syncthreads();
+        for (int d = 1; d < n; d <<= 1) {
+            if (active && (r & (2 * d - 1)) == 0 && r + d < n) acc[t] = F::add_acc(acc[t], acc[t + d * P]);
+            __syncthreads();
         }
+        if (t < P && i0 + t < a.count) res[t] = F::done(acc[t], n);
         __syncthreads();
         small_store<ESZ>(a, res, P, i0);
         __syncthreads();
@@ -414,12 +421,7 @@ hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
             break;
         case Kind::kSmallTree:
             if constexpr (VEC == 1) {
-                switch (l.depth) {
-                    case 4: hipLaunchKernelGGL((k_small_tree<DT, OP, 4>), grid, block, 0, s, a); break;
-                    case 6: hipLaunchKernelGGL((k_small_tree<DT, OP, 6>), grid, block, 0, s, a); break;
-                    case 8: hipLaunchKernelGGL((k_small_tree<DT, OP, 8>), grid, block, 0, s, a); break;
-                    default: return hipErrorInvalidValue;
-                }
+                hipLaunchKernelGGL((k_small_tree<DT, OP>), grid, block, 0, s, a);
             } else {
                 return hipErrorInvalidValue;
             }
