@@ -319,10 +319,34 @@ uint64_t small_chunk_max() {
     return v;
 }
 
+// Bound on chunk * N^2 for the small-message kernels; AR_SMALL_WORK_MAX
+// overrides it (read once per process).
+uint64_t small_work_max() {
+    static const uint64_t v = [] {
+        const char* e = std::getenv("AR_SMALL_WORK_MAX");
+        if (e != nullptr && e[0] != '\0') return static_cast<uint64_t>(std::strtoull(e, nullptr, 10));
+        return static_cast<uint64_t>(AR_SMALL_WORK_MAX);
+    }();
+    return v;
+}
+
 bool small_message(const Common& k) {
     const uint64_t n = static_cast<uint64_t>(k.n);
     const uint64_t chunk = k.count / n;
-    return k.n > 1 && chunk < small_chunk_max() && chunk * n * n <= AR_SMALL_WORK_MAX;
+    return k.n > 1 && chunk < small_chunk_max() && chunk * n * n <= small_work_max();
+}
+
+// The tree orders' bound (binomial tree, halving/doubling, double binary
+// tree): N * count elements at most AR_SMALL_TREE_WORK_MAX, which the
+// AR_SMALL_TREE_MAX environment variable overrides (read once per process);
+// AR_SMALL_CHUNK_MAX=0 turns every small-message kernel off.
+bool small_tree_message(const Common& k) {
+    static const uint64_t bound = [] {
+        const char* e = std::getenv("AR_SMALL_TREE_MAX");
+        if (e != nullptr && e[0] != '\0') return static_cast<uint64_t>(std::strtoull(e, nullptr, 10));
+        return static_cast<uint64_t>(AR_SMALL_TREE_WORK_MAX);
+    }();
+    return k.n > 1 && small_chunk_max() != 0 && k.count * static_cast<uint64_t>(k.n) <= bound;
 }
 
 // One block per P = threads / N positions; the kernels stride over the rest.
@@ -612,7 +636,7 @@ ar_result_t tree_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         if (algo == AR_ALGO_HALVING_DOUBLING)
             for (int r = 0; r < k.n; ++r) a.send[r] = static_cast<const char*>(k.send[bit_reverse(r, L)]);
         l.depth = k.n < 16 ? 4 : (k.n < 64 ? 6 : 8);
-        if (small_message(k)) {
+        if (small_tree_message(k)) {
             plan_small(a, l, k);
             return sink.emit(l, Kind::kSmallTree, a, k);
         }
@@ -672,7 +696,7 @@ ar_result_t dbt_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_b
     a.count_r = static_cast<uint32_t>(k.count % 2);
     if (algo == AR_ALGO_DOUBLE_BINARY_TREE) {
         l.depth = k.n < 16 ? 4 : 6;   // the deepest stack the trees need: 3 below 16 ranks, 6 up to 128
-        if (small_message(k)) {
+        if (small_tree_message(k)) {
             plan_small(a, l, k);
             return sink.emit(l, Kind::kSmallDbt, a, k);
         }
