@@ -336,6 +336,14 @@ bool small_message(const Common& k) {
     return k.n > 1 && chunk < small_chunk_max() && chunk * n * n <= small_work_max();
 }
 
+// The tree orders' small-message kernels reduce level by level across
+// threads, so their cost does not grow with N the way the ring's left fold
+// does: they serve every message whose ranks together hold at most this many
+// elements (N * count; measured crossover on MI355X, 4 MiB of float32).
+#ifndef AR_SMALL_TREE_WORK_MAX
+#define AR_SMALL_TREE_WORK_MAX (1ull << 20)
+#endif
+
 // The tree orders' bound (binomial tree, halving/doubling, double binary
 // tree): N * count elements at most AR_SMALL_TREE_WORK_MAX, which the
 // AR_SMALL_TREE_MAX environment variable overrides (read once per process);

@@ -108,13 +108,6 @@ constexpr int kUnroll = AR_TILE_UNROLL;
 #ifndef AR_SMALL_CHUNK_MAX_DEFAULT
 #define AR_SMALL_CHUNK_MAX_DEFAULT 8192
 #endif
-// The tree orders' small-message kernels reduce level by level across
-// threads, so their cost does not grow with N the way the ring's left fold
-// does: they serve every message whose ranks together hold at most this many
-// elements (N * count; measured crossover on MI355X, 4 MiB of float32).
-#ifndef AR_SMALL_TREE_WORK_MAX
-#define AR_SMALL_TREE_WORK_MAX (1ull << 20)
-#endif
 #ifndef AR_SMALL_WORK_MAX
 #define AR_SMALL_WORK_MAX (1ull << 19)
 #endif
