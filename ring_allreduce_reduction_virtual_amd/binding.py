@@ -12,7 +12,8 @@ reduce-scatter the receive tensors hold one chunk each, for all-gather the
 send tensors do.  ``algo`` names an ``ar_algo_t`` in lower case ("fused",
 "ring", "phases", "auto", "ring_persistent", "ring_pipelined", "staged", and the tree
 orders "tree", "tree_steps", "recursive_doubling", "halving_doubling",
-"halving_doubling_steps"); ``op`` one of "sum", "prod", "min", "max", "avg".  The element type follows
+"halving_doubling_steps", "double_binary_tree", "double_binary_tree_steps");
+``op`` one of "sum", "prod", "min", "max", "avg".  The element type follows
 the tensors (float32, bfloat16, float16, int32); ``dtype="bf16acc32"`` with
 bfloat16 tensors keeps the partial sums in float32.
 

@@ -547,11 +547,11 @@ public:
         if (debug_enabled()) {
             std::fprintf(stderr,
                          "[ar] %s dtype=%s op=%d n=%d count=%llu step=%d shift=%d mode=%d last=%d vec=%d ofs=%d "
-                         "align=2^%d tiles=[%u,%u) tiles/chunk=%u blocks=%u actors=%u cached=%d%s\n",
+                         "align=2^%d tiles=[%u,%u) tiles/chunk=%u blocks=%u actors=%u cached=%d slabs=%d%s\n",
                          kind_name(kind), dtype_name(k.dtype), static_cast<int>(k.op), k.n,
                          static_cast<unsigned long long>(k.count), a.step, a.shift, a.mode, a.last, l.vec ? 1 : 0, a.ofs,
                          a.align_shift, a.tile_first, a.tile_end, a.tiles_per_chunk, l.blocks, l.actors,
-                         l.cached ? 1 : 0, steps_ != nullptr ? " (planned)" : "");
+                         l.cached ? 1 : 0, a.xcd_slabs, steps_ != nullptr ? " (planned)" : "");
         }
         if (steps_ != nullptr) {
             steps_->push_back(Step{l, a, l.blocks});
@@ -921,7 +921,10 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
     fill_tables(a, k);
     const Residue residue = common_residue(ptrs);
     if ((rc = plan(a, l, k, residue)) != AR_SUCCESS) return rc;
-    if (algo == AR_ALGO_FUSED || k.n == 1) return sink.emit(l, Kind::kFusedReduceScatter, a, k);
+    if (algo == AR_ALGO_FUSED || k.n == 1) {
+        tile_order(a, l, k);
+        return sink.emit(l, Kind::kFusedReduceScatter, a, k);
+    }
     if ((rc = use_workspace(a, k, AR_COLL_REDUCE_SCATTER, algo, ws, ws_bytes, nullptr)) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_RING_PIPELINED) {
         a.mode = 0;
