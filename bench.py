@@ -152,6 +152,30 @@ def median_call_ms(fn, steps: int, warmup: int, stream):
     return times[len(times) // 2], times[0]
 
 
+def flushed_median_ms(fn, steps: int, stream, flush, mode: str = "write"):
+    """Median and minimum milliseconds of single calls, each preceded (outside its
+    events) by a pass over the whole `flush` tensor, 1 GiB against the 256 MB
+    last-level cache, so that every call finds its inputs in HBM.  "write"
+    fills it (the cache is then full of dirty lines, which the call's own
+    traffic pushes out to HBM, as after a kernel that wrote a lot); "read"
+    reduces over it (the cache is left holding clean lines)."""
+    import torch
+
+    fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        if mode == "write":
+            flush.fill_(i & 0xFF)
+        else:
+            flush.view(torch.int32).max()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    times = sorted(a.elapsed_time(b) for a, b in evs)
+    return times[len(times) // 2], times[0]
+
+
 def graph_ms_per_call(fn, calls: int, stream, replays: int = 5):
     """Milliseconds per call when `calls` calls are captured in one HIP graph and replayed."""
     import torch
@@ -245,7 +269,11 @@ def run_configs(args):
     esz = {"f32": 4, "bf16": 2, "i32": 4}
     # the headline first, in the state the default line measures it in, and again after the
     # heaviest workload (c5 moves 32 GiB per call) to show what that leaves behind
-    for name in ("headline", "c1", "c2", "c3", "c4", "c5", "headline"):
+    names = ("headline", "c1", "c2", "c3", "c4", "c5", "headline")
+    if args.workloads:
+        names = tuple(args.workloads.split(","))
+    flush = None
+    for name in names:
         w = WORKLOADS[name]
         n, count, dt = w.nranks, w.count, w.dtype
         s_bytes = count * esz[dt]
@@ -262,6 +290,15 @@ def run_configs(args):
                 algo_bytes = algorithmic_bytes("allreduce", n, s_bytes)
                 latency = {}
                 if s_bytes * n <= (64 << 20):
+                    # buffers that fit in the last-level cache: also timed with it flushed before each call
+                    if flush is None:
+                        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+                    for mode, key in (("write", "flushed"), ("read", "evicted")):
+                        fmed, fmn = flushed_median_ms(fn, steps, stream, flush, mode)
+                        latency[f"{key}_median_us"] = round(fmed * 1e3, 2)
+                        latency[f"{key}_min_us"] = round(fmn * 1e3, 2)
+                        latency[f"{key}_hbm_frac"] = round(algorithmic_bytes("allreduce", n, s_bytes) / (fmed / 1e3)
+                                                           / 1e9 / HBM_PEAK_GBPS, 4)
                     # small messages: the same call as a persistent plan, and replayed from a HIP graph
                     plan = ar.ar_allreduce_init(sends, recvs, op=op, algo=algo)
                     pmed, _ = median_call_ms(plan.start, steps, 3, stream)
@@ -1080,6 +1117,8 @@ def _main():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the headline line: time every workload (c1..c5) with both algorithms, "
                          "one JSON line each")
+    ap.add_argument("--workloads", default="",
+                    help="with --configs: comma-separated workload names (default: all, the headline twice)")
     ap.add_argument("--variants", action="store_true",
                     help="instead of the headline line: time the precision and operator variants "
                          "(float32 partials for bf16, avg, binary16) at full size, one JSON line each")
