@@ -1,6 +1,7 @@
 // Device-side building blocks shared by the kernel sources (ar_kernels.hip:
 // the ring schedules; ar_tree_kernels.hip: the tree-shaped orders;
-// ar_persistent_kernels.hip: the ring in one launch): element arithmetic,
+// ar_dbt_kernels.hip: the double binary tree; ar_persistent_kernels.hip: the
+// ring in one launch): element arithmetic,
 // 16-byte vector access, the fold over ranks, the chunk geometry with its
 // tile loop, the ring's step bodies, and the LDS staging of small messages.
 // Everything here is inline device code in an unnamed namespace, so each
@@ -624,12 +625,12 @@ __device__ __forceinline__ bool shard_aligned(const void* shard, uint64_t s, int
 // default), or, when the launch sets xcd_slabs, the launch's tiles cut into
 // eight contiguous slabs, slab x walked by the blocks the dispatcher deals to
 // XCD x (blocks x, x + 8, x + 16, ...).  Each XCD then touches one eighth of
-// the address range that all the blocks in flight touch, so its address
-// translation cache holds one eighth of the pages: that matters once many
-// ranks' buffers are streamed at once (measured on MI355X at 32 and more
-// ranks); with few ranks the plain order is as fast.  The host gives such a
-// launch a grid of a multiple of eight blocks; blocks past the last whole
-// group of eight walk nothing.
+// the address range that all the blocks in flight touch, and with it one
+// eighth of the pages its address translation caches must hold.  Measured on
+// MI355X it pays from 64 ranks (up to 8 % at 64 x 16 MiB); at 32 ranks it
+// gains nothing and at 8 ranks the plain order is faster.  The host gives
+// such a launch a grid of a multiple of eight blocks; blocks past the last
+// whole group of eight walk nothing.
 struct TileWalk {
     uint32_t first, end, step;
 };
@@ -810,8 +811,9 @@ __device__ __forceinline__ void ring_copy_tiles(const KernelArgs& a, int step, i
 // per batch of ranks.  The small-message kernels instead give a block
 // P = kThreads / N consecutive positions [i0, i0 + P): thread t = r*P + j
 // loads rank r's element i0 + j (one load per thread, all in flight at once)
-// into LDS, P threads fold their position from LDS, and every thread stores
-// one result to one rank.  Per-lane rank pointers are read from the kernel
+// into LDS, the positions are reduced from LDS (the ring's left fold by one
+// thread per position; the tree orders level by level across threads), and
+// every thread stores one result to one rank.  Per-lane rank pointers are read from the kernel
 // argument segment through its address, so the table is never copied.
 __device__ __forceinline__ const KernelArgs* kernarg_table() {
 #if defined(__HIP_DEVICE_COMPILE__)

@@ -1,5 +1,7 @@
 // Internal interface between the host entry points (ar_api.hip) and the
-// kernels (ar_kernels.hip).  Not installed; include/ar.h is the public ABI.
+// kernel sources (ar_kernels.hip, which dispatches to ar_tree_kernels.hip,
+// ar_dbt_kernels.hip and ar_persistent_kernels.hip).  Not installed;
+// include/ar.h is the public ABI.
 #pragma once
 
 #include <cstdint>
@@ -87,8 +89,8 @@ struct Launch {
     bool vec;                  // 16-byte vector path (all streamed buffers share a residue)
     bool cached;               // kFusedAllReduce on the vector path: cache-allocating loads
     bool half;                 // kFusedAllGather, kStagedBroadcast: one unit row of a tile per block
-    int form;                  // kStagedBroadcast: 3 one destination per block, a tile's blocks grouped
-                               // on one XCD; 0 the tile forms above
+    int form;                  // kStagedBroadcast, kFusedAllGather: 3 one destination per block, a
+                               // tile's blocks grouped on one XCD; 0 the tile forms above
     bool cached_store;         // kFusedReduceScatter: cache-allocating stores of the shards (the
                                // phases' AllReduce, whose all-gather rereads them)
     unsigned blocks;
@@ -103,8 +105,10 @@ struct Launch {
 #endif
 constexpr int kUnroll = AR_TILE_UNROLL;
 
-// Bounds below which one-pass AllReduces take the small-message kernels:
-// chunk length in elements, and chunk * N^2 (measured crossovers on MI355X).
+// Bounds below which the ring-order one-pass AllReduce takes its
+// small-message kernel: chunk length in elements, and chunk * N^2 (measured
+// crossovers on MI355X).  The tree orders' small-message kernels have a bound
+// of their own, kept with the host's dispatch.
 #ifndef AR_SMALL_CHUNK_MAX_DEFAULT
 #define AR_SMALL_CHUNK_MAX_DEFAULT 8192
 #endif
@@ -131,16 +135,6 @@ constexpr int kUnroll = AR_TILE_UNROLL;
 // call, 32 MiB / 128 MiB segments: 8 ranks 740 / 736, 16 ranks 1,513 /
 // 1,519, 32 ranks 2,979 / 3,002, 64 ranks 5,944 / 6,028, 128 ranks 11,701 /
 // 11,728.
-// Rank count from which the launches that stream every rank's buffer at once
-// walk their tiles in one contiguous slab per XCD (tile_walk); 0 never.
-// Measured on MI355X, the same buffers in one process, plain / slabs, us:
-// 64 x 16 MiB float32 fused 427 / 395, staged 386 / 370, phases 378 / 364;
-// 128 x 64 MiB fused 3,351 / 3,285, staged 2,986 / 2,934; 64 x 256 MiB
-// phases 6,412 / 6,096, fused and staged within 1 %; 32 x 256 MiB within
-// 1.5 % (staged slower); 8 x 256 MiB fused 741 / 790 (slower).
-#ifndef AR_TILE_XCD_MIN_RANKS
-#define AR_TILE_XCD_MIN_RANKS 64
-#endif
 #ifndef AR_STAGE_READ_BYTES
 #define AR_STAGE_READ_BYTES (2048ull << 20)
 #endif
@@ -151,11 +145,26 @@ constexpr int kUnroll = AR_TILE_UNROLL;
 #define AR_STAGE_BYTES_MAX (128ull << 20)
 #endif
 
+// Rank count from which the launches that stream every rank's buffer at once
+// walk their tiles in one contiguous slab per XCD (tile_walk); 0 never.
+// Measured on MI355X, the same buffers in one process, plain / slabs, us:
+// 64 x 16 MiB float32 fused 427 / 395, staged 386 / 370, phases 378 / 364;
+// 128 x 64 MiB fused 3,351 / 3,285, staged 2,986 / 2,934; 64 x 256 MiB
+// phases 6,412 / 6,096, fused and staged within 1 %; 32 x 256 MiB within
+// 1.5 % (staged slower); 8 x 256 MiB fused 741 / 790 (slower).  The
+// standalone fused reduce-scatter: 64 x 16 MiB 187.7 / 180.7, 128 x 64 MiB
+// 1,395 / 1,380, 64 x (2^26+7) 2,910 / 2,909, 32 x 256 MiB 1,551 / 1,566.
+#ifndef AR_TILE_XCD_MIN_RANKS
+#define AR_TILE_XCD_MIN_RANKS 64
+#endif
+
 // The copy launches that write one value to many ranks (the fused all-gather
 // and the staged AllReduce's broadcast) give each block one of a tile's
 // kUnroll unit rows when the ranks' buffers hold between
 // AR_HALF_TILES_MIN_TOTAL and AR_HALF_TILES_MAX_TOTAL bytes in all (N * S);
-// outside that band whole tiles per block are faster.  Measured on MI355X,
+// outside that band whole tiles per block are faster.  This applies to the
+// tile forms only (AR_BCAST_FORM=0, AR_GATHER_FORM=0); by default both copies
+// give each block one destination rank, a tile's blocks grouped on one XCD.  Measured on MI355X,
 // float32, same box, staged AllReduce whole / half tiles in us: inside the
 // band 8 x 256 MiB 736 / 723, 16 x 256 MiB 1,509 / 1,461, 64 x 64 MiB
 // 1,559 / 1,527, 32 x 128 MiB 1,519 / 1,495; below it 8 x 4 MiB 19.1 / 21.3,
@@ -177,7 +186,8 @@ void set_error_detail(const char* text);
 hipError_t launch(const Launch& l, const KernelArgs& a, hipStream_t stream);
 
 // The kernels of the tree-shaped schedules (ar_tree_kernels.hip); `launch`
-// forwards the kFusedTree, kTreeReduceStep and kTreeCopyStep kinds here.
+// forwards the kFusedTree, kSmallTree, kTreeReduceStep and kTreeCopyStep
+// kinds here.
 hipError_t launch_tree(const Launch& l, const KernelArgs& a, hipStream_t stream);
 
 // The double binary tree (ar_dbt_kernels.hip); `launch` forwards the

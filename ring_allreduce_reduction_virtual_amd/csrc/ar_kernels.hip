@@ -12,7 +12,8 @@
 // the tiled kernels use no LDS and no MFMA: each thread moves 16-byte
 // vectors, `kUnroll` of them per rank per tile, issues a batch of up to
 // `kBatch` ranks' loads before it folds them in ring order, and writes
-// results with nontemporal stores.  Chunk edges that are not 16-byte aligned
+// outputs with nontemporal stores (results that the next launch rereads with
+// cache-allocating ones).  Chunk edges that are not 16-byte aligned
 // (uneven chunks start anywhere) are done one element at a time by the first
 // tile of the chunk.  Messages whose chunks are only a few elements long take
 // k_small_allreduce instead, which stages every rank's values of a few
@@ -98,8 +99,9 @@ __global__ __launch_bounds__(kThreads) void k_staged_reduce(const KernelArgs a) 
 // Staged AllReduce, broadcasting launch: rank 0's results for the same tiles
 // (so the same elements, chunk edges included) copied to ranks 1..N-1.  Each
 // block takes one of a tile's kUnroll units per thread, so a wave issues half
-// the stores of a whole tile; HBM mostly takes the writes faster that way
-// (the host picks this form or k_staged_broadcast_tiles by measured shape).
+// the stores of a whole tile; HBM mostly takes the writes faster that way.
+// With AR_BCAST_FORM=0 the host picks this form or k_staged_broadcast_tiles
+// by measured shape; by default it takes k_staged_broadcast_xcd.
 template <int DT, int VEC>
 __global__ __launch_bounds__(kThreads) void k_staged_broadcast(const KernelArgs a) {
     using U = Unit<DT, VEC, false>;   // cache-allocating loads: the results sit in the Infinity Cache
@@ -130,8 +132,9 @@ __global__ __launch_bounds__(kThreads) void k_staged_broadcast(const KernelArgs 
     }
 }
 
-// The same broadcast with whole tiles per block (kUnroll unit rows): faster
-// when all ranks' buffers hold less than 2 GiB or more than 8 GiB in all.
+// The same broadcast with whole tiles per block (kUnroll unit rows): of the
+// two tile forms, faster when all ranks' buffers hold less than 2 GiB or
+// more than 8 GiB in all.
 template <int DT, int VEC>
 __global__ __launch_bounds__(kThreads) void k_staged_broadcast_tiles(const KernelArgs a) {
     using U = Unit<DT, VEC, false>;   // cache-allocating loads: the results sit in the Infinity Cache
@@ -278,7 +281,8 @@ __global__ __launch_bounds__(kThreads) void k_gather_shards(const KernelArgs a) 
 
 // k_gather_shards with one of a tile's kUnroll unit rows per block (grid of
 // kUnroll blocks per tile): each wave issues half the stores, which HBM
-// mostly takes faster (the host picks the form by measured shape).
+// mostly takes faster.  With AR_GATHER_FORM=0 the host picks this form or
+// k_gather_shards by measured shape; by default it takes k_gather_shards_xcd.
 template <int DT, int VEC, bool ALL>
 __global__ __launch_bounds__(kThreads) void k_gather_shards_half(const KernelArgs a) {
     using U = Unit<DT, VEC, AR_NT_LOADS_COPY>;
