@@ -141,7 +141,9 @@ struct InOrder {
     }
 };
 
-// Stack depth the trees of up to N ranks need: 3 below 16 ranks, 6 up to 128.
+// Ranks whose loads are in flight together; fewer when float32 partials fill
+// the deepest stack (D = 6 slots, for 16 to 128 ranks), whose registers they
+// share.
 template <int DT, int D>
 constexpr int dbt_batch() {
     return (D >= 6 && acc_f32<DT>()) ? 4 : 8;
