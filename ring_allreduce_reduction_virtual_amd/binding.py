@@ -34,9 +34,19 @@ from . import _lib
 _TORCH_DTYPES = {torch.float32: "f32", torch.bfloat16: "bf16", torch.int32: "i32", torch.float16: "f16"}
 
 
-def _stream_handle(stream):
+# The current stream's raw handle without building a torch.cuda.Stream object
+# (measured on MI355X: 0.07 us against 2.7 us per call, a large share of a
+# small call's host time); the public route where torch lacks the accessor.
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_handle(stream, device_index):
+    """The hipStream_t to enqueue on: `stream` when given, else the current
+    stream of device `device_index` (the device the buffers live on)."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        if _raw_current_stream is not None:
+            return _raw_current_stream(device_index)
+        return torch.cuda.current_stream(device_index).cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
@@ -182,7 +192,7 @@ def ar_allreduce(sendbufs, recvbufs=None, op: str = "sum", stream=None, dtype=No
     count = _check_counts("allreduce", sendbufs, recvbufs)
     with _on_device(dev):
         rc = _lib.lib().ar_allreduce(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
-                                     _stream_handle(stream))
+                                     _stream_handle(stream, dev.index))
     _lib.check("ar_allreduce", rc)
     return recvbufs
 
@@ -203,7 +213,7 @@ def ar_allreduce_ex(sendbufs, recvbufs=None, op: str = "sum", algo: str = "fused
         workspace = _workspace("allreduce", algo, count, dtype, len(sendbufs), workspace, dev, stream)
         wp, wb = _ws(workspace)
         rc = _lib.lib().ar_allreduce_ex(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
-                                        _lib.ALGOS[algo], wp, wb, _stream_handle(stream))
+                                        _lib.ALGOS[algo], wp, wb, _stream_handle(stream, dev.index))
     _lib.check("ar_allreduce_ex", rc)
     return recvbufs
 
@@ -214,7 +224,7 @@ def ar_reduce_scatter(sendbufs, recvbufs, op: str = "sum", stream=None, dtype=No
     count = _check_counts("reduce_scatter", sendbufs, recvbufs)
     with _on_device(dev):
         rc = _lib.lib().ar_reduce_scatter(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
-                                          _stream_handle(stream))
+                                          _stream_handle(stream, dev.index))
     _lib.check("ar_reduce_scatter", rc)
     return recvbufs
 
@@ -234,7 +244,7 @@ def ar_reduce_scatter_ex(sendbufs, recvbufs, op: str = "sum", algo: str = "fused
         workspace = _workspace("reduce_scatter", algo, count, dtype, n, workspace, dev, stream)
         wp, wb = _ws(workspace)
         rc = _lib.lib().ar_reduce_scatter_ex(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], n,
-                                             _lib.ALGOS[algo], wp, wb, _stream_handle(stream))
+                                             _lib.ALGOS[algo], wp, wb, _stream_handle(stream, dev.index))
     _lib.check("ar_reduce_scatter_ex", rc)
     return recvbufs
 
@@ -246,7 +256,7 @@ def ar_reduce_scatter_noalloc(sendbufs, recvbufs, op: str = "sum", algo: str = "
     count = _check_counts("reduce_scatter", sendbufs, recvbufs)
     with _on_device(dev):
         rc = _lib.lib().ar_reduce_scatter_noalloc(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
-                                                  _lib.ALGOS[algo], _stream_handle(stream))
+                                                  _lib.ALGOS[algo], _stream_handle(stream, dev.index))
     _lib.check("ar_reduce_scatter_noalloc", rc)
     return recvbufs
 
@@ -256,7 +266,8 @@ def ar_all_gather(sendbufs, recvbufs, stream=None):
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
     count = _check_counts("all_gather", sendbufs, recvbufs)
     with _on_device(dev):
-        rc = _lib.lib().ar_all_gather(sp, rp, count, _lib.DTYPES[dtype], len(sendbufs), _stream_handle(stream))
+        rc = _lib.lib().ar_all_gather(sp, rp, count, _lib.DTYPES[dtype], len(sendbufs),
+                                      _stream_handle(stream, dev.index))
     _lib.check("ar_all_gather", rc)
     return recvbufs
 
@@ -268,7 +279,7 @@ def ar_all_gather_ex(sendbufs, recvbufs, algo: str = "fused", workspace=None, st
     wp, wb = _ws(workspace)
     with _on_device(dev):
         rc = _lib.lib().ar_all_gather_ex(sp, rp, count, _lib.DTYPES[dtype], len(sendbufs), _lib.ALGOS[algo],
-                                         wp, wb, _stream_handle(stream))
+                                         wp, wb, _stream_handle(stream, dev.index))
     _lib.check("ar_all_gather_ex", rc)
     return recvbufs
 
@@ -288,6 +299,7 @@ class Plan:
     def __init__(self, handle, device, keep):
         self._handle = handle
         self.device = device
+        self._index = device.index if device.index is not None else torch.cuda.current_device()
         self._keep = keep
 
     @property
@@ -303,7 +315,7 @@ class Plan:
     def start(self, stream=None):
         if self._handle is None:
             raise ValueError("plan is closed")
-        _lib.check("ar_plan_start", _lib.lib().ar_plan_start(self._handle, _stream_handle(stream)))
+        _lib.check("ar_plan_start", _lib.lib().ar_plan_start(self._handle, _stream_handle(stream, self._index)))
 
     def limit_blocks(self, max_blocks: int):
         """Cap the workgroups of every launch (0: back to the planned grids)."""
