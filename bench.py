@@ -1013,14 +1013,45 @@ def run_rank_scaling(args):
     same bytes per rank, more interleaved streams.  Median of --steps single
     calls after --warmup, one JSON line per shape.  Run under rocprofv3 with
     address-translation and memory-side counters, it is the command of the
-    fused kernel's rank-count counter summary."""
+    fused kernel's rank-count counter summary.  --shapes replaces the shapes
+    (N x count pairs, e.g. 8x67108864,8x268435456: the same 8 ranks with more
+    bytes each).  --alloc-factors F1,F2,... runs every shape on views of the
+    first `count` elements of allocations F times larger, the factors
+    alternating in three rounds in one process (same bytes touched, different
+    allocations)."""
     import torch
 
     import ring_allreduce_reduction_virtual_amd as ar
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    for n, count in RANK_SCALING:
+    shapes = RANK_SCALING
+    if args.shapes:
+        shapes = tuple(tuple(int(v) for v in s.split("x")) for s in args.shapes.split(","))
+    if args.alloc_factors:
+        factors = [int(v) for v in args.alloc_factors.split(",")]
+        for n, count in shapes:
+            cases = {}
+            for f in factors:
+                base_s = [torch.randn(count * f, device=dev) for _ in range(n)]
+                base_r = [torch.empty(count * f, device=dev) for _ in range(n)]
+                cases[f] = ([t[:count] for t in base_s], [t[:count] for t in base_r])
+            times = {(f, algo): [] for f in factors for algo in ("fused", "staged")}
+            for _ in range(3):
+                for f in factors:
+                    sends, recvs = cases[f]
+                    for algo in ("fused", "staged"):
+                        med, _ = median_call_ms(lambda: ar.ar_allreduce_ex(sends, recvs, algo=algo),
+                                                max(args.steps, 1), args.warmup, stream)
+                        times[(f, algo)].append(round(med * 1e3, 1))
+            for f in factors:
+                print(json.dumps({"rank_scaling": f"{n} x {count} f32 sum", "nranks": n, "count": count,
+                                  "alloc_factor": f, "fused_us": times[(f, "fused")],
+                                  "staged_us": times[(f, "staged")]}), flush=True)
+            del cases
+            torch.cuda.empty_cache()
+        return
+    for n, count in shapes:
         sends = [torch.randn(count, device=dev) for _ in range(n)]
         recvs = [torch.empty(count, device=dev) for _ in range(n)]
         row = {"rank_scaling": f"{n} x {count} f32 sum", "nranks": n, "count": count}
@@ -1119,6 +1150,11 @@ def _main():
                          "one JSON line each")
     ap.add_argument("--workloads", default="",
                     help="with --configs: comma-separated workload names (default: all, the headline twice)")
+    ap.add_argument("--shapes", default="",
+                    help="with --rank-scaling: comma-separated NxCOUNT shapes instead of the default ones")
+    ap.add_argument("--alloc-factors", default="",
+                    help="with --rank-scaling: run each shape on views into allocations this many times larger "
+                         "(comma-separated factors, alternating in one process)")
     ap.add_argument("--variants", action="store_true",
                     help="instead of the headline line: time the precision and operator variants "
                          "(float32 partials for bf16, avg, binary16) at full size, one JSON line each")
