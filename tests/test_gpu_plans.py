@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import dbt
 from oracle.ring import chunk, same_bits
 
 from gpu_util import from_dev, require_gpu, tdtype, to_dev
@@ -130,7 +131,8 @@ def test_graph_capture_replays(algo, monkeypatch):
 
 
 @pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined", "staged", "tree", "tree_steps",
-                                  "halving_doubling_steps"])
+                                  "recursive_doubling", "halving_doubling_steps", "double_binary_tree",
+                                  "double_binary_tree_steps"])
 def test_block_limits_keep_the_bits(algo, monkeypatch):
     """A plan capped at 1, 3, 64 blocks (the kernels stride over their tiles), then
     uncapped again, gives the oracle's bits every time.  The staged form runs with
@@ -148,8 +150,10 @@ def test_block_limits_keep_the_bits(algo, monkeypatch):
     recvs = [torch.empty(length, device="cuda:0") for _ in range(n)]
     if algo in ("fused", "phases", "ring", "ring_pipelined", "staged"):
         want, _ = oracle.ring_allreduce(xs)
+    elif algo.startswith("double_binary_tree"):
+        want, _ = dbt.double_binary_tree_allreduce(xs, "sum", "f32")
     else:
-        want, _ = order_allreduce({"tree": "tree", "tree_steps": "tree",
+        want, _ = order_allreduce({"tree": "tree", "tree_steps": "tree", "recursive_doubling": "recursive_doubling",
                                    "halving_doubling_steps": "halving_doubling"}[algo], xs)
     plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
     if algo == "staged":
