@@ -92,7 +92,25 @@ def test_phase_plans(algo):
     ar.ar_plan_free(ag)
 
 
-@pytest.mark.parametrize("algo", ["fused", "phases", "ring", "ring_pipelined", "staged"])
+RING_ORDER = ("fused", "phases", "ring", "ring_pipelined", "staged")
+TREE_ORDER = {"tree": "tree", "tree_steps": "tree", "recursive_doubling": "recursive_doubling",
+              "halving_doubling": "halving_doubling", "halving_doubling_steps": "halving_doubling"}
+
+
+def _want(algo, xs):
+    """The oracle's float32 sum for an algorithm: the ring's order, a tree order's
+    executed schedule, or the double binary tree's."""
+    from oracle.orders import order_allreduce
+
+    if algo in RING_ORDER:
+        return oracle.ring_allreduce(xs)[0]
+    if algo.startswith("double_binary_tree"):
+        return dbt.double_binary_tree_allreduce(xs, "sum", "f32")[0]
+    return order_allreduce(TREE_ORDER[algo], xs)[0]
+
+
+@pytest.mark.parametrize("algo", RING_ORDER + ("tree", "tree_steps", "halving_doubling_steps", "double_binary_tree",
+                                               "double_binary_tree_steps"))
 def test_graph_capture_replays(algo, monkeypatch):
     """Capture 3 starts of a plan in a HIP graph; replay it 4 times with eager input
     changes in between, checking every replay against the oracle.  The staged form
@@ -125,7 +143,7 @@ def test_graph_capture_replays(algo, monkeypatch):
             recvs[r].fill_(-7.0)
         g.replay()
         torch.cuda.synchronize()
-        want, _ = oracle.ring_allreduce(xs)
+        want = _want(algo, xs)
         for r in range(n):
             assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32"), (rep, r)
 
@@ -139,8 +157,6 @@ def test_block_limits_keep_the_bits(algo, monkeypatch):
     one tile of results per segment (16 segments)."""
     import torch
 
-    from oracle.orders import order_allreduce
-
     if algo == "staged":
         monkeypatch.setenv("AR_STAGE_BYTES", "8192")
     ar = _ar()
@@ -148,13 +164,7 @@ def test_block_limits_keep_the_bits(algo, monkeypatch):
     xs = _draw(n, length, seed=21)
     sends = [to_dev(x, "f32") for x in xs]
     recvs = [torch.empty(length, device="cuda:0") for _ in range(n)]
-    if algo in ("fused", "phases", "ring", "ring_pipelined", "staged"):
-        want, _ = oracle.ring_allreduce(xs)
-    elif algo.startswith("double_binary_tree"):
-        want, _ = dbt.double_binary_tree_allreduce(xs, "sum", "f32")
-    else:
-        want, _ = order_allreduce({"tree": "tree", "tree_steps": "tree", "recursive_doubling": "recursive_doubling",
-                                   "halving_doubling_steps": "halving_doubling"}[algo], xs)
+    want = _want(algo, xs)
     plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
     if algo == "staged":
         assert plan.num_launches == 2 * 16
