@@ -226,10 +226,17 @@ typedef enum {
  *   / 395 / 381; 32 x 32 MiB 448 / 407 / 398; 16 x 256 MiB 1,575 / 1,420 /
  *   1,438; 64 x 64 MiB 1,694 / 1,522 / 1,546; bf16 8 x 128 MiB 396 / 413 /
  *   385, 16 x 64 MiB 415 / 403 / 389, 16 x 32 MiB 220 / 216 / 205, 32 x 32
- *   MiB 452 / 409 / 413.
+ *   MiB 452 / 409 / 413; phases / staged only, two processes each: 32 x 256
+ *   MiB 2,873 and 2,862 / 2,910 and 2,921; 16 x 512 MiB 3,518 and 3,536 /
+ *   3,178 and 3,168; 48 x 256 MiB 4,646 and 4,927 / 4,449 and 4,483; 64 x
+ *   256 MiB 6,279 and 6,087 / 5,981 and 6,098; 128 x 128 MiB 6,202 and
+ *   6,118 / 6,056 and 6,046.
  * The rules follow (b) where the two disagree, in order:
  *   1. AR_ALGO_PHASES from AR_BIG_PHASES_MIN_RANKS ranks with at least
- *      AR_BIG_PHASES_MIN_TOTAL_BYTES over all ranks;
+ *      AR_BIG_PHASES_MIN_TOTAL_BYTES and at most
+ *      AR_BIG_PHASES_MAX_TOTAL_BYTES over all ranks, and at most
+ *      AR_BIG_PHASES_MAX_RANK_BYTES per rank (beyond those the staged form
+ *      leads by 2-10 %, within them the phases by 1-2 %);
  *   2. AR_ALGO_STAGED from AR_STAGED_MIN_RANKS ranks with at least
  *      AR_STAGED_MIN_BYTES per rank and AR_STAGED_MIN_TOTAL_BYTES in all
  *      (16-bit types: the _16BIT bounds);
@@ -239,6 +246,8 @@ typedef enum {
  * Every choice gives the same bits. */
 #define AR_BIG_PHASES_MIN_RANKS 16
 #define AR_BIG_PHASES_MIN_TOTAL_BYTES (4ull << 30)
+#define AR_BIG_PHASES_MAX_TOTAL_BYTES (8ull << 30)
+#define AR_BIG_PHASES_MAX_RANK_BYTES (256ull << 20)
 #define AR_STAGED_MIN_RANKS 6
 #define AR_STAGED_MIN_BYTES (32ull << 20)
 #define AR_STAGED_MIN_TOTAL_BYTES (1024ull << 20)

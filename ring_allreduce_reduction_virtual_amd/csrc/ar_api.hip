@@ -748,8 +748,9 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     }
     // AUTO (bounds in ar.h, from timings of the three forms): two fused phases
     // from AR_BIG_PHASES_MIN_RANKS ranks once all ranks together hold
-    // AR_BIG_PHASES_MIN_TOTAL_BYTES; the staged reduce-then-broadcast for large
-    // buffers over 6 ranks or more below that; the phases again from
+    // AR_BIG_PHASES_MIN_TOTAL_BYTES, up to AR_BIG_PHASES_MAX_TOTAL_BYTES in all
+    // and AR_BIG_PHASES_MAX_RANK_BYTES per rank; the staged
+    // reduce-then-broadcast for large buffers over 6 ranks or more otherwise; the phases again from
     // AR_PHASES_MIN_RANKS ranks when every rank holds at least
     // AR_PHASES_MIN_BYTES; else the one fused kernel (and the small-message
     // kernel for the smallest messages)
@@ -759,7 +760,8 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
         const bool narrow = k.esz == 2;   // 16-bit types: other bounds (measured)
         const uint64_t min_rank = narrow ? AR_STAGED_MIN_BYTES_16BIT : AR_STAGED_MIN_BYTES;
         const uint64_t min_total = narrow ? AR_STAGED_MIN_TOTAL_BYTES_16BIT : AR_STAGED_MIN_TOTAL_BYTES;
-        const bool big_phases = k.n >= AR_BIG_PHASES_MIN_RANKS && total >= AR_BIG_PHASES_MIN_TOTAL_BYTES;
+        const bool big_phases = k.n >= AR_BIG_PHASES_MIN_RANKS && total >= AR_BIG_PHASES_MIN_TOTAL_BYTES &&
+                                total <= AR_BIG_PHASES_MAX_TOTAL_BYTES && per_rank <= AR_BIG_PHASES_MAX_RANK_BYTES;
         if (big_phases)
             algo = AR_ALGO_PHASES;
         else if (k.n >= AR_STAGED_MIN_RANKS && per_rank >= min_rank && total >= min_total)

@@ -186,6 +186,11 @@ def test_block_limits_keep_the_bits(algo, monkeypatch):
     (16, 1 << 24, "float32", "staged", 2),    # 16 x 64 MiB, 1 GiB in all: staged, one segment
     (16, 1 << 26, "float32", "phases", 2),    # 16 x 256 MiB, 4 GiB in all: the two phases
     (64, 1 << 24, "float32", "phases", 2),    # 64 x 64 MiB, 4 GiB in all: the two phases
+    (32, 1 << 26, "float32", "phases", 2),    # 32 x 256 MiB, 8 GiB in all: the two phases (upper bound)
+    (16, 1 << 27, "float32", "staged", 8),    # 16 x 512 MiB: above the per-rank bound, staged, 4 segments
+    (48, 1 << 26, "float32", "staged", 12),   # 48 x 256 MiB, 12 GiB in all: staged, 6 segments of 42.7 MiB
+    (64, (1 << 26) + 7, "float32", "staged", 16),  # the 64-rank workload, 16 GiB in all: staged, 8 segments
+    (128, 1 << 25, "float32", "staged", 8),   # 128 x 128 MiB, 16 GiB in all: staged, 4 segments of 32 MiB
     (16, 8 << 20, "float32", "fused", 1),     # 16 x 32 MiB, 512 MiB in all: fused
     (8, 48 << 20, "bfloat16", "staged", 2),   # 96 MiB per rank of bf16 at 8 ranks: staged (16-bit total)
     (8, 1 << 26, "bfloat16", "staged", 2),    # the bf16 workload (128 MiB per rank): staged, one segment
