@@ -213,14 +213,15 @@ def _to_device(x, dtype, dev):
 
 def cpu_baseline_headline(xs, s_bytes):
     """The headline line's cpu_baseline: the oracle's executed ring schedule on the
-    whole workload, single-threaded (up to 3 runs or 10 s), and beside it the
-    oracle's one-thread-per-rank ring when the host has a core per rank."""
+    whole workload, single-threaded, repeated until about 10 s of CPU work
+    (at least one run, at most 40), and beside it the oracle's one-thread-per-
+    rank ring when the host has a core per rank."""
     import oracle
     from oracle.threaded import ring_allreduce_threaded
 
     n = len(xs)
     reps, spent = 0, 0.0
-    while reps < 3 and spent < 10.0:
+    while reps < 40 and spent < 10.0:
         t = time.perf_counter()
         oracle.ring_allreduce(xs, check=False)
         spent += time.perf_counter() - t
