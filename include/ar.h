@@ -383,7 +383,10 @@ ar_result_t ar_reduce_scatter_noalloc(const void* const* sendbufs, void* const* 
  * hold the inputs, whenever the plan is started.  Starts whose work overlaps
  * on the GPU write the same outputs and race.  *_init allocates the plan in
  * host memory and sets *plan (NULL on error); ar_plan_free releases it
- * (NULL is accepted).  A plan may be started from several threads. */
+ * (NULL is accepted).  A plan may be started from several threads.  A plan
+ * belongs to the device that was current at *_init, where its buffers live
+ * and for whose compute units its grids were sized: start it on a stream of
+ * that device. */
 typedef struct ar_plan_s* ar_plan_t;
 
 ar_result_t ar_allreduce_init(const void* const* sendbufs, void* const* recvbufs, size_t count,
