@@ -27,7 +27,11 @@
  * Pointers.  `sendbufs` and `recvbufs` are HOST arrays of `nranks` DEVICE
  * pointers; the arrays are read during the call only and may be freed when
  * it returns.  The device buffers are owned by the caller and must stay
- * valid until the work enqueued on `stream` completes.  Buffers need only be
+ * valid until the work enqueued on `stream` completes.  The one-shot calls
+ * take the pointers on trust (asking the runtime about every buffer would
+ * cost as much as a small collective): a host pointer, or a count beyond a
+ * buffer's allocation, makes their kernels fault.  The *_init calls below
+ * check where the buffers live, once.  Buffers need only be
  * aligned to their element size; when all the buffers a kernel streams share
  * the same address residue modulo 16 bytes the kernels move 16-byte vectors,
  * otherwise one element at a time (same results, lower bandwidth).
@@ -376,7 +380,11 @@ ar_result_t ar_reduce_scatter_noalloc(const void* const* sendbufs, void* const* 
 /* Persistent collectives, in the manner of MPI's persistent AllReduce request
  * (bitfern.com "AllReduce Explained", section "MPI_Allreduce"): *_init
  * validates the arguments and plans the launches once, with the same
- * arguments, rules and errors as the matching *_ex call; ar_plan_start then
+ * arguments, rules and errors as the matching *_ex call, and one check more:
+ * it asks the HIP runtime where each buffer lives (hipPointerGetAttributes,
+ * hipMemGetAddressRange) and refuses with AR_ERR_INVALID_ARGUMENT plain or
+ * pinned host memory, another device's memory and a buffer (or workspace)
+ * that runs past the end of its allocation; ar_plan_start then
  * only enqueues the planned kernels on `stream`, as often as wanted, so a hot
  * loop or a HIP graph capture pays no validation.  The plan keeps the device
  * pointers it was given: the buffers (and workspace) must stay valid, and

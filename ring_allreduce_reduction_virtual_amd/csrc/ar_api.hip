@@ -146,6 +146,52 @@ ar_result_t check_overlaps(std::vector<Interval>& v, Allowed allowed) {
     return AR_SUCCESS;
 }
 
+// Where each buffer lives, checked once when a plan is made (two runtime
+// queries per buffer would cost the one-shot calls as much as a small
+// collective): device memory of the current device or managed memory, ending
+// inside its allocation.  Plain and pinned host memory, another device's
+// memory and a buffer that runs past its allocation are refused, so that a
+// plan never sends a kernel to an address it cannot reach.
+ar_result_t check_residency(const std::vector<Interval>& iv) {
+    if (iv.empty()) return AR_SUCCESS;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(AR_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    static const char* names[] = {"sendbufs", "recvbufs", "workspace"};
+    for (const Interval& b : iv) {
+        char what[32];
+        if (b.role == 2)
+            std::snprintf(what, sizeof(what), "workspace");
+        else
+            std::snprintf(what, sizeof(what), "%s[%d]", names[b.role], b.rank);
+        void* p = reinterpret_cast<void*>(b.lo);
+        hipPointerAttribute_t at{};
+        e = hipPointerGetAttributes(&at, p);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();   // the launches read the last error: leave none behind
+            return fail(AR_ERR_INVALID_ARGUMENT, "%s: the HIP runtime does not know this address (%s)", what,
+                        hipGetErrorString(e));
+        }
+        if (at.type == hipMemoryTypeUnregistered || at.type == hipMemoryTypeHost)
+            return fail(AR_ERR_INVALID_ARGUMENT, "%s is host memory, not device memory", what);
+        if (at.type == hipMemoryTypeDevice && at.device != dev)
+            return fail(AR_ERR_INVALID_ARGUMENT, "%s is memory of device %d, not of the current device %d", what,
+                        at.device, dev);
+        hipDeviceptr_t base = nullptr;
+        size_t size = 0;
+        e = hipMemGetAddressRange(&base, &size, p);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();   // extent unknown to the runtime: not checked
+            continue;
+        }
+        const uintptr_t end = reinterpret_cast<uintptr_t>(base) + size;
+        if (b.hi > end)
+            return fail(AR_ERR_INVALID_ARGUMENT, "%s runs %llu bytes past the end of its allocation", what,
+                        static_cast<unsigned long long>(b.hi - end));
+    }
+    return AR_SUCCESS;
+}
+
 struct Common {
     const void* const* send;
     void* const* recv;
@@ -540,6 +586,11 @@ public:
         if (algo_ != nullptr) *algo_ = algo;
     }
 
+    // Plans check where their buffers live; one-shot calls take them on trust.
+    ar_result_t check_buffers(const std::vector<Interval>& iv) const {
+        return steps_ != nullptr ? check_residency(iv) : AR_SUCCESS;
+    }
+
     ar_result_t emit(Launch& l, Kind kind, const KernelArgs& a, const Common& k) {
         l.kind = kind;
         l.dtype = k.dtype;
@@ -785,7 +836,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     rc = check_overlaps(iv, [&](const Interval& s, const Interval& d) {
         return s.rank == d.rank && s.lo == d.lo;   // in place: send[r] == recv[r]
     });
-    if (rc != AR_SUCCESS) return rc;
+    if (rc != AR_SUCCESS || (rc = sink.check_buffers(iv)) != AR_SUCCESS) return rc;
     if (k.count == 0) return AR_SUCCESS;
 
     if (tree_algo(algo)) return tree_allreduce(k, algo, ws, ws_bytes, ptrs, sink);
@@ -915,7 +966,7 @@ ar_result_t reduce_scatter_impl(const Common& k, ar_algo_t algo, void* ws, size_
         // in place: recv[r] == send[r] + start(r) elements
         return s.rank == d.rank && d.lo == s.lo + chunk_start(d.rank, k.count, k.n) * k.esz;
     });
-    if (rc != AR_SUCCESS) return rc;
+    if (rc != AR_SUCCESS || (rc = sink.check_buffers(iv)) != AR_SUCCESS) return rc;
     if (k.count == 0) return AR_SUCCESS;
 
     KernelArgs a{};
@@ -965,7 +1016,7 @@ ar_result_t all_gather_impl(const Common& k, ar_algo_t algo, Sink& sink) {
         // in place: send[r] == recv[r] + start(r) elements
         return s.rank == d.rank && s.lo == d.lo + chunk_start(s.rank, k.count, k.n) * k.esz;
     });
-    if (rc != AR_SUCCESS) return rc;
+    if (rc != AR_SUCCESS || (rc = sink.check_buffers(iv)) != AR_SUCCESS) return rc;
     if (k.count == 0) return AR_SUCCESS;
 
     KernelArgs a{};

@@ -213,3 +213,92 @@ def test_auto_choice(n, count, dtype, want, launches):
     assert plan.algo == want
     assert plan.num_launches == launches
     plan.close()
+
+
+def _raw_init(fn, sends, recvs, count, algo="fused", ws=None, ws_bytes=0):
+    """One of the ``*_init`` calls on raw addresses: (result code, plan handle, error detail)."""
+    import ctypes
+
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    lib = _lib.lib()
+    n = len(sends)
+    table = ctypes.c_void_p * n
+    plan = ctypes.c_void_p()
+    head = (table(*sends), table(*recvs), count, _lib.DTYPES["f32"])
+    if fn == "ar_all_gather_init":
+        rc = lib.ar_all_gather_init(*head, n, _lib.ALGOS[algo], ws, ws_bytes, ctypes.byref(plan))
+    else:
+        rc = getattr(lib, fn)(*head, _lib.OPS["sum"], n, _lib.ALGOS[algo], ws, ws_bytes, ctypes.byref(plan))
+    return rc, plan, lib.ar_get_last_error_detail().decode()
+
+
+def test_plans_refuse_buffers_the_kernels_cannot_reach():
+    """*_init asks the runtime where every buffer lives: plain and pinned host
+    memory and buffers (or a workspace) that run past the end of their
+    allocation are refused before anything is planned.  No refused plan
+    exists, so nothing is ever launched on those addresses."""
+    import ctypes
+
+    import torch
+
+    ar = _ar()
+    from ring_allreduce_reduction_virtual_amd import _lib
+
+    lib = _lib.lib()
+    hip = ctypes.CDLL("libamdhip64.so")
+    n, count = 4, 1 << 18                      # 1 MiB per rank
+    xs = _draw(n, count, seed=77)
+    sends = [to_dev(x, "f32") for x in xs]
+    recvs = [torch.empty(count, device="cuda:0") for _ in range(n)]
+    sp = [t.data_ptr() for t in sends]
+    rp = [t.data_ptr() for t in recvs]
+
+    rc, plan, _ = _raw_init("ar_allreduce_init", sp, rp, count)      # torch's own buffers pass
+    assert rc == 0 and plan.value
+    lib.ar_plan_free(plan)
+
+    host = ctypes.create_string_buffer(count * 4 + 256)
+    haddr = (ctypes.addressof(host) + 255) // 256 * 256
+    rc, plan, detail = _raw_init("ar_allreduce_init", [haddr] + sp[1:], rp, count)
+    assert rc == 1 and plan.value is None and "sendbufs[0] is host memory" in detail, detail
+    shard = count // n
+    rc, plan, detail = _raw_init("ar_all_gather_init", [sp[0], haddr] + sp[2:], rp, count)
+    assert rc == 1 and plan.value is None and "sendbufs[1] is host memory" in detail, detail
+
+    pinned = torch.empty(count, pin_memory=True)
+    rc, plan, detail = _raw_init("ar_allreduce_init", sp, rp[:3] + [pinned.data_ptr()], count)
+    assert rc == 1 and plan.value is None and "recvbufs[3] is host memory" in detail, detail
+
+    dev = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(dev), ctypes.c_size_t(count * 4)) == 0
+    wsp = ctypes.c_void_p()
+    need = ar.ar_workspace_bytes("reduce_scatter", "ring", count, "f32", n)
+    assert hip.hipMalloc(ctypes.byref(wsp), ctypes.c_size_t(need - 4096)) == 0
+    try:
+        rc, plan, _ = _raw_init("ar_allreduce_init", sp, rp[:2] + [dev.value] + rp[3:], count)   # fits exactly
+        assert rc == 0 and plan.value
+        lib.ar_plan_free(plan)
+        rc, plan, detail = _raw_init("ar_allreduce_init", sp, rp[:2] + [dev.value + 4096] + rp[3:], count)
+        assert rc == 1 and plan.value is None and "recvbufs[2] runs 4096 bytes past" in detail, detail
+        # a reduce-scatter shard at the allocation's end fits; one element further does not
+        tail = dev.value + count * 4 - shard * 4
+        rc, plan, _ = _raw_init("ar_reduce_scatter_init", sp, [tail] + rp[1:], count)
+        assert rc == 0 and plan.value
+        lib.ar_plan_free(plan)
+        rc, plan, detail = _raw_init("ar_reduce_scatter_init", sp, [tail + 4] + rp[1:], count)
+        assert rc == 1 and plan.value is None and "recvbufs[0] runs 4 bytes past" in detail, detail
+        # a workspace whose claimed size exceeds its allocation
+        rc, plan, detail = _raw_init("ar_reduce_scatter_init", sp, rp, count, algo="ring", ws=wsp.value,
+                                     ws_bytes=need)
+        assert rc == 1 and plan.value is None and "workspace runs 4096 bytes past" in detail, detail
+    finally:
+        torch.cuda.synchronize()
+        assert hip.hipFree(dev) == 0 and hip.hipFree(wsp) == 0
+
+    # the refusals leave no runtime error behind for the next launch to report
+    ar.ar_allreduce(sends, recvs)
+    torch.cuda.synchronize()
+    want, _ = oracle.ring_allreduce(xs)
+    for r in range(n):
+        assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32"), r
