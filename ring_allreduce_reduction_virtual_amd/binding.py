@@ -114,9 +114,14 @@ class _on_device:
         return False
 
 
-def _ws(workspace):
+def _ws(workspace, dev):
+    """Address and size of a workspace tensor, which must be contiguous memory of the buffers' GPU."""
     if workspace is None:
         return None, 0
+    if not isinstance(workspace, torch.Tensor) or workspace.device != dev:
+        raise ValueError("the workspace must be a tensor on the buffers' GPU")
+    if not workspace.is_contiguous():
+        raise ValueError("the workspace must be contiguous")
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
@@ -211,7 +216,7 @@ def ar_allreduce_ex(sendbufs, recvbufs=None, op: str = "sum", algo: str = "fused
     count = _check_counts("allreduce", sendbufs, recvbufs)
     with _on_device(dev):
         workspace = _workspace("allreduce", algo, count, dtype, len(sendbufs), workspace, dev, stream)
-        wp, wb = _ws(workspace)
+        wp, wb = _ws(workspace, dev)
         rc = _lib.lib().ar_allreduce_ex(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
                                         _lib.ALGOS[algo], wp, wb, _stream_handle(stream, dev.index))
     _lib.check("ar_allreduce_ex", rc)
@@ -242,7 +247,7 @@ def ar_reduce_scatter_ex(sendbufs, recvbufs, op: str = "sum", algo: str = "fused
     n = len(sendbufs)
     with _on_device(dev):
         workspace = _workspace("reduce_scatter", algo, count, dtype, n, workspace, dev, stream)
-        wp, wb = _ws(workspace)
+        wp, wb = _ws(workspace, dev)
         rc = _lib.lib().ar_reduce_scatter_ex(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], n,
                                              _lib.ALGOS[algo], wp, wb, _stream_handle(stream, dev.index))
     _lib.check("ar_reduce_scatter_ex", rc)
@@ -276,7 +281,7 @@ def ar_all_gather_ex(sendbufs, recvbufs, algo: str = "fused", workspace=None, st
     """All-gather with the algorithm chosen by the caller."""
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
     count = _check_counts("all_gather", sendbufs, recvbufs)
-    wp, wb = _ws(workspace)
+    wp, wb = _ws(workspace, dev)
     with _on_device(dev):
         rc = _lib.lib().ar_all_gather_ex(sp, rp, count, _lib.DTYPES[dtype], len(sendbufs), _lib.ALGOS[algo],
                                          wp, wb, _stream_handle(stream, dev.index))
@@ -355,7 +360,7 @@ def ar_allreduce_init(sendbufs, recvbufs=None, op: str = "sum", algo: str = "aut
     count = _check_counts("allreduce", sendbufs, recvbufs)
     with _on_device(dev):
         workspace = _workspace("allreduce", algo, count, dtype, len(sendbufs), workspace, dev, None)
-    wp, wb = _ws(workspace)
+    wp, wb = _ws(workspace, dev)
     L = _lib.lib()
     return _make_plan("ar_allreduce_init",
                       lambda h: L.ar_allreduce_init(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], len(sendbufs),
@@ -371,7 +376,7 @@ def ar_reduce_scatter_init(sendbufs, recvbufs, op: str = "sum", algo: str = "fus
     n = len(sendbufs)
     with _on_device(dev):
         workspace = _workspace("reduce_scatter", algo, count, dtype, n, workspace, dev, None)
-    wp, wb = _ws(workspace)
+    wp, wb = _ws(workspace, dev)
     L = _lib.lib()
     return _make_plan("ar_reduce_scatter_init",
                       lambda h: L.ar_reduce_scatter_init(sp, rp, count, _lib.DTYPES[dtype], _lib.OPS[op], n,
@@ -383,7 +388,7 @@ def ar_all_gather_init(sendbufs, recvbufs, algo: str = "fused", workspace=None) 
     """Persistent all-gather."""
     dev, dtype, sp, rp = _marshal(sendbufs, recvbufs)
     count = _check_counts("all_gather", sendbufs, recvbufs)
-    wp, wb = _ws(workspace)
+    wp, wb = _ws(workspace, dev)
     L = _lib.lib()
     return _make_plan("ar_all_gather_init",
                       lambda h: L.ar_all_gather_init(sp, rp, count, _lib.DTYPES[dtype], len(sendbufs),

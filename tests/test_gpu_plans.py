@@ -302,3 +302,29 @@ def test_plans_refuse_buffers_the_kernels_cannot_reach():
     want, _ = oracle.ring_allreduce(xs)
     for r in range(n):
         assert same_bits(from_dev(recvs[r], "f32"), want[r], "f32"), r
+
+
+def test_binding_refuses_a_workspace_off_the_buffers_gpu():
+    """A workspace tensor must be contiguous memory of the buffers' GPU: the
+    binding refuses a host tensor or a strided view before calling the library."""
+    import torch
+
+    ar = _ar()
+    n, count = 4, 4096
+    sends = [torch.randn(count, device="cuda:0") for _ in range(n)]
+    shards = [torch.empty(count // n, device="cuda:0") for _ in range(n)]
+    need = ar.ar_workspace_bytes("reduce_scatter", "ring", count, "f32", n)
+    for ws, msg in ((torch.empty(need, dtype=torch.uint8), "on the buffers' GPU"),
+                    (torch.empty(2 * need, dtype=torch.uint8, device="cuda:0")[::2], "contiguous")):
+        with pytest.raises(ValueError, match=msg):
+            ar.ar_reduce_scatter_ex(sends, shards, algo="ring", workspace=ws)
+        with pytest.raises(ValueError, match=msg):
+            ar.ar_reduce_scatter_init(sends, shards, algo="ring", workspace=ws)
+    # a proper workspace still works, with the oracle's bits
+    xs = [from_dev(t, "f32") for t in sends]
+    ar.ar_reduce_scatter_ex(sends, shards, algo="ring",
+                            workspace=torch.empty(need, dtype=torch.uint8, device="cuda:0"))
+    torch.cuda.synchronize()
+    want, _ = oracle.reduce_scatter(xs)
+    for r in range(n):
+        assert same_bits(from_dev(shards[r], "f32"), want[r], "f32"), r
