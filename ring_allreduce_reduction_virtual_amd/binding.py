@@ -41,13 +41,17 @@ _raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream_handle(stream, device_index):
-    """The hipStream_t to enqueue on: `stream` when given, else the current
-    stream of device `device_index` (the device the buffers live on)."""
+    """The hipStream_t to enqueue on: `stream` when given (a torch stream must
+    belong to device `device_index`, the device the buffers live on; a raw
+    handle is taken as given), else that device's current stream."""
     if stream is None:
         if _raw_current_stream is not None:
             return _raw_current_stream(device_index)
         return torch.cuda.current_stream(device_index).cuda_stream
     if isinstance(stream, torch.cuda.Stream):
+        if stream.device_index != device_index:
+            raise ValueError(f"the stream belongs to device {stream.device_index}, "
+                             f"the buffers to device {device_index}")
         return stream.cuda_stream
     return int(stream)
 

@@ -130,3 +130,37 @@ def test_noalloc_through_the_c_abi_with_a_raw_stream():
     want, _ = oracle.reduce_scatter(xs)
     for c in range(n):
         assert same_bits(from_dev(shards[c], "f32"), want[c], "f32"), c
+
+
+@pytest.mark.parametrize("algo", ["ring", "ring_pipelined"])
+def test_noalloc_replays_from_a_graph(algo):
+    """What the entry point is for: captured into a HIP graph, where nothing may
+    be allocated, then replayed with eager work between the replays (new
+    inputs, poisoned outputs), every replay giving the oracle's bits."""
+    import torch
+
+    ar = _ar()
+    n, length = 8, 8 * 4096 + 5
+    xs = _draw("f32", n, length, seed=5)
+    sends = [to_dev(x, "f32") for x in xs]
+    got = _shards(n, length, "f32")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ar.ar_reduce_scatter_noalloc(sends, got, algo=algo)     # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ar.ar_reduce_scatter_noalloc(sends, got, algo=algo)
+    for rep in range(3):
+        print(f"[noalloc graph] {algo} replay {rep}", flush=True)
+        xs = [x + np.float32(rep + 1) * np.float32(0.5) for x in xs]
+        for r in range(n):
+            sends[r].copy_(to_dev(xs[r], "f32"))
+        poison(got)
+        g.replay()
+        torch.cuda.synchronize()
+        want, _ = oracle.reduce_scatter(xs)
+        for c in range(n):
+            assert same_bits(from_dev(got[c], "f32"), want[c], "f32"), (rep, c)
