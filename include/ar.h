@@ -283,12 +283,13 @@ typedef enum {
  *                        pages for each XCD to translate; default 64; 0:
  *                        never; read at every call)
  *   AR_PHASES_MIN_RANKS  AR_ALGO_AUTO's rank bound for AR_ALGO_PHASES
- *   AR_SMALL_CHUNK_MAX   chunk length (elements) below which the one-pass
- *                        kernels stage a few positions in LDS; 0: never
- *   AR_SMALL_WORK_MAX    bound on chunk * N^2 for the same kernels (ring
- *                        order)
- *   AR_SMALL_TREE_MAX    bound on N * count for the tree orders' small-
- *                        message kernels (default 2^20 elements)
+ *   AR_SMALL_COUNT_MAX   elements per rank up to which the one-pass kernels
+ *                        stage a few positions of every rank in LDS
+ *                        (default 2^16; 0: never)
+ *   AR_SMALL_WORK_MAX    bound on N * count for the same kernels, ring order
+ *                        (default 2^21 elements)
+ *   AR_SMALL_TREE_MAX    bound on N * S, in bytes, for the tree orders'
+ *                        small-message kernels (default 8 MiB)
  *   AR_CACHED_LOADS_MAX  input bytes (N*S) up to which the fused AllReduce
  *                        reads with cache-allocating loads; 0: never
  *   AR_BLOCKS_PER_CU     cap the tiled kernels' grids at this many workgroups

@@ -348,59 +348,52 @@ int bit_reverse(int r, int bits) {
 }
 
 // When a one-pass AllReduce uses the small-message kernels (all ranks'
-// values of a few positions staged in LDS) instead of the tiled ones: chunks
-// shorter than AR_SMALL_CHUNK_MAX_DEFAULT elements, and chunk * N^2 at most
-// AR_SMALL_WORK_MAX.  A block folds kThreads / N positions, each over N
-// values, so their cost grows as chunk * N^3 where the tiled kernels' grows
-// as chunk * N; measured on MI355X the small kernels win below both bounds
-// (64 ranks x 16 elements: 5.5 against 22 us) and lose above them (128 ranks
-// x 64 elements: 38 against 30 us).  The AR_SMALL_CHUNK_MAX environment
-// variable overrides the chunk bound; 0 turns the small kernels off.
-uint64_t small_chunk_max() {
-    static const uint64_t v = [] {
-        const char* e = std::getenv("AR_SMALL_CHUNK_MAX");
-        if (e != nullptr && e[0] != '\0') return static_cast<uint64_t>(std::strtoull(e, nullptr, 10));
-        return static_cast<uint64_t>(AR_SMALL_CHUNK_MAX_DEFAULT);
-    }();
-    return v;
+// values of a few positions staged in LDS) instead of the tiled ones: at most
+// AR_SMALL_COUNT_MAX_DEFAULT elements per rank, and, in all ranks together,
+// at most AR_SMALL_WORK_MAX elements for the ring's order and
+// AR_SMALL_TREE_WORK_MAX bytes for the tree orders (binomial tree,
+// halving/doubling, double binary tree).  A block takes kThreads / N
+// positions, so the small kernels' cost grows with N * count where the tiled
+// kernels' grows with count.  The ring's left fold adds N - 1 dependent steps
+// per position, each with a conversion for bf16, so its bound counts
+// elements; the trees' levels number only log2 N, and their bound counts
+// bytes.  Measured on MI355X, per call in a graph, small / tiled: the bounds
+// are the crossovers from 2 to 128 ranks (ring order: 32 x 2^16 f32 9.6 /
+// 10.8 us, 64 x 2^16 f32 18.0 / 17.1, 64 x 2^16 bf16 23.4 / 19.4; tree: 64 x
+// 2^16 bf16 19.9 / 22.8, 128 x 2^15 f32 42.3 / 35.4 and 32.7 / 36.3 on two
+// machines, 128 x 2^14 f32 15.6 / 33.0).
+#ifndef AR_SMALL_COUNT_MAX_DEFAULT
+#define AR_SMALL_COUNT_MAX_DEFAULT (1ull << 16)
+#endif
+#ifndef AR_SMALL_WORK_MAX
+#define AR_SMALL_WORK_MAX (1ull << 21)
+#endif
+#ifndef AR_SMALL_TREE_WORK_MAX
+#define AR_SMALL_TREE_WORK_MAX (8ull << 20)
+#endif
+
+// Each bound read once per process from its environment variable, else the default.
+uint64_t env_bound(const char* name, uint64_t fallback) {
+    const char* e = std::getenv(name);
+    if (e != nullptr && e[0] != '\0') return static_cast<uint64_t>(std::strtoull(e, nullptr, 10));
+    return fallback;
 }
 
-// Bound on chunk * N^2 for the small-message kernels; AR_SMALL_WORK_MAX
-// overrides it (read once per process).
-uint64_t small_work_max() {
-    static const uint64_t v = [] {
-        const char* e = std::getenv("AR_SMALL_WORK_MAX");
-        if (e != nullptr && e[0] != '\0') return static_cast<uint64_t>(std::strtoull(e, nullptr, 10));
-        return static_cast<uint64_t>(AR_SMALL_WORK_MAX);
-    }();
+// Elements per rank; AR_SMALL_COUNT_MAX overrides it, 0 turns every
+// small-message kernel off.
+uint64_t small_count_max() {
+    static const uint64_t v = env_bound("AR_SMALL_COUNT_MAX", AR_SMALL_COUNT_MAX_DEFAULT);
     return v;
 }
 
 bool small_message(const Common& k) {
-    const uint64_t n = static_cast<uint64_t>(k.n);
-    const uint64_t chunk = k.count / n;
-    return k.n > 1 && chunk < small_chunk_max() && chunk * n * n <= small_work_max();
+    static const uint64_t work = env_bound("AR_SMALL_WORK_MAX", AR_SMALL_WORK_MAX);
+    return k.n > 1 && k.count <= small_count_max() && k.count * static_cast<uint64_t>(k.n) <= work;
 }
 
-// The tree orders' small-message kernels reduce level by level across
-// threads, so their cost does not grow with N the way the ring's left fold
-// does: they serve every message whose ranks together hold at most this many
-// elements (N * count; measured crossover on MI355X, 4 MiB of float32).
-#ifndef AR_SMALL_TREE_WORK_MAX
-#define AR_SMALL_TREE_WORK_MAX (1ull << 20)
-#endif
-
-// The tree orders' bound (binomial tree, halving/doubling, double binary
-// tree): N * count elements at most AR_SMALL_TREE_WORK_MAX, which the
-// AR_SMALL_TREE_MAX environment variable overrides (read once per process);
-// AR_SMALL_CHUNK_MAX=0 turns every small-message kernel off.
 bool small_tree_message(const Common& k) {
-    static const uint64_t bound = [] {
-        const char* e = std::getenv("AR_SMALL_TREE_MAX");
-        if (e != nullptr && e[0] != '\0') return static_cast<uint64_t>(std::strtoull(e, nullptr, 10));
-        return static_cast<uint64_t>(AR_SMALL_TREE_WORK_MAX);
-    }();
-    return k.n > 1 && small_chunk_max() != 0 && k.count * static_cast<uint64_t>(k.n) <= bound;
+    static const uint64_t bytes = env_bound("AR_SMALL_TREE_MAX", AR_SMALL_TREE_WORK_MAX);
+    return k.n > 1 && k.count <= small_count_max() && k.count * static_cast<uint64_t>(k.n) * k.esz <= bytes;
 }
 
 // One block per P = threads / N positions; the kernels stride over the rest.

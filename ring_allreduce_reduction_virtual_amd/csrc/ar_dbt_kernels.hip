@@ -255,9 +255,10 @@ __global__ __launch_bounds__(kThreads) void k_small_dbt(const KernelArgs a) {
     int levels = 0;
     while ((2u << levels) <= static_cast<uint32_t>(n)) ++levels;  // floor(log2 N): the root's height
     const uint32_t root = 1u << levels;
-    for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * P; i0 < a.count;
+    const SmallPtrs q = small_ptrs(a, P);
+    for (uint64_t i0 = static_cast<uint64_t>(xcd_grouped_block()) * P; i0 < a.count;
          i0 += static_cast<uint64_t>(gridDim.x) * P) {
-        small_stage<ESZ>(a, vals, P, i0);
+        small_stage<ESZ>(a, q, vals, P, i0);
         __syncthreads();
         const bool active = node && i0 + col < a.count;
         A own{};
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void k_small_dbt(const KernelArgs a) {
         }
         if (t < P && i0 + t < a.count) res[t] = F::done(acc[(root - 1u) * P + t], n);
         __syncthreads();
-        small_store<ESZ>(a, res, P, i0);
+        small_store<ESZ>(a, q, res, P, i0);
         __syncthreads();
     }
 }

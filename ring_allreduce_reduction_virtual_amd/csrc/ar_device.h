@@ -823,21 +823,52 @@ __device__ __forceinline__ const KernelArgs* kernarg_table() {
 #endif
 }
 
-template <int ESZ>
-__device__ __forceinline__ void small_stage(const KernelArgs& a, uint32_t* vals, int P, uint64_t i0) {
-    const int t = static_cast<int>(threadIdx.x);
-    const int r = t / P;
-    const uint64_t i = i0 + static_cast<uint64_t>(t - r * P);
-    if (r < a.nranks && i < a.count) vals[t] = load_elem<ESZ>(kernarg_table()->send[r] + i * ESZ);
+// The small-message kernels: thread t of a block loads and stores rank t / P
+// at position t mod P of the block's P positions.  Its two rank pointers are
+// read from the argument table once, ahead of the loads and stores that need
+// them.
+struct SmallPtrs {
+    const char* src;
+    char* dst;
+};
+
+__device__ __forceinline__ SmallPtrs small_ptrs(const KernelArgs& a, int P) {
+    const int r = static_cast<int>(threadIdx.x) / P;
+    if (r >= a.nranks) return {nullptr, nullptr};
+    return {kernarg_table()->send[r], kernarg_table()->recv[r]};
+}
+
+// The block's place in a small-message launch when each XCD takes one
+// contiguous run of blocks: the dispatcher deals block b to XCD b mod 8, and
+// b is mapped to x * q + min(x, rem) + b / 8 for x = b mod 8, q = G / 8,
+// rem = G mod 8 (a one-to-one map of [0, G)).  Neighbouring positions share
+// cache lines; so mapped, each line is loaded through one XCD's L2 instead
+// of all eight (measured on MI355X, ring order, per call in a graph: 128
+// ranks x 4 KiB 6.9 -> 4.2 us, 64 ranks x 64 KiB 11.8 -> 6.7 us; 2 to 16
+// ranks within +-5 %).
+__device__ __forceinline__ uint32_t xcd_grouped_block() {
+    const uint32_t g = gridDim.x, b = blockIdx.x;
+    const uint32_t x = b & 7u, q = g >> 3, rem = g & 7u;
+    return x * q + (x < rem ? x : rem) + (b >> 3);
 }
 
 template <int ESZ>
-__device__ __forceinline__ void small_store(const KernelArgs& a, const uint32_t* res, int P, uint64_t i0) {
+__device__ __forceinline__ void small_stage(const KernelArgs& a, const SmallPtrs& q, uint32_t* vals, int P,
+                                            uint64_t i0) {
+    const int t = static_cast<int>(threadIdx.x);
+    const int r = t / P;
+    const uint64_t i = i0 + static_cast<uint64_t>(t - r * P);
+    if (r < a.nranks && i < a.count) vals[t] = load_elem<ESZ>(q.src + i * ESZ);
+}
+
+template <int ESZ>
+__device__ __forceinline__ void small_store(const KernelArgs& a, const SmallPtrs& q, const uint32_t* res, int P,
+                                            uint64_t i0) {
     const int t = static_cast<int>(threadIdx.x);
     const int r = t / P;
     const int j = t - r * P;
     const uint64_t i = i0 + static_cast<uint64_t>(j);
-    if (r < a.nranks && i < a.count) store_elem<ESZ>(kernarg_table()->recv[r] + i * ESZ, res[j]);
+    if (r < a.nranks && i < a.count) store_elem<ESZ>(q.dst + i * ESZ, res[j]);
 }
 
 }  // namespace

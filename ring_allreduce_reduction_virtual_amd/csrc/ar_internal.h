@@ -105,17 +105,6 @@ struct Launch {
 #endif
 constexpr int kUnroll = AR_TILE_UNROLL;
 
-// Bounds below which the ring-order one-pass AllReduce takes its
-// small-message kernel: chunk length in elements, and chunk * N^2 (measured
-// crossovers on MI355X).  The tree orders' small-message kernels have a bound
-// of their own, kept with the host's dispatch.
-#ifndef AR_SMALL_CHUNK_MAX_DEFAULT
-#define AR_SMALL_CHUNK_MAX_DEFAULT 8192
-#endif
-#ifndef AR_SMALL_WORK_MAX
-#define AR_SMALL_WORK_MAX (1ull << 19)
-#endif
-
 // Inputs of at most this many bytes in total (N * S) are read by the fused
 // AllReduce with cache-allocating loads instead of nontemporal ones: they fit
 // in MI355X's 256 MB Infinity Cache, so a call that reads the same buffers

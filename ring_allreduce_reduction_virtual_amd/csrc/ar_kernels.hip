@@ -369,42 +369,47 @@ __global__ __launch_bounds__(kThreads) void k_gather_shards_xcd(const KernelArgs
 }
 
 // AllReduce of a small message: the ring-order fold of P = kThreads / N
-// positions per block, staged through LDS (see small_stage).  Position i
-// belongs to chunk c = floor(((i+1)*N - 1) / len), whose fold starts at rank
-// c.  In place is safe: a block loads all its positions from every rank
-// before it stores any.
+// positions per block, staged through LDS.  Position i belongs to chunk
+// c = floor(((i+1)*N - 1) / len), whose fold starts at rank c.  The thread
+// that loads rank r's value of a position stores it at slot (r - c) mod N of
+// that position's row, so the row holds the ranks in the fold's order
+// c, c+1, ..., N-1, 0, ..., c-1 and the fold reads it straight through (the
+// chunk's division is done while the loads are in flight, and the fold's
+// steps carry no index arithmetic).  Rows are N | 1 words apart: an odd
+// stride puts the lanes of a wave in distinct LDS banks.  In place is safe:
+// a block loads all its positions from every rank before it stores any.
 template <int DT, int OP>
 __global__ __launch_bounds__(kThreads) void k_small_allreduce(const KernelArgs a) {
     constexpr int ESZ = elem_size<DT>();
     using F = Fold<DT, OP, 1>;
-    __shared__ uint32_t vals[kThreads];
+    // P rows of N | 1 words: at most kThreads + P <= 3 * kThreads / 2 for N >= 2
+    __shared__ uint32_t vals[2 * kThreads];
     __shared__ uint32_t res[kThreads];
     const int n = a.nranks;
     const int P = kThreads / n;
+    const int S = n | 1;
     const int t = static_cast<int>(threadIdx.x);
-    for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * P; i0 < a.count;
+    const int r = t / P;             // the rank this thread loads and stores
+    const int j = t - r * P;         // the position it loads and stores, within the block
+    const SmallPtrs q = small_ptrs(a, P);
+    for (uint64_t i0 = static_cast<uint64_t>(xcd_grouped_block()) * P; i0 < a.count;
          i0 += static_cast<uint64_t>(gridDim.x) * P) {
-        small_stage<ESZ>(a, vals, P, i0);
+        const uint64_t i = i0 + static_cast<uint64_t>(j);
+        if (r < n && i < a.count) {
+            const uint32_t v = load_elem<ESZ>(q.src + i * ESZ);
+            const int c = static_cast<int>(((i + 1) * static_cast<uint64_t>(n) - 1) / a.count);
+            const int k = r >= c ? r - c : r - c + n;
+            vals[j * S + k] = v;
+        }
         __syncthreads();
         if (t < P && i0 + t < a.count) {
-            const uint64_t i = i0 + t;
-            const int c = static_cast<int>(((i + 1) * static_cast<uint64_t>(n) - 1) / a.count);
-            // the ring's order c, c+1, ..., N-1, 0, ..., c-1: the LDS index moves
-            // on by P and wraps once, the same N-1 steps on every lane (against
-            // a modulo and a multiply per step, measured on MI355X per call in a
-            // graph: 128 x 4 KiB 11.4 -> 9.3 us, 64 x 4 KiB 5.7 -> 5.2 us)
-            const int wrap = n * P;
-            int idx = c * P + t;
-            typename F::A acc = F::first(vals[idx]);
-            for (int k = 1; k < n; ++k) {
-                idx += P;
-                if (idx >= wrap) idx -= wrap;
-                acc = F::add(acc, vals[idx]);
-            }
+            const uint32_t* row = vals + t * S;
+            typename F::A acc = F::first(row[0]);
+            for (int k = 1; k < n; ++k) acc = F::add(acc, row[k]);
             res[t] = F::done(acc, n);
         }
         __syncthreads();
-        small_store<ESZ>(a, res, P, i0);
+        if (r < n && i < a.count) store_elem<ESZ>(q.dst + i * ESZ, res[j]);
         __syncthreads();
     }
 }

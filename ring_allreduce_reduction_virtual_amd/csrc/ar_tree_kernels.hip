@@ -195,9 +195,10 @@ __global__ __launch_bounds__(kThreads) void k_small_tree(const KernelArgs a) {
     const int t = static_cast<int>(threadIdx.x);
     const int r = t / P;                                         // this thread's leaf
     const int col = t - r * P;                                   // its column
-    for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * P; i0 < a.count;
+    const SmallPtrs q = small_ptrs(a, P);
+    for (uint64_t i0 = static_cast<uint64_t>(xcd_grouped_block()) * P; i0 < a.count;
          i0 += static_cast<uint64_t>(gridDim.x) * P) {
-        small_stage<ESZ>(a, vals, P, i0);
+        small_stage<ESZ>(a, q, vals, P, i0);
         __syncthreads();
         const bool active = r < n && i0 + col < a.count;
         if (active) acc[t] = F::first(vals[t]);
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void k_small_tree(const KernelArgs a) {
         }
         if (t < P && i0 + t < a.count) res[t] = F::done(acc[t], n);
         __syncthreads();
-        small_store<ESZ>(a, res, P, i0);
+        small_store<ESZ>(a, q, res, P, i0);
         __syncthreads();
     }
 }

@@ -34,9 +34,8 @@ def _draw(n, length, seed, dtype="f32"):
 
 
 def _small(n, length):
-    # the library's rule for the small-message kernels: chunk < 8192 and chunk * N^2 <= 2^19
-    chunk = length // n
-    return chunk < 8192 and chunk * n * n <= (1 << 19)
+    # the library's rule for the ring order's small-message kernel: count <= 2^16 and N * count <= 2^21
+    return length <= (1 << 16) and n * length <= (1 << 21)
 
 
 @pytest.mark.parametrize("algo,launches", [("fused", lambda n, m: 1), ("phases", lambda n, m: 2),

@@ -19,21 +19,21 @@ from gpu_util import from_dev, require_gpu, to_dev
 pytestmark = pytest.mark.gpu
 
 TORCH_OF = {"f16": "float16", "bf16acc32": "bfloat16", "bf16": "bfloat16", "f32": "float32", "i32": "int32"}
-# the library's bounds: for the ring's order, chunks shorter than 8192 elements with
-# chunk * N^2 <= 2^19 take the small-message kernel; for the tree orders, every message
-# with N * count <= 2^20 elements
-def threshold(n):
-    return min(8192, (1 << 19) // (n * n) + 1)
+# the library's bounds: a message takes the small-message kernel when each rank holds
+# at most 2^16 elements and all ranks together at most 2^21 elements (the ring's
+# order) or 8 MiB (the tree orders)
+ESIZE = {"f32": 4, "i32": 4, "bf16": 2, "f16": 2, "bf16acc32": 2}
 
 
-def lengths(algo, n):
-    if algo == "fused":
-        th = threshold(n)
-        edge = [(th - 1) * n, th * n - 1, th * n + 5]
-    else:
-        last = (1 << 20) // n                  # the longest buffer the tree orders' small kernels take
-        edge = [last - 1, last, last + 1]
-    return [x for x in [1, n - 1, n + 1, 7 * n + 3] + edge if x > 0]
+def last_small(algo, n, dtype):
+    """The longest per-rank buffer the small-message kernel of `algo` takes at N = n."""
+    work = (1 << 21) if algo == "fused" else (8 << 20) // ESIZE[dtype]
+    return min(1 << 16, work // n)
+
+
+def lengths(algo, n, dtype):
+    last = last_small(algo, n, dtype)
+    return [x for x in [1, n - 1, n + 1, 7 * n + 3, last - 1, last, last + 1] if x > 0]
 
 
 def _draw(dtype, n, length, seed):
@@ -79,7 +79,7 @@ def test_small_messages_across_the_threshold(algo, n, dtype, op):
     require_gpu()
     import ring_allreduce_reduction_virtual_amd as ar
 
-    for length in lengths(algo, n):
+    for length in lengths(algo, n, dtype):
         xs = _draw(dtype, n, length, seed=zlib.crc32(f"{dtype}{op}{n}{length}".encode()))
         if algo == "fused":
             want, _ = oracle.ring_allreduce(xs, op=op, dtype=dtype)
