@@ -280,8 +280,10 @@ typedef enum {
  *   AR_TILE_XCD          rank count from which the fused AllReduce, the
  *                        staged reduce and the fused reduce-scatter walk
  *                        their tiles in one contiguous slab per XCD (fewer
- *                        pages for each XCD to translate; default 64; 0:
- *                        never; read at every call)
+ *                        pages for each XCD to translate; unset: 64, and
+ *                        for the fused AllReduce 32, or any rank count when
+ *                        its inputs hold 64-256 MiB in all; 0: never; read
+ *                        at every call)
  *   AR_PHASES_MIN_RANKS  AR_ALGO_AUTO's rank bound for AR_ALGO_PHASES
  *   AR_SMALL_COUNT_MAX   elements per rank up to which the one-pass kernels
  *                        stage a few positions of every rank in LDS

@@ -417,19 +417,42 @@ uint64_t cached_loads_max() {
 }
 
 // Tile order of a launch that streams every rank's buffer at once (the fused
-// AllReduce, the staged reduce, the phases' reduce-scatter): one contiguous
-// slab of tiles per XCD from AR_TILE_XCD_MIN_RANKS ranks, else consecutive
-// tiles to consecutive blocks.  The AR_TILE_XCD environment variable sets the
-// rank bound (0: never); it is read at every call, as AR_STAGE_BYTES is.
-unsigned tile_xcd_min_ranks() {
-    const char* e = std::getenv("AR_TILE_XCD");
-    if (e != nullptr && e[0] != '\0') return static_cast<unsigned>(std::strtoul(e, nullptr, 10));
-    return AR_TILE_XCD_MIN_RANKS;
-}
+// AllReduce, the staged reduce, the phases' reduce-scatter, the fused
+// reduce-scatter): one contiguous slab of tiles per XCD, else consecutive
+// tiles to consecutive blocks.  Slabs from AR_TILE_XCD_MIN_RANKS ranks; the
+// fused AllReduce also from AR_FUSED_TILE_XCD_MIN_RANKS ranks, and at any rank
+// count when it reads its inputs through the last-level cache (at most
+// AR_CACHED_LOADS_MAX_BYTES in all) and they hold at least
+// AR_FUSED_TILE_XCD_MIN_BYTES.  Measured on MI355X, fused AllReduce, median of
+// single calls (graph replay alike), plain / slabs, us: 8 x 8 MiB 31.4 / 29.0,
+// 8 x 32 MiB 90.8 / 86.3, 16 x 4 MiB 37.8 / 33.6, 16 x 16 MiB 99.9 / 87.8,
+// 32 x 8 MiB 115 / 96, 32 x 32 MiB 436 / 406, 32 x 128 MiB 1,678 / 1,624;
+// outside those bounds 8 x 4 MiB 18.6 / 18.3, 16 x 1 MiB about 10 % slower
+// in a graph, 8 x 128 MiB 381 / 403, 16 x 64 MiB 406 / 412; the one loss
+// inside them 48 x 4 MiB 95.4 / 96.0.  The staged reduce and the phases'
+// reduce-scatter stay within +-2.5 % at 8-48 ranks either way.  The AR_TILE_XCD environment variable sets one rank bound
+// for every launch instead (0: never); it is read at every call, as
+// AR_STAGE_BYTES is.
+#ifndef AR_FUSED_TILE_XCD_MIN_RANKS
+#define AR_FUSED_TILE_XCD_MIN_RANKS 32
+#endif
+#ifndef AR_FUSED_TILE_XCD_MIN_BYTES
+#define AR_FUSED_TILE_XCD_MIN_BYTES (64ull << 20)
+#endif
 
-void tile_order(KernelArgs& a, Launch& l, const Common& k) {
-    const unsigned from = tile_xcd_min_ranks();
-    a.xcd_slabs = (from != 0 && static_cast<unsigned>(k.n) >= from && l.blocks >= 8) ? 1 : 0;
+void tile_order(KernelArgs& a, Launch& l, const Common& k, bool fused_allreduce = false) {
+    const char* e = std::getenv("AR_TILE_XCD");
+    bool slabs;
+    if (e != nullptr && e[0] != '\0') {
+        const unsigned from = static_cast<unsigned>(std::strtoul(e, nullptr, 10));
+        slabs = from != 0 && static_cast<unsigned>(k.n) >= from;
+    } else if (fused_allreduce) {
+        const uint64_t total = static_cast<uint64_t>(k.n) * k.count * k.esz;
+        slabs = k.n >= AR_FUSED_TILE_XCD_MIN_RANKS || (l.cached && total >= AR_FUSED_TILE_XCD_MIN_BYTES);
+    } else {
+        slabs = k.n >= AR_TILE_XCD_MIN_RANKS;
+    }
+    a.xcd_slabs = (slabs && l.blocks >= 8) ? 1 : 0;
     // whole groups of eight blocks, one per XCD (the kernels stride within a slab)
     if (a.xcd_slabs) l.blocks = static_cast<unsigned>(std::min<uint64_t>((l.blocks + 7ull) / 8 * 8, 0x7ffffff8u));
 }
@@ -869,7 +892,7 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     if ((rc = plan(a, l, k, common_residue(ptrs))) != AR_SUCCESS) return rc;
     if (algo == AR_ALGO_FUSED) {
         l.cached = l.vec && static_cast<uint64_t>(k.n) * k.count * k.esz <= cached_loads_max();
-        tile_order(a, l, k);
+        tile_order(a, l, k, true);
         return sink.emit(l, Kind::kFusedAllReduce, a, k);
     }
     if (algo == AR_ALGO_STAGED) {

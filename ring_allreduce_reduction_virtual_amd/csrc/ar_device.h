@@ -627,8 +627,10 @@ __device__ __forceinline__ bool shard_aligned(const void* shard, uint64_t s, int
 // XCD x (blocks x, x + 8, x + 16, ...).  Each XCD then touches one eighth of
 // the address range that all the blocks in flight touch, and with it one
 // eighth of the pages its address translation caches must hold.  Measured on
-// MI355X it pays from 64 ranks (up to 8 % at 64 x 16 MiB); at 32 ranks it
-// gains nothing and at 8 ranks the plain order is faster.  The host gives
+// MI355X it pays from 64 ranks (up to 8 % at 64 x 16 MiB), for the fused
+// AllReduce also from 32 ranks and whenever its inputs sit in the last-level
+// cache; streaming 128-256 MiB per rank from HBM at 8-16 ranks, the plain
+// order is faster.  The host gives
 // such a launch a grid of a multiple of eight blocks; blocks past the last
 // whole group of eight walk nothing.
 struct TileWalk {

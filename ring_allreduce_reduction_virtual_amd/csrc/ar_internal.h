@@ -143,6 +143,8 @@ constexpr int kUnroll = AR_TILE_UNROLL;
 // 1.5 % (staged slower); 8 x 256 MiB fused 741 / 790 (slower).  The
 // standalone fused reduce-scatter: 64 x 16 MiB 187.7 / 180.7, 128 x 64 MiB
 // 1,395 / 1,380, 64 x (2^26+7) 2,910 / 2,909, 32 x 256 MiB 1,551 / 1,566.
+// The fused AllReduce takes slabs more widely (its rule is kept with the
+// host's dispatch).
 #ifndef AR_TILE_XCD_MIN_RANKS
 #define AR_TILE_XCD_MIN_RANKS 64
 #endif

@@ -96,3 +96,33 @@ def test_slab_order_capped_grids(algo, cap, slab_order):
         for r in range(n):
             assert same_bits(_host(recvs[r], "f32"), want[r], "f32"), (cap, r)
     plan.close()
+
+
+@pytest.mark.parametrize("n,length,algo", [
+    (8, (1 << 21) + 13, "auto"),    # 64 MiB of inputs, read through the last-level cache: slabs
+    (16, 1 << 22, "auto"),          # 256 MiB, the cached-load bound: slabs
+    (8, 1 << 20, "auto"),           # 32 MiB: the plain order
+    (32, (1 << 18) + 5, "fused"),   # 32 ranks: slabs at any size
+    (12, 3 * (1 << 21) + 1, "fused"),  # 288 MiB, streamed from HBM: the plain order
+])
+def test_default_tile_order_of_the_fused_allreduce(n, length, algo, monkeypatch):
+    """The library's own rule, with no override: the fused AllReduce walks slabs
+    from 32 ranks and whenever its inputs hold 64-256 MiB in all; whole outputs
+    against the oracle on both sides of each bound."""
+    import torch
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    require_gpu()
+    monkeypatch.delenv("AR_TILE_XCD", raising=False)
+    print(f"[tile order] default rule {algo} n={n} len={length}", flush=True)
+    xs = _draw("f32", n, length, seed=n * 13 + length)
+    want = oracle.ring_allreduce(xs, op="sum", dtype="f32")[0]
+    sends = [_tensor(x, "f32") for x in xs]
+    recvs = [_empty(length, "f32") for _ in range(n)]
+    plan = ar.ar_allreduce_init(sends, recvs, algo=algo)
+    assert plan.algo == "fused"
+    plan.close()
+    ar.ar_allreduce_ex(sends, recvs, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(_host(recvs[r], "f32"), want[r], "f32"), r
