@@ -418,21 +418,25 @@ uint64_t cached_loads_max() {
 
 // Tile order of a launch that streams every rank's buffer at once (the fused
 // AllReduce, the staged reduce, the phases' reduce-scatter, the fused
-// reduce-scatter): one contiguous slab of tiles per XCD, else consecutive
-// tiles to consecutive blocks.  Slabs from AR_TILE_XCD_MIN_RANKS ranks; the
-// fused AllReduce also from AR_FUSED_TILE_XCD_MIN_RANKS ranks, and at any rank
-// count when it reads its inputs through the last-level cache (at most
+// reduce-scatter, the fused tree-order AllReduces): one contiguous slab of
+// tiles per XCD, else consecutive tiles to consecutive blocks.  Slabs from
+// AR_TILE_XCD_MIN_RANKS ranks; the one-pass AllReduces of every order also
+// from AR_FUSED_TILE_XCD_MIN_RANKS ranks, and the ring's at any rank count
+// when it reads its inputs through the last-level cache (at most
 // AR_CACHED_LOADS_MAX_BYTES in all) and they hold at least
-// AR_FUSED_TILE_XCD_MIN_BYTES.  Measured on MI355X, fused AllReduce, median of
+// AR_FUSED_TILE_XCD_MIN_BYTES (the tree orders' kernels stream their inputs
+// and gain nothing below 32 ranks: 8 x 8 MiB tree 34.2 / 35.7 us, 32 x 16
+// MiB tree 244 / 222, double binary tree 230 / 220, 64 x 16 MiB 474 / 440 and
+// 479 / 438).  Measured on MI355X, fused AllReduce, median of
 // single calls (graph replay alike), plain / slabs, us: 8 x 8 MiB 31.4 / 29.0,
 // 8 x 32 MiB 90.8 / 86.3, 16 x 4 MiB 37.8 / 33.6, 16 x 16 MiB 99.9 / 87.8,
 // 32 x 8 MiB 115 / 96, 32 x 32 MiB 436 / 406, 32 x 128 MiB 1,678 / 1,624;
 // outside those bounds 8 x 4 MiB 18.6 / 18.3, 16 x 1 MiB about 10 % slower
 // in a graph, 8 x 128 MiB 381 / 403, 16 x 64 MiB 406 / 412; the one loss
 // inside them 48 x 4 MiB 95.4 / 96.0.  The staged reduce and the phases'
-// reduce-scatter stay within +-2.5 % at 8-48 ranks either way.  The AR_TILE_XCD environment variable sets one rank bound
-// for every launch instead (0: never); it is read at every call, as
-// AR_STAGE_BYTES is.
+// reduce-scatter stay within +-2.5 % at 8-48 ranks either way.  The
+// AR_TILE_XCD environment variable sets one rank bound for every launch
+// instead (0: never); it is read at every call, as AR_STAGE_BYTES is.
 #ifndef AR_FUSED_TILE_XCD_MIN_RANKS
 #define AR_FUSED_TILE_XCD_MIN_RANKS 32
 #endif
@@ -715,6 +719,7 @@ ar_result_t tree_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_
             plan_small(a, l, k);
             return sink.emit(l, Kind::kSmallTree, a, k);
         }
+        tile_order(a, l, k, true);
         return sink.emit(l, Kind::kFusedTree, a, k);
     }
     if ((rc = use_workspace(a, k, AR_COLL_ALLREDUCE, algo, ws, ws_bytes, nullptr)) != AR_SUCCESS) return rc;
@@ -775,6 +780,7 @@ ar_result_t dbt_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_b
             plan_small(a, l, k);
             return sink.emit(l, Kind::kSmallDbt, a, k);
         }
+        tile_order(a, l, k, true);
         return sink.emit(l, Kind::kFusedDbt, a, k);
     }
     if ((rc = use_workspace(a, k, AR_COLL_ALLREDUCE, algo, ws, ws_bytes, nullptr)) != AR_SUCCESS) return rc;

@@ -43,9 +43,9 @@ namespace {
 #define AR_HALF_LOOP_BEGIN                                                                   \
     const int n = a.nranks;                                                                  \
     const uint32_t tpc = a.tiles_per_chunk;                                                  \
-    const uint32_t ntiles = a.tile_end;                                                      \
     const int64_t adj = (VEC > 1) ? static_cast<int64_t>(a.ofs) * elem_size<DT>() : 0;       \
-    for (uint32_t tile = a.tile_first + blockIdx.x; tile < ntiles; tile += gridDim.x) {      \
+    const TileWalk walk = tile_walk(a);                                                      \
+    for (uint32_t tile = walk.first; tile < walk.end; tile += walk.step) {                   \
         const int c = static_cast<int>(tile / tpc);                                          \
         const uint64_t t = tile - static_cast<uint32_t>(c) * tpc;                            \
         const Span sp = part_span<VEC>(c, 2, a);                                             \

@@ -1,6 +1,7 @@
 """The slab tile order of the launches that stream every rank's buffer at once
 (the fused AllReduce, the staged reduce, the phases' and the standalone fused
-reduce-scatter) against the oracle.
+reduce-scatter, the fused binomial-tree and double-binary-tree AllReduces)
+against the oracle.
 
 In that order the launch's tiles are cut into eight contiguous slabs, one per
 XCD, and the blocks of one XCD walk one slab; blocks past the last whole group
@@ -16,6 +17,8 @@ and are not multiples of eight, and capped below eight.
 import pytest
 
 import oracle
+from oracle.dbt import double_binary_tree_allreduce
+from oracle.orders import order_allreduce
 from oracle.ring import same_bits
 
 from gpu_util import require_gpu
@@ -126,3 +129,34 @@ def test_default_tile_order_of_the_fused_allreduce(n, length, algo, monkeypatch)
     torch.cuda.synchronize()
     for r in range(n):
         assert same_bits(_host(recvs[r], "f32"), want[r], "f32"), r
+
+
+# longer than the tree orders' small-message bound (2^16 elements per rank), so
+# the tiled kernels run
+TREE_SHAPES = [(3, 65537 + 1000, "f32", "sum"), (5, 5 * 3 * 8192 + 7, "f32", "sum"),
+               (8, 8 * 16384 + 5, "bf16", "sum"), (17, 17 * 4099, "i32", "max"), (64, 64 * 1100 + 7, "f32", "sum"),
+               (7, 7 * 10000 + 5, "bf16acc32", "avg"), (9, 9 * 8192 + 1, "f16", "min"), (16, 16 * 8192 + 3, "f32", "prod")]
+TREE_CASES = [(algo,) + shape for algo in ("tree", "halving_doubling", "double_binary_tree") for shape in TREE_SHAPES
+              if algo != "halving_doubling" or not shape[0] & (shape[0] - 1)]
+
+
+@pytest.mark.parametrize("algo,n,length,dtype,op", TREE_CASES)
+def test_slab_order_tree_orders(algo, n, length, dtype, op, slab_order):
+    """The fused tree-order kernels in the slab order, against their own
+    orders' oracles (halving/doubling: power-of-two rank counts only)."""
+    import torch
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    require_gpu()
+    print(f"[tile order] slabs {algo} n={n} len={length} {dtype} {op}", flush=True)
+    xs = _draw(dtype, n, length, seed=n * 17 + length)
+    if algo == "double_binary_tree":
+        want, _ = double_binary_tree_allreduce(xs, op, dtype)
+    else:
+        want, _ = order_allreduce(algo, xs, op, dtype)
+    sends = [_tensor(x, dtype) for x in xs]
+    recvs = [_empty(length, dtype) for _ in range(n)]
+    ar.ar_allreduce_ex(sends, recvs, op=op, algo=algo, dtype=dtype)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(_host(recvs[r], dtype), want[r], dtype), r
