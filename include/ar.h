@@ -245,7 +245,12 @@ typedef enum {
  *      AR_STAGED_MIN_BYTES per rank and AR_STAGED_MIN_TOTAL_BYTES in all
  *      (16-bit types: the _16BIT bounds);
  *   3. AR_ALGO_PHASES from AR_PHASES_MIN_RANKS ranks with at least
- *      AR_PHASES_MIN_BYTES per rank;
+ *      AR_PHASES_MIN_BYTES per rank and more than
+ *      AR_PHASES_ABOVE_TOTAL_BYTES in all (up to that size the fused kernel
+ *      reads its inputs through the last-level cache and leads: fused /
+ *      phases, median of single calls, us: 24 x 8 MiB 76 / 85, 32 x 8 MiB
+ *      97 / 109, 48 x 5 MiB 104 / 118, 64 x 4 MiB 122 / 125; above it 24 x
+ *      12 MiB 130 / 119, 32 x 12 MiB 174 / 153, 64 x 6 MiB 175 / 158);
  *   4. AR_ALGO_FUSED.
  * Every choice gives the same bits. */
 #define AR_BIG_PHASES_MIN_RANKS 16
@@ -264,6 +269,9 @@ typedef enum {
 /* Bytes per rank from which AR_ALGO_AUTO may take the two phases (measured
  * on MI355X: below it the single fused kernel is faster at every rank count). */
 #define AR_PHASES_MIN_BYTES (4u << 20)
+/* Bytes in all that rule 3 requires the inputs to exceed: the fused kernel's
+ * cache-allocating loads reach up to here. */
+#define AR_PHASES_ABOVE_TOTAL_BYTES (256ull << 20)
 
 /* Environment variables.  They tune speed only; no setting changes a
  * result's bits.

@@ -825,8 +825,9 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
     // and AR_BIG_PHASES_MAX_RANK_BYTES per rank; the staged
     // reduce-then-broadcast for large buffers over 6 ranks or more otherwise; the phases again from
     // AR_PHASES_MIN_RANKS ranks when every rank holds at least
-    // AR_PHASES_MIN_BYTES; else the one fused kernel (and the small-message
-    // kernel for the smallest messages)
+    // AR_PHASES_MIN_BYTES and all together more than
+    // AR_PHASES_ABOVE_TOTAL_BYTES; else the one fused kernel (and the
+    // small-message kernel for the smallest messages)
     if (algo == AR_ALGO_AUTO) {
         const uint64_t per_rank = k.count * k.esz;
         const uint64_t total = per_rank * static_cast<uint64_t>(k.n);
@@ -839,7 +840,8 @@ ar_result_t allreduce_impl(const Common& k, ar_algo_t algo, void* ws, size_t ws_
             algo = AR_ALGO_PHASES;
         else if (k.n >= AR_STAGED_MIN_RANKS && per_rank >= min_rank && total >= min_total)
             algo = AR_ALGO_STAGED;
-        else if (k.n >= phases_min_ranks() && per_rank >= AR_PHASES_MIN_BYTES && !small_message(k))
+        else if (k.n >= phases_min_ranks() && per_rank >= AR_PHASES_MIN_BYTES &&
+                 total > AR_PHASES_ABOVE_TOTAL_BYTES && !small_message(k))
             algo = AR_ALGO_PHASES;
         else
             algo = AR_ALGO_FUSED;

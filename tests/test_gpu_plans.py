@@ -40,7 +40,8 @@ def _small(n, length):
 
 @pytest.mark.parametrize("algo,launches", [("fused", lambda n, m: 1), ("phases", lambda n, m: 2),
                                            ("ring", lambda n, m: 2 * (n - 1)), ("ring_pipelined", lambda n, m: 1),
-                                           ("auto", lambda n, m: 1 if n < 24 or _small(n, m) or m * 4 < (4 << 20) else 2)])
+                                           ("auto", lambda n, m: 1 if n < 24 or _small(n, m) or m * 4 < (4 << 20)
+                                            or n * m * 4 <= (256 << 20) else 2)])
 @pytest.mark.parametrize("n,length", [(5, 1003), (8, 8 * 4096 + 5), (32, 32 * 257 + 3), (32, 32 * 4100 + 3),
                                       (24, (1 << 20) + 3)])
 def test_allreduce_plan_matches_and_follows_inputs(n, length, algo, launches):
@@ -197,7 +198,10 @@ def test_block_limits_keep_the_bits(algo, monkeypatch):
     (8, 1 << 24, "bfloat16", "fused", 1),     # 32 MiB per rank, 256 MiB in all: below the 16-bit total
     (4, 1 << 27, "float32", "fused", 1),      # 4 ranks: below the staged rank bound
     (6, 1 << 26, "float32", "staged", 4),     # 6 ranks x 256 MiB: staged, 2 segments of 128 MiB
-    (64, 1 << 20, "float32", "phases", 2),    # 64 ranks x 4 MiB: the two phases (many ranks)
+    (64, 1 << 20, "float32", "fused", 1),     # 64 ranks x 4 MiB, 256 MiB in all: fused (read through the cache)
+    (64, (1 << 20) + 1024, "float32", "phases", 2),  # just over 256 MiB in all: the two phases (many ranks)
+    (24, 2 << 20, "float32", "fused", 1),     # 24 x 8 MiB, 192 MiB in all: fused
+    (24, 3 << 20, "float32", "phases", 2),    # 24 x 12 MiB, 288 MiB in all: the two phases
 ])
 def test_auto_choice(n, count, dtype, want, launches):
     """Which form AR_ALGO_AUTO plans at shapes on both sides of its bounds
