@@ -719,6 +719,8 @@ ar_result_t tree_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_
             plan_small(a, l, k);
             return sink.emit(l, Kind::kSmallTree, a, k);
         }
+        // cache-allocating loads while the inputs fit in the last-level cache, as the ring's kernel
+        l.cached = l.vec && static_cast<uint64_t>(k.n) * k.count * k.esz <= cached_loads_max();
         tile_order(a, l, k, true);
         return sink.emit(l, Kind::kFusedTree, a, k);
     }
@@ -780,6 +782,8 @@ ar_result_t dbt_allreduce(const Common& k, ar_algo_t algo, void* ws, size_t ws_b
             plan_small(a, l, k);
             return sink.emit(l, Kind::kSmallDbt, a, k);
         }
+        // cache-allocating loads while the inputs fit in the last-level cache, as the ring's kernel
+        l.cached = l.vec && static_cast<uint64_t>(k.n) * k.count * k.esz <= cached_loads_max();
         tile_order(a, l, k, true);
         return sink.emit(l, Kind::kFusedDbt, a, k);
     }

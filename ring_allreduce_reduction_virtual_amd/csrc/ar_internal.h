@@ -87,7 +87,7 @@ struct Launch {
     ar_dtype_t dtype;
     ar_op_t op;
     bool vec;                  // 16-byte vector path (all streamed buffers share a residue)
-    bool cached;               // kFusedAllReduce on the vector path: cache-allocating loads
+    bool cached;               // one-pass AllReduces (ring and tree orders) on the vector path: cache-allocating loads
     bool half;                 // kFusedAllGather, kStagedBroadcast: one unit row of a tile per block
     int form;                  // kStagedBroadcast, kFusedAllGather: 3 one destination per block, a
                                // tile's blocks grouped on one XCD; 0 the tile forms above

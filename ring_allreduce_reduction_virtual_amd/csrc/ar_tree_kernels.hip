@@ -121,9 +121,9 @@ __device__ __forceinline__ uint32_t tree_element(const KernelArgs& a, uint64_t i
 // host passes the ranks in bit-reversed order for recursive halving).  In
 // place (send[r] == recv[r]) is safe: each position is read by the thread
 // that later writes it, and by no other.
-template <int DT, int OP, int VEC, int D>
+template <int DT, int OP, int VEC, int D, bool NT_LOAD>
 __global__ __launch_bounds__(kThreads) void k_fused_tree(const KernelArgs a) {
-    using U = Unit<DT, VEC>;
+    using U = Unit<DT, VEC, NT_LOAD>;
     using F = Fold<DT, OP, VEC>;
     constexpr int B = tree_batch<DT, D>();
     AR_TILE_LOOP_BEGIN
@@ -410,10 +410,21 @@ hipError_t launch_reduce(const Launch& l, const KernelArgs& a, hipStream_t s) {
     const dim3 grid(l.blocks, l.actors > 0 ? l.actors : 1), block(kThreads);
     switch (l.kind) {
         case Kind::kFusedTree:
+            if constexpr (VEC > 1) {
+                if (l.cached) {   // inputs that fit in the last-level cache: cache-allocating loads
+                    switch (l.depth) {
+                        case 4: hipLaunchKernelGGL((k_fused_tree<DT, OP, VEC, 4, false>), grid, block, 0, s, a); break;
+                        case 6: hipLaunchKernelGGL((k_fused_tree<DT, OP, VEC, 6, false>), grid, block, 0, s, a); break;
+                        case 8: hipLaunchKernelGGL((k_fused_tree<DT, OP, VEC, 8, false>), grid, block, 0, s, a); break;
+                        default: return hipErrorInvalidValue;
+                    }
+                    break;
+                }
+            }
             switch (l.depth) {
-                case 4: hipLaunchKernelGGL((k_fused_tree<DT, OP, VEC, 4>), grid, block, 0, s, a); break;
-                case 6: hipLaunchKernelGGL((k_fused_tree<DT, OP, VEC, 6>), grid, block, 0, s, a); break;
-                case 8: hipLaunchKernelGGL((k_fused_tree<DT, OP, VEC, 8>), grid, block, 0, s, a); break;
+                case 4: hipLaunchKernelGGL((k_fused_tree<DT, OP, VEC, 4, AR_NT_LOADS>), grid, block, 0, s, a); break;
+                case 6: hipLaunchKernelGGL((k_fused_tree<DT, OP, VEC, 6, AR_NT_LOADS>), grid, block, 0, s, a); break;
+                case 8: hipLaunchKernelGGL((k_fused_tree<DT, OP, VEC, 8, AR_NT_LOADS>), grid, block, 0, s, a); break;
                 default: return hipErrorInvalidValue;
             }
             break;
