@@ -160,3 +160,28 @@ def test_slab_order_tree_orders(algo, n, length, dtype, op, slab_order):
     torch.cuda.synchronize()
     for r in range(n):
         assert same_bits(_host(recvs[r], dtype), want[r], dtype), r
+
+
+@pytest.mark.parametrize("algo", ["tree", "halving_doubling", "double_binary_tree"])
+@pytest.mark.parametrize("n,length", [(8, (1 << 21) + 13), (16, (1 << 20) + 5)])
+def test_default_rule_of_the_tree_orders(algo, n, length, monkeypatch):
+    """The tree orders' one-pass kernels under the library's own rule: 64-128
+    MiB of inputs, read through the last-level cache and walked in per-XCD
+    slabs; whole outputs against each order's oracle."""
+    import torch
+    import ring_allreduce_reduction_virtual_amd as ar
+
+    require_gpu()
+    monkeypatch.delenv("AR_TILE_XCD", raising=False)
+    print(f"[tile order] default rule {algo} n={n} len={length}", flush=True)
+    xs = _draw("f32", n, length, seed=n * 19 + length)
+    if algo == "double_binary_tree":
+        want, _ = double_binary_tree_allreduce(xs, "sum", "f32")
+    else:
+        want, _ = order_allreduce(algo, xs, "sum", "f32")
+    sends = [_tensor(x, "f32") for x in xs]
+    recvs = [_empty(length, "f32") for _ in range(n)]
+    ar.ar_allreduce_ex(sends, recvs, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert same_bits(_host(recvs[r], "f32"), want[r], "f32"), r
